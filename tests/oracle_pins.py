@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics
+fix, written so that each takes an ``oracle.oracle.Oracle`` instance.
+
+``test_oracle_pins.py`` runs them on the oracle itself; ``test_oracle_mutants.py``
+runs them on deliberately broken copies of ``oracle.c`` to show that every
+planted mistake is caught by at least one pin.
+
+Sources: "RAT+ Deep Dive" (zhichai.net) S1 (tokens skip a fixed interval D),
+S2.1 (forget-gate recurrence, 64-token window, L = T, parallel prefill by an
+associative scan), S3.1 table (attention FLOPs T/D), S6 Head-Wise Hybrid;
+the RAT+ abstract (arXiv 2602.18196: FLOPs and KV cache fall by D, 64x at
+D = 64; dilated attention optionally with local windows).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _inputs(seed, B, T, H, d, gate_mean=1.0):
+    r = _rng(seed)
+    q = r.standard_normal((B, T, H, d))
+    k = r.standard_normal((B, T, H, d))
+    v = r.standard_normal((B, T, H, d))
+    lg = r.standard_normal((B, T, H, d)) + gate_mean
+    return q, k, v, lg
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append([int(x) for x in line.split()])
+    return rows
+
+
+# ---------------------------------------------------------------- gates
+def pin_gate_values(o):
+    """sigmoid pairs: limits, the midpoint and scipy's logistic function."""
+    from scipy.special import expit
+
+    x = np.array([-np.inf, -30.0, -1.5, 0.0, 0.25, 3.0, 40.0, np.inf])
+    g, gb = o.gates(x)
+    assert g[0] == 0.0 and gb[0] == 1.0  # l = -inf: forget everything
+    assert g[-1] == 1.0 and gb[-1] == 0.0  # l = +inf: keep everything
+    assert g[3] == 0.5 and gb[3] == 0.5
+    np.testing.assert_allclose(g, expit(x), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(gb, expit(-x), rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- scan
+def pin_scan_hand_example(o):
+    """T = 3, one channel, logit 0 (g = 1/2), x = 1, 2, 3, worked by hand:
+    full: h = 1/2, 1/4 + 1 = 5/4, 5/8 + 3/2 = 17/8;
+    RESTART, L = 2: the block starting at t = 2 gives h_2 = 3/2;
+    SLIDING, L = 2: h_2 = g_2 (1-g_1) x_1 + (1-g_2) x_2 = 1/2 + 3/2 = 2.
+    The values are dyadic, hence exact in fp64."""
+    x = np.array([1.0, 2.0, 3.0]).reshape(1, 3, 1, 1)
+    lg = np.zeros_like(x)
+    ks, vs = o.scan(x, 2 * x, lg, L=3)
+    assert ks.ravel().tolist() == [0.5, 1.25, 2.125]
+    assert vs.ravel().tolist() == [1.0, 2.5, 4.25]
+    ks, _ = o.scan(x, x, lg, L=2, mode=0)
+    assert ks.ravel().tolist() == [0.5, 1.25, 1.5]
+    ks, _ = o.scan(x, x, lg, L=2, mode=1)
+    assert ks.ravel().tolist() == [0.5, 1.25, 2.0]
+
+
+def pin_scan_constant_closed_form(o):
+    """Constant gate g and constant input x: h_t = x (1 - g^n_t) with
+    n_t = t+1 (full), (t mod L)+1 (RESTART), min(t+1, L) (SLIDING)."""
+    T, L, xval = 50, 7, 1.75
+    g = 0.75
+    lg = np.full((1, T, 1, 1), math.log(g / (1 - g)))
+    x = np.full((1, T, 1, 1), xval)
+    t = np.arange(T)
+    for mode, n in ((None, t + 1), (0, t % L + 1), (1, np.minimum(t + 1, L))):
+        if mode is None:
+            ks, _ = o.scan(x, x, lg, L=T)
+        else:
+            ks, _ = o.scan(x, x, lg, L=L, mode=mode)
+        np.testing.assert_allclose(ks.ravel(), xval * (1 - g ** n), rtol=1e-13, atol=0)
+
+
+def pin_scan_special_cases(o):
+    q, k, v, lg = _inputs(1, 2, 40, 2, 3)
+    # g = 0 (logit -inf): the state is the input itself, exactly
+    ks, vs = o.scan(k, v, np.full_like(lg, -np.inf), L=40)
+    assert np.array_equal(ks, k) and np.array_equal(vs, v)
+    # g = 1 (logit +inf): nothing ever enters the state
+    ks, vs = o.scan(k, v, np.full_like(lg, np.inf), L=40)
+    assert np.all(ks == 0) and np.all(vs == 0)
+    # L = 1: h = (1-g) x in both windowed modes
+    _, gb = o.gates(lg)
+    for mode in (0, 1):
+        ks, vs = o.scan(k, v, lg, L=1, mode=mode)
+        np.testing.assert_allclose(ks, gb * k, rtol=1e-15, atol=0)
+        np.testing.assert_allclose(vs, gb * v, rtol=1e-15, atol=0)
+    # L >= T: both windowed modes are the full recurrence
+    full = o.scan(k, v, lg, L=40)
+    for mode in (0, 1):
+        for L in (40, 41, 1000):
+            got = o.scan(k, v, lg, L=L, mode=mode)
+            assert np.array_equal(got[0], full[0]) and np.array_equal(got[1], full[1])
+
+
+def pin_scan_explicit_sum(o):
+    """Brute force on tiny T: the closed double sum of every mode."""
+    q, k, v, lg = _inputs(2, 2, 37, 2, 3, gate_mean=0.5)
+    for L, mode in ((37, 0), (8, 0), (8, 1), (5, 1), (1, 0), (64, 1)):
+        want = brute.scan_explicit(k, v, lg, L, mode)
+        got = o.scan(k, v, lg, L=L, mode=mode)
+        np.testing.assert_allclose(got[0], want[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(got[1], want[1], rtol=1e-12, atol=1e-14)
+
+
+def pin_scan_parallel_prefix(o):
+    """Sequential recurrence == log-depth associative scan (full and RESTART)."""
+    q, k, v, lg = _inputs(3, 2, 200, 2, 4, gate_mean=2.0)
+    for L in (200, 64, 13):
+        want = brute.scan_parallel(k, v, lg, L)
+        got = o.scan(k, v, lg, L=L, mode=0)
+        np.testing.assert_allclose(got[0], want[0], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(got[1], want[1], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- index sets
+def pin_index_sets_by_hand(o):
+    dil, loc = o.index_sets(10, 4, 3)
+    assert dil.tolist() == [10, 6, 2] and loc.tolist() == [10, 9, 8]
+    dil, loc = o.index_sets(1, 4, 3)
+    assert dil.tolist() == [1] and loc.tolist() == [1, 0]
+    dil, loc = o.index_sets(0, 1, 0)
+    assert dil.tolist() == [0] and loc.tolist() == []
+    dil, loc = o.index_sets(7, 1, 2)
+    assert dil.tolist() == [7, 6, 5, 4, 3, 2, 1, 0] and loc.tolist() == [7, 6]
+    dil, loc = o.index_sets(63, 64, 64)
+    assert dil.tolist() == [63] and loc.tolist() == list(range(63, -1, -1))
+
+
+def pin_pair_counts_closed_form(o):
+    """sum_t |S_dil(t)| = sum_r M_r (M_r+1)/2 with M_r = ceil((T-r)/D)
+    (= D M (M+1)/2 when D divides T); sum_t |S_loc(t)| = W(W+1)/2 + (T-W) W
+    for T >= W, T(T+1)/2 otherwise."""
+    for T, D, W in ((256, 4, 0), (4096, 16, 0), (16384, 64, 128), (100, 7, 13),
+                    (37, 64, 5), (10, 3, 50), (32768, 1, 0), (300, 300, 1)):
+        nd, nl = o.count_pairs(T, D, W)
+        want_d = sum(((T - r + D - 1) // D) * ((T - r + D - 1) // D + 1) // 2
+                     for r in range(min(D, T)))
+        if T % D == 0:
+            M = T // D
+            assert want_d == D * M * (M + 1) // 2
+        want_l = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+        assert (nd, nl) == (want_d, want_l), (T, D, W)
+
+
+def pin_pages_flops_table(o):
+    """Deep Dive S3.1 table: a query's attention FLOPs are T/D; the RAT+
+    abstract: the KV cache and FLOPs fall by exactly D (64x at D = 64)."""
+    T = 4096
+    for D, divisor in read_golden("flops_per_query_vs_dilation.txt"):
+        dil, loc = o.index_sets(T - 1, D, 0)
+        assert len(loc) == 0
+        assert len(dil) * divisor == T  # keys of the last query: T / D
+        assert len(dil) == (T - 1) // D + 1  # = the decode cache entries
+    for D, factor in read_golden("kv_cache_reduction.txt"):
+        dense, _ = o.index_sets(T - 1, 1, 0)
+        dil, _ = o.index_sets(T - 1, D, 0)
+        assert len(dense) == factor * len(dil)
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa_causal(q, k, v, scale):
+    """torch's scaled_dot_product_attention on the CPU in fp64; [n, d] rows."""
+    qt = torch.from_numpy(q)[None, None]
+    kt = torch.from_numpy(k)[None, None]
+    vt = torch.from_numpy(v)[None, None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                           scale=scale)
+    return out[0, 0].numpy()
+
+
+def pin_attn_dense_is_sdpa(o):
+    """g = 0 (states = raw inputs), D = 1, W = 0: dense causal softmax
+    attention, i.e. the library routine."""
+    q, k, v, lg = _inputs(4, 2, 45, 3, 8)
+    ks, vs = o.scan(k, v, np.full_like(lg, -np.inf), L=45)
+    scale = 1 / math.sqrt(8)
+    out = o.attn_prefill(q, ks, vs, None, None, 1, 0, scale)
+    for b in range(2):
+        for h in range(3):
+            want = _sdpa_causal(q[b, :, h], k[b, :, h], v[b, :, h], scale)
+            np.testing.assert_allclose(out[b, :, h], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_residue_decomposition(o):
+    """W = 0: the rows of residue r are causal attention over q[r::D],
+    states[r::D] (ragged T, several D)."""
+    q, ks, vs, _ = _inputs(5, 1, 53, 2, 8)
+    scale = 0.3
+    for D in (2, 4, 7, 16):
+        out = o.attn_prefill(q, ks, vs, None, None, D, 0, scale)
+        for h in range(2):
+            for r in range(D):
+                want = _sdpa_causal(q[0, r::D, h], ks[0, r::D, h], vs[0, r::D, h], scale)
+                np.testing.assert_allclose(out[0, r::D, h], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_single_key(o):
+    """D >= T, W = 0: one key per query, the output IS that state's value."""
+    q, ks, vs, _ = _inputs(6, 2, 20, 2, 8)
+    for D in (20, 21, 1000):
+        out = o.attn_prefill(q, ks, vs, None, None, D, 0, 0.5)
+        assert np.array_equal(out, vs)
+
+
+def pin_attn_two_key_closed_form(o):
+    """D >= T, W = 1: keys {state_t, raw_t}; the softmax of two logits a, b
+    gives sigmoid(a-b) * Vstate + sigmoid(b-a) * vraw."""
+    from scipy.special import expit
+
+    q, ks, vs, _ = _inputs(7, 1, 30, 2, 8)
+    _, kr, vr, _ = _inputs(8, 1, 30, 2, 8)
+    scale = 0.4
+    out = o.attn_prefill(q, ks, vs, kr, vr, 64, 1, scale)
+    a = scale * np.sum(q * ks, axis=-1, keepdims=True)
+    b = scale * np.sum(q * kr, axis=-1, keepdims=True)
+    want = expit(a - b) * vs + expit(b - a) * vr
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_attn_masked_matrix(o):
+    """Brute force on tiny T: the dense masked-score formulation over
+    [states ; raw] for mixed per-head (D, W)."""
+    q, ks, vs, _ = _inputs(9, 2, 70, 5, 8)
+    _, kr, vr, _ = _inputs(10, 2, 70, 5, 8)
+    D = [1, 3, 8, 64, 5]
+    W = [0, 4, 16, 9, 70]
+    out = o.attn_prefill(q, ks, vs, kr, vr, D, W, 0.35)
+    want = brute.attn_masked(q, ks, vs, kr, vr, D, W, 0.35)
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
+
+
+def pin_attn_hybrid_heads(o):
+    """Head-wise hybrid (Deep Dive S6): each head of a mixed run equals the
+    run of that head alone."""
+    q, ks, vs, _ = _inputs(11, 1, 64, 4, 8)
+    _, kr, vr, _ = _inputs(12, 1, 64, 4, 8)
+    D = [1, 1, 4, 16]
+    W = [0, 0, 8, 32]
+    out = o.attn_prefill(q, ks, vs, kr, vr, D, W, 0.3)
+    for h in range(4):
+        one = o.attn_prefill(q[:, :, h:h + 1], ks[:, :, h:h + 1], vs[:, :, h:h + 1],
+                             kr[:, :, h:h + 1], vr[:, :, h:h + 1], D[h], W[h], 0.3)
+        assert np.array_equal(out[:, :, h:h + 1], one)
+
+
+def pin_rows_match_full(o):
+    q, ks, vs, _ = _inputs(13, 2, 50, 3, 8)
+    _, kr, vr, _ = _inputs(14, 2, 50, 3, 8)
+    D, W = [1, 4, 9], [0, 6, 12]
+    full = o.attn_prefill(q, ks, vs, kr, vr, D, W, 0.3)
+    rows = [(0, 0, 0), (1, 49, 2), (0, 17, 1), (1, 8, 2)]
+    got = o.attn_prefill_rows(q, ks, vs, kr, vr, rows, D, W, 0.3)
+    for i, (b, t, h) in enumerate(rows):
+        assert np.array_equal(got[i], full[b, t, h])
+
+
+# ---------------------------------------------------------------- decode
+def decode_caches_from_prefill(ks, vs, k, v, T, D, W, nd_cap, w_cap, rng):
+    """Lay prefill states / raw tokens out as decode caches at context T:
+    dilated entry i = state at position ((T-1) mod D) + i D, ring = the
+    last min(W, T) raw tokens in a shuffled slot order."""
+    B, _, H, d = ks.shape
+    kd = np.zeros((B, H, nd_cap, d))
+    vd = np.zeros((B, H, nd_cap, d))
+    kw = np.zeros((B, H, w_cap, d))
+    vw = np.zeros((B, H, w_cap, d))
+    for h in range(H):
+        r = (T - 1) % D[h]
+        pos = np.arange(r, T, D[h])
+        kd[:, h, : len(pos)] = ks[:, pos, h]
+        vd[:, h, : len(pos)] = vs[:, pos, h]
+        nw = min(W[h], T)
+        wpos = np.arange(T - nw, T)
+        rng.shuffle(wpos)
+        kw[:, h, :nw] = k[:, wpos, h]
+        vw[:, h, :nw] = v[:, wpos, h]
+    return kd, vd, kw, vw
+
+
+def pin_decode_equals_prefill_row(o):
+    """Decode at context T equals prefill row T-1 (two separate code paths)."""
+    q, k, v, lg = _inputs(15, 2, 77, 4, 8)
+    D, W = [1, 4, 16, 100], [0, 8, 5, 3]
+    ks, vs = o.scan(k, v, lg, L=77)
+    pre = o.attn_prefill(q, ks, vs, k, v, D, W, 0.3)
+    rng = _rng(0)
+    for T in (1, 2, 33, 77):
+        nd_cap = max((T + Dh - 1) // Dh for Dh in D) + 3
+        w_cap = max(min(Wh, T) for Wh in W) + 2
+        kd, vd, kw, vw = decode_caches_from_prefill(ks[:, :T], vs[:, :T], k[:, :T], v[:, :T],
+                                                    T, D, W, nd_cap, w_cap, rng)
+        pre_T = o.attn_prefill(q[:, :T], ks[:, :T], vs[:, :T], k[:, :T], v[:, :T], D, W, 0.3)
+        got = o.attn_decode(q[:, T - 1], kd, vd, kw, vw, T, D, W, 0.3)
+        np.testing.assert_allclose(got, pre_T[:, T - 1], rtol=1e-12, atol=1e-13)
+        if T == 77:
+            np.testing.assert_allclose(got, pre[:, T - 1], rtol=1e-12, atol=1e-13)
+
+
+def pin_decode_ring_order(o):
+    """Ring slot order does not matter (a softmax is permutation invariant)."""
+    r = _rng(16)
+    B, H, d, T = 2, 3, 8, 500
+    D, W = [16, 64, 7], [10, 33, 1]
+    nd_cap, w_cap = 80, 40
+    q = r.standard_normal((B, H, d))
+    kd, vd = r.standard_normal((2, B, H, nd_cap, d))
+    kw, vw = r.standard_normal((2, B, H, w_cap, d))
+    base = o.attn_decode(q, kd, vd, kw, vw, T, D, W, 0.3)
+    perm = r.permutation(10)  # permute only the valid slots of head 0
+    kw2, vw2 = kw.copy(), vw.copy()
+    kw2[:, 0, :10] = kw[:, 0, perm]
+    vw2[:, 0, :10] = vw[:, 0, perm]
+    got = o.attn_decode(q, kd, vd, kw2, vw2, T, D, W, 0.3)
+    np.testing.assert_allclose(got, base, rtol=1e-13, atol=1e-14)
+    # entries past the valid counts are never read
+    kd3, kw3 = kd.copy(), kw.copy()
+    for h in range(H):
+        kd3[:, h, (T + D[h] - 1) // D[h]:] = np.nan  # entries past ceil(T/D)
+        kw3[:, h, min(W[h], T):] = np.nan  # slots past min(W, T)
+    got = o.attn_decode(q, kd3, vd, kw3, vw, T, D, W, 0.3)
+    np.testing.assert_array_equal(got, base)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
