@@ -1,0 +1,10 @@
+"""RAT+ recurrence-augmented dilated attention on AMD Instinct MI355X (gfx950).
+
+The hot path lives in the HIP library ``librat.so`` (C ABI in
+``include/rat.h``); ``ops`` is its thin torch binding and ``inputs`` the
+seeded synthetic workloads.  Importing the package does not load the
+library; the first call does, and raises if it has not been built.
+"""
+from .ops import (RESTART, SLIDING, RatError, decode_workspace_bytes, dilated_attn_decode,  # noqa: F401
+                  dilated_attn_prefill, load_library, rat_layer_prefill, scan_prefill,
+                  scan_workspace_bytes)

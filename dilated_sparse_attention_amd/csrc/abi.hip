@@ -1,0 +1,303 @@
+// C ABI of the RAT+ hot path (declared in include/rat.h): host-side argument
+// validation, workspace sizing, work scheduling and kernel launches.
+// Validation never touches the HIP runtime, so every error code is returned
+// before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "rat.h"
+#include "rat_internal.h"
+
+using namespace rat;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return RAT_OK;
+    g_last_hip_error = (int)e;
+    return RAT_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(rat_dtype t) { return t == RAT_DTYPE_F32 ? 4 : 2; }
+
+bool dtype_ok(int t) { return t == RAT_DTYPE_F32 || t == RAT_DTYPE_BF16; }
+
+bool d_ok(int d) { return d == 64 || d == 128; }
+
+const int64_t kMaxElems = (int64_t)1 << 31;
+
+// [B,T,H,d] (or any product of four positive ints) below 2^31 elements
+bool size_ok(int64_t a, int64_t b, int64_t c, int64_t d)
+{
+    const int64_t n = a * b;
+    if (n >= kMaxElems) return false;
+    const int64_t n2 = n * c;
+    if (n2 >= kMaxElems) return false;
+    return n2 * d < kMaxElems;
+}
+
+struct ScanPlan {
+    int tpl, chunk, nblk, nseq, nchunk, nwg;
+    size_t agg_off, incl_off, bytes;
+};
+
+ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
+{
+    ScanPlan p;
+    p.tpl = dtype == RAT_DTYPE_BF16 ? kScanTplBf16 : kScanTplF32;
+    p.chunk = 8 * p.tpl;
+    const int N = H * d;
+    p.nblk = (N + kScanBlockCh - 1) / kScanBlockCh;
+    p.nseq = B * p.nblk;
+    p.nchunk = (T + p.chunk - 1) / p.chunk;
+    p.nwg = p.nchunk * p.nseq;
+    const size_t slots = (size_t)p.nwg;
+    p.agg_off = sizeof(ScanHeader);
+    p.incl_off = p.agg_off + slots * 3 * kScanBlockCh * sizeof(uint64_t);
+    p.bytes = p.incl_off + slots * 2 * kScanBlockCh * sizeof(uint64_t);
+    return p;
+}
+
+bool scan_uses_workspace(int T, int L, rat_recur_mode mode)
+{
+    return L >= T || mode == RAT_RECUR_RESTART;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rat_status_string(int s)
+{
+    switch (s) {
+    case RAT_OK: return "ok";
+    case RAT_ERR_NULL: return "a required pointer is NULL";
+    case RAT_ERR_SHAPE: return "a size or per-head parameter is out of range";
+    case RAT_ERR_UNSUPPORTED: return "valid arguments that this build does not support";
+    case RAT_ERR_ALIAS: return "an output aliases an input";
+    case RAT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case RAT_ERR_HIP: return "a HIP launch failed";
+    case RAT_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+int rat_last_hip_error(void) { return g_last_hip_error; }
+
+size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L, rat_recur_mode mode, rat_dtype dtype)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1 || !dtype_ok(dtype)) return 0;
+    if (!scan_uses_workspace(T, L, mode)) return 0;
+    return scan_plan(B, T, H, d, dtype).bytes;
+}
+
+int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void* k_state, void* v_state,
+                     int B, int T, int H, int d, int L, rat_recur_mode mode, rat_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!k || !v || !gate_logits || !k_state || !v_state) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return RAT_ERR_SHAPE;
+    if (mode != RAT_RECUR_RESTART && mode != RAT_RECUR_SLIDING) return RAT_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
+    if (mode == RAT_RECUR_SLIDING && L < T && L > 64) return RAT_ERR_UNSUPPORTED;
+    const void* ins[3] = {k, v, gate_logits};
+    for (const void* in : ins)
+        if (in == k_state || in == v_state) return RAT_ERR_ALIAS;
+    if (k_state == v_state) return RAT_ERR_ALIAS;
+    const void* all[5] = {k, v, gate_logits, k_state, v_state};
+    for (const void* p : all)
+        if (!aligned16(p)) return RAT_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = dtype == RAT_DTYPE_BF16;
+
+    if (scan_uses_workspace(T, L, mode)) {
+        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        if (!workspace || workspace_bytes < p.bytes || ((uintptr_t)workspace & 255u)) return RAT_ERR_WORKSPACE;
+        ScanFullArgs a;
+        a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state;
+        a.T = T; a.N = H * d; a.nblk = p.nblk; a.nseq = p.nseq; a.nchunk = p.nchunk;
+        a.L = L >= T ? 0 : L; a.nwg = p.nwg;
+        char* ws = static_cast<char*>(workspace);
+        a.hdr = reinterpret_cast<ScanHeader*>(ws);
+        a.agg = reinterpret_cast<uint64_t*>(ws + p.agg_off);
+        a.incl = reinterpret_cast<uint64_t*>(ws + p.incl_off);
+        return hip_status(launch_scan_full(a, bf16, s));
+    }
+    ScanSlideArgs a;
+    a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state;
+    a.B = B; a.T = T; a.N = H * d; a.L = L;
+    const int ntiles = (T + L - 1) / L;
+    // spans of at least 256 tokens: one halo tile per span
+    a.tiles_per_span = std::max(1, (256 + L - 1) / L);
+    const int nspans = (ntiles + a.tiles_per_span - 1) / a.tiles_per_span;
+    const int cgroups = (a.N + 63) / 64;
+    return hip_status(launch_scan_sliding(a, nspans * B * cgroups, bf16, s));
+}
+
+namespace {
+
+int check_heads(int H, const int* D, const int* W, bool* any_w)
+{
+    if (!D || !W) return RAT_ERR_NULL;
+    if (H > kAttnMaxHeads) return RAT_ERR_UNSUPPORTED;
+    *any_w = false;
+    for (int h = 0; h < H; ++h) {
+        if (D[h] < 1 || W[h] < 0) return RAT_ERR_SHAPE;
+        if (W[h] > 0) *any_w = true;
+    }
+    return RAT_OK;
+}
+
+}  // namespace
+
+int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
+                             const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
+                             float scale, rat_dtype dtype, void* stream)
+{
+    if (!q || !k_state || !v_state || !out) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!k_raw || !v_raw)) return RAT_ERR_NULL;
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[5] = {q, k_state, v_state, k_raw, v_raw};
+    for (const void* in : ins)
+        if (in && in == out) return RAT_ERR_ALIAS;
+    for (const void* p : ins)
+        if (p && !aligned16(p)) return RAT_ERR_ALIGN;
+    if (!aligned16(out)) return RAT_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (dtype == RAT_DTYPE_F32) {
+        AttnF32Args a;
+        memset(&a, 0, sizeof(a));
+        a.q = (const float*)q; a.ks = (const float*)k_state; a.vs = (const float*)v_state;
+        a.kr = (const float*)k_raw; a.vr = (const float*)v_raw; a.out = (float*)out;
+        a.B = B; a.T = T; a.H = H; a.d = d; a.scale = scale;
+        for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+        return hip_status(launch_attn_prefill_f32(a, s));
+    }
+
+    // group heads by (D, W); each class becomes a range of blocks, classes
+    // with the longest single items first, each class's levels most
+    // expensive first
+    struct Cls { int D, W; std::vector<int> heads; double item_cost; };
+    std::vector<Cls> cls;
+    for (int h = 0; h < H; ++h) {
+        auto it = std::find_if(cls.begin(), cls.end(), [&](const Cls& c) { return c.D == D[h] && c.W == W[h]; });
+        if (it == cls.end()) {
+            cls.push_back(Cls{D[h], W[h], {}, 0.0});
+            it = cls.end() - 1;
+        }
+        it->heads.push_back(h);
+    }
+    if ((int)cls.size() > kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.ks = k_state; a.vs = v_state; a.kr = k_raw; a.vr = v_raw; a.out = out;
+    a.B = B; a.T = T; a.H = H;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (auto& c : cls) {
+        const int Mmax = (T + c.D - 1) / c.D;
+        if (c.W == 0) c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
+        else c.item_cost = 256.0 * (std::min(Mmax, kAttnRowsB) + c.W + 16);
+    }
+    std::stable_sort(cls.begin(), cls.end(), [](const Cls& x, const Cls& y) { return x.item_cost > y.item_cost; });
+    int blocks = 0, hoff = 0;
+    a.nclass = (int)cls.size();
+    for (int ci = 0; ci < a.nclass; ++ci) {
+        const Cls& c = cls[ci];
+        AttnClass& k = a.cls[ci];
+        k.D = c.D; k.W = c.W; k.path = c.W == 0 ? kPathA : kPathB;
+        k.nheads = (int)c.heads.size(); k.head_off = hoff;
+        for (int hh : c.heads) a.heads[hoff++] = (int16_t)hh;
+        const int Mmax = (T + c.D - 1) / c.D;
+        if (k.path == kPathA) {
+            k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
+            k.per_level = B * k.nheads * c.D;
+        } else {
+            k.levels = (Mmax + kAttnRowsB - 1) / kAttnRowsB;
+            const int ngroups = c.D >= 16 ? (c.D + 15) / 16 : 1;
+            k.per_level = B * k.nheads * ngroups;
+        }
+        const int64_t nb = (int64_t)k.levels * k.per_level;
+        if (nb + blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
+        k.block_begin = blocks;
+        blocks += (int)nb;
+    }
+    a.nblocks = blocks;
+    return hip_status(launch_attn_prefill_bf16(a, d, s));
+}
+
+namespace {
+
+int decode_nsplit(int B, int H, int T, const int* D, const int* W)
+{
+    int nmax = 1;
+    for (int h = 0; h < H; ++h) nmax = std::max(nmax, (T - 1) / D[h] + 1 + std::min(W[h], T));
+    const int bh = B * H;
+    const int want = (512 + bh - 1) / bh;          // aim at >= 512 workgroups
+    const int cap = std::max(1, nmax / 256);        // at least 256 keys per split
+    return std::max(1, std::min(want, cap));
+}
+
+}  // namespace
+
+size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, const int* W)
+{
+    if (B <= 0 || H <= 0 || d <= 0 || T <= 0 || !D || !W || H > kAttnMaxHeads) return 0;
+    for (int h = 0; h < H; ++h)
+        if (D[h] < 1 || W[h] < 0) return 0;
+    const int ns = decode_nsplit(B, H, T, D, W);
+    if (ns == 1) return 0;
+    return (size_t)B * H * ns * (d + 2) * sizeof(float);
+}
+
+int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
+                            int w_cap, void* out, int B, int T, int H, int d, const int* D, const int* W, float scale,
+                            rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !kd || !vd || !out) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || nd_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
+    for (int h = 0; h < H; ++h) {
+        if ((T - 1) / D[h] + 1 > nd_cap) return RAT_ERR_SHAPE;
+        if (std::min(W[h], T) > w_cap) return RAT_ERR_SHAPE;
+    }
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, H, nd_cap, d) || !size_ok(B, H, std::max(w_cap, 1), d))
+        return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[5] = {q, kd, vd, kw, vw};
+    for (const void* in : ins)
+        if (in && in == out) return RAT_ERR_ALIAS;
+    for (const void* p : ins)
+        if (p && !aligned16(p)) return RAT_ERR_ALIGN;
+    if (!aligned16(out)) return RAT_ERR_ALIGN;
+    const int ns = decode_nsplit(B, H, T, D, W);
+    const size_t need = ns == 1 ? 0 : (size_t)B * H * ns * (d + 2) * sizeof(float);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) return RAT_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.kd = kd; a.vd = vd; a.kw = kw ? kw : kd; a.vw = vw ? vw : vd; a.out = out;
+    a.part = static_cast<float*>(workspace);
+    a.B = B; a.H = H; a.T = T; a.nd_cap = nd_cap; a.w_cap = w_cap; a.nsplit = ns;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+    return hip_status(launch_decode(a, d, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,222 @@
+// Decode step of the RAT+ layer: the new query at position T-1 attends to
+// the dilated KV cache -- the recurrent states of its residue,
+// ((T-1) mod D) + i*D for i < ceil(T/D), a cache D times smaller than a
+// dense one ("RAT+: Train Dense, Infer Sparse", arXiv 2602.18196, Abstract;
+// "RAT+ Deep Dive", zhichai.net, section 3.1: KV cache and attention FLOPs
+// cut by D) -- plus the raw tokens of the local window (ring of the last
+// min(W, T) tokens).
+//
+// One query per (b, h): a matrix-vector product, HBM-bound at ~1 FLOP/byte,
+// so the kernel streams key/value rows with wide coalesced loads and does
+// the dot products on the VALU (no MFMA).  DK/8 lanes share one 16-byte
+// slice each of a key row, so a wave reads 64/(DK/8) whole rows per load;
+// every key group keeps its own online-softmax state, merged across lane
+// groups and waves at the end.  Long caches with few (b, h) pairs are split
+// over several workgroups whose partial states a second kernel merges.
+#include "rat_device.h"
+#include "rat_internal.h"
+
+namespace rat {
+
+template <typename E> struct Row8;
+template <> struct Row8<uint16_t> {  // 8 bf16 = 16 bytes
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8])
+    {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16_lo(w[j]);
+            x[2 * j + 1] = bf16_hi(w[j]);
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8])
+    {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(p) = w;
+    }
+};
+template <> struct Row8<float> {  // 8 fp32 = 32 bytes
+    static __device__ __forceinline__ void load(const float* p, float (&x)[8])
+    {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = a[j];
+            x[4 + j] = b[j];
+        }
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&x)[8])
+    {
+        *reinterpret_cast<floatx4*>(p) = floatx4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<floatx4*>(p + 4) = floatx4{x[4], x[5], x[6], x[7]};
+    }
+};
+
+constexpr int kDecUnroll = 4;
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(DecodeArgs a)
+{
+    constexpr int LPK = DK / 8;          // lanes per key row
+    constexpr int KPI = kWave / LPK;     // keys per wave step
+    __shared__ float s_m[kDecWaves][KPI], s_l[kDecWaves][KPI];
+    __shared__ float s_acc[kDecWaves][KPI][DK];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int slice = lane % LPK;        // dims 8*slice .. 8*slice+7
+    const int kg = lane / LPK;           // key group in the wave
+    const int split = blockIdx.x % a.nsplit;
+    const int bh = blockIdx.x / a.nsplit;
+    const int h = bh % a.H;
+    const int D = a.D[h], W = a.W[h];
+    const int nd = (a.T - 1) / D + 1;
+    const int nw = min(W, a.T);
+    const int n = nd + nw;
+    const int per_split = (n + a.nsplit - 1) / a.nsplit;
+    const int k_begin = split * per_split;
+    const int k_end = min(n, k_begin + per_split);
+    const int per_wave = (max(k_end - k_begin, 0) + kDecWaves - 1) / kDecWaves;
+    const int w_begin = k_begin + wv * per_wave;
+    const int w_end = min(k_end, w_begin + per_wave);
+
+    const E* kd = static_cast<const E*>(a.kd) + (size_t)bh * a.nd_cap * DK + 8 * slice;
+    const E* vd = static_cast<const E*>(a.vd) + (size_t)bh * a.nd_cap * DK + 8 * slice;
+    const E* kw = static_cast<const E*>(a.kw) + (size_t)bh * a.w_cap * DK + 8 * slice;
+    const E* vw = static_cast<const E*>(a.vw) + (size_t)bh * a.w_cap * DK + 8 * slice;
+
+    float q[8];
+    Row8<E>::load(static_cast<const E*>(a.q) + (size_t)bh * DK + 8 * slice, q);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] *= a.scale_log2;
+
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+
+    for (int k0 = w_begin; k0 < w_end; k0 += KPI * kDecUnroll) {
+        float kx[kDecUnroll][8], vx[kDecUnroll][8];
+        bool ok[kDecUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const int key = k0 + u * KPI + kg;
+            ok[u] = key < w_end;
+            const int kk = ok[u] ? key : w_begin;
+            const E* kr = kk < nd ? kd + (size_t)kk * DK : kw + (size_t)(kk - nd) * DK;
+            const E* vr = kk < nd ? vd + (size_t)kk * DK : vw + (size_t)(kk - nd) * DK;
+            Row8<E>::load(kr, kx[u]);
+            Row8<E>::load(vr, vx[u]);
+        }
+        float s[kDecUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dot = fmaf(q[j], kx[u][j], dot);
+#pragma unroll
+            for (int o = 1; o < LPK; o <<= 1) dot += __shfl_xor(dot, o);
+            s[u] = ok[u] ? dot : -INFINITY;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int u = 1; u < kDecUnroll; ++u) mx = fmaxf(mx, s[u]);
+        const float mn = fmaxf(m, mx);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float al = __builtin_amdgcn_exp2f(m - ms);
+        l *= al;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= al;
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const float p = __builtin_amdgcn_exp2f(s[u] - ms);
+            l += p;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = fmaf(p, vx[u][j], acc[j]);
+        }
+        m = mn;
+    }
+
+    // merge key groups and waves through LDS
+    if (slice == 0) {
+        s_m[wv][kg] = m;
+        s_l[wv][kg] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_acc[wv][kg][8 * slice + j] = acc[j];
+    __syncthreads();
+    if (wv == 0 && kg == 0) {
+        float M = -INFINITY;
+        for (int w2 = 0; w2 < kDecWaves; ++w2)
+            for (int g2 = 0; g2 < KPI; ++g2) M = fmaxf(M, s_m[w2][g2]);
+        const float Ms = M == -INFINITY ? 0.f : M;
+        float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w2 = 0; w2 < kDecWaves; ++w2)
+            for (int g2 = 0; g2 < KPI; ++g2) {
+                const float f = __builtin_amdgcn_exp2f(s_m[w2][g2] - Ms);
+                L += f * s_l[w2][g2];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = fmaf(f, s_acc[w2][g2][8 * slice + j], o[j]);
+            }
+        if (a.nsplit == 1) {
+            const float inv = 1.0f / L;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] *= inv;
+            Row8<E>::store(static_cast<E*>(a.out) + (size_t)bh * DK + 8 * slice, o);
+        } else {
+            float* pp = a.part + ((size_t)bh * a.nsplit + split) * (DK + 2);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pp[8 * slice + j] = o[j];
+            if (slice == 0) {
+                pp[DK] = M;
+                pp[DK + 1] = L;
+            }
+        }
+    }
+}
+
+// Combines the split partials of one (b, h): lanes own 8 output dims each.
+template <typename E, int DK>
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a)
+{
+    const int bh = blockIdx.x;
+    const int slice = threadIdx.x;
+    if (slice >= DK / 8) return;
+    const float* pp = a.part + (size_t)bh * a.nsplit * (DK + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pp[s * (DK + 2) + DK]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float* p = pp + s * (DK + 2);
+        const float f = __builtin_amdgcn_exp2f(p[DK] - Ms);
+        L += f * p[DK + 1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = fmaf(f, p[8 * slice + j], o[j]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] *= inv;
+    Row8<E>::store(static_cast<E*>(a.out) + (size_t)bh * DK + 8 * slice, o);
+}
+
+template <typename E, int DK>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
+{
+    const unsigned nbh = (unsigned)(a.B * a.H);
+    hipLaunchKernelGGL((decode_kernel<E, DK>), dim3(nbh * a.nsplit), dim3(kDecWaves * kWave), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<E, DK>), dim3(nbh), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream)
+{
+    if (bf16) return d == 128 ? launch_decode_t<uint16_t, 128>(a, stream) : launch_decode_t<uint16_t, 64>(a, stream);
+    return d == 128 ? launch_decode_t<float, 128>(a, stream) : launch_decode_t<float, 64>(a, stream);
+}
+
+}  // namespace rat

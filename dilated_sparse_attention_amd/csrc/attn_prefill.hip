@@ -1,0 +1,549 @@
+// Stage 2 of the RAT+ layer for prefill: causal dilated softmax attention
+// over the recurrent states, optionally joined by a window of raw tokens,
+// with a per-head (D, W) ("RAT+: Train Dense, Infer Sparse", arXiv
+// 2602.18196, Abstract; "RAT+ Deep Dive", zhichai.net, section 1 (tokens
+// skip a fixed interval D) and section 6 (Head-Wise Hybrid)).
+//
+// Query t of head h sees the states at t, t-D, t-2D, ... (>= 0) and the raw
+// tokens t, t-1, ..., t-W+1 (>= 0), in one softmax.  Queries of one residue
+// r = t mod D share their state keys: residue r is a dense causal problem
+// of length M_r = ceil((T - r) / D) over q[r::D], states[r::D].  The raw
+// window is a band over contiguous positions instead.
+//
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation and an fp32
+// online softmax in the log2 domain.  Per 16-query fragment a wave computes
+// S^T = K Q^T (keys x queries), so each lane owns one query: the softmax
+// statistics and the output O^T = V^T P^T stay per lane and P^T is the MFMA
+// B operand exactly as S^T leaves the accumulator.  V^T comes from a
+// row-major V tile in LDS through ds_read_b64_tr_b16.  LDS tiles are
+// XOR-swizzled in 16-byte chunks (chunk c of row r at c ^ (r mod 16)) so that
+// both the K-fragment reads and the transposing V reads avoid bank conflicts,
+// and are filled by direct global->LDS loads.
+//
+// Path A (heads with W = 0, including dense D = 1): one workgroup per
+// (b, h, r, 256-row chunk); its 16 waves (16 rows each) share K/V tiles of
+// 64 keys through a 4-deep LDS ring, so every state row is read from HBM
+// once per chunk.
+//
+// Path B (heads with W > 0): one workgroup per 2-D block of up to 16
+// residues x 16 rows.  Local phase: wave p takes 16 CONTIGUOUS queries
+// (for D >= 16: residues r0..r0+15 at one row) against their band of
+// W + 15 raw keys; the partial softmax state (m, l, acc) goes to LDS.
+// Dilated phase: wave g takes residue r0 + g (16 rows), starts its online
+// softmax from the local partials of those queries and runs over the
+// residue's states.  The hand-over through LDS is what lets both branches
+// use full 16-row MFMA fragments.
+#include "rat_device.h"
+#include "rat_internal.h"
+
+namespace rat {
+
+// LDS tiles are addressed through generic pointers into the workgroup's
+// shared array (the compiler keeps them in the LDS address space); the
+// builtins that need an explicit LDS pointer get one by an address-space cast.
+typedef char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) shortx4 lds_s4;
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// vmcnt-only wait (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int DK>
+struct Geo {
+    static constexpr int CH = DK / 8;           // 16-byte chunks per row
+    static constexpr int ROWB = DK * 2;         // bytes per bf16 row
+    static constexpr int KS = DK / 32;          // 32-dim k-steps of QK^T
+    static constexpr int DB = DK / 16;          // 16-dim blocks of the output
+    static constexpr int RPI = 1024 / ROWB;     // rows per 1 KiB wave load
+};
+
+// byte offset of chunk c of row r in a swizzled tile
+template <int DK>
+__device__ __forceinline__ int swz(int r, int c)
+{
+    return r * Geo<DK>::ROWB + ((c ^ (r & (Geo<DK>::CH - 1))) << 4);
+}
+
+// One wave copies RPI rows (1 KiB) global -> LDS: lane l fills row l / (CH)
+// of the group, physical chunk l % CH, with the global chunk that the
+// swizzle puts there.  `row_ptr` is the global address of the lane's row.
+template <int DK>
+__device__ __forceinline__ void copy_rows_lds(const uint16_t* row_ptr, int tile_row, lds_char* dst)
+{
+    constexpr int CH = Geo<DK>::CH;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = lane % CH;
+    const int c = p ^ (tile_row & (CH - 1));
+    __builtin_amdgcn_global_load_lds((const void*)(row_ptr + c * 8), (lds_void*)dst, 16, 0, 0);
+}
+
+// K fragment (MFMA A operand of S^T = K Q^T) for keys 16*kb .. 16*kb+15 of
+// a tile, k-step ks: lane (g, i) holds K[key 16kb+i][dims 8g+32ks .. +8].
+template <int DK>
+__device__ __forceinline__ bf16x8 k_frag_lds(const lds_char* tile, int kb, int ks)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = kb * 16 + (lane & 15);
+    const int c = (lane >> 4) + 4 * ks;
+    return *reinterpret_cast<const bf16x8*>(tile + swz<DK>(r, c));
+}
+
+// V^T fragment (MFMA A operand of O^T += V^T P^T) for 16-dim block db over
+// the 32 keys 32*hh .. 32*hh+31 of a tile.  K-slot order of lane group g:
+// slots 0-3 = keys 4g..4g+3, slots 4-7 = keys 16+4g..16+4g+3 (the order in
+// which S^T leaves them).  Lane (g, i) receives V[key][dim 16db + i].
+template <int DK>
+__device__ __forceinline__ bf16x8 v_frag_lds(const lds_char* tile, int hh, int db)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4, s = lane & 15;
+    const int dim = 16 * db + 4 * (s & 3);
+    const int c = dim >> 3, off = (dim & 7) * 2;
+    const int r0 = 32 * hh + 4 * g + (s >> 2);
+    const int r1 = r0 + 16;
+    shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<DK>(r0, c) + off));
+    shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<DK>(r1, c) + off));
+    typedef short shortx8 __attribute__((ext_vector_type(8)));
+    shortx8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Online-softmax state of one 16-query fragment (lane (g, i) owns query i;
+// m is replicated over the four lane groups, l is this lane's partial sum).
+template <int DK>
+struct Frag {
+    bf16x8 q[Geo<DK>::KS];
+    floatx4 acc[Geo<DK>::DB];
+    float m, l;
+
+    __device__ __forceinline__ void reset()
+    {
+#pragma unroll
+        for (int i = 0; i < Geo<DK>::DB; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+    }
+
+    // Q fragment (B operand): lane (g, i) holds q[row i][dims 8g + 32ks .. +8]
+    __device__ __forceinline__ void load_q(const uint16_t* row_ptr, bool valid)
+    {
+        const int g = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
+        for (int ks = 0; ks < Geo<DK>::KS; ++ks) {
+            if (valid)
+                q[ks] = *reinterpret_cast<const bf16x8*>(row_ptr + 8 * g + 32 * ks);
+            else
+                q[ks] = bf16x8{};
+        }
+    }
+
+    // Scores of 32 keys (two S^T blocks) -> masked, scaled (log2 domain) ->
+    // softmax update -> P^T fragment.  `valid[kb][j]` says whether key
+    // 16kb + 4g + j is visible to this lane's query.
+    __device__ __forceinline__ bf16x8 softmax_step(floatx4 s0, floatx4 s1, const bool (&valid)[2][4], float scale_log2)
+    {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = valid[0][j] ? s0[j] * scale_log2 : -INFINITY;
+            x[4 + j] = valid[1][j] ? s1[j] * scale_log2 : -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m, mx);
+        const float msafe = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        m = mnew;
+        float p[8], sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(x[j] - msafe);
+            sum += p[j];
+        }
+        l = l * alpha + sum;
+#pragma unroll
+        for (int i = 0; i < Geo<DK>::DB; ++i) acc[i] *= alpha;
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
+        return pb;
+    }
+
+    __device__ __forceinline__ float total_l() const
+    {
+        float t = l + __shfl_xor(l, 16);
+        return t + __shfl_xor(t, 32);
+    }
+
+    // O row of query i: lane (g, i) stores dims 16db + 4g .. +3
+    __device__ __forceinline__ void store(uint16_t* row_ptr, bool valid) const
+    {
+        const float lt = total_l();
+        if (!valid) return;
+        const float inv = 1.0f / lt;
+        const int g = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
+        for (int db = 0; db < Geo<DK>::DB; ++db) {
+            u32x2 o;
+            o[0] = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
+            o[1] = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+            *reinterpret_cast<u32x2*>(row_ptr + 16 * db + 4 * g) = o;
+        }
+    }
+};
+
+// ------------------------------------------------------------------ path A
+template <int DK>
+__device__ void path_a(const AttnArgs& a, int b, int h, int D, int r, int chunk, lds_char* smem)
+{
+    typedef Geo<DK> G;
+    constexpr int KT = 64;                        // keys per tile
+    constexpr int NBUF = 4;                       // LDS ring depth
+    constexpr int TILE_BYTES = 2 * KT * G::ROWB;  // K then V
+    constexpr int INSTR = 2 * KT / G::RPI;        // 1 KiB wave loads per tile
+    constexpr int PER_WAVE = INSTR / kAttnWaves;
+    static_assert(INSTR % kAttnWaves == 0, "tile loads split evenly over waves");
+
+    const int T = a.T, pitch = a.H * DK;
+    const int M = (T - r + D - 1) / D;            // rows of residue r
+    const int R0 = chunk * kAttnRowsA;
+    if (R0 >= M) return;
+    const int R1 = min(R0 + kAttnRowsA, M);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int g = lane >> 4, i = lane & 15;
+    const size_t base = ((size_t)b * T * a.H + h) * DK;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.ks) + base;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.vs) + base;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + base;
+
+    const int rs = R0 + 16 * wv;                  // first row of this wave
+    const int row = rs + i;
+    const bool rvalid = row < R1;
+    Frag<DK> f;
+    f.reset();
+    f.load_q(qp + (size_t)(r + row * D) * pitch, rvalid);
+
+    const int ntile = (R1 + KT - 1) / KT;
+    auto issue = [&](int tt) {
+        lds_char* buf = smem + (tt % NBUF) * TILE_BYTES;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int instr = wv * PER_WAVE + j;         // 0 .. INSTR-1
+            const int trow = instr * G::RPI + lane / G::CH;  // 0 .. 2*KT-1 (K rows then V rows)
+            const bool isv = trow >= KT;
+            const int kr = isv ? trow - KT : trow;
+            const int key = min(tt * KT + kr, R1 - 1);
+            const uint16_t* src = (isv ? vp : kp) + (size_t)(r + key * D) * pitch;
+            copy_rows_lds<DK>(src, kr, buf + instr * 1024);
+        }
+    };
+#pragma unroll
+    for (int tt = 0; tt < NBUF - 1; ++tt)
+        if (tt < ntile) issue(tt);
+
+    for (int tt = 0; tt < ntile; ++tt) {
+        const int ahead = min(NBUF - 2, ntile - 1 - tt);
+        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
+        else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (tt + NBUF - 1 < ntile) issue(tt + NBUF - 1);
+
+        const lds_char* kt = smem + (tt % NBUF) * TILE_BYTES;
+        const lds_char* vt = kt + KT * G::ROWB;
+#pragma unroll
+        for (int hh = 0; hh < KT / 32; ++hh) {
+            const int k0 = tt * KT + 32 * hh;            // first key of the half
+            if (k0 > rs + 15 || rs >= R1) continue;       // wholly above this wave's rows
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                s0 = mfma16(k_frag_lds<DK>(kt, 2 * hh, ks), f.q[ks], s0);
+                s1 = mfma16(k_frag_lds<DK>(kt, 2 * hh + 1, ks), f.q[ks], s1);
+            }
+            bool valid[2][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                valid[0][j] = rvalid && (k0 + 4 * g + j <= row);
+                valid[1][j] = rvalid && (k0 + 16 + 4 * g + j <= row);
+            }
+            const bf16x8 pb = f.softmax_step(s0, s1, valid, a.scale_log2);
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) f.acc[db] = mfma16(v_frag_lds<DK>(vt, hh, db), pb, f.acc[db]);
+        }
+    }
+    f.store(op + (size_t)(r + row * D) * pitch, rvalid);
+}
+
+// ------------------------------------------------------------------ path B
+// Each wave streams its own 32-key tiles: K fragments straight from HBM into
+// registers, V rows into the wave's private swizzled LDS tile.
+template <int DK>
+struct WaveStream {
+    typedef Geo<DK> G;
+    static constexpr int TILE = 32;
+
+    // key rows: position of key j of the tile is pos0 + j * step (clamped to last)
+    __device__ __forceinline__ static void load_v(const uint16_t* vbase, size_t pitch, int pos0, int step, int nkeys,
+                                                  lds_char* vt)
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int j = 0; j < TILE / G::RPI; ++j) {
+            const int tr = j * G::RPI + lane / G::CH;
+            const int key = min(tr, nkeys - 1);
+            copy_rows_lds<DK>(vbase + (size_t)(pos0 + key * step) * pitch, tr, vt + j * 1024);
+        }
+    }
+
+    __device__ __forceinline__ static void load_k(const uint16_t* kbase, size_t pitch, int pos0, int step, int nkeys,
+                                                  bf16x8 (&kf)[2][G::KS])
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = min(16 * kb + i, nkeys - 1);
+            const uint16_t* p = kbase + (size_t)(pos0 + key * step) * pitch + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) kf[kb][ks] = *reinterpret_cast<const bf16x8*>(p + 32 * ks);
+        }
+    }
+};
+
+// Streams keys at positions pos0 + j*step, j in [0, nkeys), through fragment
+// f; `vis(j)` tells whether key j is visible to this lane's query.
+template <int DK, typename Vis>
+__device__ __forceinline__ void stream_keys(Frag<DK>& f, const uint16_t* kbase, const uint16_t* vbase, size_t pitch,
+                                            int pos0, int step, int nkeys, lds_char* vt, float scale_log2, Vis vis)
+{
+    typedef Geo<DK> G;
+    const int g = (threadIdx.x & (kWave - 1)) >> 4;
+    for (int k0 = 0; k0 < nkeys; k0 += 32) {
+        const int n = min(32, nkeys - k0);
+        bf16x8 kf[2][G::KS];
+        WaveStream<DK>::load_v(vbase, pitch, pos0 + k0 * step, step, n, vt);
+        WaveStream<DK>::load_k(kbase, pitch, pos0 + k0 * step, step, n, kf);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_wave_barrier();
+        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            s0 = mfma16(kf[0][ks], f.q[ks], s0);
+            s1 = mfma16(kf[1][ks], f.q[ks], s1);
+        }
+        bool valid[2][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ka = k0 + 4 * g + j, kb = k0 + 16 + 4 * g + j;
+            valid[0][j] = ka < nkeys && vis(ka);
+            valid[1][j] = kb < nkeys && vis(kb);
+        }
+        const bf16x8 pb = f.softmax_step(s0, s1, valid, scale_log2);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) f.acc[db] = mfma16(v_frag_lds<DK>(vt, 0, db), pb, f.acc[db]);
+        __builtin_amdgcn_wave_barrier();  // tr reads done before the tile is refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads retired
+    }
+}
+
+template <int DK>
+__device__ void path_b(const AttnArgs& a, int b, int h, int D, int W, int rgroup, int iblock, lds_char* smem)
+{
+    typedef Geo<DK> G;
+    const int T = a.T, pitch = a.H * DK;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int i = lane & 15, g = lane >> 4;
+    const size_t base = ((size_t)b * T * a.H + h) * DK;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* ksp = static_cast<const uint16_t*>(a.ks) + base;
+    const uint16_t* vsp = static_cast<const uint16_t*>(a.vs) + base;
+    const uint16_t* krp = static_cast<const uint16_t*>(a.kr) + base;
+    const uint16_t* vrp = static_cast<const uint16_t*>(a.vr) + base;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + base;
+
+    const int r0 = D >= 16 ? 16 * rgroup : 0;
+    const int R = D >= 16 ? min(16, D - r0) : D;      // residues in the block
+    const int i0 = kAttnRowsB * iblock;               // first row
+    const int npieces = D >= 16 ? 16 : D;
+
+    // exchange area: slot = (residue - r0) * 16 + (row - i0)
+    float* xacc = reinterpret_cast<float*>(smem);
+    float* xm = xacc + 256 * DK;
+    float* xl = xm + 256;
+    lds_char* vt = smem + wv * (32 * G::ROWB);         // this wave's V tile
+
+    // ---- local phase: piece wv = contiguous positions [P, P + n)
+    Frag<DK> f;
+    f.reset();
+    int P = 0, n = 0;
+    if (wv < npieces) {
+        P = D >= 16 ? r0 + (i0 + wv) * D : i0 * D + 16 * wv;
+        const int len = D >= 16 ? R : 16;
+        n = P < T ? min(len, T - P) : 0;
+    }
+    const int tq = P + i;                               // this lane's query
+    const bool lvalid = i < n;
+    if (n > 0) {
+        f.load_q(qp + (size_t)tq * pitch, lvalid);
+        const int u0 = max(0, P - W + 1);
+        const int nk = P + n - u0;
+        stream_keys<DK>(f, krp, vrp, (size_t)pitch, u0, 1, nk, vt, a.scale_log2,
+                        [&](int j) { const int u = u0 + j; return lvalid && u <= tq && tq - u < W; });
+    }
+    const float lt = f.total_l();
+    __syncthreads();  // V tiles retired; the area becomes the exchange buffer
+    if (n > 0 && lvalid) {
+        const int slot = ((tq % D) - r0) * 16 + (tq / D - i0);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+            *reinterpret_cast<floatx4*>(xacc + slot * DK + 16 * db + 4 * g) = f.acc[db];
+        if (g == 0) {
+            xm[slot] = f.m;
+            xl[slot] = lt;
+        }
+    }
+    __syncthreads();
+
+    // ---- dilated phase: residue r0 + wv, rows i0 .. i0+15, seeded by the local partials
+    const int r = r0 + wv;
+    const int M = r < D && r < T ? (T - r + D - 1) / D : 0;
+    const int row = i0 + i;
+    const bool dvalid = wv < R && row < M;
+    Frag<DK> fd;
+    fd.reset();
+    if (dvalid) {
+        const int slot = wv * 16 + i;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+            fd.acc[db] = *reinterpret_cast<const floatx4*>(xacc + slot * DK + 16 * db + 4 * g);
+        fd.m = xm[slot];
+        fd.l = g == 0 ? xl[slot] : 0.f;
+    }
+    __syncthreads();  // exchange read; the area returns to V tiles
+    if (wv < R && i0 < M) {
+        fd.load_q(qp + (size_t)(r + row * D) * pitch, dvalid);
+        const int nk = min(i0 + 16, M);
+        stream_keys<DK>(fd, ksp, vsp, (size_t)pitch, r, D, nk, vt, a.scale_log2,
+                        [&](int j) { return dvalid && j <= row; });
+        fd.store(op + (size_t)(r + row * D) * pitch, dvalid);
+    }
+}
+
+// ------------------------------------------------------------------ kernel
+template <int DK>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_prefill_kernel(AttnArgs a)
+{
+    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+    lds_char* smem = smem_raw;
+    const int blk = blockIdx.x;
+    int c = 0;
+    while (c + 1 < a.nclass && blk >= a.cls[c + 1].block_begin) ++c;
+    const AttnClass& k = a.cls[c];
+    const int local = blk - k.block_begin;
+    const int level = k.levels - 1 - local / k.per_level;  // most expensive first
+    int idx = local % k.per_level;
+    if (k.path == kPathA) {
+        const int r = idx % k.D;
+        idx /= k.D;
+        const int h = a.heads[k.head_off + idx % k.nheads];
+        const int b = idx / k.nheads;
+        path_a<DK>(a, b, h, k.D, r, level, smem);
+    } else {
+        const int ngroups = k.D >= 16 ? (k.D + 15) / 16 : 1;
+        const int rg = idx % ngroups;
+        idx /= ngroups;
+        const int h = a.heads[k.head_off + idx % k.nheads];
+        const int b = idx / k.nheads;
+        path_b<DK>(a, b, h, k.D, k.W, rg, level, smem);
+    }
+}
+
+size_t attn_lds_bytes(int d)
+{
+    const size_t ring = 4 * 2 * 64 * (size_t)d * 2;           // path A
+    const size_t vt = kAttnWaves * 32 * (size_t)d * 2;         // path B V tiles
+    const size_t xch = 256 * (size_t)d * 4 + 2 * 256 * 4;      // path B exchange
+    size_t m = ring > vt ? ring : vt;
+    return m > xch ? m : xch;
+}
+
+hipError_t launch_attn_prefill_bf16(const AttnArgs& a, int d, hipStream_t stream)
+{
+    const size_t lds = attn_lds_bytes(d);
+    if (d == 128) {
+        static bool attr = false;
+        if (!attr) {
+            (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            attr = true;
+        }
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+    } else {
+        static bool attr = false;
+        if (!attr) {
+            (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            attr = true;
+        }
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fp32
+// One workgroup (one wave) per query row; lanes split the head dimension.
+// Exact fp32 FMA dot products and expf; meant for small fp32 problems.
+__global__ __launch_bounds__(kWave) void attn_prefill_f32_kernel(AttnF32Args a)
+{
+    const int lane = threadIdx.x;
+    const int t = blockIdx.x % a.T;
+    const int bh = blockIdx.x / a.T;
+    const int h = bh % a.H, b = bh / a.H;
+    const int d = a.d, D = a.D[h], W = a.W[h];
+    const size_t pitch = (size_t)a.H * d;
+    const size_t base = ((size_t)b * a.T * a.H + h) * d;
+    const float q0 = lane < d ? a.q[base + t * pitch + lane] : 0.f;
+    const float q1 = lane + kWave < d ? a.q[base + t * pitch + lane + kWave] : 0.f;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    auto visit = [&](const float* kbase, const float* vbase, int s) {
+        const float* kr = kbase + base + s * pitch;
+        float dot = (lane < d ? q0 * kr[lane] : 0.f) + (lane + kWave < d ? q1 * kr[lane + kWave] : 0.f);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+        const float z = dot * a.scale;
+        const float mn = fmaxf(m, z);
+        const float al = expf(m - mn), p = expf(z - mn);
+        const float* vr = vbase + base + s * pitch;
+        o0 = o0 * al + p * (lane < d ? vr[lane] : 0.f);
+        o1 = o1 * al + p * (lane + kWave < d ? vr[lane + kWave] : 0.f);
+        l = l * al + p;
+        m = mn;
+    };
+    for (int s = t; s >= 0; s -= D) visit(a.ks, a.vs, s);
+    for (int w = 0; w < W && t - w >= 0; ++w) visit(a.kr, a.vr, t - w);
+    if (lane < d) a.out[base + t * pitch + lane] = o0 / l;
+    if (lane + kWave < d) a.out[base + t * pitch + lane + kWave] = o1 / l;
+}
+
+hipError_t launch_attn_prefill_f32(const AttnF32Args& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(attn_prefill_f32_kernel, dim3((unsigned)(a.B * a.H * a.T)), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace rat

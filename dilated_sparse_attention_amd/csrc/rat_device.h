@@ -1,0 +1,58 @@
+// Device-side helpers shared by the RAT+ kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rat {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 <-> fp32.  bf16 -> fp32 is exact (a shift); fp32 -> bf16 rounds to
+// nearest even in hardware (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Forget gate and its complement for a logit l: g = 1/(1+e^-l), 1-g = 1/(1+e^l),
+// with one exp2 and one reciprocal.  Working from e = e^-|l| in [0, 1] keeps
+// both outputs free of cancellation and exact at l = +-inf ((1,0) / (0,1)).
+__device__ __forceinline__ void forget_gate(float logit, float& g, float& gbar)
+{
+    const float e = __builtin_amdgcn_exp2f(-fabsf(logit) * kLog2e);
+    const float s = __builtin_amdgcn_rcpf(1.0f + e);
+    const float es = e * s;
+    const bool pos = logit >= 0.0f;
+    g = pos ? s : es;
+    gbar = pos ? es : s;
+}
+
+// Relaxed agent-scope atomics: each 64-bit word carries (value bits, tag) and
+// validates itself, so no fence is needed between producer and consumer.
+__device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag)
+{
+    uint32_t bits = __float_as_uint(v);
+    if ((bits & 0x7fffffffu) > 0x7f800000u) bits = 0x7fc00000u;  // canonical NaN
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool load_tagged(const uint64_t* p, uint32_t tag, float& v)
+{
+    uint64_t w = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = __uint_as_float((uint32_t)w);
+    return (uint32_t)(w >> 32) == tag;
+}
+
+}  // namespace rat

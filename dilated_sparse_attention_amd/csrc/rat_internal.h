@@ -1,0 +1,122 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rat {
+
+// ---------------------------------------------------------------- scan
+constexpr int kScanTplBf16 = 32;  // tokens per lane (bf16): chunk = 8 waves x 32
+constexpr int kScanTplF32 = 16;   // tokens per lane (fp32): chunk = 8 waves x 16
+constexpr int kScanBlockCh = 128; // channels per workgroup
+
+struct ScanHeader {
+    uint32_t ticket;  // next chunk ticket of the running call
+    uint32_t done;    // workgroups finished in the running call
+    uint32_t epoch;   // calls completed on this workspace (tags = epoch + 1)
+    uint32_t pad[61];
+};
+
+struct ScanFullArgs {
+    const void* k;
+    const void* v;
+    const void* g;
+    void* ks;
+    void* vs;
+    int T, N;      // tokens; channels per token (H*d)
+    int nblk;      // 128-channel blocks per token row
+    int nseq;      // B * nblk
+    int nchunk;    // chunks along T
+    int L;         // RESTART period, 0 for none
+    int nwg;       // nchunk * nseq
+    uint64_t* agg;   // [nchunk*nseq][3][128] tagged words
+    uint64_t* incl;  // [nchunk*nseq][2][128] tagged words
+    ScanHeader* hdr;
+};
+
+struct ScanSlideArgs {
+    const void* k;
+    const void* v;
+    const void* g;
+    void* ks;
+    void* vs;
+    int B, T, N, L, tiles_per_span;
+};
+
+hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+constexpr int kAttnMaxClasses = 8;
+constexpr int kAttnMaxHeads = 256;
+constexpr int kAttnWaves = 16;
+constexpr int kAttnRowsA = 256;   // query rows of one residue per path-A item
+constexpr int kAttnRowsB = 16;    // rows per residue in a path-B block
+
+enum { kPathA = 0, kPathB = 1 };
+
+struct AttnClass {
+    int D, W;
+    int path;        // kPathA (W == 0) or kPathB (W > 0)
+    int nheads;      // heads in this class
+    int head_off;    // first entry in AttnArgs::heads
+    int levels;      // cost levels (dispatched most expensive first)
+    int per_level;   // items per level
+    int block_begin; // first blockIdx.x of the class
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* ks;
+    const void* vs;
+    const void* kr;
+    const void* vr;
+    void* out;
+    int B, T, H;
+    float scale_log2;  // softmax scale * log2(e)
+    int nclass;
+    int nblocks;
+    AttnClass cls[kAttnMaxClasses];
+    int16_t heads[kAttnMaxHeads];
+};
+
+size_t attn_lds_bytes(int d);
+hipError_t launch_attn_prefill_bf16(const AttnArgs& a, int d, hipStream_t stream);
+
+// Simple fp32 path (one workgroup per query row; exact fp32 arithmetic).
+struct AttnF32Args {
+    const float* q;
+    const float* ks;
+    const float* vs;
+    const float* kr;
+    const float* vr;
+    float* out;
+    int B, T, H, d;
+    float scale;
+    const int* dummy;
+    int D[kAttnMaxHeads];
+    int W[kAttnMaxHeads];
+};
+hipError_t launch_attn_prefill_f32(const AttnF32Args& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+constexpr int kDecWaves = 4;
+
+struct DecodeArgs {
+    const void* q;
+    const void* kd;
+    const void* vd;
+    const void* kw;
+    const void* vw;
+    void* out;
+    float* part;     // split partials [B*H][nsplit][d + 2] (NULL when nsplit == 1)
+    int B, H, T, nd_cap, w_cap;
+    int nsplit;      // key-range splits per (b, h)
+    float scale_log2;
+    int D[kAttnMaxHeads];
+    int W[kAttnMaxHeads];
+};
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
+
+}  // namespace rat

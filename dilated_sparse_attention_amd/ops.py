@@ -1,0 +1,202 @@
+"""Python binding of the RAT+ C ABI (``include/rat.h``) on torch tensors.
+
+Argument marshalling only: every step runs in the HIP library ``librat.so``
+that sits next to this file.  There is no CPU fallback; if the library is
+missing or no GPU is present the calls raise.  Tensors must be contiguous
+CUDA (ROCm) tensors; work is enqueued on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "librat.so")
+
+RESTART = 0
+SLIDING = 1
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPPORTED",
+          4: "RAT_ERR_ALIAS", 5: "RAT_ERR_WORKSPACE", 6: "RAT_ERR_HIP", 7: "RAT_ERR_ALIGN"}
+
+# every symbol include/rat.h declares
+EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
+           "rat_decode_workspace_bytes", "rat_dilated_attn_decode", "rat_status_string",
+           "rat_last_hip_error")
+
+
+class RatError(RuntimeError):
+    def __init__(self, fn, code, lib):
+        msg = lib.rat_status_string(code).decode()
+        extra = ""
+        if code == 6:
+            extra = f" (hipError {lib.rat_last_hip_error()})"
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}: {msg}{extra}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIBRARY):
+    """Load librat.so and declare the C signatures (raises if absent)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m dilated_sparse_attention_amd.build` "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(path)
+    vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.rat_scan_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.rat_scan_workspace_bytes.restype = sz
+    lib.rat_scan_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.rat_scan_prefill.restype = i
+    lib.rat_dilated_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ip, ip, f, i, vp]
+    lib.rat_dilated_attn_prefill.restype = i
+    lib.rat_decode_workspace_bytes.argtypes = [i, i, i, i, ip, ip]
+    lib.rat_decode_workspace_bytes.restype = sz
+    lib.rat_dilated_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
+    lib.rat_dilated_attn_decode.restype = i
+    lib.rat_status_string.argtypes = [i]
+    lib.rat_status_string.restype = ctypes.c_char_p
+    lib.rat_last_hip_error.argtypes = []
+    lib.rat_last_hip_error.restype = i
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _heads(x, H):
+    vals = list(x) if hasattr(x, "__len__") else [int(x)] * H
+    if len(vals) != H:
+        raise ValueError(f"expected {H} per-head values, got {len(vals)}")
+    return (ctypes.c_int * H)(*[int(v) for v in vals])
+
+
+def _check_tensor(name, t, dtype, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn, rc, lib):
+    if rc != 0:
+        raise RatError(fn, rc, lib)
+
+
+# ------------------------------------------------------------------ scan
+def scan_workspace_bytes(B, T, H, d, L, mode=RESTART, dtype=torch.bfloat16):
+    return int(load_library().rat_scan_workspace_bytes(B, T, H, d, L, mode, _DTYPES[dtype]))
+
+
+_workspaces = {}
+
+
+def scan_workspace(nbytes, device):
+    """A zero-filled scan workspace of at least ``nbytes`` on ``device``,
+    kept per device and reused (the library keeps it consistent itself)."""
+    key = torch.device(device).index
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def scan_prefill(k, v, gate_logits, L=None, mode=RESTART, k_state=None, v_state=None, workspace=None):
+    """Recurrent states (k_state, v_state) of [B,T,H,d] keys / values with
+    forget-gate logits ``gate_logits`` (L defaults to T: full recurrence)."""
+    lib = load_library()
+    B, T, H, d = k.shape
+    L = T if L is None else int(L)
+    for name, t in (("k", k), ("v", v), ("gate_logits", gate_logits)):
+        _check_tensor(name, t, k.dtype, k.shape)
+    k_state = torch.empty_like(k) if k_state is None else k_state
+    v_state = torch.empty_like(v) if v_state is None else v_state
+    _check_tensor("k_state", k_state, k.dtype, k.shape)
+    _check_tensor("v_state", v_state, k.dtype, k.shape)
+    nbytes = lib.rat_scan_workspace_bytes(B, T, H, d, L, mode, _DTYPES[k.dtype])
+    if workspace is None and nbytes:
+        workspace = scan_workspace(nbytes, k.device)
+    rc = lib.rat_scan_prefill(_ptr(k), _ptr(v), _ptr(gate_logits), _ptr(k_state), _ptr(v_state),
+                              B, T, H, d, L, mode, _DTYPES[k.dtype], _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), _stream())
+    _raise("rat_scan_prefill", rc, lib)
+    return k_state, v_state
+
+
+# ------------------------------------------------------------------ attention
+def dilated_attn_prefill(q, k_state, v_state, k_raw=None, v_raw=None, D=1, W=0, scale=None, out=None):
+    """Dilated (+ local window) causal attention over the recurrent states."""
+    lib = load_library()
+    B, T, H, d = q.shape
+    for name, t in (("q", q), ("k_state", k_state), ("v_state", v_state), ("k_raw", k_raw), ("v_raw", v_raw)):
+        _check_tensor(name, t, q.dtype, q.shape)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib.rat_dilated_attn_prefill(_ptr(q), _ptr(k_state), _ptr(v_state), _ptr(k_raw), _ptr(v_raw),
+                                      _ptr(out), B, T, H, d, _heads(D, H), _heads(W, H), scale,
+                                      _DTYPES[q.dtype], _stream())
+    _raise("rat_dilated_attn_prefill", rc, lib)
+    return out
+
+
+def decode_workspace_bytes(B, H, d, T, D, W):
+    return int(load_library().rat_decode_workspace_bytes(B, H, d, T, _heads(D, H), _heads(W, H)))
+
+
+def dilated_attn_decode(q, kd, vd, kw, vw, T, D, W, scale=None, out=None, workspace=None):
+    """Decode attention of the query at position T-1 over the dilated cache
+    (kd, vd: [B,H,nd_cap,d]) and the raw ring (kw, vw: [B,H,w_cap,d])."""
+    lib = load_library()
+    B, H, d = q.shape
+    _check_tensor("q", q, q.dtype)
+    _check_tensor("kd", kd, q.dtype)
+    _check_tensor("vd", vd, q.dtype, kd.shape)
+    _check_tensor("kw", kw, q.dtype)
+    _check_tensor("vw", vw, q.dtype, None if kw is None else kw.shape)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    nbytes = lib.rat_decode_workspace_bytes(B, H, d, int(T), Dh, Wh)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    w_cap = 0 if kw is None else kw.shape[2]
+    rc = lib.rat_dilated_attn_decode(_ptr(q), _ptr(kd), _ptr(vd), kd.shape[2], _ptr(kw), _ptr(vw), w_cap,
+                                     _ptr(out), B, int(T), H, d, Dh, Wh, scale, _DTYPES[q.dtype],
+                                     _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                     _stream())
+    _raise("rat_dilated_attn_decode", rc, lib)
+    return out
+
+
+def rat_layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None):
+    """The whole prefill hot path: recurrence, then dilated attention."""
+    ks, vs = scan_prefill(k, v, gate_logits, L=L, mode=mode)
+    need_raw = any(int(w) > 0 for w in (W if hasattr(W, "__len__") else [W]))
+    return dilated_attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None,
+                                D=D, W=W, scale=scale)

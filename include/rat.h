@@ -1,0 +1,140 @@
+/*
+ * rat.h -- C ABI of the RAT+ layer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The RAT+ layer ("RAT+: Train Dense, Infer Sparse -- Recurrence Augmented
+ * Attention for Dilated Inference", arXiv 2602.18196, Abstract; "RAT+ Deep
+ * Dive: A New KV Cache Compression Paradigm with Dense Pretraining and
+ * Dilated Inference", zhichai.net, sections 1, 2.1 and 6) has two stages:
+ *
+ *   1. a gated linear recurrence over keys and values,
+ *        h_t = g_t * h_{t-1} + (1 - g_t) * x_t,   g_t = sigmoid(logit_t),
+ *      computed for prefill as a parallel scan (Deep Dive 2.1, 7.3), over
+ *      the whole sequence or a recurrence window of L tokens;
+ *   2. causal dilated softmax attention: the query at position t attends to
+ *      the recurrent states at t, t-D, t-2D, ... and, optionally, to the raw
+ *      keys/values of the last W tokens (RAT+ Abstract: "dilated attention
+ *      (optionally with local windows)"), with a per-head (D, W) so that
+ *      dense and dilated heads mix in one layer (Deep Dive 6, Head-Wise
+ *      Hybrid).  Decode reads a KV cache that is D times smaller (Abstract).
+ *
+ * Common conventions
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *    library never allocates or frees device memory and keeps no pointer
+ *    after a call returns.  Host arrays (D, W) are read during the call only.
+ *  - Prefill tensors are [B, T, H, d] contiguous (d fastest).  Decode query
+ *    and output are [B, H, d]; decode caches are [B, H, N, d].
+ *  - dtype: RAT_DTYPE_F32 (float) or RAT_DTYPE_BF16 (bfloat16, round to
+ *    nearest even on output).  All arithmetic is fp32.
+ *  - Supported head size d: 64 or 128.  Every pointer must be 16-byte
+ *    aligned.  B*T*H*d (and B*H*N*d for caches) must be below 2^31.
+ *  - Every call only enqueues work on `stream` (a hipStream_t, may be NULL
+ *    for the default stream) and returns without synchronising.
+ *  - All validation happens on the host before any HIP call: on an error
+ *    nothing is enqueued and no output is touched.  RAT_ERR_HIP reports a
+ *    failed launch (outputs undefined); rat_last_hip_error() then returns
+ *    the hipError_t of the calling thread's last failure.
+ *  - No call prints, aborts or throws.  Calls are re-entrant; concurrent
+ *    calls must not share a workspace.
+ */
+#ifndef RAT_H
+#define RAT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RAT_DTYPE_F32 = 0, RAT_DTYPE_BF16 = 1 } rat_dtype;
+
+/* Meaning of a recurrence window L < T (Deep Dive 2.1 gives a fixed window of
+ * L* = 64 tokens "looking back" from the current one; the layer is also
+ * described as restarting every L* tokens).  Both readings are offered:
+ *   RESTART: the state is cleared at every position t with t mod L == 0;
+ *   SLIDING: h_t sums exactly the last L inputs (requires L <= 64).
+ * With L >= T both modes are the full-sequence recurrence (Deep Dive 2.1). */
+typedef enum { RAT_RECUR_RESTART = 0, RAT_RECUR_SLIDING = 1 } rat_recur_mode;
+
+typedef enum {
+    RAT_OK = 0,
+    RAT_ERR_NULL = 1,        /* a required pointer is NULL */
+    RAT_ERR_SHAPE = 2,       /* a size or per-head parameter is out of range */
+    RAT_ERR_UNSUPPORTED = 3, /* valid but not implemented (d, dtype, L, sizes) */
+    RAT_ERR_ALIAS = 4,       /* an output aliases an input */
+    RAT_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
+    RAT_ERR_HIP = 6,         /* a HIP launch failed */
+    RAT_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
+} rat_status;
+
+/* Bytes of device workspace rat_scan_prefill needs for these sizes (0 when
+ * none).  The workspace carries the cross-workgroup carries of the parallel
+ * scan; it must be 256-byte aligned and ZERO-FILLED BEFORE ITS FIRST USE,
+ * after which the library keeps it consistent by itself (it is reusable by
+ * later scan calls of any size up to its capacity, one stream at a time). */
+size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L,
+                                rat_recur_mode mode, rat_dtype dtype);
+
+/* Stage 1 (Deep Dive 2.1): recurrent key and value states.
+ *   k, v, gate_logits : [B,T,H,d] inputs; the forget gate is
+ *                       g = sigmoid(gate_logits), elementwise, shared by
+ *                       keys and values; logits of +-inf are allowed.
+ *   k_state, v_state  : [B,T,H,d] outputs,
+ *                       k_state[t] = g_t*k_state[t-1] + (1-g_t)*k[t], state
+ *                       zero before t = 0 (and at RESTART boundaries).
+ *   L                 : recurrence window, >= 1; L >= T means full sequence.
+ * Errors: RAT_ERR_NULL, _SHAPE (B,T,H,d,L < 1), _UNSUPPORTED (d, dtype,
+ * SLIDING with 64 < L < T, sizes), _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
+int rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
+                     void* k_state, void* v_state,
+                     int B, int T, int H, int d, int L, rat_recur_mode mode,
+                     rat_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Stage 2, prefill (RAT+ Abstract; Deep Dive 1 and 6): for every query
+ * (b, t, h) one softmax over
+ *   the recurrent states  k_state/v_state at t, t-D[h], t-2D[h], ... >= 0,
+ *   then the raw tokens   k_raw/v_raw     at t, t-1, ..., t-W[h]+1 >= 0,
+ * with logits scale * <q, key>; out = sum softmax * value.
+ *   q, k_state, v_state, k_raw, v_raw, out : [B,T,H,d];
+ *   k_raw / v_raw may be NULL iff every W[h] == 0;
+ *   D, W : host int[H], D[h] >= 1, W[h] >= 0 (D[h] = 1, W[h] = 0 is dense
+ *          causal attention over the states).
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
+int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state,
+                             const void* k_raw, const void* v_raw, void* out,
+                             int B, int T, int H, int d, const int* D, const int* W,
+                             float scale, rat_dtype dtype, void* stream);
+
+/* Bytes of device workspace rat_dilated_attn_decode needs (0 when none; it
+ * holds split-key partial softmax states when B*H is small). 256-byte
+ * aligned; no initialisation needed. */
+size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, const int* W);
+
+/* Stage 2, decode (RAT+ Abstract: the KV cache holds T/D states per head):
+ * one new query per sequence at position T-1 of a T-token context.
+ *   q, out   : [B,H,d];
+ *   kd, vd   : [B,H,nd_cap,d] dilated cache of head h, entry i = recurrent
+ *              state at position ((T-1) mod D[h]) + i*D[h], for
+ *              i = 0 .. ceil(T/D[h])-1 (the last entry is the query's own
+ *              state); nd_cap >= ceil(T/D[h]) for every h;
+ *   kw, vw   : [B,H,w_cap,d] raw ring of the last min(W[h], T) tokens in
+ *              slots 0 .. min(W[h],T)-1, in any order; may be NULL iff every
+ *              W[h] == 0; w_cap >= min(W[h], T).
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
+int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap,
+                            const void* kw, const void* vw, int w_cap, void* out,
+                            int B, int T, int H, int d, const int* D, const int* W,
+                            float scale, rat_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* rat_status_string(int status);
+
+/* hipError_t of the calling thread's last RAT_ERR_HIP (0 if none). */
+int rat_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAT_H */

@@ -1,0 +1,141 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol
+``include/rat.h`` declares, sizes workspaces, and rejects invalid arguments
+with the documented status codes before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dilated_sparse_attention_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rat.h")
+
+OK, NULL, SHAPE, UNSUP, ALIAS, WSPACE, HIP, ALIGN = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIBRARY):
+        from dilated_sparse_attention_amd import build
+        build.build()
+    return ops.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rat_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(ops.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.rat_status_string(code)
+    assert lib.rat_status_string(99) == b"unknown status"
+    assert lib.rat_last_hip_error() == 0
+
+
+# fake, 256-byte aligned "device" addresses: validation must reject every
+# case below before any of them is dereferenced or handed to HIP
+P = [ctypes.c_void_p(0x10000 + 0x100000 * i) for i in range(8)]
+MIS = ctypes.c_void_p(0x10008)
+
+
+def heads(vals):
+    return (ctypes.c_int * len(vals))(*vals)
+
+
+def scan(lib, k=P[0], v=P[1], g=P[2], ks=P[3], vs=P[4], B=1, T=64, H=2, d=64, L=64, mode=0, dtype=1,
+         ws=P[5], wsb=1 << 30):
+    return lib.rat_scan_prefill(k, v, g, ks, vs, B, T, H, d, L, mode, dtype, ws, wsb, None)
+
+
+def test_scan_validation(lib):
+    assert scan(lib, k=None) == NULL
+    assert scan(lib, vs=None) == NULL
+    assert scan(lib, B=0) == SHAPE
+    assert scan(lib, T=-1) == SHAPE
+    assert scan(lib, L=0) == SHAPE
+    assert scan(lib, mode=7) == SHAPE
+    assert scan(lib, d=96) == UNSUP
+    assert scan(lib, dtype=5) == UNSUP
+    assert scan(lib, B=1 << 10, T=1 << 12, H=64, d=128) == UNSUP  # >= 2^31 elements
+    assert scan(lib, T=1000, L=100, mode=1) == UNSUP  # SLIDING window above 64
+    assert scan(lib, ks=P[0]) == ALIAS
+    assert scan(lib, vs=P[3]) == ALIAS
+    assert scan(lib, k=MIS) == ALIGN
+    assert scan(lib, ws=None) == WSPACE
+    assert scan(lib, wsb=16) == WSPACE
+    assert scan(lib, ws=ctypes.c_void_p(0x10040)) == WSPACE  # not 256-byte aligned
+
+
+def test_scan_workspace_sizes(lib):
+    # full and RESTART need a workspace; a SLIDING window needs none
+    assert lib.rat_scan_workspace_bytes(4, 4096, 16, 128, 4096, 0, 1) > 0
+    assert lib.rat_scan_workspace_bytes(1, 16384, 16, 128, 64, 0, 1) > 0
+    assert lib.rat_scan_workspace_bytes(1, 16384, 16, 128, 64, 1, 1) == 0
+    assert lib.rat_scan_workspace_bytes(1, 100, 2, 64, 1000, 1, 1) > 0  # L >= T: full
+    assert lib.rat_scan_workspace_bytes(0, 100, 2, 64, 100, 0, 1) == 0
+    small = lib.rat_scan_workspace_bytes(1, 256, 2, 64, 256, 0, 1)
+    big = lib.rat_scan_workspace_bytes(2, 4096, 2, 64, 4096, 0, 1)
+    assert 256 <= small < big
+
+
+def attn(lib, q=P[0], ks=P[1], vs=P[2], kr=P[3], vr=P[4], out=P[5], B=1, T=64, H=2, d=128,
+         D=(4, 4), W=(0, 8), scale=0.1, dtype=1):
+    Dh = None if D is None else heads(D)
+    Wh = None if W is None else heads(W)
+    return lib.rat_dilated_attn_prefill(q, ks, vs, kr, vr, out, B, T, H, d, Dh, Wh, scale, dtype, None)
+
+
+def test_attn_validation(lib):
+    assert attn(lib, q=None) == NULL
+    assert attn(lib, out=None) == NULL
+    assert attn(lib, kr=None) == NULL  # head 1 has a window
+    assert attn(lib, D=None) == NULL
+    assert attn(lib, T=0) == SHAPE
+    assert attn(lib, D=(0, 4)) == SHAPE
+    assert attn(lib, W=(0, -1)) == SHAPE
+    assert attn(lib, d=32) == UNSUP
+    assert attn(lib, dtype=3) == UNSUP
+    assert attn(lib, scale=float("nan")) == SHAPE
+    assert attn(lib, out=P[1]) == ALIAS
+    assert attn(lib, out=P[3]) == ALIAS
+    assert attn(lib, vs=MIS) == ALIGN
+    H = 300
+    assert attn(lib, H=H, D=[1] * H, W=[0] * H) == UNSUP  # more heads than the kernel table
+    many = [(i % 9) + 1 for i in range(16)]
+    assert attn(lib, H=16, D=many, W=[0] * 16) == UNSUP  # more than 8 (D, W) classes
+
+
+def decode(lib, q=P[0], kd=P[1], vd=P[2], nd_cap=512, kw=P[3], vw=P[4], w_cap=64, out=P[5], B=4, T=32768,
+           H=2, d=128, D=(64, 64), W=(64, 64), scale=0.1, dtype=1, ws=P[6], wsb=1 << 30):
+    return lib.rat_dilated_attn_decode(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, heads(D), heads(W),
+                                       scale, dtype, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q=None) == NULL
+    assert decode(lib, kw=None) == NULL
+    assert decode(lib, T=0) == SHAPE
+    assert decode(lib, nd_cap=511) == SHAPE  # ceil(32768 / 64) = 512 entries needed
+    assert decode(lib, w_cap=63) == SHAPE
+    assert decode(lib, D=(64, 0)) == SHAPE
+    assert decode(lib, d=256) == UNSUP
+    assert decode(lib, out=P[2]) == ALIAS
+    assert decode(lib, kd=MIS) == ALIGN
+    # one long head, few pairs: split-key partials need a workspace
+    need = lib.rat_decode_workspace_bytes(1, 1, 128, 1 << 20, heads([1]), heads([0]))
+    assert need > 0
+    assert decode(lib, B=1, H=1, T=1 << 20, D=(1,), W=(0,), nd_cap=1 << 20, w_cap=0, ws=None) == WSPACE
+    assert lib.rat_decode_workspace_bytes(64, 20, 128, 32768, heads([64] * 20), heads([64] * 20)) == 0
