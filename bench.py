@@ -1,0 +1,359 @@
+"""Benchmark of the RAT+ layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+
+A step is one pass of the prefill hot path -- the gated recurrence (scan)
+then dilated attention -- over one batch of the 1.5B-scale layer workload
+(B=4, T=4096, H=16, d=128, D=16, full recurrence, bf16), with inputs already
+resident in HBM.  Three input/output sets rotate so that consecutive steps
+do not find their data in the 256 MB Infinity Cache.  ``value`` is prefill
+tokens per second per layer, B*T / step time.
+
+Per-kernel durations come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream).  The JSON line also
+carries the roofline of the dominant kernel, the oracle timed on the host
+cores on a bounded sample (``cpu_baseline``) and, under ``extra``, the other
+workloads: long prefill with a window (both recurrence readings), the 7.6B
+hybrid prefill and the 2.6B decode at D = 64 and D = 16.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default=None, help="run one workload of --list by name (profiling)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+def progress(*parts):
+    print("[bench]", *parts, file=sys.stderr, flush=True)
+
+
+def kernel_sources_hash():
+    """Hash of the HIP sources: profiles record it so that stale counter
+    readings are not reported for a changed kernel."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dilated_sparse_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it is absent or was taken from other kernel sources."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("sources_hash") != kernel_sources_hash():
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+class Timer:
+    """Events around the launches of each kernel on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def mark(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        out = fn()
+        ev1.record()
+        self.pairs.setdefault(name, []).append((ev0, ev1))
+        return out
+
+    def mean_ms(self, name):
+        return sum(a.elapsed_time(b) for a, b in self.pairs[name]) / len(self.pairs[name])
+
+
+def attn_pairs(T, D, W):
+    """(dilated pairs, local pairs) of one head: closed forms of the index-set
+    sizes summed over the T queries."""
+    M = [(T - r + D - 1) // D for r in range(min(D, T))]
+    dil = sum(m * (m + 1) // 2 for m in M)
+    loc = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+    return dil, loc
+
+
+# ------------------------------------------------------------------ workloads
+def prefill_units(w):
+    """Algorithmic bytes / FLOPs of the scan and of the attention."""
+    E = w.B * w.T * w.H * w.d
+    s = 2 if "bfloat16" in str(w.dtype) else 4
+    scan_bytes = 5 * E * s
+    raw_heads = sum(1 for x in w.W if x > 0)
+    attn_bytes = 4 * E * s + 2 * (E // w.H) * raw_heads * s
+    pairs = 0
+    for Dh, Wh in zip(w.D, w.W):
+        a, b = attn_pairs(w.T, Dh, Wh)
+        pairs += a + b
+    attn_flops = 4 * w.d * pairs * w.B
+    return scan_bytes, attn_bytes, attn_flops
+
+
+def run_prefill(torch, rat, w, steps, warmup, mode=0, nsets=3):
+    from dilated_sparse_attention_amd import inputs
+
+    need_raw = any(x > 0 for x in w.W)
+    sets = []
+    for i in range(nsets):
+        x = inputs.make_prefill(w, seed=i, device="cuda")
+        ks = torch.empty_like(x["k"])
+        vs = torch.empty_like(x["v"])
+        out = torch.empty_like(x["q"])
+        sets.append((x, ks, vs, out))
+    D, W = list(w.D), list(w.W)
+
+    def step(i, timer=None):
+        x, ks, vs, out = sets[i % nsets]
+        scan = lambda: rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)  # noqa: E731
+        attn = lambda: rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None,  # noqa: E731
+                                                x["v"] if need_raw else None, D=D, W=W, out=out)
+        if timer is None:
+            scan()
+            attn()
+        else:
+            timer.mark("scan", scan)
+            timer.mark("attn", attn)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / steps
+    # per-kernel durations in a second timed pass (events between launches)
+    timer = Timer(torch)
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    scan_ms, attn_ms = timer.mean_ms("scan"), timer.mean_ms("attn")
+    del sets
+    torch.cuda.empty_cache()
+    return ms_step, wall, scan_ms, attn_ms
+
+
+def run_decode(torch, rat, w, steps, warmup, nsets=3):
+    from dilated_sparse_attention_amd import inputs
+
+    sets = []
+    for i in range(nsets):
+        x = inputs.make_decode(w, seed=i, device="cuda")
+        x["out"] = torch.empty_like(x["q"])
+        sets.append(x)
+    D, W = list(w.D), list(w.W)
+    ws_bytes = rat.decode_workspace_bytes(w.B, w.H, w.d, w.T, D, W)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        x = sets[i % nsets]
+        rat.dilated_attn_decode(x["q"], x["kd"], x["vd"], x["kw"], x["vw"], w.T, D, W, out=x["out"],
+                                workspace=ws if ws_bytes else None)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for i in range(steps):
+        timer.mark("decode", lambda: call(i))
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("decode")
+    nd = [(w.T + Dh - 1) // Dh for Dh in w.D]
+    nw = [min(Wh, w.T) for Wh in w.W]
+    s = 2
+    nbytes = w.B * sum((a + b) * 2 * w.d * s for a, b in zip(nd, nw)) + 2 * w.B * w.H * w.d * s
+    del sets
+    torch.cuda.empty_cache()
+    return ms, nbytes
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w):
+    """The fp64 oracle on the host cores, on a bounded sample of the
+    headline workload: the scan over every token of the first 8 heads of
+    batch 0, and attention for 1/64 of the query rows of batch 0 (all heads),
+    scaled to whole-workload tokens/s per layer."""
+    import numpy as np
+    import torch
+
+    from dilated_sparse_attention_amd import inputs
+    from oracle import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    oracle.build(force=False)
+    x = inputs.make_prefill(w, seed=0, B=1)
+    hs = min(8, w.H)
+    k, v, g = (x[n][:, :, :hs].contiguous() for n in ("k", "v", "gate"))
+    t0 = time.perf_counter()
+    ks, vs = oracle.scan(k, v, g, w.L, 0)
+    t_scan = time.perf_counter() - t0
+    scan_frac = hs / (w.H * w.B)
+    full_ks, full_vs = oracle.scan(x["k"], x["v"], x["gate"], w.L, 0) if hs < w.H else (ks, vs)
+    rows = [(0, t, h) for t in range(w.T - 1, -1, -64) for h in range(w.H)]
+    t0 = time.perf_counter()
+    oracle.attn_prefill_rows(x["q"], full_ks, full_vs, None, None, rows, w.D, w.W, w.scale)
+    t_attn = time.perf_counter() - t0
+    # attention cost grows with the row's key count: scale by pairs
+    pair_sample = sum((t // w.D[h]) + 1 for (_, t, h) in rows)
+    pair_total = w.B * sum(attn_pairs(w.T, Dh, Wh)[0] for Dh, Wh in zip(w.D, w.W))
+    est = t_scan / scan_frac + t_attn * pair_total / pair_sample
+    tok_s = w.B * w.T / est
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
+            "kind": "oracle",
+            "sample": (f"fp64 oracle: scan of batch 0, heads 0-{hs - 1}, all {w.T} tokens "
+                       f"({t_scan:.2f} s); attention of {len(rows)} query rows (every 64th row of "
+                       f"batch 0, all heads; {t_attn:.2f} s); extrapolated to the whole workload by "
+                       f"channel count and by (query, key) pair count: {est:.1f} s per step")}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} is not supported "
+              "(the layer shards by (batch, head) with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dilated_sparse_attention_amd as rat
+    from dilated_sparse_attention_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rat.load_library()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    w = inputs.PREFILL_1P5B
+    if args.only is None or args.only == w.name:
+        progress("prefill", w.name)
+        ms, wall, scan_ms, attn_ms = run_prefill(torch, rat, w, args.steps, args.warmup)
+    else:
+        ms = wall = scan_ms = attn_ms = None
+    scan_bytes, attn_bytes, attn_flops = prefill_units(w)
+
+    extra = {}
+    if not args.no_extra:
+        for pw in (inputs.PREFILL_LONG, inputs.PREFILL_7P6B_HYBRID):
+            for mode in pw.modes:
+                key = pw.name + ("" if len(pw.modes) == 1 else ("_restart" if mode == 0 else "_sliding"))
+                if args.only is not None and args.only != key:
+                    continue
+                progress("prefill", key)
+                m2, _, s_ms, a_ms = run_prefill(torch, rat, pw, max(3, args.steps // 4), 2, mode=mode)
+                sb, ab, af = prefill_units(pw)
+                extra[key] = {
+                    "prefill_tokens_per_s": pw.B * pw.T / (m2 / 1e3), "ms_per_step": m2,
+                    "scan_ms": s_ms, "scan_GBps": sb / (s_ms / 1e3) / 1e9,
+                    "scan_hbm_frac": sb / (s_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "attn_ms": a_ms, "attn_GBps": ab / (a_ms / 1e3) / 1e9,
+                    "attn_TFLOPs": af / (a_ms / 1e3) / 1e12,
+                    "attn_mfma_frac": af / (a_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "attn_roofline_frac": (max(ab / HBM_PEAK_GBS / 1e9, af / MFMA_BF16_PEAK_TFLOPS / 1e12)
+                                           / (a_ms / 1e3)),
+                    "config": pw.describe(), "mode": "restart" if mode == 0 else "sliding"}
+        for dw in inputs.DECODE_WORKLOADS:
+            if args.only is not None and args.only != dw.name:
+                continue
+            progress("decode", dw.name)
+            dms, dbytes = run_decode(torch, rat, dw, max(5, args.steps), 3)
+            extra[dw.name] = {"decode_tokens_per_s": dw.B / (dms / 1e3), "decode_ms": dms,
+                              "GBps": dbytes / (dms / 1e3) / 1e9,
+                              "hbm_frac": dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                              "config": dw.describe()}
+
+    if ms is None:  # a profiling run of one extra workload
+        print(json.dumps({"extra": extra}))
+        return
+
+    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
+    attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9
+    if scan_ms >= attn_ms:
+        dom, dom_bytes, dom_ms, dom_kernel = "scan", scan_bytes, scan_ms, "scan_full_kernel"
+    else:
+        dom, dom_bytes, dom_ms, dom_kernel = "attn", attn_bytes, attn_ms, "attn_prefill_kernel"
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom_kernel),
+                "kernel": dom_kernel, "algorithmic_bytes_per_launch": dom_bytes,
+                "kernel_ms": round(dom_ms, 4)}
+    line = {
+        "metric": "prefill tokens/s per layer and decode tokens/s at D=16/64; % HBM / MFMA peak",
+        "value": w.B * w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": w.describe(),
+        "roofline": roofline,
+        "kernels": {
+            "scan_full_kernel": {"ms": scan_ms, "GBps": scan_gbs, "hbm_frac": scan_gbs / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": scan_bytes},
+            "attn_prefill_kernel": {"ms": attn_ms, "GBps": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS,
+                                    "TFLOPs": attn_flops / (attn_ms / 1e3) / 1e12,
+                                    "mfma_frac": attn_flops / (attn_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                    "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops},
+        },
+        "wall_s_timed": wall,
+        "sources_hash": kernel_sources_hash(),
+    }
+    if extra:
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        progress("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -53,7 +53,7 @@ ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
 {
     ScanPlan p;
     p.tpl = dtype == RAT_DTYPE_BF16 ? kScanTplBf16 : kScanTplF32;
-    p.chunk = 8 * p.tpl;
+    p.chunk = kScanWaves * p.tpl;
     const int N = H * d;
     p.nblk = (N + kScanBlockCh - 1) / kScanBlockCh;
     p.nseq = B * p.nblk;
@@ -64,6 +64,20 @@ ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
     p.incl_off = p.agg_off + slots * 3 * kScanBlockCh * sizeof(uint64_t);
     p.bytes = p.incl_off + slots * 2 * kScanBlockCh * sizeof(uint64_t);
     return p;
+}
+
+// compute units of the current device (cached per device)
+int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 bool scan_uses_workspace(int T, int L, rat_recur_mode mode)
@@ -188,9 +202,10 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         return hip_status(launch_attn_prefill_f32(a, s));
     }
 
-    // group heads by (D, W); each class becomes a range of blocks, classes
-    // with the longest single items first, each class's levels most
-    // expensive first
+    // group heads by (D, W); window-free classes go to the persistent
+    // dilated kernel (items = (b, h, r, 256-row chunk)), windowed classes to
+    // the 2-D block kernel; within each, classes with the longest single
+    // items come first and each class's levels most expensive first
     struct Cls { int D, W; std::vector<int> heads; double item_cost; };
     std::vector<Cls> cls;
     for (int h = 0; h < H; ++h) {
@@ -201,42 +216,51 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         }
         it->heads.push_back(h);
     }
-    if ((int)cls.size() > kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
-    AttnArgs a;
-    memset(&a, 0, sizeof(a));
-    a.q = q; a.ks = k_state; a.vs = v_state; a.kr = k_raw; a.vr = v_raw; a.out = out;
-    a.B = B; a.T = T; a.H = H;
-    a.scale_log2 = scale * 1.4426950408889634f;
     for (auto& c : cls) {
         const int Mmax = (T + c.D - 1) / c.D;
         if (c.W == 0) c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
         else c.item_cost = 256.0 * (std::min(Mmax, kAttnRowsB) + c.W + 16);
     }
     std::stable_sort(cls.begin(), cls.end(), [](const Cls& x, const Cls& y) { return x.item_cost > y.item_cost; });
-    int blocks = 0, hoff = 0;
-    a.nclass = (int)cls.size();
-    for (int ci = 0; ci < a.nclass; ++ci) {
-        const Cls& c = cls[ci];
-        AttnClass& k = a.cls[ci];
-        k.D = c.D; k.W = c.W; k.path = c.W == 0 ? kPathA : kPathB;
-        k.nheads = (int)c.heads.size(); k.head_off = hoff;
-        for (int hh : c.heads) a.heads[hoff++] = (int16_t)hh;
-        const int Mmax = (T + c.D - 1) / c.D;
-        if (k.path == kPathA) {
-            k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
-            k.per_level = B * k.nheads * c.D;
-        } else {
-            k.levels = (Mmax + kAttnRowsB - 1) / kAttnRowsB;
-            const int ngroups = c.D >= 16 ? (c.D + 15) / 16 : 1;
-            k.per_level = B * k.nheads * ngroups;
+
+    AttnArgs args[2];
+    for (int path = 0; path < 2; ++path) {
+        AttnArgs& a = args[path];
+        memset(&a, 0, sizeof(a));
+        a.q = q; a.ks = k_state; a.vs = v_state; a.kr = k_raw; a.vr = v_raw; a.out = out;
+        a.B = B; a.T = T; a.H = H;
+        a.scale_log2 = scale * 1.4426950408889634f;
+        int blocks = 0, hoff = 0;
+        for (const Cls& c : cls) {
+            if ((c.W == 0) != (path == kPathA)) continue;
+            if (a.nclass == kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
+            AttnClass& k = a.cls[a.nclass++];
+            k.D = c.D; k.W = c.W; k.path = path;
+            k.nheads = (int)c.heads.size(); k.head_off = hoff;
+            for (int hh : c.heads) a.heads[hoff++] = (int16_t)hh;
+            const int Mmax = (T + c.D - 1) / c.D;
+            if (path == kPathA) {
+                k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
+                k.per_level = B * k.nheads * c.D;
+            } else {
+                k.levels = (Mmax + kAttnRowsB - 1) / kAttnRowsB;
+                const int ngroups = c.D >= 16 ? (c.D + 15) / 16 : 1;
+                k.per_level = B * k.nheads * ngroups;
+            }
+            const int64_t nb = (int64_t)k.levels * k.per_level;
+            if (nb + blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
+            k.block_begin = blocks;
+            blocks += (int)nb;
         }
-        const int64_t nb = (int64_t)k.levels * k.per_level;
-        if (nb + blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
-        k.block_begin = blocks;
-        blocks += (int)nb;
+        a.nblocks = blocks;
     }
-    a.nblocks = blocks;
-    return hip_status(launch_attn_prefill_bf16(a, d, s));
+    if (args[kPathA].nblocks > 0) {
+        const int grid = std::min(args[kPathA].nblocks, device_cu_count());
+        const int rc = hip_status(launch_attn_dilated_bf16(args[kPathA], d, grid, s));
+        if (rc != RAT_OK) return rc;
+    }
+    if (args[kPathB].nblocks > 0) return hip_status(launch_attn_window_bf16(args[kPathB], d, s));
+    return RAT_OK;
 }
 
 namespace {

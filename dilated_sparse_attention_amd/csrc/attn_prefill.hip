@@ -16,14 +16,17 @@
 // statistics and the output O^T = V^T P^T stay per lane and P^T is the MFMA
 // B operand exactly as S^T leaves the accumulator.  V^T comes from a
 // row-major V tile in LDS through ds_read_b64_tr_b16.  LDS tiles are
-// XOR-swizzled in 16-byte chunks (chunk c of row r at c ^ (r mod 16)) so that
-// both the K-fragment reads and the transposing V reads avoid bank conflicts,
-// and are filled by direct global->LDS loads.
+// XOR-swizzled in 16-byte chunks so that both the K-fragment reads and the
+// transposing V reads avoid bank conflicts, and are filled by direct
+// global->LDS loads.
 //
-// Path A (heads with W = 0, including dense D = 1): one workgroup per
-// (b, h, r, 256-row chunk); its 16 waves (16 rows each) share K/V tiles of
-// 64 keys through a 4-deep LDS ring, so every state row is read from HBM
-// once per chunk.
+// Path A (heads with W = 0, including dense D = 1): work items are
+// (b, h, r, 256-row chunk).  Persistent workgroups of 8 waves take items in
+// a snake order over the cost-sorted item list; each wave owns two 16-row
+// blocks (w and 15-w, which balances the causal work) so that every K/V
+// fragment read from LDS feeds two MFMA row blocks.  K/V tiles of 64 keys
+// stream through a 4-deep LDS ring whose prefetch runs on into the next
+// item, so every state row is read from HBM once per chunk.
 //
 // Path B (heads with W > 0): one workgroup per 2-D block of up to 16
 // residues x 16 rows.  Local phase: wave p takes 16 CONTIGUOUS queries
@@ -67,11 +70,35 @@ struct Geo {
     static constexpr int RPI = 1024 / ROWB;     // rows per 1 KiB wave load
 };
 
+// XOR key of row r: the low bits of r rotated left by one.  Over any CH
+// consecutive rows it is a permutation (conflict-free K-fragment reads of
+// one logical chunk), and over CH/2 consecutive rows it maps the chunk pair
+// (2j, 2j+1) onto CH distinct chunks (conflict-free transposing V reads).
+template <int DK>
+__device__ __forceinline__ int swz_key(int r)
+{
+    constexpr int HALF = Geo<DK>::CH / 2;
+    return ((r & (HALF - 1)) << 1) | ((r / HALF) & 1);
+}
+
 // byte offset of chunk c of row r in a swizzled tile
 template <int DK>
 __device__ __forceinline__ int swz(int r, int c)
 {
-    return r * Geo<DK>::ROWB + ((c ^ (r & (Geo<DK>::CH - 1))) << 4);
+    return r * Geo<DK>::ROWB + ((c ^ swz_key<DK>(r)) << 4);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at dst + 16 l, dst being wave-uniform (M0).  It is
+// issued from inline assembly so that the compiler does not track it as an
+// LDS write: its own tracking cannot tell the ring buffers apart and would
+// wait for every load in flight before each LDS read.  Completion is
+// awaited explicitly (wait_vmcnt + barrier) before the data is read; the
+// instruction returns no registers.
+__device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
 // One wave copies RPI rows (1 KiB) global -> LDS: lane l fills row l / (CH)
@@ -83,8 +110,8 @@ __device__ __forceinline__ void copy_rows_lds(const uint16_t* row_ptr, int tile_
     constexpr int CH = Geo<DK>::CH;
     const int lane = threadIdx.x & (kWave - 1);
     const int p = lane % CH;
-    const int c = p ^ (tile_row & (CH - 1));
-    __builtin_amdgcn_global_load_lds((const void*)(row_ptr + c * 8), (lds_void*)dst, 16, 0, 0);
+    const int c = p ^ swz_key<DK>(tile_row);
+    dma16(row_ptr + c * 8, dst);
 }
 
 // K fragment (MFMA A operand of S^T = K Q^T) for keys 16*kb .. 16*kb+15 of
@@ -116,6 +143,16 @@ __device__ __forceinline__ bf16x8 v_frag_lds(const lds_char* tile, int hh, int d
     typedef short shortx8 __attribute__((ext_vector_type(8)));
     shortx8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(bf16x8, v);
+}
+
+// max over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows) with
+// the gfx950 row-swap permutes (VALU only, no LDS traffic)
+__device__ __forceinline__ float max_over_rows(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Online-softmax state of one 16-query fragment (lane (g, i) owns query i;
@@ -206,88 +243,274 @@ struct Frag {
 };
 
 // ------------------------------------------------------------------ path A
+constexpr int kWavesA = 8;
+constexpr int kTileA = 64;   // keys per K/V tile
+constexpr int kRingA = 4;    // LDS ring depth
+
+struct ItemA {
+    int b, h, D, r, R0, R1;
+    bool valid;
+};
+
+// Item `item` of the cost-sorted list: class by block range, levels (the
+// 256-row chunk index) most expensive first, then head fastest, residue,
+// batch -- consecutive items read the same positions of different heads,
+// i.e. whole contiguous token rows.
+__device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
+{
+    ItemA it;
+    it.valid = false;
+    if (item < 0 || item >= a.nblocks) return it;
+    int c = 0;
+    while (c + 1 < a.nclass && item >= a.cls[c + 1].block_begin) ++c;
+    const AttnClass& k = a.cls[c];
+    const int local = item - k.block_begin;
+    const int level = k.levels - 1 - local / k.per_level;
+    int idx = local % k.per_level;
+    it.h = a.heads[k.head_off + idx % k.nheads];
+    idx /= k.nheads;
+    it.r = idx % k.D;
+    it.b = idx / k.D;
+    it.D = k.D;
+    const int M = it.r < a.T ? (a.T - it.r + k.D - 1) / k.D : 0;
+    it.R0 = level * kAttnRowsA;
+    it.R1 = min(it.R0 + kAttnRowsA, M);
+    it.valid = it.R0 < M;
+    return it;
+}
+
+// Walks this workgroup's items (snake order over rounds of gridDim.x) and
+// their tiles; the DMA issue cursor and the compute cursor are two copies.
+struct CursorA {
+    int round, t, ntile;
+    ItemA it;
+
+    __device__ __forceinline__ int item_of(int rnd) const
+    {
+        const int G = gridDim.x;
+        return rnd * G + ((rnd & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    }
+    // first valid item at or after round `rnd`; it.valid false when none
+    __device__ __forceinline__ void seek(const AttnArgs& a, int rnd)
+    {
+        for (round = rnd; round * (int)gridDim.x < a.nblocks; ++round) {
+            it = decode_item_a(a, item_of(round));
+            if (it.valid) {
+                t = 0;
+                ntile = (it.R1 + kTileA - 1) / kTileA;
+                return;
+            }
+        }
+        it.valid = false;
+    }
+    __device__ __forceinline__ void advance(const AttnArgs& a)
+    {
+        if (++t == ntile) seek(a, round + 1);
+    }
+};
+
 template <int DK>
-__device__ void path_a(const AttnArgs& a, int b, int h, int D, int r, int chunk, lds_char* smem)
+__device__ __forceinline__ void issue_tile_a(const AttnArgs& a, const CursorA& c, lds_char* buf)
 {
     typedef Geo<DK> G;
-    constexpr int KT = 64;                        // keys per tile
-    constexpr int NBUF = 4;                       // LDS ring depth
-    constexpr int TILE_BYTES = 2 * KT * G::ROWB;  // K then V
-    constexpr int INSTR = 2 * KT / G::RPI;        // 1 KiB wave loads per tile
-    constexpr int PER_WAVE = INSTR / kAttnWaves;
-    static_assert(INSTR % kAttnWaves == 0, "tile loads split evenly over waves");
-
-    const int T = a.T, pitch = a.H * DK;
-    const int M = (T - r + D - 1) / D;            // rows of residue r
-    const int R0 = chunk * kAttnRowsA;
-    if (R0 >= M) return;
-    const int R1 = min(R0 + kAttnRowsA, M);
+    constexpr int INSTR = 2 * kTileA / G::RPI;
+    constexpr int PER_WAVE = INSTR / kWavesA;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    const int g = lane >> 4, i = lane & 15;
-    const size_t base = ((size_t)b * T * a.H + h) * DK;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.ks) + base;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.vs) + base;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + base;
+    const int pitch = a.H * DK;
+    const size_t base = ((size_t)c.it.b * a.T * a.H + c.it.h) * DK;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+        const int instr = wv * PER_WAVE + j;
+        const int trow = instr * G::RPI + lane / G::CH;  // K rows then V rows
+        const bool isv = trow >= kTileA;
+        const int kr = isv ? trow - kTileA : trow;
+        const int key = min(c.t * kTileA + kr, c.it.R1 - 1);
+        const uint16_t* src = static_cast<const uint16_t*>(isv ? a.vs : a.ks) + base +
+                              (size_t)(c.it.r + key * c.it.D) * pitch;
+        copy_rows_lds<DK>(src, kr, buf + instr * 1024);
+    }
+}
 
-    const int rs = R0 + 16 * wv;                  // first row of this wave
-    const int row = rs + i;
-    const bool rvalid = row < R1;
-    Frag<DK> f;
-    f.reset();
-    f.load_q(qp + (size_t)(r + row * D) * pitch, rvalid);
+// Per-lane byte offsets inside a swizzled tile, hoisted out of the tile
+// loop: K fragment of k-step ks for key block 0 (key block kb adds
+// kb * 16 rows), and the first transposing V read of 16-dim block db for
+// key half 0 (half hh adds 32 rows, the second read 16 rows).
+template <int DK>
+struct LaneOffsets {
+    int k[Geo<DK>::KS];
+    int v[Geo<DK>::DB];
 
-    const int ntile = (R1 + KT - 1) / KT;
-    auto issue = [&](int tt) {
-        lds_char* buf = smem + (tt % NBUF) * TILE_BYTES;
+    __device__ __forceinline__ void init()
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int g = lane >> 4, i = lane & 15, s = lane & 15;
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int instr = wv * PER_WAVE + j;         // 0 .. INSTR-1
-            const int trow = instr * G::RPI + lane / G::CH;  // 0 .. 2*KT-1 (K rows then V rows)
-            const bool isv = trow >= KT;
-            const int kr = isv ? trow - KT : trow;
-            const int key = min(tt * KT + kr, R1 - 1);
-            const uint16_t* src = (isv ? vp : kp) + (size_t)(r + key * D) * pitch;
-            copy_rows_lds<DK>(src, kr, buf + instr * 1024);
-        }
-    };
+        for (int ks = 0; ks < Geo<DK>::KS; ++ks) k[ks] = swz<DK>(i, g + 4 * ks);
+        const int r0 = 4 * g + (s >> 2);
 #pragma unroll
-    for (int tt = 0; tt < NBUF - 1; ++tt)
-        if (tt < ntile) issue(tt);
-
-    for (int tt = 0; tt < ntile; ++tt) {
-        const int ahead = min(NBUF - 2, ntile - 1 - tt);
-        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
-        else if (ahead == 1) wait_vmcnt<PER_WAVE>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (tt + NBUF - 1 < ntile) issue(tt + NBUF - 1);
-
-        const lds_char* kt = smem + (tt % NBUF) * TILE_BYTES;
-        const lds_char* vt = kt + KT * G::ROWB;
-#pragma unroll
-        for (int hh = 0; hh < KT / 32; ++hh) {
-            const int k0 = tt * KT + 32 * hh;            // first key of the half
-            if (k0 > rs + 15 || rs >= R1) continue;       // wholly above this wave's rows
-            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks) {
-                s0 = mfma16(k_frag_lds<DK>(kt, 2 * hh, ks), f.q[ks], s0);
-                s1 = mfma16(k_frag_lds<DK>(kt, 2 * hh + 1, ks), f.q[ks], s1);
-            }
-            bool valid[2][4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                valid[0][j] = rvalid && (k0 + 4 * g + j <= row);
-                valid[1][j] = rvalid && (k0 + 16 + 4 * g + j <= row);
-            }
-            const bf16x8 pb = f.softmax_step(s0, s1, valid, a.scale_log2);
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db) f.acc[db] = mfma16(v_frag_lds<DK>(vt, hh, db), pb, f.acc[db]);
+        for (int db = 0; db < Geo<DK>::DB; ++db) {
+            const int dim = 16 * db + 4 * (s & 3);
+            v[db] = swz<DK>(r0, dim >> 3) + (dim & 7) * 2;
         }
     }
-    f.store(op + (size_t)(r + row * D) * pitch, rvalid);
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ shortx4 lds_tr(const lds_char* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+}
+
+// Online softmax over one 64-key tile for one 16-row block.  Scores s[kb]
+// hold keys 16kb + 4g + j of the lane's query (raw q.k).  The running max
+// m (log2 domain) is only raised -- with the rescale of acc and l -- when
+// some query's tile max exceeds it by more than kLazyRescale; otherwise the
+// stale max stays the exponent reference (weights up to 2^kLazyRescale, the
+// result is the same softmax).  Returns P^T operands for the two key halves.
+constexpr float kLazyRescale = 8.0f;
+
+template <int DK, bool MASK>
+__device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row, int k0, float c, bf16x8 (&pb)[2])
+{
+    const int g = (threadIdx.x & (kWave - 1)) >> 4;
+    if (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (k0 + 16 * kb + 4 * g + j > row) s[kb][j] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+    mx = max_over_rows(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > f.m + kLazyRescale)) {
+        const float mn = fmaxf(f.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(f.m - (mn == -INFINITY ? 0.f : mn));
+        f.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < Geo<DK>::DB; ++db) f.acc[db] *= alpha;
+        f.m = mn;
+    }
+    const float nm = f.m == -INFINITY ? 0.f : -f.m;
+    float sum = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * hh][j], c, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * hh + 1][j], c, nm));
+            sum += p0 + p1;
+            pb[hh][j] = (__bf16)p0;
+            pb[hh][4 + j] = (__bf16)p1;
+        }
+    }
+    f.l += sum;
+}
+
+template <int DK>
+__global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs a)
+{
+    typedef Geo<DK> G;
+    constexpr int TILE_BYTES = 2 * kTileA * G::ROWB;
+    constexpr int PER_WAVE = (2 * kTileA / G::RPI) / kWavesA;
+    static_assert((2 * kTileA / G::RPI) % kWavesA == 0, "tile loads split evenly over waves");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int i = lane & 15;
+    const int pitch = a.H * DK;
+
+    LaneOffsets<DK> off;
+    off.init();
+    CursorA issue, comp;
+    issue.seek(a, 0);
+    comp = issue;
+    int issued = 0, consumed = 0;
+#pragma unroll
+    for (int j = 0; j < kRingA - 1; ++j) {
+        if (issue.it.valid) {
+            issue_tile_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES);
+            ++issued;
+            issue.advance(a);
+        }
+    }
+
+    while (comp.it.valid) {
+        const ItemA it = comp.it;
+        const size_t base = ((size_t)it.b * a.T * a.H + it.h) * DK;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
+        uint16_t* op = static_cast<uint16_t*>(a.out) + base;
+        const int rsA = it.R0 + 16 * wv, rsB = it.R0 + 16 * (15 - wv);
+        const bool hasA = rsA < it.R1, hasB = rsB < it.R1;
+        Frag<DK> fA, fB;
+        fA.reset();
+        fB.reset();
+        fA.load_q(qp + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
+        fB.load_q(qp + (size_t)(it.r + (rsB + i) * it.D) * pitch, rsB + i < it.R1);
+
+        for (int tt = 0; tt < comp.ntile; ++tt) {
+            const int ahead = issued - consumed - 1;  // tiles issued after this one
+            if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
+            else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (issue.it.valid) {
+                issue_tile_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES);
+                ++issued;
+                issue.advance(a);
+            }
+            const lds_char* kt = smem + (consumed % kRingA) * TILE_BYTES;
+            const lds_char* vt = kt + kTileA * G::ROWB;
+            const int k0 = tt * kTileA;
+            const bool needA = hasA && k0 <= rsA + 15;
+            const bool needB = hasB && k0 <= rsB + 15;
+            if (needA || needB) {
+                floatx4 sA[4], sB[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    sA[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    sB[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < G::KS; ++ks) {
+                        const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
+                        if (needA) sA[kb] = mfma16(kf, fA.q[ks], sA[kb]);
+                        if (needB) sB[kb] = mfma16(kf, fB.q[ks], sB[kb]);
+                    }
+                }
+                bf16x8 pA[2], pB[2];
+                if (needA) {
+                    if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, k0, a.scale_log2, pA);
+                    else softmax64<DK, true>(fA, sA, rsA + i, k0, a.scale_log2, pA);
+                }
+                if (needB) {
+                    if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, k0, a.scale_log2, pB);
+                    else softmax64<DK, true>(fB, sB, rsB + i, k0, a.scale_log2, pB);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int db = 0; db < G::DB; ++db) {
+                        const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
+                        const shortx4 x0 = lds_tr(vp);
+                        const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
+                        typedef short shortx8 __attribute__((ext_vector_type(8)));
+                        const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+                        if (needA) fA.acc[db] = mfma16(vf, pA[hh], fA.acc[db]);
+                        if (needB) fB.acc[db] = mfma16(vf, pB[hh], fB.acc[db]);
+                    }
+                }
+            }
+            ++consumed;
+        }
+        fA.store(op + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
+        fB.store(op + (size_t)(it.r + (rsB + i) * it.D) * pitch, rsB + i < it.R1);
+        comp.seek(a, comp.round + 1);
+    }
 }
 
 // ------------------------------------------------------------------ path B
@@ -446,12 +669,11 @@ __device__ void path_b(const AttnArgs& a, int b, int h, int D, int W, int rgroup
     }
 }
 
-// ------------------------------------------------------------------ kernel
+// ------------------------------------------------------------------ kernels
 template <int DK>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_prefill_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_window_kernel(AttnArgs a)
 {
-    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-    lds_char* smem = smem_raw;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int blk = blockIdx.x;
     int c = 0;
     while (c + 1 < a.nclass && blk >= a.cls[c + 1].block_begin) ++c;
@@ -459,48 +681,56 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_prefill_kernel(AttnAr
     const int local = blk - k.block_begin;
     const int level = k.levels - 1 - local / k.per_level;  // most expensive first
     int idx = local % k.per_level;
-    if (k.path == kPathA) {
-        const int r = idx % k.D;
-        idx /= k.D;
-        const int h = a.heads[k.head_off + idx % k.nheads];
-        const int b = idx / k.nheads;
-        path_a<DK>(a, b, h, k.D, r, level, smem);
-    } else {
-        const int ngroups = k.D >= 16 ? (k.D + 15) / 16 : 1;
-        const int rg = idx % ngroups;
-        idx /= ngroups;
-        const int h = a.heads[k.head_off + idx % k.nheads];
-        const int b = idx / k.nheads;
-        path_b<DK>(a, b, h, k.D, k.W, rg, level, smem);
+    const int ngroups = k.D >= 16 ? (k.D + 15) / 16 : 1;
+    const int rg = idx % ngroups;
+    idx /= ngroups;
+    const int h = a.heads[k.head_off + idx % k.nheads];
+    const int b = idx / k.nheads;
+    path_b<DK>(a, b, h, k.D, k.W, rg, level, smem);
+}
+
+size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * 2 * kTileA * d * 2; }
+
+size_t attn_lds_bytes_b(int d)
+{
+    const size_t vt = kAttnWaves * 32 * (size_t)d * 2;     // V tiles
+    const size_t xch = 256 * (size_t)d * 4 + 2 * 256 * 4;  // exchange
+    return vt > xch ? vt : xch;
+}
+
+template <typename K>
+static void set_lds(K kernel, size_t lds, bool& done)
+{
+    if (!done) {
+        (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        done = true;
     }
 }
 
-size_t attn_lds_bytes(int d)
+hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
-    const size_t ring = 4 * 2 * 64 * (size_t)d * 2;           // path A
-    const size_t vt = kAttnWaves * 32 * (size_t)d * 2;         // path B V tiles
-    const size_t xch = 256 * (size_t)d * 4 + 2 * 256 * 4;      // path B exchange
-    size_t m = ring > vt ? ring : vt;
-    return m > xch ? m : xch;
+    const size_t lds = attn_lds_bytes_a(d);
+    static bool s128 = false, s64 = false;
+    if (d == 128) {
+        set_lds(attn_dilated_kernel<128>, lds, s128);
+        hipLaunchKernelGGL(attn_dilated_kernel<128>, dim3(grid), dim3(kWavesA * kWave), lds, stream, a);
+    } else {
+        set_lds(attn_dilated_kernel<64>, lds, s64);
+        hipLaunchKernelGGL(attn_dilated_kernel<64>, dim3(grid), dim3(kWavesA * kWave), lds, stream, a);
+    }
+    return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill_bf16(const AttnArgs& a, int d, hipStream_t stream)
+hipError_t launch_attn_window_bf16(const AttnArgs& a, int d, hipStream_t stream)
 {
-    const size_t lds = attn_lds_bytes(d);
+    const size_t lds = attn_lds_bytes_b(d);
+    static bool s128 = false, s64 = false;
     if (d == 128) {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            attr = true;
-        }
-        hipLaunchKernelGGL(attn_prefill_kernel<128>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+        set_lds(attn_window_kernel<128>, lds, s128);
+        hipLaunchKernelGGL(attn_window_kernel<128>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
     } else {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            attr = true;
-        }
-        hipLaunchKernelGGL(attn_prefill_kernel<64>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+        set_lds(attn_window_kernel<64>, lds, s64);
+        hipLaunchKernelGGL(attn_window_kernel<64>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
     }
     return hipGetLastError();
 }

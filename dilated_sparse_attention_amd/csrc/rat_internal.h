@@ -7,15 +7,29 @@
 namespace rat {
 
 // ---------------------------------------------------------------- scan
-constexpr int kScanTplBf16 = 32;  // tokens per lane (bf16): chunk = 8 waves x 32
-constexpr int kScanTplF32 = 16;   // tokens per lane (fp32): chunk = 8 waves x 16
-constexpr int kScanBlockCh = 128; // channels per workgroup
+// Tile of the full / RESTART scan: a workgroup of kScanWaves waves, each
+// lane two channels x TPL tokens (build-time tunables).
+#ifndef RAT_SCAN_WAVES
+#define RAT_SCAN_WAVES 8
+#endif
+#ifndef RAT_SCAN_TPL_BF16
+#define RAT_SCAN_TPL_BF16 16
+#endif
+#ifndef RAT_SCAN_TPL_F32
+#define RAT_SCAN_TPL_F32 8
+#endif
+constexpr int kScanWaves = RAT_SCAN_WAVES;
+constexpr int kScanTplBf16 = RAT_SCAN_TPL_BF16;  // tokens per lane (bf16)
+constexpr int kScanTplF32 = RAT_SCAN_TPL_F32;    // tokens per lane (fp32)
+constexpr int kScanBlockCh = 128;                // channels per workgroup
 
 struct ScanHeader {
-    uint32_t ticket;  // next chunk ticket of the running call
-    uint32_t done;    // workgroups finished in the running call
-    uint32_t epoch;   // calls completed on this workspace (tags = epoch + 1)
-    uint32_t pad[61];
+    // low 32 bits: next chunk ticket of the running call; high 32 bits:
+    // calls completed on this workspace (carry tags are epoch + 1).  One
+    // atomic add hands a workgroup both; the workgroup that draws the last
+    // ticket starts the next epoch with ticket 0.
+    uint64_t tick;
+    uint32_t pad[62];
 };
 
 struct ScanFullArgs {
@@ -81,8 +95,10 @@ struct AttnArgs {
     int16_t heads[kAttnMaxHeads];
 };
 
-size_t attn_lds_bytes(int d);
-hipError_t launch_attn_prefill_bf16(const AttnArgs& a, int d, hipStream_t stream);
+// heads with W == 0: persistent kernel, `grid` workgroups (nblocks = items)
+hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
+// heads with W > 0: one workgroup per 2-D block (nblocks = blocks)
+hipError_t launch_attn_window_bf16(const AttnArgs& a, int d, hipStream_t stream);
 
 // Simple fp32 path (one workgroup per query row; exact fp32 arithmetic).
 struct AttnF32Args {
