@@ -316,7 +316,7 @@ __device__ __forceinline__ void issue_tile_a(const AttnArgs& a, const CursorA& c
     constexpr int INSTR = 2 * kTileA / G::RPI;
     constexpr int PER_WAVE = INSTR / kWavesA;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int pitch = a.H * DK;
     const size_t base = ((size_t)c.it.b * a.T * a.H + c.it.h) * DK;
 #pragma unroll
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int i = lane & 15;
     const int pitch = a.H * DK;
 
@@ -452,59 +452,100 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
         fA.load_q(qp + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
         fB.load_q(qp + (size_t)(it.r + (rsB + i) * it.D) * pitch, rsB + i < it.R1);
 
-        for (int tt = 0; tt < comp.ntile; ++tt) {
-            const int ahead = issued - consumed - 1;  // tiles issued after this one
+        // Tiles wholly below the chunk's first row are visible to every row
+        // of the chunk: they run software-pipelined (the QK^T MFMAs of tile
+        // t+1 are issued before the softmax of tile t, so MFMA and VALU work
+        // overlap within a wave) with no masks; the diagonal tiles follow on
+        // the general path.
+        const int nfull = min(it.R0 / kTileA, comp.ntile - 1);
+        // Wait until ring tile `seq` has landed, then barrier; refill the
+        // ring when the slot after tile `oldest` (the oldest tile still read
+        // after this barrier) is free.
+        auto wait_tile = [&](int seq, int oldest) {
+            const int ahead = issued - seq - 1;
             if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
             else if (ahead == 1) wait_vmcnt<PER_WAVE>();
             else wait_vmcnt<0>();
             __syncthreads();
-            if (issue.it.valid) {
+            if (issue.it.valid && issued < oldest + kRingA) {
                 issue_tile_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES);
                 ++issued;
                 issue.advance(a);
             }
-            const lds_char* kt = smem + (consumed % kRingA) * TILE_BYTES;
-            const lds_char* vt = kt + kTileA * G::ROWB;
+        };
+        auto qk = [&](int seq, floatx4 (&sa)[4], floatx4 (&sb)[4]) {
+            const lds_char* kt = smem + (seq % kRingA) * TILE_BYTES;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sa[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                sb[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks) {
+                    const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
+                    sa[kb] = mfma16(kf, fA.q[ks], sa[kb]);
+                    sb[kb] = mfma16(kf, fB.q[ks], sb[kb]);
+                }
+            }
+        };
+        auto pv = [&](int seq, const bf16x8 (&pa)[2], const bf16x8 (&pbb)[2]) {
+            const lds_char* vt = smem + (seq % kRingA) * TILE_BYTES + kTileA * G::ROWB;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int db = 0; db < G::DB; ++db) {
+                    const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
+                    const shortx4 x0 = lds_tr(vp);
+                    const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
+                    typedef short shortx8 __attribute__((ext_vector_type(8)));
+                    const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+                    fA.acc[db] = mfma16(vf, pa[hh], fA.acc[db]);
+                    fB.acc[db] = mfma16(vf, pbb[hh], fB.acc[db]);
+                }
+            }
+        };
+
+        floatx4 sA[4], sB[4];
+        bool have_scores = false;
+        if (nfull > 0) {
+            wait_tile(consumed, consumed);
+            qk(consumed, sA, sB);
+            for (int tt = 0; tt < nfull; ++tt) {
+                wait_tile(consumed + 1, consumed);  // tile `consumed` still feeds P V
+                floatx4 nA[4], nB[4];
+                qk(consumed + 1, nA, nB);
+                bf16x8 pA[2], pB[2];
+                softmax64<DK, false>(fA, sA, 0, 0, a.scale_log2, pA);
+                softmax64<DK, false>(fB, sB, 0, 0, a.scale_log2, pB);
+                pv(consumed, pA, pB);
+                ++consumed;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    sA[kb] = nA[kb];
+                    sB[kb] = nB[kb];
+                }
+            }
+            have_scores = true;  // tile nfull's scores are in sA / sB
+        }
+        for (int tt = nfull; tt < comp.ntile; ++tt) {
+            if (!have_scores) {
+                wait_tile(consumed, consumed);
+                qk(consumed, sA, sB);
+            }
+            have_scores = false;
             const int k0 = tt * kTileA;
             const bool needA = hasA && k0 <= rsA + 15;
             const bool needB = hasB && k0 <= rsB + 15;
-            if (needA || needB) {
-                floatx4 sA[4], sB[4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    sA[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    sB[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < G::KS; ++ks) {
-                        const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
-                        if (needA) sA[kb] = mfma16(kf, fA.q[ks], sA[kb]);
-                        if (needB) sB[kb] = mfma16(kf, fB.q[ks], sB[kb]);
-                    }
-                }
-                bf16x8 pA[2], pB[2];
-                if (needA) {
-                    if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, k0, a.scale_log2, pA);
-                    else softmax64<DK, true>(fA, sA, rsA + i, k0, a.scale_log2, pA);
-                }
-                if (needB) {
-                    if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, k0, a.scale_log2, pB);
-                    else softmax64<DK, true>(fB, sB, rsB + i, k0, a.scale_log2, pB);
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                    for (int db = 0; db < G::DB; ++db) {
-                        const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
-                        const shortx4 x0 = lds_tr(vp);
-                        const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
-                        typedef short shortx8 __attribute__((ext_vector_type(8)));
-                        const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-                        if (needA) fA.acc[db] = mfma16(vf, pA[hh], fA.acc[db]);
-                        if (needB) fB.acc[db] = mfma16(vf, pB[hh], fB.acc[db]);
-                    }
-                }
+            bf16x8 pA[2] = {}, pB[2] = {};
+            if (needA) {
+                if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, k0, a.scale_log2, pA);
+                else softmax64<DK, true>(fA, sA, rsA + i, k0, a.scale_log2, pA);
             }
+            if (needB) {
+                if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, k0, a.scale_log2, pB);
+                else softmax64<DK, true>(fB, sB, rsB + i, k0, a.scale_log2, pB);
+            }
+            pv(consumed, pA, pB);
             ++consumed;
         }
         fA.store(op + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
@@ -591,7 +632,7 @@ __device__ void path_b(const AttnArgs& a, int b, int h, int D, int W, int rgroup
     typedef Geo<DK> G;
     const int T = a.T, pitch = a.H * DK;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int i = lane & 15, g = lane >> 4;
     const size_t base = ((size_t)b * T * a.H + h) * DK;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
