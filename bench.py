@@ -19,7 +19,6 @@ hybrid prefill and the 2.6B decode at D = 64 and D = 16.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -29,6 +28,10 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+# kernel names as the profiler lists them (bf16, d = 128, full recurrence)
+SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, 16>"
+ATTN_KERNEL = "rat::attn_dilated_kernel<128>"
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
@@ -52,17 +55,6 @@ def progress(*parts):
     print("[bench]", *parts, file=sys.stderr, flush=True)
 
 
-def kernel_sources_hash():
-    """Hash of the HIP sources: profiles record it so that stale counter
-    readings are not reported for a changed kernel."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dilated_sparse_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when it is absent or was taken from other kernel sources."""
@@ -71,6 +63,8 @@ def load_traffic(kernel):
         return None
     with open(path) as f:
         data = json.load(f)
+    from dilated_sparse_attention_amd.profiling import kernel_sources_hash
+
     if data.get("sources_hash") != kernel_sources_hash():
         return None
     ent = data.get("kernels", {}).get(kernel)
@@ -206,43 +200,35 @@ def run_decode(torch, rat, w, steps, warmup, nsets=3):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w):
-    """The fp64 oracle on the host cores, on a bounded sample of the
-    headline workload: the scan over every token of the first 8 heads of
-    batch 0, and attention for 1/64 of the query rows of batch 0 (all heads),
-    scaled to whole-workload tokens/s per layer."""
+def cpu_baseline(w, min_s=12.0, max_reps=100):
+    """The fp64 oracle on the host cores, timed on the headline workload
+    itself: one oracle step is the recurrence over every (batch, token, head,
+    channel) followed by attention for every query row, from inputs already
+    widened to float64.  Steps repeat until ``min_s`` seconds have passed
+    (bounded by ``max_reps``); the value is whole-workload tokens/s."""
     import numpy as np
-    import torch
 
     from dilated_sparse_attention_amd import inputs
     from oracle import oracle
 
-    cores = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     oracle.build(force=False)
-    x = inputs.make_prefill(w, seed=0, B=1)
-    hs = min(8, w.H)
-    k, v, g = (x[n][:, :, :hs].contiguous() for n in ("k", "v", "gate"))
-    t0 = time.perf_counter()
-    ks, vs = oracle.scan(k, v, g, w.L, 0)
-    t_scan = time.perf_counter() - t0
-    scan_frac = hs / (w.H * w.B)
-    full_ks, full_vs = oracle.scan(x["k"], x["v"], x["gate"], w.L, 0) if hs < w.H else (ks, vs)
-    rows = [(0, t, h) for t in range(w.T - 1, -1, -64) for h in range(w.H)]
-    t0 = time.perf_counter()
-    oracle.attn_prefill_rows(x["q"], full_ks, full_vs, None, None, rows, w.D, w.W, w.scale)
-    t_attn = time.perf_counter() - t0
-    # attention cost grows with the row's key count: scale by pairs
-    pair_sample = sum((t // w.D[h]) + 1 for (_, t, h) in rows)
-    pair_total = w.B * sum(attn_pairs(w.T, Dh, Wh)[0] for Dh, Wh in zip(w.D, w.W))
-    est = t_scan / scan_frac + t_attn * pair_total / pair_sample
-    tok_s = w.B * w.T / est
-    return {"value": tok_s, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", cores)),
+    orc = oracle.default()
+    x = inputs.make_prefill(w, seed=0)
+    q, k, v, g = (np.ascontiguousarray(x[n].double().numpy()) for n in ("q", "k", "v", "gate"))
+    need_raw = any(wh > 0 for wh in w.W)
+    reps, t_total = 0, 0.0
+    while (t_total < min_s and reps < max_reps) or reps == 0:
+        t0 = time.perf_counter()
+        ks, vs = orc.scan(k, v, g, w.L, 0)
+        orc.attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None, w.D, w.W, w.scale)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_step = t_total / reps
+    return {"value": w.B * w.T / per_step, "unit": "tokens/s", "cores": orc.num_threads(),
             "kind": "oracle",
-            "sample": (f"fp64 oracle: scan of batch 0, heads 0-{hs - 1}, all {w.T} tokens "
-                       f"({t_scan:.2f} s); attention of {len(rows)} query rows (every 64th row of "
-                       f"batch 0, all heads; {t_attn:.2f} s); extrapolated to the whole workload by "
-                       f"channel count and by (query, key) pair count: {est:.1f} s per step")}
+            "sample": (f"fp64 C oracle (OpenMP), the whole {w.name} step (recurrence over all "
+                       f"{w.B}x{w.T}x{w.H}x{w.d} elements, then attention for all {w.B * w.T * w.H} query "
+                       f"rows) repeated {reps} times in {t_total:.1f} s: {per_step:.2f} s per step")}
 
 
 # ------------------------------------------------------------------ main
@@ -257,19 +243,20 @@ def main():
     import torch
 
     import dilated_sparse_attention_amd as rat
-    from dilated_sparse_attention_amd import inputs
+    from dilated_sparse_attention_amd import inputs, profiling
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rat.load_library()
 
-    if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    if args.copy_calibration:  # known-size elementwise pass: 1 GiB read, 1 GiB written
+        a = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
+        del a, b
 
     w = inputs.PREFILL_1P5B
     if args.only is None or args.only == w.name:
@@ -316,9 +303,9 @@ def main():
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
     attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9
     if scan_ms >= attn_ms:
-        dom, dom_bytes, dom_ms, dom_kernel = "scan", scan_bytes, scan_ms, "scan_full_kernel"
+        dom, dom_bytes, dom_ms, dom_kernel = "scan", scan_bytes, scan_ms, SCAN_KERNEL
     else:
-        dom, dom_bytes, dom_ms, dom_kernel = "attn", attn_bytes, attn_ms, "attn_prefill_kernel"
+        dom, dom_bytes, dom_ms, dom_kernel = "attn", attn_bytes, attn_ms, ATTN_KERNEL
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom_kernel),
@@ -335,15 +322,15 @@ def main():
         "config": w.describe(),
         "roofline": roofline,
         "kernels": {
-            "scan_full_kernel": {"ms": scan_ms, "GBps": scan_gbs, "hbm_frac": scan_gbs / HBM_PEAK_GBS,
+            SCAN_KERNEL: {"ms": scan_ms, "GBps": scan_gbs, "hbm_frac": scan_gbs / HBM_PEAK_GBS,
                                  "algorithmic_bytes": scan_bytes},
-            "attn_prefill_kernel": {"ms": attn_ms, "GBps": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS,
+            ATTN_KERNEL: {"ms": attn_ms, "GBps": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS,
                                     "TFLOPs": attn_flops / (attn_ms / 1e3) / 1e12,
                                     "mfma_frac": attn_flops / (attn_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                     "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops},
         },
         "wall_s_timed": wall,
-        "sources_hash": kernel_sources_hash(),
+        "sources_hash": profiling.kernel_sources_hash(),
     }
     if extra:
         line["extra"] = extra

@@ -47,6 +47,7 @@
  * number on invalid arguments (no output written then).
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdlib.h>
 
@@ -374,4 +375,10 @@ int oracle_count_pairs(int T, int D, int W, long long* n_dil_total, long long* n
     *n_dil_total = a;
     *n_loc_total = b;
     return 0;
+}
+
+/* Threads an OpenMP region of this library runs on (for reporting timings). */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
 }

@@ -93,6 +93,7 @@ class Oracle:
                                                  i, i, i, i, ip, ip, d]
         lib.oracle_attn_decode.argtypes = [dp, dp, dp, i, dp, dp, i, dp, i, i, i, i, ip, ip, d]
         lib.oracle_count_pairs.argtypes = [i, i, i, lp, lp]
+        lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -123,6 +124,10 @@ class Oracle:
         self.lib.oracle_index_sets(t, D, W, _iptr(dil), ctypes.byref(nd), _iptr(loc),
                                    ctypes.byref(nl))
         return dil[: nd.value].copy(), loc[: nl.value].copy()
+
+    def num_threads(self):
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self.lib.oracle_num_threads())
 
     def count_pairs(self, T, D, W):
         """(sum_t |S_dil(t)|, sum_t |S_loc(t)|) over the T queries of one head."""
