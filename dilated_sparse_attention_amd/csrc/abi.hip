@@ -45,24 +45,24 @@ bool size_ok(int64_t a, int64_t b, int64_t c, int64_t d)
 }
 
 struct ScanPlan {
-    int tpl, chunk, nblk, nseq, nchunk, nwg;
+    int chunk, nblk, nseq, nchunk, nwg;
     size_t agg_off, incl_off, bytes;
 };
 
 ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
 {
     ScanPlan p;
-    p.tpl = dtype == RAT_DTYPE_BF16 ? kScanTplBf16 : kScanTplF32;
-    p.chunk = kScanWaves * p.tpl;
+    p.chunk = kScanChunk;
     const int N = H * d;
-    p.nblk = (N + kScanBlockCh - 1) / kScanBlockCh;
+    const int bw = dtype == RAT_DTYPE_BF16 ? ScanBlock<uint16_t>::value : ScanBlock<float>::value;
+    p.nblk = (N + bw - 1) / bw;
     p.nseq = B * p.nblk;
     p.nchunk = (T + p.chunk - 1) / p.chunk;
     p.nwg = p.nchunk * p.nseq;
     const size_t slots = (size_t)p.nwg;
     p.agg_off = sizeof(ScanHeader);
-    p.incl_off = p.agg_off + slots * 3 * kScanBlockCh * sizeof(uint64_t);
-    p.bytes = p.incl_off + slots * 2 * kScanBlockCh * sizeof(uint64_t);
+    p.incl_off = p.agg_off + slots * 3 * bw * sizeof(uint64_t);
+    p.bytes = p.incl_off + slots * 2 * bw * sizeof(uint64_t);
     return p;
 }
 

@@ -41,11 +41,6 @@
 
 namespace rat {
 
-// LDS tiles are addressed through generic pointers into the workgroup's
-// shared array (the compiler keeps them in the LDS address space); the
-// builtins that need an explicit LDS pointer get one by an address-space cast.
-typedef char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_s4;
 
 __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
@@ -53,13 +48,6 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// vmcnt-only wait (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <int DK>
 struct Geo {
@@ -86,19 +74,6 @@ template <int DK>
 __device__ __forceinline__ int swz(int r, int c)
 {
     return r * Geo<DK>::ROWB + ((c ^ swz_key<DK>(r)) << 4);
-}
-
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's bytes land at dst + 16 l, dst being wave-uniform (M0).  It is
-// issued from inline assembly so that the compiler does not track it as an
-// LDS write: its own tracking cannot tell the ring buffers apart and would
-// wait for every load in flight before each LDS read.  Completion is
-// awaited explicitly (wait_vmcnt + barrier) before the data is read; the
-// instruction returns no registers.
-__device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
 // One wave copies RPI rows (1 KiB) global -> LDS: lane l fills row l / (CH)

@@ -55,4 +55,31 @@ __device__ __forceinline__ bool load_tagged(const uint64_t* p, uint32_t tag, flo
     return (uint32_t)(w >> 32) == tag;
 }
 
+// LDS buffers are addressed through generic pointers into the workgroup's
+// shared arrays (the compiler keeps them in the LDS address space); the
+// builtins that need an explicit LDS pointer get one by an address-space cast.
+typedef char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// vmcnt-only wait (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at dst + 16 l, dst being wave-uniform (M0).  It is
+// issued from inline assembly so that the compiler does not track it as an
+// LDS write: its own tracking cannot tell the ring buffers apart and would
+// wait for every load in flight before each LDS read.  Completion is
+// awaited explicitly (wait_vmcnt + barrier) before the data is read; the
+// instruction returns no registers.
+__device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
 }  // namespace rat

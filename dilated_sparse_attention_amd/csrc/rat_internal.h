@@ -7,21 +7,14 @@
 namespace rat {
 
 // ---------------------------------------------------------------- scan
-// Tile of the full / RESTART scan: a workgroup of kScanWaves waves, each
-// lane two channels x TPL tokens (build-time tunables).
-#ifndef RAT_SCAN_WAVES
-#define RAT_SCAN_WAVES 8
-#endif
-#ifndef RAT_SCAN_TPL_BF16
-#define RAT_SCAN_TPL_BF16 16
-#endif
-#ifndef RAT_SCAN_TPL_F32
-#define RAT_SCAN_TPL_F32 8
-#endif
-constexpr int kScanWaves = RAT_SCAN_WAVES;
-constexpr int kScanTplBf16 = RAT_SCAN_TPL_BF16;  // tokens per lane (bf16)
-constexpr int kScanTplF32 = RAT_SCAN_TPL_F32;    // tokens per lane (fp32)
-constexpr int kScanBlockCh = 128;                // channels per workgroup
+// Tile of the full / RESTART scan: a workgroup of kScanWaves waves covers
+// one block of channels (128 bf16 / 64 fp32: a 256-byte row segment) x
+// kScanChunk tokens; each lane holds 16 bytes of a row (8 bf16 / 4 fp32
+// channels) for kScanTpl consecutive tokens.
+constexpr int kScanWaves = 8;
+constexpr int kScanTpl = 4;
+constexpr int kScanChunk = kScanWaves * 4 * kScanTpl;  // 4 token segments per wave
+template <typename E> struct ScanBlock { static constexpr int value = 256 / sizeof(E); };
 
 struct ScanHeader {
     // low 32 bits: next chunk ticket of the running call; high 32 bits:

@@ -6,29 +6,34 @@
 // page's text; this is the forget-gate reading of its surrounding words.
 //
 // Layout [B,T,H,d] puts the scan axis T slowest, so lanes map to channels
-// (each lane owns two adjacent channels) and every token row is one
-// coalesced 256-byte (bf16) / 512-byte (fp32) load per wave; the scan along
-// T is then a per-lane sequential recurrence with no cross-lane traffic.
+// (each lane owns two adjacent channels) and the scan along T is a per-lane
+// sequential recurrence with no cross-lane traffic.
 //
 // FULL / RESTART kernel (one pass over HBM):
-//   * a workgroup owns a chunk of C = 8 waves x TPL tokens of one
-//     (batch, 128-channel block); each wave holds its TPL tokens in
-//     registers;
-//   * pass 1: each wave runs the recurrence over its tokens from a zero
-//     state, keeping per token the local state H_t and the gate product
-//     P_t since its first token; the last ones form the wave's affine map
-//     h -> A*h + B (A = prod g, B = gated sum), per channel;
-//   * waves combine their maps through LDS; the chunk's map is published
-//     and the carry-in is found by a decoupled look-back over the chunks
-//     before it (Merrill & Garland's single-pass scan), through 64-bit
-//     words that carry (value, epoch tag) and so need no memory fence;
-//   * pass 2 applies the carry c of the wave: h_t = H_t + P_t * c (one FMA
-//     per element; the gates are evaluated once).
+//   * a workgroup owns a chunk of 128 tokens of one block of channels (a
+//     256-byte row segment: 128 bf16 / 64 fp32 channels); lane (r, c) of a
+//     wave holds 16 bytes of the row (8 bf16 / 4 fp32 channels) for 4
+//     consecutive tokens, so every access is a 16-byte load or store and a
+//     wave instruction covers 4 whole row segments.  The chunk stays in
+//     registers from load to store (no LDS staging); 2 workgroups fit on a
+//     compute unit;
+//   * pass 1: each lane runs the recurrence over its 4 tokens from a zero
+//     state, keeping the local states H_t; its last ones with the gate
+//     product form the segment's affine map h -> A*h + B per channel;
+//   * one wave turns the 32 segment maps into exclusive prefixes (and the
+//     chunk's map, which it publishes) while another finds the chunk's
+//     carry-in by a decoupled look-back over the chunks before it (Merrill
+//     & Garland's single-pass scan), through 64-bit words that carry
+//     (value, epoch tag) and so need no memory fence;
+//   * pass 2 evaluates the gates again, h_t = H_t + P_t * carry with P_t
+//     the gate product since the segment start, and stores the states.
 //   Chunk order comes from a ticket counter so that every chunk a
 //   workgroup waits for belongs to a workgroup that is already running;
 //   the same 64-bit atomic returns the call's epoch.
 //   RESTART (state cleared where t mod L == 0) is the same recurrence with
-//   g forced to 0 at those positions; a map with A == 0 ends the look-back.
+//   g forced to 0 at those positions; a chunk that starts at a restart
+//   needs no carry, and a map with A == 0 is published as an inclusive
+//   prefix at once and ends the look-back of its successors.
 //
 // SLIDING kernel (h_t sums exactly the last L <= 64 inputs):
 //   with tiles aligned to multiples of L, t = mL + j, the window of t is
@@ -43,42 +48,52 @@
 namespace rat {
 
 constexpr int kScanThreads = kScanWaves * kWave;
-constexpr int kScanCh = 2 * kWave;  // channels per workgroup
-constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // polls before the watchdog fires
+constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before the watchdog fires
 
-// Two adjacent channels of one token row.
-template <typename E> struct Pair2;
-// Inputs are read once and outputs written once: nontemporal accesses keep
-// the stream from displacing other data in the caches (measured ~5-10%
-// faster on this access pattern).
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-template <> struct Pair2<float> {
-    typedef floatx2 raw;
-    static __device__ __forceinline__ raw load(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const floatx2*>(p)); }
-    static __device__ __forceinline__ float lo(raw r) { return r[0]; }
-    static __device__ __forceinline__ float hi(raw r) { return r[1]; }
-    static __device__ __forceinline__ raw zero() { return floatx2{0.f, 0.f}; }
-    static __device__ __forceinline__ void store(float* p, float a, float b) { __builtin_nontemporal_store(floatx2{a, b}, reinterpret_cast<floatx2*>(p)); }
+// 16 bytes of one token row: CPL = 16 / sizeof(E) adjacent channels.
+template <typename E> struct Row16;
+template <> struct Row16<uint16_t> {
+    static constexpr int CPL = 8;
+    static __device__ __forceinline__ float get(const u32x4& r, int j)
+    {
+        return (j & 1) ? bf16_hi(r[j >> 1]) : bf16_lo(r[j >> 1]);
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&x)[8])
+    {
+        return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+    }
 };
-template <> struct Pair2<uint16_t> {
-    typedef uint32_t raw;
-    static __device__ __forceinline__ raw load(const uint16_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
-    static __device__ __forceinline__ float lo(raw r) { return bf16_lo(r); }
-    static __device__ __forceinline__ float hi(raw r) { return bf16_hi(r); }
-    static __device__ __forceinline__ raw zero() { return 0u; }
-    static __device__ __forceinline__ void store(uint16_t* p, float a, float b) { __builtin_nontemporal_store(pack_bf16x2(a, b), reinterpret_cast<uint32_t*>(p)); }
+template <> struct Row16<float> {
+    static constexpr int CPL = 4;
+    static __device__ __forceinline__ float get(const u32x4& r, int j) { return __uint_as_float(r[j]); }
+    static __device__ __forceinline__ u32x4 pack(const float (&x)[4])
+    {
+        return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    }
 };
 
-template <typename E, int TPL>
-__global__ __launch_bounds__(kScanThreads) void scan_full_kernel(ScanFullArgs a)
+template <typename E>
+__global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs a)
 {
-    typedef Pair2<E> P;
+    typedef Row16<E> R16;
+    constexpr int CPL = R16::CPL;           // channels per lane
+    constexpr int LPR = 16;                 // lanes per token row of the block
+    constexpr int BW = LPR * CPL;           // channels per block
+    constexpr int GPW = kWave / LPR;        // token segments per wave
+    constexpr int NSEG = kScanWaves * GPW;  // segments per chunk
+    constexpr int TPL = kScanTpl;           // tokens per segment
+    constexpr int CT = NSEG * TPL;          // tokens per chunk
+    constexpr int C0 = BW / kWave;          // channels per lane of the single-wave steps
+    static_assert(CT == kScanChunk && BW == ScanBlock<E>::value, "geometry shared with the host plan");
+    // segment maps (A, K, V) per channel; then their exclusive prefixes
+    __shared__ float s_seg[NSEG][3][BW];
+    __shared__ float s_carry[2][BW];  // chunk carry-in (hk, hv)
+    __shared__ float s_tot[3][BW];    // the chunk's map
     __shared__ uint32_t s_ticket, s_epoch;
-    __shared__ float s_map[kScanWaves][3][kScanCh];  // per-wave (A, Bk, Bv)
-    __shared__ float s_carry[2][kScanCh];            // chunk carry-in (hk, hv)
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (threadIdx.x == 0) {
         const uint64_t old = __hip_atomic_fetch_add(&a.hdr->tick, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_ticket = (uint32_t)old;
@@ -93,174 +108,231 @@ __global__ __launch_bounds__(kScanThreads) void scan_full_kernel(ScanFullArgs a)
     const int chunk = (int)(ticket / (uint32_t)a.nseq);
     const int seq = (int)(ticket % (uint32_t)a.nseq);
     const int b = seq / a.nblk;
-    const int cl = lane * 2;                       // channel within the block
-    const int c = (seq % a.nblk) * kScanCh + cl;   // channel within the row
-    const bool cvalid = c < a.N;
-    const int t0 = chunk * (kScanWaves * TPL) + w * TPL;
-    const size_t base = (size_t)b * a.T * a.N + c;
+    const int cblk = (seq % a.nblk) * BW;  // first channel of the block
+    const int tb = chunk * CT;              // first token of the chunk
 
-    const E* kp = static_cast<const E*>(a.k) + base;
-    const E* vp = static_cast<const E*>(a.v) + base;
-    const E* gp = static_cast<const E*>(a.g) + base;
+    // lane (r, c): channels cblk + CPL c .. +CPL, tokens t0 .. t0 + TPL - 1
+    const int c = lane % LPR;
+    const int seg = w * GPW + lane / LPR;
+    const int ch0 = cblk + c * CPL;
+    const bool cvalid = ch0 < a.N;
+    const int t0 = tb + seg * TPL;
+    const size_t rowbase = (size_t)b * a.T * a.N + ch0;
 
-    // RESTART positions (t mod L == 0) of this wave's tokens, as a
-    // wave-uniform bit mask
+    u32x4 rk[TPL], rv[TPL], rg[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        if (cvalid && t0 + i < a.T) {
+            const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+            rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + o));
+            rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + o));
+            rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + o));
+        } else {
+            rk[i] = rv[i] = rg[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // RESTART positions (t mod L == 0) of this segment, as a bit mask
     uint32_t rmask = 0;
     if (a.L > 0) {
         for (int t = ((t0 + a.L - 1) / a.L) * a.L; t < t0 + TPL; t += a.L) rmask |= 1u << (t - t0);
     }
-    rmask = __builtin_amdgcn_readfirstlane(rmask);
 
-    typename P::raw rk[TPL], rv[TPL], rg[TPL];
+    // pass 1: the segment's recurrence from a zero state
+    float A[CPL], K[CPL], V[CPL];
+    float hk[TPL][CPL], hv[TPL][CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) { A[j] = 1.f; K[j] = 0.f; V[j] = 0.f; }
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-        const int t = t0 + i;
-        if (cvalid && t < a.T) {
-            const size_t o = (size_t)t * a.N;
-            rk[i] = P::load(kp + o);
-            rv[i] = P::load(vp + o);
-            rg[i] = P::load(gp + o);
-        } else {
-            rk[i] = P::zero();
-            rv[i] = P::zero();
-            rg[i] = P::zero();
-        }
-    }
-
-    // pass 1: local recurrence from zero; H (k, v) and gate product per token
-    float A0 = 1.f, A1 = 1.f, K0 = 0.f, K1 = 0.f, V0 = 0.f, V1 = 0.f;
-    float hk[TPL][2], hv[TPL][2], pg[TPL][2];
+        const bool live = t0 + i < a.T;
+        const bool restart = (rmask >> i) & 1u;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        if (t0 + i < a.T) {
-            float g0, gb0, g1, gb1;
-            forget_gate(P::lo(rg[i]), g0, gb0);
-            forget_gate(P::hi(rg[i]), g1, gb1);
-            if ((rmask >> i) & 1u) { g0 = 0.f; g1 = 0.f; }
-            A0 *= g0; A1 *= g1;
-            K0 = fmaf(g0, K0, gb0 * P::lo(rk[i]));
-            K1 = fmaf(g1, K1, gb1 * P::hi(rk[i]));
-            V0 = fmaf(g0, V0, gb0 * P::lo(rv[i]));
-            V1 = fmaf(g1, V1, gb1 * P::hi(rv[i]));
+        for (int j = 0; j < CPL; ++j) {
+            float g, gb;
+            forget_gate(R16::get(rg[i], j), g, gb);
+            if (restart) g = 0.f;
+            if (live) {
+                A[j] *= g;
+                K[j] = fmaf(g, K[j], gb * R16::get(rk[i], j));
+                V[j] = fmaf(g, V[j], gb * R16::get(rv[i], j));
+            }
+            hk[i][j] = K[j];
+            hv[i][j] = V[j];
         }
-        hk[i][0] = K0; hk[i][1] = K1;
-        hv[i][0] = V0; hv[i][1] = V1;
-        pg[i][0] = A0; pg[i][1] = A1;
     }
-    s_map[w][0][cl] = A0; s_map[w][0][cl + 1] = A1;
-    s_map[w][1][cl] = K0; s_map[w][1][cl + 1] = K1;
-    s_map[w][2][cl] = V0; s_map[w][2][cl + 1] = V1;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        s_seg[seg][0][c * CPL + j] = A[j];
+        s_seg[seg][1][c * CPL + j] = K[j];
+        s_seg[seg][2][c * CPL + j] = V[j];
+    }
     __syncthreads();
 
+    const size_t slot = (size_t)chunk * a.nseq + seq;
+    const bool has_next = chunk + 1 < a.nchunk;
+    uint64_t* ic_out = a.incl + slot * (2 * BW);
     if (w == 0) {
-        // the chunk's map: waves in token order
-        float cA[2] = {1.f, 1.f}, cK[2] = {0.f, 0.f}, cV[2] = {0.f, 0.f};
+        // the carry-in (decoupled look-back); no carry is needed at the first
+        // chunk or when the chunk starts at a restart
+        float inK[C0], inV[C0];
 #pragma unroll
-        for (int ww = 0; ww < kScanWaves; ++ww)
+        for (int j = 0; j < C0; ++j) { inK[j] = 0.f; inV[j] = 0.f; }
+        if (chunk > 0 && !(a.L > 0 && tb % a.L == 0)) {
+            // (rA, rK, rV): map of the chunks strictly between the one
+            // examined and this one
+            float rA[C0], rK[C0], rV[C0];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float wa = s_map[ww][0][cl + j];
-                cK[j] = fmaf(wa, cK[j], s_map[ww][1][cl + j]);
-                cV[j] = fmaf(wa, cV[j], s_map[ww][2][cl + j]);
-                cA[j] *= wa;
-            }
-        const size_t slot = (size_t)chunk * a.nseq + seq;
-        const bool has_next = chunk + 1 < a.nchunk;
-        if (has_next) {
-            uint64_t* ag = a.agg + slot * (3 * kScanCh);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                store_tagged(ag + cl + j, cA[j], tag);
-                store_tagged(ag + kScanCh + cl + j, cK[j], tag);
-                store_tagged(ag + 2 * kScanCh + cl + j, cV[j], tag);
-            }
-        }
-        // look back for the carry-in: (rA, rK, rV) is the map of the chunks
-        // strictly between the one examined and this one
-        float inK[2] = {0.f, 0.f}, inV[2] = {0.f, 0.f};
-        if (chunk > 0) {
-            float rA[2] = {1.f, 1.f}, rK[2] = {0.f, 0.f}, rV[2] = {0.f, 0.f};
+            for (int j = 0; j < C0; ++j) { rA[j] = 1.f; rK[j] = 0.f; rV[j] = 0.f; }
             int p = chunk - 1;
-            bool done = false;
             uint32_t spins = 0;
-            while (!done) {
+            while (true) {
                 if (p < 0) {
-                    inK[0] = rK[0]; inK[1] = rK[1]; inV[0] = rV[0]; inV[1] = rV[1];
-                    done = true;
+#pragma unroll
+                    for (int j = 0; j < C0; ++j) { inK[j] = rK[j]; inV[j] = rV[j]; }
                     break;
                 }
                 const size_t ps = (size_t)p * a.nseq + seq;
-                const uint64_t* ic = a.incl + ps * (2 * kScanCh);
-                float x0, x1, y0, y1;
-                bool ok = load_tagged(ic + cl, tag, x0);
-                ok &= load_tagged(ic + cl + 1, tag, x1);
-                ok &= load_tagged(ic + kScanCh + cl, tag, y0);
-                ok &= load_tagged(ic + kScanCh + cl + 1, tag, y1);
+                const uint64_t* ic = a.incl + ps * (2 * BW);
+                const uint64_t* ag = a.agg + ps * (3 * BW);
+                float x[C0], y[C0], pa[C0], pk[C0], pv[C0];
+                bool ok = true, ok2 = true;
+#pragma unroll
+                for (int j = 0; j < C0; ++j) {
+                    ok &= load_tagged(ic + lane * C0 + j, tag, x[j]);
+                    ok &= load_tagged(ic + BW + lane * C0 + j, tag, y[j]);
+                    ok2 &= load_tagged(ag + lane * C0 + j, tag, pa[j]);
+                    ok2 &= load_tagged(ag + BW + lane * C0 + j, tag, pk[j]);
+                    ok2 &= load_tagged(ag + 2 * BW + lane * C0 + j, tag, pv[j]);
+                }
                 if (ok) {
-                    inK[0] = fmaf(rA[0], x0, rK[0]); inK[1] = fmaf(rA[1], x1, rK[1]);
-                    inV[0] = fmaf(rA[0], y0, rV[0]); inV[1] = fmaf(rA[1], y1, rV[1]);
-                    done = true;
+#pragma unroll
+                    for (int j = 0; j < C0; ++j) {
+                        inK[j] = fmaf(rA[j], x[j], rK[j]);
+                        inV[j] = fmaf(rA[j], y[j], rV[j]);
+                    }
                     break;
                 }
-                const uint64_t* pg = a.agg + ps * (3 * kScanCh);
-                float pa0, pa1, pk0, pk1, pv0, pv1;
-                bool ok2 = load_tagged(pg + cl, tag, pa0);
-                ok2 &= load_tagged(pg + cl + 1, tag, pa1);
-                ok2 &= load_tagged(pg + kScanCh + cl, tag, pk0);
-                ok2 &= load_tagged(pg + kScanCh + cl + 1, tag, pk1);
-                ok2 &= load_tagged(pg + 2 * kScanCh + cl, tag, pv0);
-                ok2 &= load_tagged(pg + 2 * kScanCh + cl + 1, tag, pv1);
                 if (ok2) {
-                    rK[0] = fmaf(rA[0], pk0, rK[0]); rK[1] = fmaf(rA[1], pk1, rK[1]);
-                    rV[0] = fmaf(rA[0], pv0, rV[0]); rV[1] = fmaf(rA[1], pv1, rV[1]);
-                    rA[0] *= pa0; rA[1] *= pa1;
+                    bool zero = true;
+#pragma unroll
+                    for (int j = 0; j < C0; ++j) {
+                        rK[j] = fmaf(rA[j], pk[j], rK[j]);
+                        rV[j] = fmaf(rA[j], pv[j], rV[j]);
+                        rA[j] *= pa[j];
+                        zero &= rA[j] == 0.f;
+                    }
                     --p;
-                    if (rA[0] == 0.f && rA[1] == 0.f) p = -1;  // nothing earlier reaches us
+                    if (zero) p = -1;  // nothing earlier reaches this chunk
                 } else if (++spins > kLookbackSpinLimit) {
                     // watchdog: a carry that never appears poisons the output
                     // instead of hanging the device
-                    inK[0] = inK[1] = inV[0] = inV[1] = __builtin_nanf("");
-                    done = true;
+#pragma unroll
+                    for (int j = 0; j < C0; ++j) inK[j] = inV[j] = __builtin_nanf("");
+                    break;
                 } else {
-                    __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
         }
-        if (has_next) {
-            uint64_t* ic = a.incl + slot * (2 * kScanCh);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                store_tagged(ic + cl + j, fmaf(cA[j], inK[j], cK[j]), tag);
-                store_tagged(ic + kScanCh + cl + j, fmaf(cA[j], inV[j], cV[j]), tag);
+        for (int j = 0; j < C0; ++j) {
+            s_carry[0][lane * C0 + j] = inK[j];
+            s_carry[1][lane * C0 + j] = inV[j];
+        }
+    } else if (w == 1) {
+        // meanwhile: exclusive prefix maps of the segments (in place), the
+        // chunk's map and its publication (the aggregate, or at once the
+        // inclusive prefix when a restart makes the map ignore its carry-in)
+        bool closed = true;
+        float cA[C0], cK[C0], cV[C0];
+#pragma unroll
+        for (int j = 0; j < C0; ++j) {
+            const int ch = lane * C0 + j;
+            float pA = 1.f, pK = 0.f, pV = 0.f;
+#pragma unroll 4
+            for (int s2 = 0; s2 < NSEG; ++s2) {
+                const float sa = s_seg[s2][0][ch], sk = s_seg[s2][1][ch], sv = s_seg[s2][2][ch];
+                s_seg[s2][0][ch] = pA;
+                s_seg[s2][1][ch] = pK;
+                s_seg[s2][2][ch] = pV;
+                pK = fmaf(sa, pK, sk);
+                pV = fmaf(sa, pV, sv);
+                pA *= sa;
+            }
+            cA[j] = pA; cK[j] = pK; cV[j] = pV;
+            s_tot[0][ch] = pA; s_tot[1][ch] = pK; s_tot[2][ch] = pV;
+            closed &= pA == 0.f;
+        }
+        if (has_next) {
+            if (closed) {
+#pragma unroll
+                for (int j = 0; j < C0; ++j) {
+                    store_tagged(ic_out + lane * C0 + j, cK[j], tag);
+                    store_tagged(ic_out + BW + lane * C0 + j, cV[j], tag);
+                }
+            } else {
+                uint64_t* ag = a.agg + slot * (3 * BW);
+#pragma unroll
+                for (int j = 0; j < C0; ++j) {
+                    store_tagged(ag + lane * C0 + j, cA[j], tag);
+                    store_tagged(ag + BW + lane * C0 + j, cK[j], tag);
+                    store_tagged(ag + 2 * BW + lane * C0 + j, cV[j], tag);
+                }
             }
         }
-        s_carry[0][cl] = inK[0]; s_carry[0][cl + 1] = inK[1];
-        s_carry[1][cl] = inV[0]; s_carry[1][cl + 1] = inV[1];
     }
     __syncthreads();
-
-    // carry into this wave: chunk carry-in, then the waves before it
-    float hk0 = s_carry[0][cl], hk1 = s_carry[0][cl + 1];
-    float hv0 = s_carry[1][cl], hv1 = s_carry[1][cl + 1];
-    for (int ww = 0; ww < w; ++ww) {
-        const float a0 = s_map[ww][0][cl], a1 = s_map[ww][0][cl + 1];
-        hk0 = fmaf(a0, hk0, s_map[ww][1][cl]); hk1 = fmaf(a1, hk1, s_map[ww][1][cl + 1]);
-        hv0 = fmaf(a0, hv0, s_map[ww][2][cl]); hv1 = fmaf(a1, hv1, s_map[ww][2][cl + 1]);
-    }
-
-    // pass 2: the states, h_t = H_t + P_t * carry
-    E* ksp = static_cast<E*>(a.ks) + base;
-    E* vsp = static_cast<E*>(a.vs) + base;
+    if (w == 0 && has_next) {
+        // the inclusive prefix of this chunk (already out when closed)
+        bool closed = true;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        const int t = t0 + i;
-        if (cvalid && t < a.T) {
-            const size_t o = (size_t)t * a.N;
-            P::store(ksp + o, fmaf(pg[i][0], hk0, hk[i][0]), fmaf(pg[i][1], hk1, hk[i][1]));
-            P::store(vsp + o, fmaf(pg[i][0], hv0, hv[i][0]), fmaf(pg[i][1], hv1, hv[i][1]));
+        for (int j = 0; j < C0; ++j) closed &= s_tot[0][lane * C0 + j] == 0.f;
+        if (!closed) {
+#pragma unroll
+            for (int j = 0; j < C0; ++j) {
+                const int ch = lane * C0 + j;
+                store_tagged(ic_out + ch, fmaf(s_tot[0][ch], s_carry[0][ch], s_tot[1][ch]), tag);
+                store_tagged(ic_out + BW + ch, fmaf(s_tot[0][ch], s_carry[1][ch], s_tot[2][ch]), tag);
+            }
         }
     }
 
+    // pass 2: carry into the segment, then h_t = H_t + P_t * carry with P_t
+    // the gate product since the segment start (gates evaluated again)
+    float ck[CPL], cv[CPL], P[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int ch = c * CPL + j;
+        const float pa = s_seg[seg][0][ch];
+        ck[j] = fmaf(pa, s_carry[0][ch], s_seg[seg][1][ch]);
+        cv[j] = fmaf(pa, s_carry[1][ch], s_seg[seg][2][ch]);
+        P[j] = 1.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+        // the gates are evaluated again rather than kept from pass 1 (the
+        // empty asm hides the logits' identity from common-subexpression
+        // elimination, which would hold 8 more registers per token)
+        asm volatile("" : "+v"(rg[i]));
+        const bool restart = (rmask >> i) & 1u;
+        float ok[CPL], ov[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            float g, gb;
+            forget_gate(R16::get(rg[i], j), g, gb);
+            if (restart) g = 0.f;
+            P[j] *= g;
+            ok[j] = fmaf(P[j], ck[j], hk[i][j]);
+            ov[j] = fmaf(P[j], cv[j], hv[i][j]);
+        }
+        // ordinary (cacheable) stores: the attention reads the states right
+        // after, and part of them is still in the Infinity Cache then
+        if (cvalid && t0 + i < a.T) {
+            const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+            *reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o) = R16::pack(ok);
+            *reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o) = R16::pack(ov);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- SLIDING
@@ -356,9 +428,9 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
 hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream)
 {
     if (bf16)
-        hipLaunchKernelGGL((scan_full_kernel<uint16_t, kScanTplBf16>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
+        hipLaunchKernelGGL((scan_full_kernel<uint16_t>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((scan_full_kernel<float, kScanTplF32>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
+        hipLaunchKernelGGL((scan_full_kernel<float>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
     return hipGetLastError();
 }
 
