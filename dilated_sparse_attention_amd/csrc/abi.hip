@@ -148,6 +148,7 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void
     ScanSlideArgs a;
     a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state;
     a.B = B; a.T = T; a.N = H * d; a.L = L;
+    if (bf16 && L == 64 && a.N % 64 == 0) return hip_status(launch_scan_slide64(a, s));
     const int ntiles = (T + L - 1) / L;
     // spans of at least 256 tokens: one halo tile per span
     a.tiles_per_span = std::max(1, (256 + L - 1) / L);
@@ -172,9 +173,17 @@ int check_heads(int H, const int* D, const int* W, bool* any_w)
 
 }  // namespace
 
+size_t rat_attn_prefill_workspace_bytes(int B, int T, int H, int d, const int* D, const int* W, rat_dtype dtype)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || !dtype_ok(dtype)) return 0;
+    bool any_w = false;
+    if (check_heads(H, D, W, &any_w) != RAT_OK || !any_w || dtype != RAT_DTYPE_BF16) return 0;
+    return (size_t)B * T * H * 2 * sizeof(float);
+}
+
 int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
                              const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
-                             float scale, rat_dtype dtype, void* stream)
+                             float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!q || !k_state || !v_state || !out) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
@@ -202,10 +211,17 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         return hip_status(launch_attn_prefill_f32(a, s));
     }
 
-    // group heads by (D, W); window-free classes go to the persistent
-    // dilated kernel (items = (b, h, r, 256-row chunk)), windowed classes to
-    // the 2-D block kernel; within each, classes with the longest single
-    // items come first and each class's levels most expensive first
+    // Heads with W > 0 first get their raw-key band (one workgroup per 256
+    // contiguous queries), which leaves a partial softmax state per query
+    // in `out` and the workspace; then every head runs the persistent
+    // dilated kernel (items = (b, h, r, 256-row chunk)), which continues
+    // from those states.  Heads are grouped into (D, W) classes; classes
+    // with the longest single items come first, each class's levels most
+    // expensive first.
+    if (any_w) {
+        const size_t need = (size_t)B * T * H * 2 * sizeof(float);
+        if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RAT_ERR_WORKSPACE;
+    }
     struct Cls { int D, W; std::vector<int> heads; double item_cost; };
     std::vector<Cls> cls;
     for (int h = 0; h < H; ++h) {
@@ -216,51 +232,50 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         }
         it->heads.push_back(h);
     }
+    if ((int)cls.size() > kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
     for (auto& c : cls) {
         const int Mmax = (T + c.D - 1) / c.D;
-        if (c.W == 0) c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
-        else c.item_cost = 256.0 * (std::min(Mmax, kAttnRowsB) + c.W + 16);
+        c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
     }
     std::stable_sort(cls.begin(), cls.end(), [](const Cls& x, const Cls& y) { return x.item_cost > y.item_cost; });
 
-    AttnArgs args[2];
-    for (int path = 0; path < 2; ++path) {
-        AttnArgs& a = args[path];
-        memset(&a, 0, sizeof(a));
-        a.q = q; a.ks = k_state; a.vs = v_state; a.kr = k_raw; a.vr = v_raw; a.out = out;
-        a.B = B; a.T = T; a.H = H;
-        a.scale_log2 = scale * 1.4426950408889634f;
-        int blocks = 0, hoff = 0;
-        for (const Cls& c : cls) {
-            if ((c.W == 0) != (path == kPathA)) continue;
-            if (a.nclass == kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
-            AttnClass& k = a.cls[a.nclass++];
-            k.D = c.D; k.W = c.W; k.path = path;
-            k.nheads = (int)c.heads.size(); k.head_off = hoff;
-            for (int hh : c.heads) a.heads[hoff++] = (int16_t)hh;
-            const int Mmax = (T + c.D - 1) / c.D;
-            if (path == kPathA) {
-                k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
-                k.per_level = B * k.nheads * c.D;
-            } else {
-                k.levels = (Mmax + kAttnRowsB - 1) / kAttnRowsB;
-                const int ngroups = c.D >= 16 ? (c.D + 15) / 16 : 1;
-                k.per_level = B * k.nheads * ngroups;
-            }
-            const int64_t nb = (int64_t)k.levels * k.per_level;
-            if (nb + blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
-            k.block_begin = blocks;
-            blocks += (int)nb;
+    AttnArgs dil, band;
+    memset(&dil, 0, sizeof(dil));
+    dil.q = q; dil.ks = k_state; dil.vs = v_state; dil.kr = k_raw; dil.vr = v_raw; dil.out = out;
+    dil.ml = static_cast<float*>(workspace);
+    dil.B = B; dil.T = T; dil.H = H;
+    dil.scale_log2 = scale * 1.4426950408889634f;
+    band = dil;
+    int64_t items = 0, blocks = 0;
+    int hoff = 0;
+    for (const Cls& c : cls) {
+        AttnClass& k = dil.cls[dil.nclass++];
+        k.D = c.D; k.W = c.W;
+        k.nheads = (int)c.heads.size(); k.head_off = hoff;
+        for (int hh : c.heads) { dil.heads[hoff] = (int16_t)hh; band.heads[hoff] = (int16_t)hh; ++hoff; }
+        const int Mmax = (T + c.D - 1) / c.D;
+        k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
+        k.per_level = B * k.nheads * c.D;
+        k.block_begin = (int)items;
+        items += (int64_t)k.levels * k.per_level;
+        if (c.W > 0) {
+            AttnClass& kb = band.cls[band.nclass++];
+            kb = k;
+            kb.levels = (T + kAttnRowsA - 1) / kAttnRowsA;
+            kb.per_level = B * k.nheads;
+            kb.block_begin = (int)blocks;
+            blocks += (int64_t)kb.levels * kb.per_level;
         }
-        a.nblocks = blocks;
+        if (items >= ((int64_t)1 << 31) || blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
     }
-    if (args[kPathA].nblocks > 0) {
-        const int grid = std::min(args[kPathA].nblocks, device_cu_count());
-        const int rc = hip_status(launch_attn_dilated_bf16(args[kPathA], d, grid, s));
+    dil.nblocks = (int)items;
+    band.nblocks = (int)blocks;
+    if (band.nblocks > 0) {
+        const int rc = hip_status(launch_attn_band_bf16(band, d, s));
         if (rc != RAT_OK) return rc;
     }
-    if (args[kPathB].nblocks > 0) return hip_status(launch_attn_window_bf16(args[kPathB], d, s));
-    return RAT_OK;
+    const int grid = std::min(dil.nblocks, device_cu_count());
+    return hip_status(launch_attn_dilated_bf16(dil, d, grid, s));
 }
 
 namespace {

@@ -20,7 +20,7 @@
 // transposing V reads avoid bank conflicts, and are filled by direct
 // global->LDS loads.
 //
-// Path A (heads with W = 0, including dense D = 1): work items are
+// Path A (every head, including dense D = 1): work items are
 // (b, h, r, 256-row chunk).  Persistent workgroups of 8 waves take items in
 // a snake order over the cost-sorted item list; each wave owns two 16-row
 // blocks (w and 15-w, which balances the causal work) so that every K/V
@@ -28,14 +28,12 @@
 // stream through a 4-deep LDS ring whose prefetch runs on into the next
 // item, so every state row is read from HBM once per chunk.
 //
-// Path B (heads with W > 0): one workgroup per 2-D block of up to 16
-// residues x 16 rows.  Local phase: wave p takes 16 CONTIGUOUS queries
-// (for D >= 16: residues r0..r0+15 at one row) against their band of
-// W + 15 raw keys; the partial softmax state (m, l, acc) goes to LDS.
-// Dilated phase: wave g takes residue r0 + g (16 rows), starts its online
-// softmax from the local partials of those queries and runs over the
-// residue's states.  The hand-over through LDS is what lets both branches
-// use full 16-row MFMA fragments.
+// Local window (heads with W > 0): the raw-key band runs first, over
+// contiguous queries (where the band is dense), in a kernel that leaves a
+// partial softmax state per query -- normalised output in `out`, (m, l) in
+// a small workspace; path A then starts each query's online softmax from
+// that state and continues over the dilated states, so both branches share
+// one softmax and each runs on full 16-row MFMA fragments.
 #include "rat_device.h"
 #include "rat_internal.h"
 
@@ -89,37 +87,6 @@ __device__ __forceinline__ void copy_rows_lds(const uint16_t* row_ptr, int tile_
     dma16(row_ptr + c * 8, dst);
 }
 
-// K fragment (MFMA A operand of S^T = K Q^T) for keys 16*kb .. 16*kb+15 of
-// a tile, k-step ks: lane (g, i) holds K[key 16kb+i][dims 8g+32ks .. +8].
-template <int DK>
-__device__ __forceinline__ bf16x8 k_frag_lds(const lds_char* tile, int kb, int ks)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = kb * 16 + (lane & 15);
-    const int c = (lane >> 4) + 4 * ks;
-    return *reinterpret_cast<const bf16x8*>(tile + swz<DK>(r, c));
-}
-
-// V^T fragment (MFMA A operand of O^T += V^T P^T) for 16-dim block db over
-// the 32 keys 32*hh .. 32*hh+31 of a tile.  K-slot order of lane group g:
-// slots 0-3 = keys 4g..4g+3, slots 4-7 = keys 16+4g..16+4g+3 (the order in
-// which S^T leaves them).  Lane (g, i) receives V[key][dim 16db + i].
-template <int DK>
-__device__ __forceinline__ bf16x8 v_frag_lds(const lds_char* tile, int hh, int db)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane >> 4, s = lane & 15;
-    const int dim = 16 * db + 4 * (s & 3);
-    const int c = dim >> 3, off = (dim & 7) * 2;
-    const int r0 = 32 * hh + 4 * g + (s >> 2);
-    const int r1 = r0 + 16;
-    shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<DK>(r0, c) + off));
-    shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<DK>(r1, c) + off));
-    typedef short shortx8 __attribute__((ext_vector_type(8)));
-    shortx8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
 // max over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows) with
 // the gfx950 row-swap permutes (VALU only, no LDS traffic)
 __device__ __forceinline__ float max_over_rows(float x)
@@ -159,39 +126,26 @@ struct Frag {
         }
     }
 
-    // Scores of 32 keys (two S^T blocks) -> masked, scaled (log2 domain) ->
-    // softmax update -> P^T fragment.  `valid[kb][j]` says whether key
-    // 16kb + 4g + j is visible to this lane's query.
-    __device__ __forceinline__ bf16x8 softmax_step(floatx4 s0, floatx4 s1, const bool (&valid)[2][4], float scale_log2)
+    // Start from a partial softmax state over other keys of the same
+    // queries: its running max m (log2 domain), its sum l and its
+    // normalised output o (acc = o * l).  `rows` is the first of the
+    // block's 16 rows of o in a swizzled LDS slot, `ml` its (m, l) pairs.
+    // Lane (g, i) of query i takes dims 16db + 4g .. +3; only lane group 0
+    // carries l.
+    __device__ __forceinline__ void init_partial_lds(const lds_char* rows, const float* ml, bool valid)
     {
-        float x[8];
+        if (!valid) return;
+        const int lane = threadIdx.x & (kWave - 1);
+        const int g = lane >> 4, i = lane & 15;
+        const float pm = ml[2 * i], pl = ml[2 * i + 1];
+        m = pm;
+        l = g == 0 ? pl : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = valid[0][j] ? s0[j] * scale_log2 : -INFINITY;
-            x[4 + j] = valid[1][j] ? s1[j] * scale_log2 : -INFINITY;
+        for (int db = 0; db < Geo<DK>::DB; ++db) {
+            const int dim = 16 * db + 4 * g;
+            const u32x2 o = *reinterpret_cast<const u32x2*>(rows + swz<DK>(i, dim >> 3) + (dim & 7) * 2);
+            acc[db] = floatx4{bf16_lo(o[0]) * pl, bf16_hi(o[0]) * pl, bf16_lo(o[1]) * pl, bf16_hi(o[1]) * pl};
         }
-        float mx = x[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float msafe = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-        m = mnew;
-        float p[8], sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(x[j] - msafe);
-            sum += p[j];
-        }
-        l = l * alpha + sum;
-#pragma unroll
-        for (int i = 0; i < Geo<DK>::DB; ++i) acc[i] *= alpha;
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-        return pb;
     }
 
     __device__ __forceinline__ float total_l() const
@@ -215,6 +169,17 @@ struct Frag {
             *reinterpret_cast<u32x2*>(row_ptr + 16 * db + 4 * g) = o;
         }
     }
+
+    // Partial state for a later pass: normalised o in bf16 and (m, l)
+    __device__ __forceinline__ void store_partial(uint16_t* o_row, float* ml, bool valid) const
+    {
+        const float lt = total_l();
+        store(o_row, valid);
+        if (valid && (threadIdx.x & (kWave - 1)) < 16) {
+            ml[0] = m;
+            ml[1] = lt;
+        }
+    }
 };
 
 // ------------------------------------------------------------------ path A
@@ -223,7 +188,7 @@ constexpr int kTileA = 64;   // keys per K/V tile
 constexpr int kRingA = 4;    // LDS ring depth
 
 struct ItemA {
-    int b, h, D, r, R0, R1;
+    int b, h, D, W, r, R0, R1;
     bool valid;
 };
 
@@ -247,6 +212,7 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
     it.r = idx % k.D;
     it.b = idx / k.D;
     it.D = k.D;
+    it.W = k.W;
     const int M = it.r < a.T ? (a.T - it.r + k.D - 1) / k.D : 0;
     it.R0 = level * kAttnRowsA;
     it.R1 = min(it.R0 + kAttnRowsA, M);
@@ -255,9 +221,13 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 }
 
 // Walks this workgroup's items (snake order over rounds of gridDim.x) and
-// their tiles; the DMA issue cursor and the compute cursor are two copies.
+// the ring steps of each: nq slots of query rows (128 rows each), for
+// windowed classes as many slots of partial outputs, then the key tiles.
+// The DMA issue cursor and the compute cursor are two copies.
+constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
+
 struct CursorA {
-    int round, t, ntile;
+    int round, t, nq, no, ntile;
     ItemA it;
 
     __device__ __forceinline__ int item_of(int rnd) const
@@ -272,6 +242,8 @@ struct CursorA {
             it = decode_item_a(a, item_of(round));
             if (it.valid) {
                 t = 0;
+                nq = (it.R1 - it.R0 + kSlotRows - 1) / kSlotRows;
+                no = it.W > 0 ? nq : 0;
                 ntile = (it.R1 + kTileA - 1) / kTileA;
                 return;
             }
@@ -280,30 +252,50 @@ struct CursorA {
     }
     __device__ __forceinline__ void advance(const AttnArgs& a)
     {
-        if (++t == ntile) seek(a, round + 1);
+        if (++t == nq + no + ntile) seek(a, round + 1);
     }
 };
 
+// DMA of the cursor's ring step into slot `buf` (every wave issues the same
+// PER_WAVE row copies; partial-output steps add one copy of their (m, l)
+// words into `side` on waves 0-3).
 template <int DK>
-__device__ __forceinline__ void issue_tile_a(const AttnArgs& a, const CursorA& c, lds_char* buf)
+__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA& c, lds_char* buf, lds_char* side)
 {
     typedef Geo<DK> G;
-    constexpr int INSTR = 2 * kTileA / G::RPI;
+    constexpr int INSTR = kSlotRows / G::RPI;
     constexpr int PER_WAVE = INSTR / kWavesA;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int pitch = a.H * DK;
     const size_t base = ((size_t)c.it.b * a.T * a.H + c.it.h) * DK;
+    const int kt = c.t - c.nq - c.no;  // key tile index, < 0 for query / partial steps
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
         const int instr = wv * PER_WAVE + j;
-        const int trow = instr * G::RPI + lane / G::CH;  // K rows then V rows
-        const bool isv = trow >= kTileA;
-        const int kr = isv ? trow - kTileA : trow;
-        const int key = min(c.t * kTileA + kr, c.it.R1 - 1);
-        const uint16_t* src = static_cast<const uint16_t*>(isv ? a.vs : a.ks) + base +
-                              (size_t)(c.it.r + key * c.it.D) * pitch;
-        copy_rows_lds<DK>(src, kr, buf + instr * 1024);
+        const int trow = instr * G::RPI + lane / G::CH;  // row within the slot
+        const void* src;
+        int row;
+        if (kt < 0) {  // query rows, or partial outputs, R0 + 128 s + trow
+            const int s = c.t < c.nq ? c.t : c.t - c.nq;
+            row = min(c.it.R0 + s * kSlotRows + trow, c.it.R1 - 1);
+            src = c.t < c.nq ? a.q : a.out;
+        } else {       // K rows then V rows of key tile kt
+            const bool isv = trow >= kTileA;
+            row = min(kt * kTileA + (isv ? trow - kTileA : trow), c.it.R1 - 1);
+            src = isv ? a.vs : a.ks;
+        }
+        copy_rows_lds<DK>(static_cast<const uint16_t*>(src) + base + (size_t)(c.it.r + row * c.it.D) * pitch, trow,
+                          buf + instr * 1024);
+    }
+    if (kt < 0 && c.t >= c.nq && wv < 4) {
+        // (m, l) of the slot's 128 rows: 64 words per wave, lane l -> word l
+        const int w = wv * kWave + lane;
+        const int row = min(c.it.R0 + (c.t - c.nq) * kSlotRows + (w >> 1), c.it.R1 - 1);
+        const size_t t = (size_t)c.it.b * a.T + c.it.r + (size_t)row * c.it.D;
+        const float* src = a.ml + (t * a.H + c.it.h) * 2 + (w & 1);
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(side + wv * 256));
+        asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
     }
 }
 
@@ -346,16 +338,20 @@ __device__ __forceinline__ shortx4 lds_tr(const lds_char* p)
 // result is the same softmax).  Returns P^T operands for the two key halves.
 constexpr float kLazyRescale = 8.0f;
 
+// MASK: only keys in [lo, row] are visible to the lane's query.
 template <int DK, bool MASK>
-__device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row, int k0, float c, bf16x8 (&pb)[2])
+__device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row, int lo, int k0, float c,
+                                          bf16x8 (&pb)[2])
 {
     const int g = (threadIdx.x & (kWave - 1)) >> 4;
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (k0 + 16 * kb + 4 * g + j > row) s[kb][j] = -INFINITY;
+            for (int j = 0; j < 4; ++j) {
+                const int key = k0 + 16 * kb + 4 * g + j;
+                if (key > row || key < lo) s[kb][j] = -INFINITY;
+            }
     }
     float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
@@ -389,10 +385,11 @@ template <int DK>
 __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
-    constexpr int TILE_BYTES = 2 * kTileA * G::ROWB;
-    constexpr int PER_WAVE = (2 * kTileA / G::RPI) / kWavesA;
-    static_assert((2 * kTileA / G::RPI) % kWavesA == 0, "tile loads split evenly over waves");
+    constexpr int TILE_BYTES = kSlotRows * G::ROWB;
+    constexpr int PER_WAVE = (kSlotRows / G::RPI) / kWavesA;
+    static_assert((kSlotRows / G::RPI) % kWavesA == 0, "slot loads split evenly over waves");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
+    lds_char* side = smem + kRingA * TILE_BYTES;  // (m, l) words of partial-output slots, 1 KiB each
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -408,24 +405,63 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
 #pragma unroll
     for (int j = 0; j < kRingA - 1; ++j) {
         if (issue.it.valid) {
-            issue_tile_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES);
+            issue_step_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
             ++issued;
             issue.advance(a);
         }
     }
+    // Wait until ring step `seq` has landed, then barrier; refill the ring
+    // when the slot after step `oldest` (the oldest step still read after
+    // this barrier) is free.
+    auto wait_tile = [&](int seq, int oldest) {
+        const int ahead = issued - seq - 1;
+        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
+        else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (issue.it.valid && issued < oldest + kRingA) {
+            issue_step_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
+            ++issued;
+            issue.advance(a);
+        }
+    };
 
     while (comp.it.valid) {
         const ItemA it = comp.it;
         const size_t base = ((size_t)it.b * a.T * a.H + it.h) * DK;
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
         uint16_t* op = static_cast<uint16_t*>(a.out) + base;
         const int rsA = it.R0 + 16 * wv, rsB = it.R0 + 16 * (15 - wv);
         const bool hasA = rsA < it.R1, hasB = rsB < it.R1;
+        const int sA_ = (16 * wv) / kSlotRows, sB_ = (16 * (15 - wv)) / kSlotRows;  // slot of each block
+        const int oA = ((16 * wv) % kSlotRows) * G::ROWB, oB = ((16 * (15 - wv)) % kSlotRows) * G::ROWB;
         Frag<DK> fA, fB;
         fA.reset();
         fB.reset();
-        fA.load_q(qp + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
-        fB.load_q(qp + (size_t)(it.r + (rsB + i) * it.D) * pitch, rsB + i < it.R1);
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) { fA.q[ks] = bf16x8{}; fB.q[ks] = bf16x8{}; }
+        // query rows from the ring (lane (g, i): row i, dims 8g + 32ks .. +8)
+        for (int s = 0; s < comp.nq; ++s) {
+            wait_tile(consumed, consumed);
+            const lds_char* qt = smem + (consumed % kRingA) * TILE_BYTES;
+            if (sA_ == s) {
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks) fA.q[ks] = lds_b128(qt + oA + off.k[ks]);
+            }
+            if (sB_ == s) {
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks) fB.q[ks] = lds_b128(qt + oB + off.k[ks]);
+            }
+            ++consumed;
+        }
+        // windowed classes: continue from the band pass's partial state
+        for (int s = 0; s < comp.no; ++s) {
+            wait_tile(consumed, consumed);
+            const lds_char* ot = smem + (consumed % kRingA) * TILE_BYTES;
+            const float* ml = reinterpret_cast<const float*>(side + (consumed % kRingA) * 1024);
+            if (sA_ == s) fA.init_partial_lds(ot + oA, ml + ((16 * wv) % kSlotRows) * 2, rsA + i < it.R1);
+            if (sB_ == s) fB.init_partial_lds(ot + oB, ml + ((16 * (15 - wv)) % kSlotRows) * 2, rsB + i < it.R1);
+            ++consumed;
+        }
 
         // Tiles wholly below the chunk's first row are visible to every row
         // of the chunk: they run software-pipelined (the QK^T MFMAs of tile
@@ -433,21 +469,6 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
         // overlap within a wave) with no masks; the diagonal tiles follow on
         // the general path.
         const int nfull = min(it.R0 / kTileA, comp.ntile - 1);
-        // Wait until ring tile `seq` has landed, then barrier; refill the
-        // ring when the slot after tile `oldest` (the oldest tile still read
-        // after this barrier) is free.
-        auto wait_tile = [&](int seq, int oldest) {
-            const int ahead = issued - seq - 1;
-            if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
-            else if (ahead == 1) wait_vmcnt<PER_WAVE>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-            if (issue.it.valid && issued < oldest + kRingA) {
-                issue_tile_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES);
-                ++issued;
-                issue.advance(a);
-            }
-        };
         auto qk = [&](int seq, floatx4 (&sa)[4], floatx4 (&sb)[4]) {
             const lds_char* kt = smem + (seq % kRingA) * TILE_BYTES;
 #pragma unroll
@@ -490,8 +511,8 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
                 floatx4 nA[4], nB[4];
                 qk(consumed + 1, nA, nB);
                 bf16x8 pA[2], pB[2];
-                softmax64<DK, false>(fA, sA, 0, 0, a.scale_log2, pA);
-                softmax64<DK, false>(fB, sB, 0, 0, a.scale_log2, pB);
+                softmax64<DK, false>(fA, sA, 0, 0, 0, a.scale_log2, pA);
+                softmax64<DK, false>(fB, sB, 0, 0, 0, a.scale_log2, pB);
                 pv(consumed, pA, pB);
                 ++consumed;
 #pragma unroll
@@ -513,12 +534,12 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
             const bool needB = hasB && k0 <= rsB + 15;
             bf16x8 pA[2] = {}, pB[2] = {};
             if (needA) {
-                if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, k0, a.scale_log2, pA);
-                else softmax64<DK, true>(fA, sA, rsA + i, k0, a.scale_log2, pA);
+                if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, 0, k0, a.scale_log2, pA);
+                else softmax64<DK, true>(fA, sA, rsA + i, 0, k0, a.scale_log2, pA);
             }
             if (needB) {
-                if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, k0, a.scale_log2, pB);
-                else softmax64<DK, true>(fB, sB, rsB + i, k0, a.scale_log2, pB);
+                if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, 0, k0, a.scale_log2, pB);
+                else softmax64<DK, true>(fB, sB, rsB + i, 0, k0, a.scale_log2, pB);
             }
             pv(consumed, pA, pB);
             ++consumed;
@@ -529,190 +550,139 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
     }
 }
 
-// ------------------------------------------------------------------ path B
-// Each wave streams its own 32-key tiles: K fragments straight from HBM into
-// registers, V rows into the wave's private swizzled LDS tile.
-template <int DK>
-struct WaveStream {
-    typedef Geo<DK> G;
-    static constexpr int TILE = 32;
-
-    // key rows: position of key j of the tile is pos0 + j * step (clamped to last)
-    __device__ __forceinline__ static void load_v(const uint16_t* vbase, size_t pitch, int pos0, int step, int nkeys,
-                                                  lds_char* vt)
-    {
-        const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-        for (int j = 0; j < TILE / G::RPI; ++j) {
-            const int tr = j * G::RPI + lane / G::CH;
-            const int key = min(tr, nkeys - 1);
-            copy_rows_lds<DK>(vbase + (size_t)(pos0 + key * step) * pitch, tr, vt + j * 1024);
-        }
-    }
-
-    __device__ __forceinline__ static void load_k(const uint16_t* kbase, size_t pitch, int pos0, int step, int nkeys,
-                                                  bf16x8 (&kf)[2][G::KS])
-    {
-        const int lane = threadIdx.x & (kWave - 1);
-        const int g = lane >> 4, i = lane & 15;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int key = min(16 * kb + i, nkeys - 1);
-            const uint16_t* p = kbase + (size_t)(pos0 + key * step) * pitch + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks) kf[kb][ks] = *reinterpret_cast<const bf16x8*>(p + 32 * ks);
-        }
-    }
-};
-
-// Streams keys at positions pos0 + j*step, j in [0, nkeys), through fragment
-// f; `vis(j)` tells whether key j is visible to this lane's query.
-template <int DK, typename Vis>
-__device__ __forceinline__ void stream_keys(Frag<DK>& f, const uint16_t* kbase, const uint16_t* vbase, size_t pitch,
-                                            int pos0, int step, int nkeys, lds_char* vt, float scale_log2, Vis vis)
+// ------------------------------------------------------------------ band pass
+// Local window of raw keys for heads with W > 0: query t sees the raw keys
+// t-W+1 .. t.  A workgroup takes 256 contiguous queries of one (b, h) (two
+// 16-row blocks per wave, w and 15-w, as in path A) and streams the raw
+// key/value band [t0-W+1, t0+255] through the same 64-key LDS ring; a wave
+// skips the tiles that neither of its blocks sees.  It leaves a partial
+// softmax state per query -- the normalised output in `out` and (m, l) in
+// the workspace -- from which path A continues over the dilated states.
+__device__ __forceinline__ void decode_band(const AttnArgs& a, int block, int& b, int& h, int& W, int& t0)
 {
-    typedef Geo<DK> G;
-    const int g = (threadIdx.x & (kWave - 1)) >> 4;
-    for (int k0 = 0; k0 < nkeys; k0 += 32) {
-        const int n = min(32, nkeys - k0);
-        bf16x8 kf[2][G::KS];
-        WaveStream<DK>::load_v(vbase, pitch, pos0 + k0 * step, step, n, vt);
-        WaveStream<DK>::load_k(kbase, pitch, pos0 + k0 * step, step, n, kf);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_wave_barrier();
-        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            s0 = mfma16(kf[0][ks], f.q[ks], s0);
-            s1 = mfma16(kf[1][ks], f.q[ks], s1);
-        }
-        bool valid[2][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ka = k0 + 4 * g + j, kb = k0 + 16 + 4 * g + j;
-            valid[0][j] = ka < nkeys && vis(ka);
-            valid[1][j] = kb < nkeys && vis(kb);
-        }
-        const bf16x8 pb = f.softmax_step(s0, s1, valid, scale_log2);
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) f.acc[db] = mfma16(v_frag_lds<DK>(vt, 0, db), pb, f.acc[db]);
-        __builtin_amdgcn_wave_barrier();  // tr reads done before the tile is refilled
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads retired
-    }
+    int c = 0;
+    while (c + 1 < a.nclass && block >= a.cls[c + 1].block_begin) ++c;
+    const AttnClass& k = a.cls[c];
+    const int local = block - k.block_begin;
+    const int idx = local % k.per_level;
+    t0 = (local / k.per_level) * kAttnRowsA;
+    h = a.heads[k.head_off + idx % k.nheads];
+    b = idx / k.nheads;
+    W = k.W;
 }
 
 template <int DK>
-__device__ void path_b(const AttnArgs& a, int b, int h, int D, int W, int rgroup, int iblock, lds_char* smem)
+__global__ __launch_bounds__(kWavesA * kWave) void attn_band_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
-    const int T = a.T, pitch = a.H * DK;
+    constexpr int TILE_BYTES = 2 * kTileA * G::ROWB;
+    constexpr int PER_WAVE = (2 * kTileA / G::RPI) / kWavesA;
+    static_assert((2 * kTileA / G::RPI) % kWavesA == 0, "tile loads split evenly over waves");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int i = lane & 15, g = lane >> 4;
-    const size_t base = ((size_t)b * T * a.H + h) * DK;
+    const int i = lane & 15;
+    const int pitch = a.H * DK;
+    int b, h, W, t0;
+    decode_band(a, blockIdx.x, b, h, W, t0);
+    const int t1 = min(t0 + kAttnRowsA, a.T);
+    const int kbeg = max(0, t0 - W + 1) & ~(kTileA - 1);  // first tile, 64-aligned
+    const int ntile = (t1 - kbeg + kTileA - 1) / kTileA;
+    const size_t base = ((size_t)b * a.T * a.H + h) * DK;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
-    const uint16_t* ksp = static_cast<const uint16_t*>(a.ks) + base;
-    const uint16_t* vsp = static_cast<const uint16_t*>(a.vs) + base;
-    const uint16_t* krp = static_cast<const uint16_t*>(a.kr) + base;
-    const uint16_t* vrp = static_cast<const uint16_t*>(a.vr) + base;
     uint16_t* op = static_cast<uint16_t*>(a.out) + base;
 
-    const int r0 = D >= 16 ? 16 * rgroup : 0;
-    const int R = D >= 16 ? min(16, D - r0) : D;      // residues in the block
-    const int i0 = kAttnRowsB * iblock;               // first row
-    const int npieces = D >= 16 ? 16 : D;
-
-    // exchange area: slot = (residue - r0) * 16 + (row - i0)
-    float* xacc = reinterpret_cast<float*>(smem);
-    float* xm = xacc + 256 * DK;
-    float* xl = xm + 256;
-    lds_char* vt = smem + wv * (32 * G::ROWB);         // this wave's V tile
-
-    // ---- local phase: piece wv = contiguous positions [P, P + n)
-    Frag<DK> f;
-    f.reset();
-    int P = 0, n = 0;
-    if (wv < npieces) {
-        P = D >= 16 ? r0 + (i0 + wv) * D : i0 * D + 16 * wv;
-        const int len = D >= 16 ? R : 16;
-        n = P < T ? min(len, T - P) : 0;
-    }
-    const int tq = P + i;                               // this lane's query
-    const bool lvalid = i < n;
-    if (n > 0) {
-        f.load_q(qp + (size_t)tq * pitch, lvalid);
-        const int u0 = max(0, P - W + 1);
-        const int nk = P + n - u0;
-        stream_keys<DK>(f, krp, vrp, (size_t)pitch, u0, 1, nk, vt, a.scale_log2,
-                        [&](int j) { const int u = u0 + j; return lvalid && u <= tq && tq - u < W; });
-    }
-    const float lt = f.total_l();
-    __syncthreads();  // V tiles retired; the area becomes the exchange buffer
-    if (n > 0 && lvalid) {
-        const int slot = ((tq % D) - r0) * 16 + (tq / D - i0);
+    auto issue = [&](int tt) {
+        lds_char* buf = smem + (tt % kRingA) * TILE_BYTES;
 #pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-            *reinterpret_cast<floatx4*>(xacc + slot * DK + 16 * db + 4 * g) = f.acc[db];
-        if (g == 0) {
-            xm[slot] = f.m;
-            xl[slot] = lt;
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int instr = wv * PER_WAVE + j;
+            const int trow = instr * G::RPI + lane / G::CH;  // K rows then V rows
+            const bool isv = trow >= kTileA;
+            const int kr = isv ? trow - kTileA : trow;
+            const int key = min(kbeg + tt * kTileA + kr, t1 - 1);
+            const uint16_t* src = static_cast<const uint16_t*>(isv ? a.vr : a.kr) + base + (size_t)key * pitch;
+            copy_rows_lds<DK>(src, kr, buf + instr * 1024);
+        }
+    };
+    int issued = 0;
+#pragma unroll
+    for (int j = 0; j < kRingA - 1; ++j)
+        if (issued < ntile) issue(issued++);
+
+    LaneOffsets<DK> off;
+    off.init();
+    const int rsA = t0 + 16 * wv, rsB = t0 + 16 * (15 - wv);
+    const bool hasA = rsA < t1, hasB = rsB < t1;
+    Frag<DK> fA, fB;
+    fA.reset();
+    fB.reset();
+    fA.load_q(qp + (size_t)(rsA + i) * pitch, rsA + i < t1);
+    fB.load_q(qp + (size_t)(rsB + i) * pitch, rsB + i < t1);
+
+    for (int tt = 0; tt < ntile; ++tt) {
+        const int ahead = issued - tt - 1;
+        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
+        else if (ahead == 1) wait_vmcnt<PER_WAVE>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (issued < ntile) issue(issued++);
+        const int k0 = kbeg + tt * kTileA;
+        // block rows rs .. rs+15 see keys rs-W+1 .. rs+15 (each row its own band)
+        const bool needA = hasA && k0 <= rsA + 15 && k0 + kTileA - 1 >= rsA - W + 1;
+        const bool needB = hasB && k0 <= rsB + 15 && k0 + kTileA - 1 >= rsB - W + 1;
+        if (!(needA || needB)) continue;
+        const lds_char* kt = smem + (tt % kRingA) * TILE_BYTES;
+        const lds_char* vt = kt + kTileA * G::ROWB;
+        floatx4 sA[4], sB[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            sA[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            sB[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
+                sA[kb] = mfma16(kf, fA.q[ks], sA[kb]);
+                sB[kb] = mfma16(kf, fB.q[ks], sB[kb]);
+            }
+        }
+        bf16x8 pA[2] = {}, pB[2] = {};
+        // a tile inside every row's band needs no mask
+        if (needA) {
+            if (k0 >= rsA + 16 - W && k0 + kTileA - 1 <= rsA)
+                softmax64<DK, false>(fA, sA, 0, 0, 0, a.scale_log2, pA);
+            else
+                softmax64<DK, true>(fA, sA, rsA + i, rsA + i - W + 1, k0, a.scale_log2, pA);
+        }
+        if (needB) {
+            if (k0 >= rsB + 16 - W && k0 + kTileA - 1 <= rsB)
+                softmax64<DK, false>(fB, sB, 0, 0, 0, a.scale_log2, pB);
+            else
+                softmax64<DK, true>(fB, sB, rsB + i, rsB + i - W + 1, k0, a.scale_log2, pB);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
+                const shortx4 x0 = lds_tr(vp);
+                const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
+                typedef short shortx8 __attribute__((ext_vector_type(8)));
+                const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+                fA.acc[db] = mfma16(vf, pA[hh], fA.acc[db]);
+                fB.acc[db] = mfma16(vf, pB[hh], fB.acc[db]);
+            }
         }
     }
-    __syncthreads();
-
-    // ---- dilated phase: residue r0 + wv, rows i0 .. i0+15, seeded by the local partials
-    const int r = r0 + wv;
-    const int M = r < D && r < T ? (T - r + D - 1) / D : 0;
-    const int row = i0 + i;
-    const bool dvalid = wv < R && row < M;
-    Frag<DK> fd;
-    fd.reset();
-    if (dvalid) {
-        const int slot = wv * 16 + i;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-            fd.acc[db] = *reinterpret_cast<const floatx4*>(xacc + slot * DK + 16 * db + 4 * g);
-        fd.m = xm[slot];
-        fd.l = g == 0 ? xl[slot] : 0.f;
-    }
-    __syncthreads();  // exchange read; the area returns to V tiles
-    if (wv < R && i0 < M) {
-        fd.load_q(qp + (size_t)(r + row * D) * pitch, dvalid);
-        const int nk = min(i0 + 16, M);
-        stream_keys<DK>(fd, ksp, vsp, (size_t)pitch, r, D, nk, vt, a.scale_log2,
-                        [&](int j) { return dvalid && j <= row; });
-        fd.store(op + (size_t)(r + row * D) * pitch, dvalid);
-    }
+    const size_t rowA = (size_t)b * a.T + rsA + i, rowB = (size_t)b * a.T + rsB + i;
+    fA.store_partial(op + (size_t)(rsA + i) * pitch, a.ml + (rowA * a.H + h) * 2, rsA + i < t1);
+    fB.store_partial(op + (size_t)(rsB + i) * pitch, a.ml + (rowB * a.H + h) * 2, rsB + i < t1);
 }
 
-// ------------------------------------------------------------------ kernels
-template <int DK>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_window_kernel(AttnArgs a)
-{
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int blk = blockIdx.x;
-    int c = 0;
-    while (c + 1 < a.nclass && blk >= a.cls[c + 1].block_begin) ++c;
-    const AttnClass& k = a.cls[c];
-    const int local = blk - k.block_begin;
-    const int level = k.levels - 1 - local / k.per_level;  // most expensive first
-    int idx = local % k.per_level;
-    const int ngroups = k.D >= 16 ? (k.D + 15) / 16 : 1;
-    const int rg = idx % ngroups;
-    idx /= ngroups;
-    const int h = a.heads[k.head_off + idx % k.nheads];
-    const int b = idx / k.nheads;
-    path_b<DK>(a, b, h, k.D, k.W, rg, level, smem);
-}
-
-size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * 2 * kTileA * d * 2; }
-
-size_t attn_lds_bytes_b(int d)
-{
-    const size_t vt = kAttnWaves * 32 * (size_t)d * 2;     // V tiles
-    const size_t xch = 256 * (size_t)d * 4 + 2 * 256 * 4;  // exchange
-    return vt > xch ? vt : xch;
-}
+// ring slots plus the (m, l) side buffers of path A
+size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * (2 * kTileA * d * 2 + 1024); }
 
 template <typename K>
 static void set_lds(K kernel, size_t lds, bool& done)
@@ -737,16 +707,16 @@ hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_attn_window_bf16(const AttnArgs& a, int d, hipStream_t stream)
+hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, hipStream_t stream)
 {
-    const size_t lds = attn_lds_bytes_b(d);
+    const size_t lds = attn_lds_bytes_a(d);
     static bool s128 = false, s64 = false;
     if (d == 128) {
-        set_lds(attn_window_kernel<128>, lds, s128);
-        hipLaunchKernelGGL(attn_window_kernel<128>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+        set_lds(attn_band_kernel<128>, lds, s128);
+        hipLaunchKernelGGL(attn_band_kernel<128>, dim3(a.nblocks), dim3(kWavesA * kWave), lds, stream, a);
     } else {
-        set_lds(attn_window_kernel<64>, lds, s64);
-        hipLaunchKernelGGL(attn_window_kernel<64>, dim3(a.nblocks), dim3(kAttnWaves * kWave), lds, stream, a);
+        set_lds(attn_band_kernel<64>, lds, s64);
+        hipLaunchKernelGGL(attn_band_kernel<64>, dim3(a.nblocks), dim3(kWavesA * kWave), lds, stream, a);
     }
     return hipGetLastError();
 }

@@ -53,24 +53,21 @@ struct ScanSlideArgs {
 
 hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, hipStream_t stream);
+// SLIDING with L = 64 in bf16 (N a multiple of 64)
+hipError_t launch_scan_slide64(const ScanSlideArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnMaxClasses = 8;
 constexpr int kAttnMaxHeads = 256;
-constexpr int kAttnWaves = 16;
-constexpr int kAttnRowsA = 256;   // query rows of one residue per path-A item
-constexpr int kAttnRowsB = 16;    // rows per residue in a path-B block
-
-enum { kPathA = 0, kPathB = 1 };
+constexpr int kAttnRowsA = 256;   // query rows of one residue per path-A item / band block
 
 struct AttnClass {
     int D, W;
-    int path;        // kPathA (W == 0) or kPathB (W > 0)
     int nheads;      // heads in this class
     int head_off;    // first entry in AttnArgs::heads
     int levels;      // cost levels (dispatched most expensive first)
     int per_level;   // items per level
-    int block_begin; // first blockIdx.x of the class
+    int block_begin; // first item of the class
 };
 
 struct AttnArgs {
@@ -80,6 +77,7 @@ struct AttnArgs {
     const void* kr;
     const void* vr;
     void* out;
+    float* ml;         // [B][T][H][2] partial (m, l) of the band pass (heads with W > 0)
     int B, T, H;
     float scale_log2;  // softmax scale * log2(e)
     int nclass;
@@ -88,10 +86,10 @@ struct AttnArgs {
     int16_t heads[kAttnMaxHeads];
 };
 
-// heads with W == 0: persistent kernel, `grid` workgroups (nblocks = items)
+// dilated states, every head: persistent kernel, `grid` workgroups (nblocks = items)
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
-// heads with W > 0: one workgroup per 2-D block (nblocks = blocks)
-hipError_t launch_attn_window_bf16(const AttnArgs& a, int d, hipStream_t stream);
+// raw-key band of heads with W > 0: one workgroup per 256 queries (nblocks)
+hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, hipStream_t stream);
 
 // Simple fp32 path (one workgroup per query row; exact fp32 arithmetic).
 struct AttnF32Args {

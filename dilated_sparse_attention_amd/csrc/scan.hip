@@ -424,6 +424,144 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
     }
 }
 
+// ------------------------------------------------------- SLIDING, L = 64
+// bf16 fast path of the pages' window L* = 64: a workgroup takes 128 tokens
+// (two 64-token tiles) of one 64-channel block plus the 64 tokens before
+// them, copied into LDS 16 bytes per lane.  Wave w owns tokens 16w .. 16w+15
+// of the chunk, lane = channel: a forward recurrence from zero over its
+// tokens, the in-tile carry from the waves before it through LDS, then a
+// reverse pass over the previous tile gives each token its suffix
+// X_j = sum_{s=j+1}^{63} (prod_{r=s+1}^{63} g_r)(1-g_s) x_s, and
+// h_t = H_t + P_t * X_j with H_t, P_t the in-tile state and gate product.
+// The previous tile is re-read once per chunk (1.5x input bytes); two
+// workgroups fit on a compute unit.
+constexpr int kSlideCT = 128, kSlideHalo = 64, kSlideBW = 64;
+
+__global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArgs a)
+{
+    constexpr int ROWB = kSlideBW * 2;           // bytes of a 64-channel bf16 row
+    constexpr int NROW = kSlideCT + kSlideHalo;  // rows per tensor in LDS
+    constexpr int RPG = 1024 / ROWB;             // rows per 1 KiB wave copy
+    constexpr int LPR = ROWB / 16;               // lanes per row in a wave copy
+    constexpr int TPW = kSlideCT / kScanWaves;   // tokens per wave
+    constexpr int NIN = 3 * NROW / RPG;
+    constexpr int NOUT = 2 * kSlideCT / RPG;
+    static_assert(NIN % kScanWaves == 0 && NOUT % kScanWaves == 0 && NROW % RPG == 0, "even copies");
+    static_assert(kSlideBW == kWave, "one channel per lane");
+    extern __shared__ __attribute__((aligned(1024))) char s_tile[];  // [3][NROW][ROWB]: k, v, logits
+    __shared__ float s_map[kScanWaves][3][kSlideBW];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nblk = a.N / kSlideBW;
+    const int blk = blockIdx.x % nblk;
+    const int b = (blockIdx.x / nblk) % a.B;
+    const int chunk = blockIdx.x / (nblk * a.B);
+    const int tb = chunk * kSlideCT;             // first token of the chunk
+    const int r0 = tb - kSlideHalo;              // token of LDS row 0
+    const size_t rowbase = (size_t)b * a.T * a.N + (size_t)blk * kSlideBW;
+
+    {
+        const uint16_t* src[3] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                                  static_cast<const uint16_t*>(a.g)};
+#pragma unroll
+        for (int j = 0; j < NIN / kScanWaves; ++j) {
+            const int q = j * kScanWaves + w;
+            const int row = q * RPG + lane / LPR;
+            const int t = min(max(r0 + row % NROW, 0), a.T - 1);
+            dma16(src[row / NROW] + rowbase + (size_t)t * a.N + (lane % LPR) * 8, s_tile + q * 1024);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    auto at = [&](int tensor, int row) -> float {  // channel `lane` of an LDS row
+        const uint16_t x = *reinterpret_cast<const uint16_t*>(s_tile + (tensor * NROW + row) * ROWB + lane * 2);
+        return __uint_as_float((uint32_t)x << 16);
+    };
+
+    // forward: local recurrence over this wave's tokens from a zero state
+    const int rw = kSlideHalo + w * TPW;  // LDS row of the wave's first token
+    float A = 1.f, K = 0.f, V = 0.f;
+    float hk[TPW], hv[TPW], pg[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        float g, gb;
+        forget_gate(at(2, rw + i), g, gb);
+        A *= g;
+        K = fmaf(g, K, gb * at(0, rw + i));
+        V = fmaf(g, V, gb * at(1, rw + i));
+        hk[i] = K; hv[i] = V; pg[i] = A;
+    }
+    s_map[w][0][lane] = A;
+    s_map[w][1][lane] = K;
+    s_map[w][2][lane] = V;
+    __syncthreads();
+
+    // in-tile carry: the waves of this tile before this one
+    const int tl = w / 4, wt = w % 4;
+    float cA = 1.f, cK = 0.f, cV = 0.f;
+    for (int ww = 4 * tl; ww < w; ++ww) {
+        const float sa = s_map[ww][0][lane];
+        cK = fmaf(sa, cK, s_map[ww][1][lane]);
+        cV = fmaf(sa, cV, s_map[ww][2][lane]);
+        cA *= sa;
+    }
+
+    // reverse over the previous tile (LDS rows 64 tl .. 64 tl + 63): the
+    // suffix X_j of offset j = 16 wt + i, then h = H + P (carry + A X_j)
+    float Xk = 0.f, Xv = 0.f, Q = 1.f;
+    const bool has_prev = tb + 64 * tl > 0;
+    const int pr = 64 * tl;
+    if (has_prev) {
+        for (int s2 = 63; s2 >= 16 * wt + TPW; --s2) {
+            float g, gb;
+            forget_gate(at(2, pr + s2), g, gb);
+            const float qg = Q * gb;
+            Xk = fmaf(qg, at(0, pr + s2), Xk);
+            Xv = fmaf(qg, at(1, pr + s2), Xv);
+            Q *= g;
+        }
+    }
+#pragma unroll
+    for (int i = TPW - 1; i >= 0; --i) {
+        hk[i] = fmaf(pg[i], fmaf(cA, Xk, cK), hk[i]);
+        hv[i] = fmaf(pg[i], fmaf(cA, Xv, cV), hv[i]);
+        if (has_prev) {
+            const int s2 = 16 * wt + i;
+            float g, gb;
+            forget_gate(at(2, pr + s2), g, gb);
+            const float qg = Q * gb;
+            Xk = fmaf(qg, at(0, pr + s2), Xk);
+            Xv = fmaf(qg, at(1, pr + s2), Xv);
+            Q *= g;
+        }
+    }
+    __syncthreads();  // every wave is done reading the inputs
+
+    // states over the chunk's key / value rows, then 16-byte stores
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        *reinterpret_cast<uint16_t*>(s_tile + (rw + i) * ROWB + lane * 2) = __builtin_bit_cast(uint16_t, (__bf16)hk[i]);
+        *reinterpret_cast<uint16_t*>(s_tile + (NROW + rw + i) * ROWB + lane * 2) =
+            __builtin_bit_cast(uint16_t, (__bf16)hv[i]);
+    }
+    __syncthreads();
+    {
+        uint16_t* dst[2] = {static_cast<uint16_t*>(a.ks), static_cast<uint16_t*>(a.vs)};
+#pragma unroll
+        for (int j = 0; j < NOUT / kScanWaves; ++j) {
+            const int q = j * kScanWaves + w;
+            const int row = q * RPG + lane / LPR;  // 0 .. 2 CT - 1
+            const int tensor = row / kSlideCT, tok = row % kSlideCT;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(
+                s_tile + (tensor * NROW + kSlideHalo + tok) * ROWB + (lane % LPR) * 16);
+            if (tb + tok < a.T)
+                *reinterpret_cast<u32x4*>(dst[tensor] + rowbase + (size_t)(tb + tok) * a.N + (lane % LPR) * 8) = val;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launches
 hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream)
 {
@@ -443,4 +581,19 @@ hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, h
     return hipGetLastError();
 }
 
+}  // namespace rat
+
+namespace rat {
+hipError_t launch_scan_slide64(const ScanSlideArgs& a, hipStream_t stream)
+{
+    static bool attr = false;
+    const size_t lds = 3 * (size_t)(kSlideCT + kSlideHalo) * kSlideBW * 2;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)scan_slide64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        attr = true;
+    }
+    const int nchunk = (a.T + kSlideCT - 1) / kSlideCT;
+    hipLaunchKernelGGL(scan_slide64_kernel, dim3(nchunk * a.B * (a.N / kSlideBW)), dim3(kScanThreads), lds, stream, a);
+    return hipGetLastError();
+}
 }  // namespace rat

@@ -25,7 +25,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
           4: "RAT_ERR_ALIAS", 5: "RAT_ERR_WORKSPACE", 6: "RAT_ERR_HIP", 7: "RAT_ERR_ALIGN"}
 
 # every symbol include/rat.h declares
-EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_dilated_attn_prefill",
+EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
            "rat_decode_workspace_bytes", "rat_dilated_attn_decode", "rat_status_string",
            "rat_last_hip_error")
 
@@ -58,7 +58,9 @@ def load_library(path: str = LIBRARY):
     lib.rat_scan_workspace_bytes.restype = sz
     lib.rat_scan_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.rat_scan_prefill.restype = i
-    lib.rat_dilated_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ip, ip, f, i, vp]
+    lib.rat_attn_prefill_workspace_bytes.argtypes = [i, i, i, i, ip, ip, i]
+    lib.rat_attn_prefill_workspace_bytes.restype = sz
+    lib.rat_dilated_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
     lib.rat_dilated_attn_prefill.restype = i
     lib.rat_decode_workspace_bytes.argtypes = [i, i, i, i, ip, ip]
     lib.rat_decode_workspace_bytes.restype = sz
@@ -148,7 +150,27 @@ def scan_prefill(k, v, gate_logits, L=None, mode=RESTART, k_state=None, v_state=
 
 
 # ------------------------------------------------------------------ attention
-def dilated_attn_prefill(q, k_state, v_state, k_raw=None, v_raw=None, D=1, W=0, scale=None, out=None):
+def attn_prefill_workspace_bytes(B, T, H, d, D, W, dtype=torch.bfloat16):
+    return int(load_library().rat_attn_prefill_workspace_bytes(B, T, H, d, _heads(D, H), _heads(W, H),
+                                                               _DTYPES[dtype]))
+
+
+_attn_workspaces = {}
+
+
+def attn_workspace(nbytes, device):
+    """Scratch for the local-window pass of prefill attention (no
+    initialisation needed), kept per device and grown on demand."""
+    key = torch.device(device).index
+    ws = _attn_workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _attn_workspaces[key] = ws
+    return ws
+
+
+def dilated_attn_prefill(q, k_state, v_state, k_raw=None, v_raw=None, D=1, W=0, scale=None, out=None,
+                         workspace=None):
     """Dilated (+ local window) causal attention over the recurrent states."""
     lib = load_library()
     B, T, H, d = q.shape
@@ -157,9 +179,13 @@ def dilated_attn_prefill(q, k_state, v_state, k_raw=None, v_raw=None, D=1, W=0, 
     out = torch.empty_like(q) if out is None else out
     _check_tensor("out", out, q.dtype, q.shape)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    nbytes = lib.rat_attn_prefill_workspace_bytes(B, T, H, d, Dh, Wh, _DTYPES[q.dtype])
+    if workspace is None and nbytes:
+        workspace = attn_workspace(nbytes, q.device)
     rc = lib.rat_dilated_attn_prefill(_ptr(q), _ptr(k_state), _ptr(v_state), _ptr(k_raw), _ptr(v_raw),
-                                      _ptr(out), B, T, H, d, _heads(D, H), _heads(W, H), scale,
-                                      _DTYPES[q.dtype], _stream())
+                                      _ptr(out), B, T, H, d, Dh, Wh, scale, _DTYPES[q.dtype], _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _stream())
     _raise("rat_dilated_attn_prefill", rc, lib)
     return out
 

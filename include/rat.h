@@ -90,6 +90,12 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
                      rat_dtype dtype, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Bytes of device workspace rat_dilated_attn_prefill needs (0 when no head
+ * has a local window, or for fp32): B*T*H*2 floats holding the partial
+ * softmax state of the window pass.  16-byte aligned; no initialisation. */
+size_t rat_attn_prefill_workspace_bytes(int B, int T, int H, int d, const int* D, const int* W,
+                                        rat_dtype dtype);
+
 /* Stage 2, prefill (RAT+ Abstract; Deep Dive 1 and 6): for every query
  * (b, t, h) one softmax over
  *   the recurrent states  k_state/v_state at t, t-D[h], t-2D[h], ... >= 0,
@@ -98,12 +104,15 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
  *   q, k_state, v_state, k_raw, v_raw, out : [B,T,H,d];
  *   k_raw / v_raw may be NULL iff every W[h] == 0;
  *   D, W : host int[H], D[h] >= 1, W[h] >= 0 (D[h] = 1, W[h] = 0 is dense
- *          causal attention over the states).
- * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
+ *          causal attention over the states);
+ *   workspace : at least rat_attn_prefill_workspace_bytes(...) bytes, may
+ *          be NULL when that is 0.  Calls in flight must not share it.
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
 int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state,
                              const void* k_raw, const void* v_raw, void* out,
                              int B, int T, int H, int d, const int* D, const int* W,
-                             float scale, rat_dtype dtype, void* stream);
+                             float scale, rat_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace rat_dilated_attn_decode needs (0 when none; it
  * holds split-key partial softmax states when B*H is small). 256-byte

@@ -92,10 +92,10 @@ def test_scan_workspace_sizes(lib):
 
 
 def attn(lib, q=P[0], ks=P[1], vs=P[2], kr=P[3], vr=P[4], out=P[5], B=1, T=64, H=2, d=128,
-         D=(4, 4), W=(0, 8), scale=0.1, dtype=1):
+         D=(4, 4), W=(0, 8), scale=0.1, dtype=1, ws=P[6], wsb=1 << 30):
     Dh = None if D is None else heads(D)
     Wh = None if W is None else heads(W)
-    return lib.rat_dilated_attn_prefill(q, ks, vs, kr, vr, out, B, T, H, d, Dh, Wh, scale, dtype, None)
+    return lib.rat_dilated_attn_prefill(q, ks, vs, kr, vr, out, B, T, H, d, Dh, Wh, scale, dtype, ws, wsb, None)
 
 
 def test_attn_validation(lib):
@@ -116,6 +116,15 @@ def test_attn_validation(lib):
     assert attn(lib, H=H, D=[1] * H, W=[0] * H) == UNSUP  # more heads than the kernel table
     many = [(i % 9) + 1 for i in range(16)]
     assert attn(lib, H=16, D=many, W=[0] * 16) == UNSUP  # more than 8 (D, W) classes
+    # a head with a window needs the partial-state workspace
+    assert attn(lib, ws=None) == WSPACE
+    assert attn(lib, wsb=8) == WSPACE
+
+
+def test_attn_workspace_sizes(lib):
+    assert lib.rat_attn_prefill_workspace_bytes(1, 64, 2, 128, heads([4, 4]), heads([0, 8]), 1) == 64 * 2 * 8
+    assert lib.rat_attn_prefill_workspace_bytes(4, 4096, 16, 128, heads([16] * 16), heads([0] * 16), 1) == 0
+    assert lib.rat_attn_prefill_workspace_bytes(1, 64, 2, 128, heads([4, 4]), heads([0, 8]), 0) == 0  # fp32
 
 
 def decode(lib, q=P[0], kd=P[1], vd=P[2], nd_cap=512, kw=P[3], vw=P[4], w_cap=64, out=P[5], B=4, T=32768,

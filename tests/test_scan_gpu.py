@@ -23,6 +23,9 @@ CASES = [
     (1, 700, 2, 128, 64, 0, torch.bfloat16),      # RESTART at L* = 64
     (1, 700, 2, 128, 7, 0, torch.bfloat16),
     (1, 700, 2, 128, 64, 1, torch.bfloat16),      # SLIDING at L* = 64
+    (2, 1000, 3, 64, 64, 1, torch.bfloat16),      # SLIDING L = 64: ragged chunks, 192 channels
+    (1, 65, 2, 128, 64, 1, torch.bfloat16),       # one token past the first tile
+    (1, 129, 1, 64, 64, 1, torch.bfloat16),       # one token past the first chunk
     (2, 333, 1, 64, 16, 1, torch.bfloat16),
     (1, 200, 1, 64, 1, 1, torch.bfloat16),
     (1, 90, 1, 128, 5, 1, torch.bfloat16),
