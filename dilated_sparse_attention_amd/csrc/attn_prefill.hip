@@ -87,6 +87,16 @@ __device__ __forceinline__ void copy_rows_lds(const uint16_t* row_ptr, int tile_
     dma16(row_ptr + c * 8, dst);
 }
 
+// max of three scores in one v_max3_f32: the operands come straight from
+// MFMA accumulators or -inf masks, so the quieting of signalling NaNs that
+// fmaxf implies (an extra v_max per operand) is not needed
+__device__ __forceinline__ float max3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // max over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows) with
 // the gfx950 row-swap permutes (VALU only, no LDS traffic)
 __device__ __forceinline__ float max_over_rows(float x)
@@ -353,9 +363,14 @@ __device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row,
                 if (key > row || key < lo) s[kb][j] = -INFINITY;
             }
     }
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-#pragma unroll
-    for (int kb = 1; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+    float mx = max3(s[0][0], s[0][1], s[0][2]);
+    mx = max3(mx, s[0][3], s[1][0]);
+    mx = max3(mx, s[1][1], s[1][2]);
+    mx = max3(mx, s[1][3], s[2][0]);
+    mx = max3(mx, s[2][1], s[2][2]);
+    mx = max3(mx, s[2][3], s[3][0]);
+    mx = max3(mx, s[3][1], s[3][2]);
+    mx = fmaxf(mx, s[3][3]);
     mx = max_over_rows(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > f.m + kLazyRescale)) {
         const float mn = fmaxf(f.m, mx);
