@@ -269,12 +269,12 @@ struct CursorA {
 // DMA of the cursor's ring step into slot `buf` (every wave issues the same
 // PER_WAVE row copies; partial-output steps add one copy of their (m, l)
 // words into `side` on waves 0-3).
-template <int DK>
+template <int DK, int NW>
 __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA& c, lds_char* buf, lds_char* side)
 {
     typedef Geo<DK> G;
     constexpr int INSTR = kSlotRows / G::RPI;
-    constexpr int PER_WAVE = INSTR / kWavesA;
+    constexpr int PER_WAVE = INSTR / NW;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int pitch = a.H * DK;
@@ -299,7 +299,7 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA& c
                           buf + instr * 1024);
     }
     if (kt < 0 && c.t >= c.nq && wv < 4) {
-        // (m, l) of the slot's 128 rows: 64 words per wave, lane l -> word l
+        // (m, l) of the slot's 128 rows: 64 words per wave on waves 0-3, lane l -> word l
         const int w = wv * kWave + lane;
         const int row = min(c.it.R0 + (c.t - c.nq) * kSlotRows + (w >> 1), c.it.R1 - 1);
         const size_t t = (size_t)c.it.b * a.T + c.it.r + (size_t)row * c.it.D;
@@ -396,13 +396,25 @@ __device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row,
     f.l += sum;
 }
 
-template <int DK>
-__global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs a)
+// NW waves per workgroup, NB = 16 / NW row blocks of 16 queries per wave
+// (block w and its mirror 15 - w, with NB = 4 also 7 - w and 8 + w, so that
+// every wave has the same causal work).  Every K / V fragment read from LDS
+// feeds NB MFMAs: more rows per wave means less LDS traffic per FLOP.
+template <int NB>
+__device__ __forceinline__ int row_block(int wv, int j)
+{
+    return j == 0 ? wv : j == 1 ? 15 - wv : j == 2 ? 7 - wv : 8 + wv;
+}
+
+template <int DK, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
+    constexpr int NB = 16 / NW;
+    static_assert(NB == 2 || NB == 4, "two or four row blocks per wave");
     constexpr int TILE_BYTES = kSlotRows * G::ROWB;
-    constexpr int PER_WAVE = (kSlotRows / G::RPI) / kWavesA;
-    static_assert((kSlotRows / G::RPI) % kWavesA == 0, "slot loads split evenly over waves");
+    constexpr int PER_WAVE = (kSlotRows / G::RPI) / NW;
+    static_assert((kSlotRows / G::RPI) % NW == 0, "slot loads split evenly over waves");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     lds_char* side = smem + kRingA * TILE_BYTES;  // (m, l) words of partial-output slots, 1 KiB each
 
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
 #pragma unroll
     for (int j = 0; j < kRingA - 1; ++j) {
         if (issue.it.valid) {
-            issue_step_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
+            issue_step_a<DK, NW>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
             ++issued;
             issue.advance(a);
         }
@@ -435,36 +447,38 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
         else wait_vmcnt<0>();
         __syncthreads();
         if (issue.it.valid && issued < oldest + kRingA) {
-            issue_step_a<DK>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
+            issue_step_a<DK, NW>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
             ++issued;
             issue.advance(a);
         }
     };
 
+    Frag<DK> f[NB];
     while (comp.it.valid) {
         const ItemA it = comp.it;
         const size_t base = ((size_t)it.b * a.T * a.H + it.h) * DK;
         uint16_t* op = static_cast<uint16_t*>(a.out) + base;
-        const int rsA = it.R0 + 16 * wv, rsB = it.R0 + 16 * (15 - wv);
-        const bool hasA = rsA < it.R1, hasB = rsB < it.R1;
-        const int sA_ = (16 * wv) / kSlotRows, sB_ = (16 * (15 - wv)) / kSlotRows;  // slot of each block
-        const int oA = ((16 * wv) % kSlotRows) * G::ROWB, oB = ((16 * (15 - wv)) % kSlotRows) * G::ROWB;
-        Frag<DK> fA, fB;
-        fA.reset();
-        fB.reset();
+        int rs[NB];    // first row of each block
+        bool has[NB];  // block holds rows of the item
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) { fA.q[ks] = bf16x8{}; fB.q[ks] = bf16x8{}; }
+        for (int j = 0; j < NB; ++j) {
+            rs[j] = it.R0 + 16 * row_block<NB>(wv, j);
+            has[j] = rs[j] < it.R1;
+            f[j].reset();
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) f[j].q[ks] = bf16x8{};
+        }
         // query rows from the ring (lane (g, i): row i, dims 8g + 32ks .. +8)
         for (int s = 0; s < comp.nq; ++s) {
             wait_tile(consumed, consumed);
             const lds_char* qt = smem + (consumed % kRingA) * TILE_BYTES;
-            if (sA_ == s) {
 #pragma unroll
-                for (int ks = 0; ks < G::KS; ++ks) fA.q[ks] = lds_b128(qt + oA + off.k[ks]);
-            }
-            if (sB_ == s) {
+            for (int j = 0; j < NB; ++j) {
+                const int r = 16 * row_block<NB>(wv, j);
+                if (r / kSlotRows == s) {
 #pragma unroll
-                for (int ks = 0; ks < G::KS; ++ks) fB.q[ks] = lds_b128(qt + oB + off.k[ks]);
+                    for (int ks = 0; ks < G::KS; ++ks) f[j].q[ks] = lds_b128(qt + (r % kSlotRows) * G::ROWB + off.k[ks]);
+                }
             }
             ++consumed;
         }
@@ -473,32 +487,30 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
             wait_tile(consumed, consumed);
             const lds_char* ot = smem + (consumed % kRingA) * TILE_BYTES;
             const float* ml = reinterpret_cast<const float*>(side + (consumed % kRingA) * 1024);
-            if (sA_ == s) fA.init_partial_lds(ot + oA, ml + ((16 * wv) % kSlotRows) * 2, rsA + i < it.R1);
-            if (sB_ == s) fB.init_partial_lds(ot + oB, ml + ((16 * (15 - wv)) % kSlotRows) * 2, rsB + i < it.R1);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int r = 16 * row_block<NB>(wv, j);
+                if (r / kSlotRows == s)
+                    f[j].init_partial_lds(ot + (r % kSlotRows) * G::ROWB, ml + (r % kSlotRows) * 2, rs[j] + i < it.R1);
+            }
             ++consumed;
         }
 
-        // Tiles wholly below the chunk's first row are visible to every row
-        // of the chunk: they run software-pipelined (the QK^T MFMAs of tile
-        // t+1 are issued before the softmax of tile t, so MFMA and VALU work
-        // overlap within a wave) with no masks; the diagonal tiles follow on
-        // the general path.
-        const int nfull = min(it.R0 / kTileA, comp.ntile - 1);
-        auto qk = [&](int seq, floatx4 (&sa)[4], floatx4 (&sb)[4]) {
+        auto qk = [&](int seq, floatx4 (&sc)[NB][4]) {
             const lds_char* kt = smem + (seq % kRingA) * TILE_BYTES;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                sa[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-                sb[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < NB; ++j) sc[j][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < G::KS; ++ks) {
                     const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
-                    sa[kb] = mfma16(kf, fA.q[ks], sa[kb]);
-                    sb[kb] = mfma16(kf, fB.q[ks], sb[kb]);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) sc[j][kb] = mfma16(kf, f[j].q[ks], sc[j][kb]);
                 }
             }
         };
-        auto pv = [&](int seq, const bf16x8 (&pa)[2], const bf16x8 (&pbb)[2]) {
+        auto pv = [&](int seq, const bf16x8 (&pb)[NB][2]) {
             const lds_char* vt = smem + (seq % kRingA) * TILE_BYTES + kTileA * G::ROWB;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -510,57 +522,65 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_dilated_kernel(AttnArgs 
                     typedef short shortx8 __attribute__((ext_vector_type(8)));
                     const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
                     const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-                    fA.acc[db] = mfma16(vf, pa[hh], fA.acc[db]);
-                    fB.acc[db] = mfma16(vf, pbb[hh], fB.acc[db]);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) f[j].acc[db] = mfma16(vf, pb[j][hh], f[j].acc[db]);
                 }
             }
         };
 
-        floatx4 sA[4], sB[4];
+        // Tiles wholly below the chunk's first row are visible to every row
+        // of the chunk and need no mask.  With two blocks per wave they run
+        // software-pipelined (the QK^T MFMAs of tile t+1 are issued before
+        // the softmax of tile t); four blocks have no registers for a
+        // second set of scores and rely on the MFMAs of one block running
+        // while the softmax of another is computed.
+        const int nfull = min(it.R0 / kTileA, comp.ntile - 1);
+        floatx4 sc[NB][4];
         bool have_scores = false;
-        if (nfull > 0) {
-            wait_tile(consumed, consumed);
-            qk(consumed, sA, sB);
-            for (int tt = 0; tt < nfull; ++tt) {
-                wait_tile(consumed + 1, consumed);  // tile `consumed` still feeds P V
-                floatx4 nA[4], nB[4];
-                qk(consumed + 1, nA, nB);
-                bf16x8 pA[2], pB[2];
-                softmax64<DK, false>(fA, sA, 0, 0, 0, a.scale_log2, pA);
-                softmax64<DK, false>(fB, sB, 0, 0, 0, a.scale_log2, pB);
-                pv(consumed, pA, pB);
-                ++consumed;
+        int tt = 0;
+        if constexpr (NB == 2) {
+            if (nfull > 0) {
+                wait_tile(consumed, consumed);
+                qk(consumed, sc);
+                for (; tt < nfull; ++tt) {
+                    wait_tile(consumed + 1, consumed);  // tile `consumed` still feeds P V
+                    floatx4 nx[NB][4];
+                    qk(consumed + 1, nx);
+                    bf16x8 pb[NB][2];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    sA[kb] = nA[kb];
-                    sB[kb] = nB[kb];
+                    for (int j = 0; j < NB; ++j) softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
+                    pv(consumed, pb);
+                    ++consumed;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) sc[j][kb] = nx[j][kb];
                 }
+                have_scores = true;  // tile nfull's scores are in sc
             }
-            have_scores = true;  // tile nfull's scores are in sA / sB
         }
-        for (int tt = nfull; tt < comp.ntile; ++tt) {
+        for (; tt < comp.ntile; ++tt) {
             if (!have_scores) {
                 wait_tile(consumed, consumed);
-                qk(consumed, sA, sB);
+                qk(consumed, sc);
             }
             have_scores = false;
             const int k0 = tt * kTileA;
-            const bool needA = hasA && k0 <= rsA + 15;
-            const bool needB = hasB && k0 <= rsB + 15;
-            bf16x8 pA[2] = {}, pB[2] = {};
-            if (needA) {
-                if (k0 + kTileA - 1 <= rsA) softmax64<DK, false>(fA, sA, rsA + i, 0, k0, a.scale_log2, pA);
-                else softmax64<DK, true>(fA, sA, rsA + i, 0, k0, a.scale_log2, pA);
+            bf16x8 pb[NB][2];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                pb[j][0] = bf16x8{};
+                pb[j][1] = bf16x8{};
+                if (has[j] && k0 <= rs[j] + 15) {
+                    if (k0 + kTileA - 1 <= rs[j]) softmax64<DK, false>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
+                    else softmax64<DK, true>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
+                }
             }
-            if (needB) {
-                if (k0 + kTileA - 1 <= rsB) softmax64<DK, false>(fB, sB, rsB + i, 0, k0, a.scale_log2, pB);
-                else softmax64<DK, true>(fB, sB, rsB + i, 0, k0, a.scale_log2, pB);
-            }
-            pv(consumed, pA, pB);
+            pv(consumed, pb);
             ++consumed;
         }
-        fA.store(op + (size_t)(it.r + (rsA + i) * it.D) * pitch, rsA + i < it.R1);
-        fB.store(op + (size_t)(it.r + (rsB + i) * it.D) * pitch, rsB + i < it.R1);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) f[j].store(op + (size_t)(it.r + (rs[j] + i) * it.D) * pitch, rs[j] + i < it.R1);
         comp.seek(a, comp.round + 1);
     }
 }
@@ -708,16 +728,21 @@ static void set_lds(K kernel, size_t lds, bool& done)
     }
 }
 
+#ifndef RAT_ATTN_WAVES
+#define RAT_ATTN_WAVES 8
+#endif
+constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated kernel
+
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
     const size_t lds = attn_lds_bytes_a(d);
     static bool s128 = false, s64 = false;
     if (d == 128) {
-        set_lds(attn_dilated_kernel<128>, lds, s128);
-        hipLaunchKernelGGL(attn_dilated_kernel<128>, dim3(grid), dim3(kWavesA * kWave), lds, stream, a);
+        set_lds(attn_dilated_kernel<128, kWavesDil>, lds, s128);
+        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil>), dim3(grid), dim3(kWavesDil * kWave), lds, stream, a);
     } else {
-        set_lds(attn_dilated_kernel<64>, lds, s64);
-        hipLaunchKernelGGL(attn_dilated_kernel<64>, dim3(grid), dim3(kWavesA * kWave), lds, stream, a);
+        set_lds(attn_dilated_kernel<64, kWavesDil>, lds, s64);
+        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil>), dim3(grid), dim3(kWavesDil * kWave), lds, stream, a);
     }
     return hipGetLastError();
 }
