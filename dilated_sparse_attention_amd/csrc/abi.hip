@@ -115,7 +115,7 @@ size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L, rat_recur_mod
 
 int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void* k_state, void* v_state,
                      int B, int T, int H, int d, int L, rat_recur_mode mode, rat_dtype dtype,
-                     void* workspace, size_t workspace_bytes, void* stream)
+                     void* workspace, size_t workspace_bytes, float* final_state, void* stream)
 {
     if (!k || !v || !gate_logits || !k_state || !v_state) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return RAT_ERR_SHAPE;
@@ -129,6 +129,12 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void
     const void* all[5] = {k, v, gate_logits, k_state, v_state};
     for (const void* p : all)
         if (!aligned16(p)) return RAT_ERR_ALIGN;
+    if (final_state) {
+        if (!scan_uses_workspace(T, L, mode)) return RAT_ERR_UNSUPPORTED;  // SLIDING keeps no single state
+        for (const void* p : all)
+            if (p == final_state) return RAT_ERR_ALIAS;
+        if (!aligned16(final_state)) return RAT_ERR_ALIGN;
+    }
     hipStream_t s = (hipStream_t)stream;
     const bool bf16 = dtype == RAT_DTYPE_BF16;
 
@@ -143,6 +149,8 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void
         a.hdr = reinterpret_cast<ScanHeader*>(ws);
         a.agg = reinterpret_cast<uint64_t*>(ws + p.agg_off);
         a.incl = reinterpret_cast<uint64_t*>(ws + p.incl_off);
+        a.fin = final_state;
+        a.d = d;
         return hip_status(launch_scan_full(a, bf16, s));
     }
     ScanSlideArgs a;
@@ -337,6 +345,65 @@ int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int n
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
     return hip_status(launch_decode(a, d, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
+}
+
+int rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new, float* state,
+                    void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap, void* out, int B, int T, int H,
+                    int d, int L, const int* D, const int* W, float scale, rat_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    if (!q || !k_new || !v_new || !gate_new || !state || !kc || !vc || !out) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n_cap <= 0 || w_cap < 0 || L < 1) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
+    const int p = T - 1;  // position of the new token
+    for (int h = 0; h < H; ++h) {
+        if (p / D[h] >= n_cap / D[h]) return RAT_ERR_SHAPE;  // history rows of the residue
+        if (W[h] > w_cap) return RAT_ERR_SHAPE;               // ring slot p mod W
+    }
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, H, n_cap, d) || !size_ok(B, H, std::max(w_cap, 1), d))
+        return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[5] = {q, k_new, v_new, gate_new, state};
+    const void* outs[5] = {kc, vc, kw, vw, out};
+    for (const void* o : outs)
+        for (const void* in : ins)
+            if (o && o == in) return RAT_ERR_ALIAS;
+    if (kc == vc || (kw && (kw == vw || kw == kc || kw == vc)) || out == kc || out == vc) return RAT_ERR_ALIAS;
+    for (const void* x : ins)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (x && !aligned16(x)) return RAT_ERR_ALIGN;
+    const int ns = decode_nsplit(B, H, T, D, W);
+    const size_t need = ns == 1 ? 0 : (size_t)B * H * ns * (d + 2) * sizeof(float);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) return RAT_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = dtype == RAT_DTYPE_BF16;
+
+    StepArgs st;
+    memset(&st, 0, sizeof(st));
+    st.k_new = k_new; st.v_new = v_new; st.g_new = gate_new; st.state = state;
+    st.kc = kc; st.vc = vc; st.kw = kw; st.vw = vw;
+    st.B = B; st.H = H; st.d = d; st.n_cap = n_cap; st.w_cap = w_cap;
+    st.restart = (L < T && p % L == 0) ? 1 : 0;
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.kd = kc; a.vd = vc; a.kw = kw ? kw : kc; a.vw = vw ? vw : vc; a.out = out;
+    a.part = static_cast<float*>(workspace);
+    a.B = B; a.H = H; a.T = T; a.nd_cap = n_cap; a.w_cap = w_cap; a.nsplit = ns;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (int h = 0; h < H; ++h) {
+        const int mcap = n_cap / D[h];
+        st.slot_c[h] = (p % D[h]) * mcap + p / D[h];
+        st.slot_w[h] = W[h] > 0 ? p % W[h] : -1;
+        a.D[h] = D[h]; a.W[h] = W[h];
+        a.dil_off[h] = (p % D[h]) * mcap;
+    }
+    const int rc = hip_status(launch_decode_step(st, bf16, s));
+    if (rc != RAT_OK) return rc;
+    return hip_status(launch_decode(a, d, bf16, s));
 }
 
 }  // extern "C"

@@ -83,8 +83,9 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(DecodeArgs a)
     const int w_begin = k_begin + wv * per_wave;
     const int w_end = min(k_end, w_begin + per_wave);
 
-    const E* kd = static_cast<const E*>(a.kd) + (size_t)bh * a.nd_cap * DK + 8 * slice;
-    const E* vd = static_cast<const E*>(a.vd) + (size_t)bh * a.nd_cap * DK + 8 * slice;
+    const size_t drow = (size_t)bh * a.nd_cap + a.dil_off[h];
+    const E* kd = static_cast<const E*>(a.kd) + drow * DK + 8 * slice;
+    const E* vd = static_cast<const E*>(a.vd) + drow * DK + 8 * slice;
     const E* kw = static_cast<const E*>(a.kw) + (size_t)bh * a.w_cap * DK + 8 * slice;
     const E* vw = static_cast<const E*>(a.vw) + (size_t)bh * a.w_cap * DK + 8 * slice;
 
@@ -210,6 +211,59 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL((decode_merge_kernel<E, DK>), dim3(nbh), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
+// One thread per (b, h, channel): h = g * h_prev + (1 - g) * x for keys and
+// values (the recurrence of "RAT+ Deep Dive" section 2.1, one token), kept
+// in fp32 in `state`, stored in the element type into the state history
+// and, with the raw token, into the window ring.
+template <typename E> __device__ __forceinline__ float ld1(const void* p, size_t i);
+template <> __device__ __forceinline__ float ld1<uint16_t>(const void* p, size_t i)
+{
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+}
+template <> __device__ __forceinline__ float ld1<float>(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
+template <typename E> __device__ __forceinline__ void st1(void* p, size_t i, float x);
+template <> __device__ __forceinline__ void st1<uint16_t>(void* p, size_t i, float x)
+{
+    static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <> __device__ __forceinline__ void st1<float>(void* p, size_t i, float x) { static_cast<float*>(p)[i] = x; }
+
+template <typename E>
+__global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a)
+{
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)a.B * a.H * a.d) return;
+    const int c = (int)(idx % a.d);
+    const size_t bh = idx / a.d;
+    const int h = (int)(bh % a.H);
+    float g, gb;
+    forget_gate(ld1<E>(a.g_new, idx), g, gb);
+    if (a.restart) g = 0.f;
+    const float xk = ld1<E>(a.k_new, idx), xv = ld1<E>(a.v_new, idx);
+    float* st = a.state + bh * 2 * a.d + c;
+    const float hk = fmaf(g, st[0], gb * xk);
+    const float hv = fmaf(g, st[a.d], gb * xv);
+    st[0] = hk;
+    st[a.d] = hv;
+    const size_t rc = (bh * a.n_cap + a.slot_c[h]) * a.d + c;
+    st1<E>(a.kc, rc, hk);
+    st1<E>(a.vc, rc, hv);
+    if (a.slot_w[h] >= 0) {
+        const size_t rw = (bh * a.w_cap + a.slot_w[h]) * a.d + c;
+        st1<E>(a.kw, rw, xk);
+        st1<E>(a.vw, rw, xv);
+    }
+}
+
+hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream)
+{
+    const size_t n = (size_t)a.B * a.H * a.d;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(decode_step_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -37,9 +37,11 @@ struct ScanFullArgs {
     int nchunk;    // chunks along T
     int L;         // RESTART period, 0 for none
     int nwg;       // nchunk * nseq
-    uint64_t* agg;   // [nchunk*nseq][3][128] tagged words
-    uint64_t* incl;  // [nchunk*nseq][2][128] tagged words
+    uint64_t* agg;   // [nchunk*nseq][3][block] tagged words
+    uint64_t* incl;  // [nchunk*nseq][2][block] tagged words
     ScanHeader* hdr;
+    float* fin;      // optional fp32 states at t = T-1, [B][H][2][d] (NULL: none)
+    int d;           // head size (for `fin`)
 };
 
 struct ScanSlideArgs {
@@ -123,7 +125,26 @@ struct DecodeArgs {
     float scale_log2;
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
+    int dil_off[kAttnMaxHeads];  // first cache row of head h's dilated entries
 };
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
+
+// Recurrence step of the decode loop: the new token's state from the
+// running fp32 state, written to the state history and the raw ring.
+struct StepArgs {
+    const void* k_new;
+    const void* v_new;
+    const void* g_new;   // [B][H][d]
+    float* state;        // [B][H][2][d] running states (k, v), in / out
+    void* kc;
+    void* vc;            // [B][H][n_cap][d] state history
+    void* kw;
+    void* vw;            // [B][H][w_cap][d] raw ring
+    int B, H, d, n_cap, w_cap;
+    int restart;         // 1: the new position starts a RESTART period (state cleared)
+    int slot_c[kAttnMaxHeads];  // history row of the new position
+    int slot_w[kAttnMaxHeads];  // ring slot of the new position, -1 without a window
+};
+hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace rat

@@ -332,6 +332,16 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             *reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o) = R16::pack(ok);
             *reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o) = R16::pack(ov);
         }
+        // the last position's states in fp32, for a decode loop to continue from
+        if (a.fin && cvalid && t0 + i == a.T - 1) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int ch = ch0 + j, hh = ch / a.d, cc = ch - hh * a.d;
+                float* f = a.fin + ((size_t)(b * (a.N / a.d) + hh) * 2) * a.d + cc;
+                f[0] = ok[j];
+                f[a.d] = ov[j];
+            }
+        }
     }
 }
 

@@ -26,7 +26,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 
 # every symbol include/rat.h declares
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
-           "rat_decode_workspace_bytes", "rat_dilated_attn_decode", "rat_status_string",
+           "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_status_string",
            "rat_last_hip_error")
 
 
@@ -56,7 +56,7 @@ def load_library(path: str = LIBRARY):
     ip = ctypes.POINTER(ctypes.c_int)
     lib.rat_scan_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.rat_scan_workspace_bytes.restype = sz
-    lib.rat_scan_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.rat_scan_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp, vp]
     lib.rat_scan_prefill.restype = i
     lib.rat_attn_prefill_workspace_bytes.argtypes = [i, i, i, i, ip, ip, i]
     lib.rat_attn_prefill_workspace_bytes.restype = sz
@@ -66,6 +66,9 @@ def load_library(path: str = LIBRARY):
     lib.rat_decode_workspace_bytes.restype = sz
     lib.rat_dilated_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
     lib.rat_dilated_attn_decode.restype = i
+    lib.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, ip, ip, f, i, vp, sz,
+                                    vp]
+    lib.rat_decode_step.restype = i
     lib.rat_status_string.argtypes = [i]
     lib.rat_status_string.restype = ctypes.c_char_p
     lib.rat_last_hip_error.argtypes = []
@@ -127,9 +130,11 @@ def scan_workspace(nbytes, device):
     return ws
 
 
-def scan_prefill(k, v, gate_logits, L=None, mode=RESTART, k_state=None, v_state=None, workspace=None):
+def scan_prefill(k, v, gate_logits, L=None, mode=RESTART, k_state=None, v_state=None, workspace=None,
+                 final_state=None):
     """Recurrent states (k_state, v_state) of [B,T,H,d] keys / values with
-    forget-gate logits ``gate_logits`` (L defaults to T: full recurrence)."""
+    forget-gate logits ``gate_logits`` (L defaults to T: full recurrence).
+    ``final_state`` (fp32 [B,H,2,d]) receives the states at T-1 unrounded."""
     lib = load_library()
     B, T, H, d = k.shape
     L = T if L is None else int(L)
@@ -142,9 +147,11 @@ def scan_prefill(k, v, gate_logits, L=None, mode=RESTART, k_state=None, v_state=
     nbytes = lib.rat_scan_workspace_bytes(B, T, H, d, L, mode, _DTYPES[k.dtype])
     if workspace is None and nbytes:
         workspace = scan_workspace(nbytes, k.device)
+    if final_state is not None:
+        _check_tensor("final_state", final_state, torch.float32, (B, H, 2, d))
     rc = lib.rat_scan_prefill(_ptr(k), _ptr(v), _ptr(gate_logits), _ptr(k_state), _ptr(v_state),
                               B, T, H, d, L, mode, _DTYPES[k.dtype], _ptr(workspace),
-                              0 if workspace is None else workspace.numel(), _stream())
+                              0 if workspace is None else workspace.numel(), _ptr(final_state), _stream())
     _raise("rat_scan_prefill", rc, lib)
     return k_state, v_state
 
@@ -226,3 +233,38 @@ def rat_layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=No
     need_raw = any(int(w) > 0 for w in (W if hasattr(W, "__len__") else [W]))
     return dilated_attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None,
                                 D=D, W=W, scale=scale)
+
+
+def decode_step(q, k_new, v_new, gate_new, state, kc, vc, kw, vw, T, D, W, L=None, scale=None, out=None,
+                workspace=None):
+    """One decode-loop step at context length T (the new token at position
+    T-1): advances the fp32 ``state`` [B,H,2,d] by the token's (k_new, v_new,
+    gate_new), writes its state into the per-residue history (kc, vc:
+    [B,H,n_cap,d]) and its raw key / value into the ring (kw, vw:
+    [B,H,w_cap,d]), then attends as dilated_attn_decode."""
+    lib = load_library()
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("gate_new", gate_new)):
+        _check_tensor(name, t, q.dtype, (B, H, d))
+    _check_tensor("state", state, torch.float32, (B, H, 2, d))
+    n_cap = kc.shape[2]
+    _check_tensor("kc", kc, q.dtype, (B, H, n_cap, d))
+    _check_tensor("vc", vc, q.dtype, (B, H, n_cap, d))
+    w_cap = 0 if kw is None else kw.shape[2]
+    if kw is not None:
+        _check_tensor("kw", kw, q.dtype, (B, H, w_cap, d))
+        _check_tensor("vw", vw, q.dtype, (B, H, w_cap, d))
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, (B, H, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    L = int(T) if L is None else int(L)
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    nbytes = lib.rat_decode_workspace_bytes(B, H, d, int(T), Dh, Wh)
+    if workspace is None and nbytes:
+        workspace = attn_workspace(nbytes, q.device)
+    rc = lib.rat_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(gate_new), _ptr(state), _ptr(kc), _ptr(vc),
+                             n_cap, _ptr(kw), _ptr(vw), w_cap, _ptr(out), B, int(T), H, d, L, Dh, Wh, scale,
+                             _DTYPES[q.dtype], _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                             _stream())
+    _raise("rat_decode_step", rc, lib)
+    return out

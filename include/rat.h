@@ -82,13 +82,17 @@ size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L,
  *                       k_state[t] = g_t*k_state[t-1] + (1-g_t)*k[t], state
  *                       zero before t = 0 (and at RESTART boundaries).
  *   L                 : recurrence window, >= 1; L >= T means full sequence.
+ *   final_state       : optional (NULL for none) fp32 [B,H,2,d] output: the
+ *                       key and value states at t = T-1 before rounding to
+ *                       dtype, from which rat_decode_step continues.  Not
+ *                       available for SLIDING with L < T (RAT_ERR_UNSUPPORTED).
  * Errors: RAT_ERR_NULL, _SHAPE (B,T,H,d,L < 1), _UNSUPPORTED (d, dtype,
  * SLIDING with 64 < L < T, sizes), _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
 int rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
                      void* k_state, void* v_state,
                      int B, int T, int H, int d, int L, rat_recur_mode mode,
                      rat_dtype dtype, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     float* final_state, void* stream);
 
 /* Bytes of device workspace rat_dilated_attn_prefill needs (0 when no head
  * has a local window, or for fp32): B*T*H*2 floats holding the partial
@@ -135,6 +139,33 @@ int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int n
                             int B, int T, int H, int d, const int* D, const int* W,
                             float scale, rat_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* One step of a decode loop (the recurrence of Deep Dive 2.1 for one new
+ * token, then the decode attention above): the token at position T-1 of a
+ * T-token context arrives with its query q, raw key / value k_new, v_new
+ * and gate logit gate_new ([B,H,d] each).
+ *   state  : fp32 [B,H,2,d], in: the key and value states at T-2 (zeros
+ *            for T = 1, or rat_scan_prefill's final_state), out: the states
+ *            at T-1.  With L < T the state is cleared first when (T-1) mod
+ *            L == 0 (RESTART); SLIDING windows are not supported here.
+ *   kc, vc : [B,H,n_cap,d] history of the states, kept per residue: the
+ *            state of position p of head h is row
+ *            (p mod D[h]) * (n_cap / D[h]) + p / D[h], so that the entries a
+ *            query reads -- its own residue's -- are contiguous; this call
+ *            writes the row of position T-1 and needs
+ *            (T-1) / D[h] < n_cap / D[h].
+ *   kw, vw : [B,H,w_cap,d] ring of raw keys / values, position p in slot
+ *            p mod W[h] (w_cap >= W[h]); this call writes slot (T-1) mod W[h].
+ *            May be NULL iff every W[h] == 0.
+ *   out    : [B,H,d], as rat_dilated_attn_decode at context T over the
+ *            residue rows and ring slots above.
+ *   workspace: rat_decode_workspace_bytes(B, H, d, T, D, W) bytes.
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
+int rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new,
+                    float* state, void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
+                    void* out, int B, int T, int H, int d, int L, const int* D, const int* W,
+                    float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Static text for a status code. */
 const char* rat_status_string(int status);

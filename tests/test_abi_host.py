@@ -56,8 +56,14 @@ def heads(vals):
 
 
 def scan(lib, k=P[0], v=P[1], g=P[2], ks=P[3], vs=P[4], B=1, T=64, H=2, d=64, L=64, mode=0, dtype=1,
-         ws=P[5], wsb=1 << 30):
-    return lib.rat_scan_prefill(k, v, g, ks, vs, B, T, H, d, L, mode, dtype, ws, wsb, None)
+         ws=P[5], wsb=1 << 30, fin=None):
+    return lib.rat_scan_prefill(k, v, g, ks, vs, B, T, H, d, L, mode, dtype, ws, wsb, fin, None)
+
+
+def test_scan_final_state_validation(lib):
+    assert scan(lib, T=200, L=64, mode=1, fin=P[6]) == UNSUP  # SLIDING keeps no single state
+    assert scan(lib, fin=P[3]) == ALIAS
+    assert scan(lib, fin=MIS) == ALIGN
 
 
 def test_scan_validation(lib):
@@ -148,3 +154,25 @@ def test_decode_validation(lib):
     assert need > 0
     assert decode(lib, B=1, H=1, T=1 << 20, D=(1,), W=(0,), nd_cap=1 << 20, w_cap=0, ws=None) == WSPACE
     assert lib.rat_decode_workspace_bytes(64, 20, 128, 32768, heads([64] * 20), heads([64] * 20)) == 0
+
+
+def step(lib, q=P[0], kn=P[1], vn=P[2], gn=P[3], st=P[4], kc=P[5], vc=P[6], n_cap=1024, kw=P[7],
+         vw=ctypes.c_void_p(0x10000 + 0x100000 * 9), w_cap=64, out=ctypes.c_void_p(0x10000 + 0x100000 * 10),
+         B=2, T=1000, H=2, d=128, L=1 << 30, D=(64, 16), W=(64, 0), scale=0.1, dtype=1,
+         ws=ctypes.c_void_p(0x10000 + 0x100000 * 11), wsb=1 << 30):
+    return lib.rat_decode_step(q, kn, vn, gn, st, kc, vc, n_cap, kw, vw, w_cap, out, B, T, H, d, L, heads(D),
+                               heads(W), scale, dtype, ws, wsb, None)
+
+
+def test_decode_step_validation(lib):
+    assert step(lib, st=None) == NULL
+    assert step(lib, kw=None) == NULL          # head 0 has a window
+    assert step(lib, L=0) == SHAPE
+    assert step(lib, w_cap=63) == SHAPE        # ring slot (T-1) mod 64 needs 64 slots
+    # position 999 of the D = 64 head sits at row 15 of its residue: 16 rows per residue needed
+    assert step(lib, n_cap=64 * 15) == SHAPE
+    assert step(lib, d=32) == UNSUP
+    assert step(lib, out=P[0]) == ALIAS
+    assert step(lib, kc=P[1]) == ALIAS
+    assert step(lib, vc=P[5]) == ALIAS
+    assert step(lib, st=MIS) == ALIGN

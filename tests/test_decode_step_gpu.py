@@ -1,0 +1,113 @@
+"""GPU parity of the decode loop: prefill hands its fp32 final state to
+rat_decode_step, which advances the recurrence one token at a time, appends
+to the per-residue state history and the raw ring, and attends.  Every
+step's output must equal the oracle's prefill output at that position, and
+the running state the oracle's recurrence."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dilated_sparse_attention_amd as rat
+from dilated_sparse_attention_amd import inputs
+from oracle import oracle
+from tests.parity import FP32_ATOL, FP32_RTOL, announce, assert_parity, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _history(ks, vs, T0, D, n_cap):
+    """[B,H,n_cap,d] per-residue histories of the first T0 states (row of
+    position p: (p mod D[h]) * (n_cap // D[h]) + p // D[h])."""
+    B, _, H, d = ks.shape
+    kc = torch.zeros((B, H, n_cap, d), dtype=ks.dtype, device=ks.device)
+    vc = torch.zeros_like(kc)
+    for h, Dh in enumerate(D):
+        p = torch.arange(T0, device=ks.device)
+        rows = (p % Dh) * (n_cap // Dh) + p // Dh
+        kc[:, h, rows] = ks[:, :T0, h]
+        vc[:, h, rows] = vs[:, :T0, h]
+    return kc, vc
+
+
+def _ring(k, v, T0, W, w_cap):
+    """[B,H,w_cap,d] rings holding raw position p in slot p mod W[h]."""
+    B, _, H, d = k.shape
+    kw = torch.zeros((B, H, max(w_cap, 1), d), dtype=k.dtype, device=k.device)
+    vw = torch.zeros_like(kw)
+    for h, Wh in enumerate(W):
+        if Wh == 0:
+            continue
+        p = torch.arange(max(0, T0 - Wh), T0, device=k.device)
+        kw[:, h, p % Wh] = k[:, p, h]
+        vw[:, h, p % Wh] = v[:, p, h]
+    return kw, vw
+
+
+CASES = [
+    # (B, T0, steps, H, d, D, W, L)
+    (2, 50, 24, 3, 128, [1, 4, 16], [0, 8, 5], None),          # full recurrence
+    (1, 0, 40, 2, 64, [16, 3], [16, 0], None),                 # decoding from the first token
+    (2, 60, 30, 2, 128, [64, 5], [64, 7], 16),                  # RESTART every 16 positions
+    (1, 1000, 8, 2, 128, [64, 1], [128, 0], None),              # long prefill, split keys on the dense head
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}T{c[1]}+{c[2]}H{c[3]}d{c[4]}D{c[5]}W{c[6]}L{c[7]}")
+def test_decode_loop(case):
+    B, T0, steps, H, d, D, W, L = case
+    Tt = T0 + steps
+    Lr = Tt if L is None else L
+    x = inputs.make_random_prefill(B, Tt, H, d, torch.bfloat16, seed=3, gate_mean=1.5)
+    q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
+    n_cap = max(Dh * ((Tt + Dh - 1) // Dh) for Dh in D) + 16
+    w_cap = max(W) + 3
+    state = torch.zeros((B, H, 2, d), dtype=torch.float32, device="cuda")
+    if T0 > 0:
+        announce("decode loop prefill", case)
+        ks, vs = rat.scan_prefill(k[:, :T0].contiguous(), v[:, :T0].contiguous(), g[:, :T0].contiguous(),
+                                  L=min(Lr, T0) if Lr < T0 else T0, final_state=state)
+        kc, vc = _history(ks, vs, T0, D, n_cap)
+    else:
+        kc = torch.zeros((B, H, n_cap, d), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+    kw, vw = _ring(k, v, T0, W, w_cap)
+
+    wk, wv = oracle.scan(x["k"], x["v"], x["gate"], Lr, 0)
+    rows = np.array([(b, t, h) for t in range(T0, Tt) for b in range(B) for h in range(H)], np.int32)
+    want = oracle.attn_prefill_rows(x["q"], wk, wv, x["k"], x["v"], rows, D, W, 1 / math.sqrt(d))
+    want = want.reshape(steps, B, H, d)
+
+    got = []
+    for T in range(T0 + 1, Tt + 1):
+        announce("decode step", case, "T", T)
+        t = T - 1
+        out = rat.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                              g[:, t].contiguous(), state, kc, vc, kw, vw, T, D, W, L=Lr)
+        got.append(out.clone())
+    torch.cuda.synchronize()
+    assert_parity(torch.stack(got), want, torch.bfloat16, "decode loop outputs")
+    # the running state is the fp32 recurrence of every token so far
+    st = state.cpu().double().numpy()
+    ref = np.stack([wk[:, Tt - 1], wv[:, Tt - 1]], axis=2)  # [B,H,2,d]
+    err = np.abs(st - ref)
+    assert (err <= 1e-3 * np.abs(ref) + 1e-5).all(), f"running state: max err {err.max():.3g}"
+
+
+@pytest.mark.parametrize("mode,L", [(0, None), (0, 64), (0, 100)])
+def test_scan_final_state(mode, L):
+    """rat_scan_prefill's fp32 final state equals the oracle state at T-1
+    (to fp32 rounding of a long recurrence)."""
+    B, T, H, d = 2, 777, 3, 64
+    x = inputs.make_random_prefill(B, T, H, d, torch.bfloat16, seed=11, gate_mean=2.0)
+    fin = torch.full((B, H, 2, d), float("nan"), dtype=torch.float32, device="cuda")
+    announce("scan final state", mode, L)
+    rat.scan_prefill(x["k"].cuda(), x["v"].cuda(), x["gate"].cuda(), L=L, mode=mode, final_state=fin)
+    torch.cuda.synchronize()
+    wk, wv = oracle.scan(x["k"], x["v"], x["gate"], T if L is None else L, mode)
+    ref = np.stack([wk[:, T - 1], wv[:, T - 1]], axis=2)
+    got = fin.cpu().double().numpy()
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert (err <= FP32_RTOL * np.abs(ref) + FP32_ATOL).all(), f"max err {err.max():.3g}"
