@@ -406,7 +406,7 @@ __device__ __forceinline__ int row_block(int wv, int j)
     return j == 0 ? wv : j == 1 ? 15 - wv : j == 2 ? 7 - wv : 8 + wv;
 }
 
-template <int DK, int NW>
+template <int DK, int NW, int RING>
 __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
@@ -416,7 +416,9 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     constexpr int PER_WAVE = (kSlotRows / G::RPI) / NW;
     static_assert((kSlotRows / G::RPI) % NW == 0, "slot loads split evenly over waves");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    lds_char* side = smem + kRingA * TILE_BYTES;  // (m, l) words of partial-output slots, 1 KiB each
+    // (m, l) words of partial-output slots, 1 KiB each; a ring of more than
+    // four slots is only used without windowed classes and has no side buffers
+    lds_char* side = smem + (RING > 4 ? 0 : RING * TILE_BYTES);
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -430,9 +432,9 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     comp = issue;
     int issued = 0, consumed = 0;
 #pragma unroll
-    for (int j = 0; j < kRingA - 1; ++j) {
+    for (int j = 0; j < RING - 1; ++j) {
         if (issue.it.valid) {
-            issue_step_a<DK, NW>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
+            issue_step_a<DK, NW>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
             ++issued;
             issue.advance(a);
         }
@@ -441,13 +443,14 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     // when the slot after step `oldest` (the oldest step still read after
     // this barrier) is free.
     auto wait_tile = [&](int seq, int oldest) {
-        const int ahead = issued - seq - 1;
-        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
+        const int ahead = issued - seq - 1;  // ring steps issued after `seq`
+        if (RING > 4 && ahead >= 3) wait_vmcnt<3 * PER_WAVE>();
+        else if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
         else if (ahead == 1) wait_vmcnt<PER_WAVE>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (issue.it.valid && issued < oldest + kRingA) {
-            issue_step_a<DK, NW>(a, issue, smem + (issued % kRingA) * TILE_BYTES, side + (issued % kRingA) * 1024);
+        if (issue.it.valid && issued < oldest + RING) {
+            issue_step_a<DK, NW>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
             ++issued;
             issue.advance(a);
         }
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         // query rows from the ring (lane (g, i): row i, dims 8g + 32ks .. +8)
         for (int s = 0; s < comp.nq; ++s) {
             wait_tile(consumed, consumed);
-            const lds_char* qt = smem + (consumed % kRingA) * TILE_BYTES;
+            const lds_char* qt = smem + (consumed % RING) * TILE_BYTES;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int r = 16 * row_block<NB>(wv, j);
@@ -485,8 +488,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         // windowed classes: continue from the band pass's partial state
         for (int s = 0; s < comp.no; ++s) {
             wait_tile(consumed, consumed);
-            const lds_char* ot = smem + (consumed % kRingA) * TILE_BYTES;
-            const float* ml = reinterpret_cast<const float*>(side + (consumed % kRingA) * 1024);
+            const lds_char* ot = smem + (consumed % RING) * TILE_BYTES;
+            const float* ml = reinterpret_cast<const float*>(side + (consumed % RING) * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int r = 16 * row_block<NB>(wv, j);
@@ -496,14 +499,19 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             ++consumed;
         }
 
+        // k-steps outermost: 4 x NB independent accumulation chains sit
+        // between two MFMAs of the same chain, so no MFMA waits for the
+        // result of the one before it
         auto qk = [&](int seq, floatx4 (&sc)[NB][4]) {
-            const lds_char* kt = smem + (seq % kRingA) * TILE_BYTES;
+            const lds_char* kt = smem + (seq % RING) * TILE_BYTES;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int j = 0; j < NB; ++j) sc[j][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < G::KS; ++ks) {
+            for (int ks = 0; ks < G::KS; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
                     const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
 #pragma unroll
                     for (int j = 0; j < NB; ++j) sc[j][kb] = mfma16(kf, f[j].q[ks], sc[j][kb]);
@@ -511,7 +519,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             }
         };
         auto pv = [&](int seq, const bf16x8 (&pb)[NB][2]) {
-            const lds_char* vt = smem + (seq % kRingA) * TILE_BYTES + kTileA * G::ROWB;
+            const lds_char* vt = smem + (seq % RING) * TILE_BYTES + kTileA * G::ROWB;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
@@ -675,8 +683,11 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_band_kernel(AttnArgs a)
         for (int kb = 0; kb < 4; ++kb) {
             sA[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
             sB[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks) {
+        for (int ks = 0; ks < G::KS; ++ks) {  // k-steps outermost: independent chains interleave
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
                 const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
                 sA[kb] = mfma16(kf, fA.q[ks], sA[kb]);
                 sB[kb] = mfma16(kf, fB.q[ks], sB[kb]);
@@ -718,6 +729,8 @@ __global__ __launch_bounds__(kWavesA * kWave) void attn_band_kernel(AttnArgs a)
 
 // ring slots plus the (m, l) side buffers of path A
 size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * (2 * kTileA * d * 2 + 1024); }
+// five slots, no side buffers (no windowed classes): 160 KiB at d = 128
+size_t attn_lds_bytes_a5(int d) { return (size_t)5 * 2 * kTileA * d * 2; }
 
 template <typename K>
 static void set_lds(K kernel, size_t lds, bool& done)
@@ -735,14 +748,28 @@ constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated
 
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
+    bool windowed = false;
+    for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
+    static bool s128 = false, s64 = false, s128r = false, s64r = false;
+    const dim3 block(kWavesDil * kWave);
+    if (!windowed) {  // deeper prefetch: five ring slots
+        const size_t lds = attn_lds_bytes_a5(d);
+        if (d == 128) {
+            set_lds(attn_dilated_kernel<128, kWavesDil, 5>, lds, s128r);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5>), dim3(grid), block, lds, stream, a);
+        } else {
+            set_lds(attn_dilated_kernel<64, kWavesDil, 5>, lds, s64r);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5>), dim3(grid), block, lds, stream, a);
+        }
+        return hipGetLastError();
+    }
     const size_t lds = attn_lds_bytes_a(d);
-    static bool s128 = false, s64 = false;
     if (d == 128) {
-        set_lds(attn_dilated_kernel<128, kWavesDil>, lds, s128);
-        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil>), dim3(grid), dim3(kWavesDil * kWave), lds, stream, a);
+        set_lds(attn_dilated_kernel<128, kWavesDil, kRingA>, lds, s128);
+        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA>), dim3(grid), block, lds, stream, a);
     } else {
-        set_lds(attn_dilated_kernel<64, kWavesDil>, lds, s64);
-        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil>), dim3(grid), dim3(kWavesDil * kWave), lds, stream, a);
+        set_lds(attn_dilated_kernel<64, kWavesDil, kRingA>, lds, s64);
+        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA>), dim3(grid), block, lds, stream, a);
     }
     return hipGetLastError();
 }
