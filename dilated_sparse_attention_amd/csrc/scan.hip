@@ -18,15 +18,16 @@
 //     registers from load to store (no LDS staging); 2 workgroups fit on a
 //     compute unit;
 //   * pass 1: each lane runs the recurrence over its 4 tokens from a zero
-//     state, keeping the local states H_t; its last ones with the gate
-//     product form the segment's affine map h -> A*h + B per channel;
+//     state; the last state with the gate product forms the segment's
+//     affine map h -> A*h + B per channel (the raw inputs stay in
+//     registers);
 //   * one wave turns the 32 segment maps into exclusive prefixes (and the
 //     chunk's map, which it publishes) while another finds the chunk's
 //     carry-in by a decoupled look-back over the chunks before it (Merrill
 //     & Garland's single-pass scan), through 64-bit words that carry
 //     (value, epoch tag) and so need no memory fence;
-//   * pass 2 evaluates the gates again, h_t = H_t + P_t * carry with P_t
-//     the gate product since the segment start, and stores the states.
+//   * pass 2 runs the recurrence again from the segment's carry-in (gates
+//     evaluated again) and stores the states.
 //   Chunk order comes from a ticket counter so that every chunk a
 //   workgroup waits for belongs to a workgroup that is already running;
 //   the same 64-bit atomic returns the call's epoch.
@@ -49,6 +50,10 @@ namespace rat {
 
 constexpr int kScanThreads = kScanWaves * kWave;
 constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before the watchdog fires
+#ifndef RAT_SCAN_LOOKBACK
+#define RAT_SCAN_LOOKBACK 1
+#endif
+constexpr int kLookbackWindow = RAT_SCAN_LOOKBACK;  // predecessors examined per round
 
 // 16 bytes of one token row: CPL = 16 / sizeof(E) adjacent channels.
 template <typename E> struct Row16;
@@ -137,9 +142,9 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
         for (int t = ((t0 + a.L - 1) / a.L) * a.L; t < t0 + TPL; t += a.L) rmask |= 1u << (t - t0);
     }
 
-    // pass 1: the segment's recurrence from a zero state
+    // pass 1: the segment's map h -> A h + (K, V), its recurrence from a
+    // zero state (the raw inputs stay in registers for pass 2)
     float A[CPL], K[CPL], V[CPL];
-    float hk[TPL][CPL], hv[TPL][CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) { A[j] = 1.f; K[j] = 0.f; V[j] = 0.f; }
 #pragma unroll
@@ -156,8 +161,6 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
                 K[j] = fmaf(g, K[j], gb * R16::get(rk[i], j));
                 V[j] = fmaf(g, V[j], gb * R16::get(rv[i], j));
             }
-            hk[i][j] = K[j];
-            hv[i][j] = V[j];
         }
     }
 #pragma unroll
@@ -183,54 +186,77 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             float rA[C0], rK[C0], rV[C0];
 #pragma unroll
             for (int j = 0; j < C0; ++j) { rA[j] = 1.f; rK[j] = 0.f; rV[j] = 0.f; }
+            // each round loads the words of kLookbackWindow predecessors at
+            // once (one memory latency), then walks them newest first
             int p = chunk - 1;
             uint32_t spins = 0;
-            while (true) {
-                if (p < 0) {
+            bool done = false;
+            while (!done) {
+                float x[kLookbackWindow][C0], y[kLookbackWindow][C0];
+                float pa[kLookbackWindow][C0], pk[kLookbackWindow][C0], pv[kLookbackWindow][C0];
+                bool ok[kLookbackWindow], ok2[kLookbackWindow];
+#pragma unroll
+                for (int q = 0; q < kLookbackWindow; ++q) {
+                    ok[q] = ok2[q] = false;
+                    if (p - q < 0) continue;
+                    const size_t ps = (size_t)(p - q) * a.nseq + seq;
+                    const uint64_t* ic = a.incl + ps * (2 * BW);
+                    const uint64_t* ag = a.agg + ps * (3 * BW);
+                    ok[q] = ok2[q] = true;
+#pragma unroll
+                    for (int j = 0; j < C0; ++j) {
+                        ok[q] &= load_tagged(ic + lane * C0 + j, tag, x[q][j]);
+                        ok[q] &= load_tagged(ic + BW + lane * C0 + j, tag, y[q][j]);
+                        ok2[q] &= load_tagged(ag + lane * C0 + j, tag, pa[q][j]);
+                        ok2[q] &= load_tagged(ag + BW + lane * C0 + j, tag, pk[q][j]);
+                        ok2[q] &= load_tagged(ag + 2 * BW + lane * C0 + j, tag, pv[q][j]);
+                    }
+                }
+                bool stalled = false;
+#pragma unroll
+                for (int q = 0; q < kLookbackWindow; ++q) {
+                    if (done || stalled) continue;
+                    if (p < 0) {  // before the first chunk: the carry is the map of zero
+#pragma unroll
+                        for (int j = 0; j < C0; ++j) { inK[j] = rK[j]; inV[j] = rV[j]; }
+                        done = true;
+                    } else if (ok[q]) {  // inclusive prefix of chunk p
+#pragma unroll
+                        for (int j = 0; j < C0; ++j) {
+                            inK[j] = fmaf(rA[j], x[q][j], rK[j]);
+                            inV[j] = fmaf(rA[j], y[q][j], rV[j]);
+                        }
+                        done = true;
+                    } else if (ok2[q]) {  // aggregate of chunk p: fold it in, go on
+                        bool zero = true;
+#pragma unroll
+                        for (int j = 0; j < C0; ++j) {
+                            rK[j] = fmaf(rA[j], pk[q][j], rK[j]);
+                            rV[j] = fmaf(rA[j], pv[q][j], rV[j]);
+                            rA[j] *= pa[q][j];
+                            zero &= rA[j] == 0.f;
+                        }
+                        --p;
+                        if (zero) p = -1;  // nothing earlier reaches this chunk
+                    } else {
+                        stalled = true;  // chunk p has published nothing yet
+                    }
+                }
+                if (!done && p < 0) {
 #pragma unroll
                     for (int j = 0; j < C0; ++j) { inK[j] = rK[j]; inV[j] = rV[j]; }
-                    break;
+                    done = true;
                 }
-                const size_t ps = (size_t)p * a.nseq + seq;
-                const uint64_t* ic = a.incl + ps * (2 * BW);
-                const uint64_t* ag = a.agg + ps * (3 * BW);
-                float x[C0], y[C0], pa[C0], pk[C0], pv[C0];
-                bool ok = true, ok2 = true;
+                if (!done && stalled) {
+                    if (++spins > kLookbackSpinLimit) {
+                        // watchdog: a carry that never appears poisons the
+                        // output instead of hanging the device
 #pragma unroll
-                for (int j = 0; j < C0; ++j) {
-                    ok &= load_tagged(ic + lane * C0 + j, tag, x[j]);
-                    ok &= load_tagged(ic + BW + lane * C0 + j, tag, y[j]);
-                    ok2 &= load_tagged(ag + lane * C0 + j, tag, pa[j]);
-                    ok2 &= load_tagged(ag + BW + lane * C0 + j, tag, pk[j]);
-                    ok2 &= load_tagged(ag + 2 * BW + lane * C0 + j, tag, pv[j]);
-                }
-                if (ok) {
-#pragma unroll
-                    for (int j = 0; j < C0; ++j) {
-                        inK[j] = fmaf(rA[j], x[j], rK[j]);
-                        inV[j] = fmaf(rA[j], y[j], rV[j]);
+                        for (int j = 0; j < C0; ++j) inK[j] = inV[j] = __builtin_nanf("");
+                        done = true;
+                    } else {
+                        __builtin_amdgcn_s_sleep(1);
                     }
-                    break;
-                }
-                if (ok2) {
-                    bool zero = true;
-#pragma unroll
-                    for (int j = 0; j < C0; ++j) {
-                        rK[j] = fmaf(rA[j], pk[j], rK[j]);
-                        rV[j] = fmaf(rA[j], pv[j], rV[j]);
-                        rA[j] *= pa[j];
-                        zero &= rA[j] == 0.f;
-                    }
-                    --p;
-                    if (zero) p = -1;  // nothing earlier reaches this chunk
-                } else if (++spins > kLookbackSpinLimit) {
-                    // watchdog: a carry that never appears poisons the output
-                    // instead of hanging the device
-#pragma unroll
-                    for (int j = 0; j < C0; ++j) inK[j] = inV[j] = __builtin_nanf("");
-                    break;
-                } else {
-                    __builtin_amdgcn_s_sleep(1);
                 }
             }
         }
@@ -297,22 +323,20 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
         }
     }
 
-    // pass 2: carry into the segment, then h_t = H_t + P_t * carry with P_t
-    // the gate product since the segment start (gates evaluated again)
-    float ck[CPL], cv[CPL], P[CPL];
+    // pass 2: the recurrence again, from the segment's carry-in (gates
+    // evaluated again; the empty asm hides the logits' identity from
+    // common-subexpression elimination, which would keep pass 1's gates in
+    // 8 more registers per token)
+    float ck[CPL], cv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int ch = c * CPL + j;
         const float pa = s_seg[seg][0][ch];
         ck[j] = fmaf(pa, s_carry[0][ch], s_seg[seg][1][ch]);
         cv[j] = fmaf(pa, s_carry[1][ch], s_seg[seg][2][ch]);
-        P[j] = 1.f;
     }
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-        // the gates are evaluated again rather than kept from pass 1 (the
-        // empty asm hides the logits' identity from common-subexpression
-        // elimination, which would hold 8 more registers per token)
         asm volatile("" : "+v"(rg[i]));
         const bool restart = (rmask >> i) & 1u;
         float ok[CPL], ov[CPL];
@@ -321,9 +345,10 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             float g, gb;
             forget_gate(R16::get(rg[i], j), g, gb);
             if (restart) g = 0.f;
-            P[j] *= g;
-            ok[j] = fmaf(P[j], ck[j], hk[i][j]);
-            ov[j] = fmaf(P[j], cv[j], hv[i][j]);
+            ck[j] = fmaf(g, ck[j], gb * R16::get(rk[i], j));
+            cv[j] = fmaf(g, cv[j], gb * R16::get(rv[i], j));
+            ok[j] = ck[j];
+            ov[j] = cv[j];
         }
         // ordinary (cacheable) stores: the attention reads the states right
         // after, and part of them is still in the Infinity Cache then
