@@ -279,7 +279,7 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
     dil.nblocks = (int)items;
     band.nblocks = (int)blocks;
     if (band.nblocks > 0) {
-        const int rc = hip_status(launch_attn_band_bf16(band, d, s));
+        const int rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, device_cu_count()), s));
         if (rc != RAT_OK) return rc;
     }
     const int grid = std::min(dil.nblocks, device_cu_count());

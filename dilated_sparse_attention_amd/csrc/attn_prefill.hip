@@ -199,6 +199,7 @@ constexpr int kRingA = 4;    // LDS ring depth
 
 struct ItemA {
     int b, h, D, W, r, R0, R1;
+    int kbeg;  // first key (0, or the start of a band item's key range)
     bool valid;
 };
 
@@ -206,6 +207,7 @@ struct ItemA {
 // 256-row chunk index) most expensive first, then head fastest, residue,
 // batch -- consecutive items read the same positions of different heads,
 // i.e. whole contiguous token rows.
+template <bool BAND>
 __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 {
     ItemA it;
@@ -215,6 +217,20 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
     while (c + 1 < a.nclass && item >= a.cls[c + 1].block_begin) ++c;
     const AttnClass& k = a.cls[c];
     const int local = item - k.block_begin;
+    it.W = k.W;
+    if (BAND) {
+        // band item: 256 contiguous queries of (b, h), keys t0-W+1 .. t0+255
+        const int idx = local % k.per_level;
+        it.h = a.heads[k.head_off + idx % k.nheads];
+        it.b = idx / k.nheads;
+        it.r = 0;
+        it.D = 1;
+        it.R0 = (local / k.per_level) * kAttnRowsA;
+        it.R1 = min(it.R0 + kAttnRowsA, a.T);
+        it.kbeg = max(0, it.R0 - k.W + 1) & ~(kTileA - 1);
+        it.valid = it.R0 < a.T;
+        return it;
+    }
     const int level = k.levels - 1 - local / k.per_level;
     int idx = local % k.per_level;
     it.h = a.heads[k.head_off + idx % k.nheads];
@@ -222,10 +238,10 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
     it.r = idx % k.D;
     it.b = idx / k.D;
     it.D = k.D;
-    it.W = k.W;
     const int M = it.r < a.T ? (a.T - it.r + k.D - 1) / k.D : 0;
     it.R0 = level * kAttnRowsA;
     it.R1 = min(it.R0 + kAttnRowsA, M);
+    it.kbeg = 0;
     it.valid = it.R0 < M;
     return it;
 }
@@ -236,6 +252,7 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 // The DMA issue cursor and the compute cursor are two copies.
 constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
 
+template <bool BAND>
 struct CursorA {
     int round, t, nq, no, ntile;
     ItemA it;
@@ -249,12 +266,12 @@ struct CursorA {
     __device__ __forceinline__ void seek(const AttnArgs& a, int rnd)
     {
         for (round = rnd; round * (int)gridDim.x < a.nblocks; ++round) {
-            it = decode_item_a(a, item_of(round));
+            it = decode_item_a<BAND>(a, item_of(round));
             if (it.valid) {
                 t = 0;
                 nq = (it.R1 - it.R0 + kSlotRows - 1) / kSlotRows;
-                no = it.W > 0 ? nq : 0;
-                ntile = (it.R1 + kTileA - 1) / kTileA;
+                no = (!BAND && it.W > 0) ? nq : 0;
+                ntile = (it.R1 - it.kbeg + kTileA - 1) / kTileA;
                 return;
             }
         }
@@ -269,8 +286,8 @@ struct CursorA {
 // DMA of the cursor's ring step into slot `buf` (every wave issues the same
 // PER_WAVE row copies; partial-output steps add one copy of their (m, l)
 // words into `side` on waves 0-3).
-template <int DK, int NW>
-__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA& c, lds_char* buf, lds_char* side)
+template <int DK, int NW, bool BAND>
+__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND>& c, lds_char* buf, lds_char* side)
 {
     typedef Geo<DK> G;
     constexpr int INSTR = kSlotRows / G::RPI;
@@ -290,10 +307,10 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA& c
             const int s = c.t < c.nq ? c.t : c.t - c.nq;
             row = min(c.it.R0 + s * kSlotRows + trow, c.it.R1 - 1);
             src = c.t < c.nq ? a.q : a.out;
-        } else {       // K rows then V rows of key tile kt
+        } else {       // K rows then V rows of key tile kt (raw keys for a band item)
             const bool isv = trow >= kTileA;
-            row = min(kt * kTileA + (isv ? trow - kTileA : trow), c.it.R1 - 1);
-            src = isv ? a.vs : a.ks;
+            row = min(c.it.kbeg + kt * kTileA + (isv ? trow - kTileA : trow), c.it.R1 - 1);
+            src = BAND ? (isv ? a.vr : a.kr) : (isv ? a.vs : a.ks);
         }
         copy_rows_lds<DK>(static_cast<const uint16_t*>(src) + base + (size_t)(c.it.r + row * c.it.D) * pitch, trow,
                           buf + instr * 1024);
@@ -406,7 +423,7 @@ __device__ __forceinline__ int row_block(int wv, int j)
     return j == 0 ? wv : j == 1 ? 15 - wv : j == 2 ? 7 - wv : 8 + wv;
 }
 
-template <int DK, int NW, int RING>
+template <int DK, int NW, int RING, bool BAND>
 __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
@@ -427,14 +444,14 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 
     LaneOffsets<DK> off;
     off.init();
-    CursorA issue, comp;
+    CursorA<BAND> issue, comp;
     issue.seek(a, 0);
     comp = issue;
     int issued = 0, consumed = 0;
 #pragma unroll
     for (int j = 0; j < RING - 1; ++j) {
         if (issue.it.valid) {
-            issue_step_a<DK, NW>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
+            issue_step_a<DK, NW, BAND>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
             ++issued;
             issue.advance(a);
         }
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         else wait_vmcnt<0>();
         __syncthreads();
         if (issue.it.valid && issued < oldest + RING) {
-            issue_step_a<DK, NW>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
+            issue_step_a<DK, NW, BAND>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
             ++issued;
             issue.advance(a);
         }
@@ -542,11 +559,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         // the softmax of tile t); four blocks have no registers for a
         // second set of scores and rely on the MFMAs of one block running
         // while the softmax of another is computed.
-        const int nfull = min(it.R0 / kTileA, comp.ntile - 1);
+        const int nfull = BAND ? 0 : min(it.R0 / kTileA, comp.ntile - 1);
         floatx4 sc[NB][4];
         bool have_scores = false;
         int tt = 0;
-        if constexpr (NB == 2) {
+        if constexpr (NB == 2 && !BAND) {
             if (nfull > 0) {
                 wait_tile(consumed, consumed);
                 qk(consumed, sc);
@@ -568,18 +585,38 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             }
         }
         for (; tt < comp.ntile; ++tt) {
+            const int k0 = it.kbeg + tt * kTileA;
+            // a band item's block rows rs .. rs+15 see keys rs-W+1 .. rs+15
+            bool skip = false;
+            if (BAND) {
+                skip = true;
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    skip &= !(has[j] && k0 <= rs[j] + 15 && k0 + kTileA - 1 >= rs[j] - it.W + 1);
+            }
             if (!have_scores) {
                 wait_tile(consumed, consumed);
-                qk(consumed, sc);
+                if (!skip) qk(consumed, sc);
             }
             have_scores = false;
-            const int k0 = tt * kTileA;
+            if (skip) {  // neither block sees this tile (the wave still keeps the ring in step)
+                ++consumed;
+                continue;
+            }
             bf16x8 pb[NB][2];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 pb[j][0] = bf16x8{};
                 pb[j][1] = bf16x8{};
-                if (has[j] && k0 <= rs[j] + 15) {
+                if (BAND) {
+                    if (has[j] && k0 <= rs[j] + 15 && k0 + kTileA - 1 >= rs[j] - it.W + 1) {
+                        // a tile inside every row's band needs no mask
+                        if (k0 >= rs[j] + 16 - it.W && k0 + kTileA - 1 <= rs[j])
+                            softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
+                        else
+                            softmax64<DK, true>(f[j], sc[j], rs[j] + i, rs[j] + i - it.W + 1, k0, a.scale_log2, pb[j]);
+                    }
+                } else if (has[j] && k0 <= rs[j] + 15) {
                     if (k0 + kTileA - 1 <= rs[j]) softmax64<DK, false>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
                     else softmax64<DK, true>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
                 }
@@ -587,145 +624,27 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             pv(consumed, pb);
             ++consumed;
         }
+        if (BAND) {  // partial state for the dilated pass: o in `out`, (m, l) in the workspace
 #pragma unroll
-        for (int j = 0; j < NB; ++j) f[j].store(op + (size_t)(it.r + (rs[j] + i) * it.D) * pitch, rs[j] + i < it.R1);
+            for (int j = 0; j < NB; ++j) {
+                const size_t row = (size_t)it.b * a.T + rs[j] + i;
+                f[j].store_partial(op + (size_t)(rs[j] + i) * pitch, a.ml + (row * a.H + it.h) * 2, rs[j] + i < it.R1);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) f[j].store(op + (size_t)(it.r + (rs[j] + i) * it.D) * pitch, rs[j] + i < it.R1);
+        }
         comp.seek(a, comp.round + 1);
     }
 }
 
 // ------------------------------------------------------------------ band pass
-// Local window of raw keys for heads with W > 0: query t sees the raw keys
-// t-W+1 .. t.  A workgroup takes 256 contiguous queries of one (b, h) (two
-// 16-row blocks per wave, w and 15-w, as in path A) and streams the raw
-// key/value band [t0-W+1, t0+255] through the same 64-key LDS ring; a wave
-// skips the tiles that neither of its blocks sees.  It leaves a partial
+// Local window of raw keys for heads with W > 0 runs through the same
+// persistent kernel with BAND = true: an item is 256 contiguous queries of
+// one (b, h) and the key tiles cover [t0-W+1, t0+255]; waves skip the tiles
+// that neither of their blocks sees, and the item ends with a partial
 // softmax state per query -- the normalised output in `out` and (m, l) in
-// the workspace -- from which path A continues over the dilated states.
-__device__ __forceinline__ void decode_band(const AttnArgs& a, int block, int& b, int& h, int& W, int& t0)
-{
-    int c = 0;
-    while (c + 1 < a.nclass && block >= a.cls[c + 1].block_begin) ++c;
-    const AttnClass& k = a.cls[c];
-    const int local = block - k.block_begin;
-    const int idx = local % k.per_level;
-    t0 = (local / k.per_level) * kAttnRowsA;
-    h = a.heads[k.head_off + idx % k.nheads];
-    b = idx / k.nheads;
-    W = k.W;
-}
-
-template <int DK>
-__global__ __launch_bounds__(kWavesA * kWave) void attn_band_kernel(AttnArgs a)
-{
-    typedef Geo<DK> G;
-    constexpr int TILE_BYTES = 2 * kTileA * G::ROWB;
-    constexpr int PER_WAVE = (2 * kTileA / G::RPI) / kWavesA;
-    static_assert((2 * kTileA / G::RPI) % kWavesA == 0, "tile loads split evenly over waves");
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int i = lane & 15;
-    const int pitch = a.H * DK;
-    int b, h, W, t0;
-    decode_band(a, blockIdx.x, b, h, W, t0);
-    const int t1 = min(t0 + kAttnRowsA, a.T);
-    const int kbeg = max(0, t0 - W + 1) & ~(kTileA - 1);  // first tile, 64-aligned
-    const int ntile = (t1 - kbeg + kTileA - 1) / kTileA;
-    const size_t base = ((size_t)b * a.T * a.H + h) * DK;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + base;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + base;
-
-    auto issue = [&](int tt) {
-        lds_char* buf = smem + (tt % kRingA) * TILE_BYTES;
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int instr = wv * PER_WAVE + j;
-            const int trow = instr * G::RPI + lane / G::CH;  // K rows then V rows
-            const bool isv = trow >= kTileA;
-            const int kr = isv ? trow - kTileA : trow;
-            const int key = min(kbeg + tt * kTileA + kr, t1 - 1);
-            const uint16_t* src = static_cast<const uint16_t*>(isv ? a.vr : a.kr) + base + (size_t)key * pitch;
-            copy_rows_lds<DK>(src, kr, buf + instr * 1024);
-        }
-    };
-    int issued = 0;
-#pragma unroll
-    for (int j = 0; j < kRingA - 1; ++j)
-        if (issued < ntile) issue(issued++);
-
-    LaneOffsets<DK> off;
-    off.init();
-    const int rsA = t0 + 16 * wv, rsB = t0 + 16 * (15 - wv);
-    const bool hasA = rsA < t1, hasB = rsB < t1;
-    Frag<DK> fA, fB;
-    fA.reset();
-    fB.reset();
-    fA.load_q(qp + (size_t)(rsA + i) * pitch, rsA + i < t1);
-    fB.load_q(qp + (size_t)(rsB + i) * pitch, rsB + i < t1);
-
-    for (int tt = 0; tt < ntile; ++tt) {
-        const int ahead = issued - tt - 1;
-        if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
-        else if (ahead == 1) wait_vmcnt<PER_WAVE>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (issued < ntile) issue(issued++);
-        const int k0 = kbeg + tt * kTileA;
-        // block rows rs .. rs+15 see keys rs-W+1 .. rs+15 (each row its own band)
-        const bool needA = hasA && k0 <= rsA + 15 && k0 + kTileA - 1 >= rsA - W + 1;
-        const bool needB = hasB && k0 <= rsB + 15 && k0 + kTileA - 1 >= rsB - W + 1;
-        if (!(needA || needB)) continue;
-        const lds_char* kt = smem + (tt % kRingA) * TILE_BYTES;
-        const lds_char* vt = kt + kTileA * G::ROWB;
-        floatx4 sA[4], sB[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sA[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            sB[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {  // k-steps outermost: independent chains interleave
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
-                sA[kb] = mfma16(kf, fA.q[ks], sA[kb]);
-                sB[kb] = mfma16(kf, fB.q[ks], sB[kb]);
-            }
-        }
-        bf16x8 pA[2] = {}, pB[2] = {};
-        // a tile inside every row's band needs no mask
-        if (needA) {
-            if (k0 >= rsA + 16 - W && k0 + kTileA - 1 <= rsA)
-                softmax64<DK, false>(fA, sA, 0, 0, 0, a.scale_log2, pA);
-            else
-                softmax64<DK, true>(fA, sA, rsA + i, rsA + i - W + 1, k0, a.scale_log2, pA);
-        }
-        if (needB) {
-            if (k0 >= rsB + 16 - W && k0 + kTileA - 1 <= rsB)
-                softmax64<DK, false>(fB, sB, 0, 0, 0, a.scale_log2, pB);
-            else
-                softmax64<DK, true>(fB, sB, rsB + i, rsB + i - W + 1, k0, a.scale_log2, pB);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
-                const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
-                const shortx4 x0 = lds_tr(vp);
-                const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
-                typedef short shortx8 __attribute__((ext_vector_type(8)));
-                const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-                fA.acc[db] = mfma16(vf, pA[hh], fA.acc[db]);
-                fB.acc[db] = mfma16(vf, pB[hh], fB.acc[db]);
-            }
-        }
-    }
-    const size_t rowA = (size_t)b * a.T + rsA + i, rowB = (size_t)b * a.T + rsB + i;
-    fA.store_partial(op + (size_t)(rsA + i) * pitch, a.ml + (rowA * a.H + h) * 2, rsA + i < t1);
-    fB.store_partial(op + (size_t)(rsB + i) * pitch, a.ml + (rowB * a.H + h) * 2, rsB + i < t1);
-}
+// the workspace -- from which the dilated pass continues.
 
 // ring slots plus the (m, l) side buffers of path A
 size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * (2 * kTileA * d * 2 + 1024); }
@@ -746,46 +665,43 @@ static void set_lds(K kernel, size_t lds, bool& done)
 #endif
 constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated kernel
 
-hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
+template <bool BAND>
+static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, hipStream_t stream)
 {
-    bool windowed = false;
-    for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
-    static bool s128 = false, s64 = false, s128r = false, s64r = false;
+    static bool s[2][2] = {{false, false}, {false, false}};
     const dim3 block(kWavesDil * kWave);
-    if (!windowed) {  // deeper prefetch: five ring slots
+    if (ring5) {  // deeper prefetch: five ring slots (no side buffers)
         const size_t lds = attn_lds_bytes_a5(d);
         if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, 5>, lds, s128r);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND>, lds, s[0][0]);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND>), dim3(grid), block, lds, stream, a);
         } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, 5>, lds, s64r);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND>, lds, s[0][1]);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND>), dim3(grid), block, lds, stream, a);
         }
         return hipGetLastError();
     }
     const size_t lds = attn_lds_bytes_a(d);
     if (d == 128) {
-        set_lds(attn_dilated_kernel<128, kWavesDil, kRingA>, lds, s128);
-        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA>), dim3(grid), block, lds, stream, a);
+        set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND>, lds, s[1][0]);
+        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND>), dim3(grid), block, lds, stream, a);
     } else {
-        set_lds(attn_dilated_kernel<64, kWavesDil, kRingA>, lds, s64);
-        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA>), dim3(grid), block, lds, stream, a);
+        set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND>, lds, s[1][1]);
+        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND>), dim3(grid), block, lds, stream, a);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, hipStream_t stream)
+hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
-    const size_t lds = attn_lds_bytes_a(d);
-    static bool s128 = false, s64 = false;
-    if (d == 128) {
-        set_lds(attn_band_kernel<128>, lds, s128);
-        hipLaunchKernelGGL(attn_band_kernel<128>, dim3(a.nblocks), dim3(kWavesA * kWave), lds, stream, a);
-    } else {
-        set_lds(attn_band_kernel<64>, lds, s64);
-        hipLaunchKernelGGL(attn_band_kernel<64>, dim3(a.nblocks), dim3(kWavesA * kWave), lds, stream, a);
-    }
-    return hipGetLastError();
+    bool windowed = false;
+    for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
+    return launch_path_a<false>(a, d, grid, !windowed, stream);
+}
+
+hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
+{
+    return launch_path_a<true>(a, d, grid, true, stream);
 }
 
 // ------------------------------------------------------------------ fp32

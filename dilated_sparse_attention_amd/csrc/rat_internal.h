@@ -90,8 +90,9 @@ struct AttnArgs {
 
 // dilated states, every head: persistent kernel, `grid` workgroups (nblocks = items)
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
-// raw-key band of heads with W > 0: one workgroup per 256 queries (nblocks)
-hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, hipStream_t stream);
+// raw-key band of heads with W > 0: persistent kernel, `grid` workgroups,
+// items of 256 contiguous queries (nblocks = items)
+hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
 
 // Simple fp32 path (one workgroup per query row; exact fp32 arithmetic).
 struct AttnF32Args {
