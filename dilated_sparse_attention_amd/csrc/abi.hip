@@ -260,7 +260,7 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         AttnClass& k = dil.cls[dil.nclass++];
         k.D = c.D; k.W = c.W;
         k.nheads = (int)c.heads.size(); k.head_off = hoff;
-        for (int hh : c.heads) { dil.heads[hoff] = (int16_t)hh; band.heads[hoff] = (int16_t)hh; ++hoff; }
+        for (int hh : c.heads) { dil.heads[hoff] = hh; band.heads[hoff] = hh; ++hoff; }
         const int Mmax = (T + c.D - 1) / c.D;
         k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
         k.per_level = B * k.nheads * c.D;

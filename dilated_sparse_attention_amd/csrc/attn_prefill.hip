@@ -74,21 +74,8 @@ __device__ __forceinline__ int swz(int r, int c)
     return r * Geo<DK>::ROWB + ((c ^ swz_key<DK>(r)) << 4);
 }
 
-// One wave copies RPI rows (1 KiB) global -> LDS: lane l fills row l / (CH)
-// of the group, physical chunk l % CH, with the global chunk that the
-// swizzle puts there.  `row_ptr` is the global address of the lane's row.
-template <int DK>
-__device__ __forceinline__ void copy_rows_lds(const uint16_t* row_ptr, int tile_row, lds_char* dst)
-{
-    constexpr int CH = Geo<DK>::CH;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int p = lane % CH;
-    const int c = p ^ swz_key<DK>(tile_row);
-    dma16(row_ptr + c * 8, dst);
-}
-
-// max of three scores in one v_max3_f32: the operands come straight from
-// MFMA accumulators or -inf masks, so the quieting of signalling NaNs that
+// max of three scores in one v_max3_f32: the operands are MFMA results,
+// -inf masks or maxima of these, so the quieting of signalling NaNs that
 // fmaxf implies (an extra v_max per operand) is not needed
 __device__ __forceinline__ float max3(float a, float b, float c)
 {
@@ -102,9 +89,9 @@ __device__ __forceinline__ float max3(float a, float b, float c)
 __device__ __forceinline__ float max_over_rows(float x)
 {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max3(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max3(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
 }
 
 // Online-softmax state of one 16-query fragment (lane (g, i) owns query i;
@@ -255,6 +242,8 @@ constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
 template <bool BAND>
 struct CursorA {
     int round, t, nq, no, ntile;
+    int rowidx;   // (b T + r) H + h: first row of the item in units of head rows
+    int dstride;  // min(D, T) H: head rows between consecutive rows of the item
     ItemA it;
 
     __device__ __forceinline__ int item_of(int rnd) const
@@ -272,6 +261,10 @@ struct CursorA {
                 nq = (it.R1 - it.R0 + kSlotRows - 1) / kSlotRows;
                 no = (!BAND && it.W > 0) ? nq : 0;
                 ntile = (it.R1 - it.kbeg + kTileA - 1) / kTileA;
+                rowidx = (it.b * a.T + it.r) * a.H + it.h;
+                // a residue of D >= T holds one row: min(D, T) keeps byte
+                // strides below 2^32 without changing any address
+                dstride = min(it.D, a.T) * a.H;
                 return;
             }
         }
@@ -283,70 +276,154 @@ struct CursorA {
     }
 };
 
+// Source tensors of the ring DMA, held in scalar registers for the whole
+// kernel and handed to the issue as values (a selection among kernel
+// argument fields, or among fields of a struct in memory, inside the loop
+// becomes a memory load of the selected field on every step).
+struct DmaSrc {
+    uint64_t q, out, kv;  // kv: this wave's half of a key tile (K or V rows)
+};
+
+template <int NW, bool BAND>
+__device__ __forceinline__ DmaSrc dma_sources(const AttnArgs& a, int wv)
+{
+    uint64_t q = (uint64_t)(uintptr_t)a.q, out = (uint64_t)(uintptr_t)a.out;
+    uint64_t k = (uint64_t)(uintptr_t)(BAND ? a.kr : a.ks), v = (uint64_t)(uintptr_t)(BAND ? a.vr : a.vs);
+    asm volatile("" : "+s"(q), "+s"(out), "+s"(k), "+s"(v));
+    uint64_t kv = wv >= NW / 2 ? v : k;
+    asm volatile("" : "+s"(kv));
+    return DmaSrc{q, out, kv};
+}
+
+// global_load_lds_dwordx4 with a scalar base and a 32-bit per-lane byte
+// offset: lane l's 16 bytes at base + voff land at dst + 16 l (M0 = dst).
+__device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t m0)
+{
+    // readfirstlane returns int: widen each half through uint32_t (no sign extension)
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+    base = ((uint64_t)hi << 32) | lo;
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+
+// Per-lane constants of the ring DMA: row lq = lane / CH of each RPI-row
+// copy, and the swizzled 16-byte chunk the lane fetches for a copy whose
+// first slot row is a multiple of RPI (the XOR key is linear in the row
+// bits, so copy j only XORs in the key of row RPI j, a uniform value).
+template <int DK>
+struct DmaLane {
+    uint32_t lq, col16;
+    __device__ __forceinline__ void init()
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        lq = lane / Geo<DK>::CH;
+        col16 = (uint32_t)(((lane % Geo<DK>::CH) ^ swz_key<DK>(lq)) << 4);
+    }
+};
+
 // DMA of the cursor's ring step into slot `buf` (every wave issues the same
-// PER_WAVE row copies; partial-output steps add one copy of their (m, l)
-// words into `side` on waves 0-3).
+// PER_WAVE row copies of RPI rows each; partial-output steps add one copy
+// of their (m, l) words into `side` on waves 0-3).  Rows past the item's
+// last row R1 - 1 are clamped to it.
 template <int DK, int NW, bool BAND>
-__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND>& c, lds_char* buf, lds_char* side)
+__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND>& c, uint64_t src_q,
+                                             uint64_t src_out, uint64_t src_kv, const DmaLane<DK>& dl, uint32_t buf,
+                                             uint32_t side)
 {
     typedef Geo<DK> G;
     constexpr int INSTR = kSlotRows / G::RPI;
     constexpr int PER_WAVE = INSTR / NW;
-    const int lane = threadIdx.x & (kWave - 1);
+    static_assert(PER_WAVE * G::RPI <= kTileA && kTileA % (PER_WAVE * G::RPI) == 0, "a wave copies K or V rows only");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int pitch = a.H * DK;
-    const size_t base = ((size_t)c.it.b * a.T * a.H + c.it.h) * DK;
+    const int lane = threadIdx.x & (kWave - 1);
     const int kt = c.t - c.nq - c.no;  // key tile index, < 0 for query / partial steps
+    // first row of the wave's share of the slot, and the tensor it comes from
+    int row0;
+    uint64_t tsrc;
+    if (kt < 0) {  // query rows, or partial outputs, R0 + 128 s + 16 PER_WAVE wv ...
+        const int s = c.t < c.nq ? c.t : c.t - c.nq;
+        row0 = c.it.R0 + s * kSlotRows + wv * PER_WAVE * G::RPI;
+        tsrc = c.t < c.nq ? src_q : src_out;
+    } else {       // K rows (waves 0 .. NW/2-1) or V rows of key tile kt
+        row0 = c.it.kbeg + kt * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
+        tsrc = src_kv;
+    }
+    const uint32_t item_el = (uint32_t)c.rowidx * DK;
+    const uint32_t dp2 = (uint32_t)c.dstride * (2 * DK);  // bytes between rows r and r + 1 of the item
+    const int last = c.it.R1 - 1;
+    const uint32_t slot = buf + wv * PER_WAVE * 1024;  // LDS byte address of the wave's first copy
+    if (row0 + PER_WAVE * G::RPI - 1 <= last) {
+        // every row of the wave's share exists: copy j starts RPI rows after
+        // copy j - 1 (one 64-bit scalar add), lane offsets need no clamp
+        uint64_t base = tsrc + 2ull * item_el + (uint64_t)(uint32_t)row0 * dp2;
+        const uint64_t step = (uint64_t)G::RPI * dp2;
+        const uint32_t lrow = dl.lq * dp2;  // < 2^32: the row exists
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-        const int instr = wv * PER_WAVE + j;
-        const int trow = instr * G::RPI + lane / G::CH;  // row within the slot
-        const void* src;
-        int row;
-        if (kt < 0) {  // query rows, or partial outputs, R0 + 128 s + trow
-            const int s = c.t < c.nq ? c.t : c.t - c.nq;
-            row = min(c.it.R0 + s * kSlotRows + trow, c.it.R1 - 1);
-            src = c.t < c.nq ? a.q : a.out;
-        } else {       // K rows then V rows of key tile kt (raw keys for a band item)
-            const bool isv = trow >= kTileA;
-            row = min(c.it.kbeg + kt * kTileA + (isv ? trow - kTileA : trow), c.it.R1 - 1);
-            src = BAND ? (isv ? a.vr : a.kr) : (isv ? a.vs : a.ks);
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int instr = wv * PER_WAVE + j;
+            const uint32_t voff = lrow + (dl.col16 ^ (uint32_t)(swz_key<DK>(instr * G::RPI) << 4));
+            dma16_s(base, voff, slot + j * 1024);
+            base += step;
         }
-        copy_rows_lds<DK>(static_cast<const uint16_t*>(src) + base + (size_t)(c.it.r + row * c.it.D) * pitch, trow,
-                          buf + instr * 1024);
+    } else {
+        // the item ends inside the wave's share: rows past R1 - 1 read row R1 - 1
+        const uint64_t lrow64 = (uint64_t)dl.lq * dp2;  // saturated: only its min with lim is used
+        const uint32_t lrow = lrow64 > 0xffffffffull ? 0xffffffffu : (uint32_t)lrow64;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int instr = wv * PER_WAVE + j;
+            const int first = min(row0 + j * G::RPI, last);
+            const uint32_t lim = (uint32_t)(last - first) * dp2;
+            const uint64_t base = tsrc + 2ull * (item_el + (uint32_t)first * (dp2 >> 1));
+            const uint32_t voff = min(lrow, lim) + (dl.col16 ^ (uint32_t)(swz_key<DK>(instr * G::RPI) << 4));
+            dma16_s(base, voff, slot + j * 1024);
+        }
     }
     if (kt < 0 && c.t >= c.nq && wv < 4) {
         // (m, l) of the slot's 128 rows: 64 words per wave on waves 0-3, lane l -> word l
         const int w = wv * kWave + lane;
         const int row = min(c.it.R0 + (c.t - c.nq) * kSlotRows + (w >> 1), c.it.R1 - 1);
         const size_t t = (size_t)c.it.b * a.T + c.it.r + (size_t)row * c.it.D;
-        const float* src = a.ml + (t * a.H + c.it.h) * 2 + (w & 1);
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(side + wv * 256));
-        asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+        const float* p = a.ml + (t * a.H + c.it.h) * 2 + (w & 1);
+        asm volatile("global_load_lds_dword %0, off" ::"v"(p), "{m0}"(side + wv * 256) : "memory");
     }
 }
 
-// Per-lane byte offsets inside a swizzled tile, hoisted out of the tile
-// loop: K fragment of k-step ks for key block 0 (key block kb adds
-// kb * 16 rows), and the first transposing V read of 16-dim block db for
-// key half 0 (half hh adds 32 rows, the second read 16 rows).
+// Per-lane byte offsets inside a swizzled tile: K fragment of k-step ks for
+// key block 0 (key block kb adds kb * 16 rows), and the first transposing V
+// read of 16-dim block db for key half 0 (half hh adds 32 rows, the second
+// read 16 rows).  Only the offsets of ks = 0 and db = 0 are kept: the
+// fragment index enters the swizzled chunk as a plain XOR (chunk g + 4 ks
+// = g | 4 ks, and chunk 2 db + c = 2 db | c, while the XOR key of the row
+// touches neither bit range), which also leaves the row and in-chunk bits
+// of the offset alone.  Two registers instead of KS + DB.
 template <int DK>
 struct LaneOffsets {
-    int k[Geo<DK>::KS];
-    int v[Geo<DK>::DB];
+    int k0, v0;
 
     __device__ __forceinline__ void init()
     {
         const int lane = threadIdx.x & (kWave - 1);
         const int g = lane >> 4, i = lane & 15, s = lane & 15;
-#pragma unroll
-        for (int ks = 0; ks < Geo<DK>::KS; ++ks) k[ks] = swz<DK>(i, g + 4 * ks);
+        k0 = swz<DK>(i, g);
         const int r0 = 4 * g + (s >> 2);
-#pragma unroll
-        for (int db = 0; db < Geo<DK>::DB; ++db) {
-            const int dim = 16 * db + 4 * (s & 3);
-            v[db] = swz<DK>(r0, dim >> 3) + (dim & 7) * 2;
-        }
+        const int dim = 4 * (s & 3);
+        v0 = swz<DK>(r0, dim >> 3) + (dim & 7) * 2;
+    }
+    // The per-fragment offsets are recomputed at every use (one XOR each):
+    // an empty asm hides the base so that the compiler neither hoists the
+    // KS + DB values out of the tile loop nor spills them there.
+    __device__ __forceinline__ int kbase() const
+    {
+        int x = k0;
+        asm volatile("" : "+v"(x));
+        return x;
+    }
+    __device__ __forceinline__ int vbase() const
+    {
+        int x = v0;
+        asm volatile("" : "+v"(x));
+        return x;
     }
 };
 
@@ -387,7 +464,7 @@ __device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row,
     mx = max3(mx, s[2][1], s[2][2]);
     mx = max3(mx, s[2][3], s[3][0]);
     mx = max3(mx, s[3][1], s[3][2]);
-    mx = fmaxf(mx, s[3][3]);
+    mx = max3(mx, s[3][3], s[3][3]);
     mx = max_over_rows(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > f.m + kLazyRescale)) {
         const float mn = fmaxf(f.m, mx);
@@ -398,20 +475,30 @@ __device__ __forceinline__ void softmax64(Frag<DK>& f, floatx4 (&s)[4], int row,
         f.m = mn;
     }
     const float nm = f.m == -INFINITY ? 0.f : -f.m;
-    float sum = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * hh][j], c, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * hh + 1][j], c, nm));
-            sum += p0 + p1;
-            pb[hh][j] = (__bf16)p0;
-            pb[hh][4 + j] = (__bf16)p1;
+            pb[hh][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * hh][j], c, nm));
+            pb[hh][4 + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * hh + 1][j], c, nm));
         }
     }
-    f.l += sum;
+    // the denominator sums the same bf16-rounded weights that multiply V
+    // (one v_dot2 with (1, 1) per weight pair, exact products, fp32 sums)
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * q], pb[0][2 * q + 1]}, one, s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * q], pb[1][2 * q + 1]}, one, s1, false);
+    }
+    f.l += s0 + s1;
 }
+
+template <int BITS>
+struct Mask {
+    static constexpr int value = BITS;
+};
 
 // NW waves per workgroup, NB = 16 / NW row blocks of 16 queries per wave
 // (block w and its mirror 15 - w, with NB = 4 also 7 - w and 8 + w, so that
@@ -444,33 +531,40 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 
     LaneOffsets<DK> off;
     off.init();
+    DmaLane<DK> dl;
+    dl.init();
+    const DmaSrc dsrc = dma_sources<NW, BAND>(a, wv);
     CursorA<BAND> issue, comp;
     issue.seek(a, 0);
     comp = issue;
+    // ring steps issued and consumed; step n lives in slot n mod RING (a
+    // wrapping slot counter instead raises the register use of the band
+    // kernel past the point where it spills)
     int issued = 0, consumed = 0;
+    const uint32_t smem_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+    const uint32_t side_lds = smem_lds + (uint32_t)(side - smem);
+    auto issue_next = [&]() {
+        const int sl = issued % RING;
+        issue_step_a<DK, NW, BAND>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
+                                   side_lds + sl * 1024);
+        ++issued;
+        issue.advance(a);
+    };
+    auto consume = [&]() { ++consumed; };
 #pragma unroll
-    for (int j = 0; j < RING - 1; ++j) {
-        if (issue.it.valid) {
-            issue_step_a<DK, NW, BAND>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
-            ++issued;
-            issue.advance(a);
-        }
-    }
-    // Wait until ring step `seq` has landed, then barrier; refill the ring
-    // when the slot after step `oldest` (the oldest step still read after
-    // this barrier) is free.
-    auto wait_tile = [&](int seq, int oldest) {
-        const int ahead = issued - seq - 1;  // ring steps issued after `seq`
+    for (int j = 0; j < RING - 1; ++j)
+        if (issue.it.valid) issue_next();
+    // Wait until ring step `consumed + d` has landed, then barrier; refill
+    // the ring when a slot is free (the oldest step still read after this
+    // barrier is `consumed`).
+    auto wait_tile = [&](int d) {
+        const int ahead = issued - consumed - d - 1;  // ring steps issued after the awaited one
         if (RING > 4 && ahead >= 3) wait_vmcnt<3 * PER_WAVE>();
         else if (ahead >= 2) wait_vmcnt<2 * PER_WAVE>();
         else if (ahead == 1) wait_vmcnt<PER_WAVE>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (issue.it.valid && issued < oldest + RING) {
-            issue_step_a<DK, NW, BAND>(a, issue, smem + (issued % RING) * TILE_BYTES, side + (issued % RING) * 1024);
-            ++issued;
-            issue.advance(a);
-        }
+        if (issue.it.valid && issued < consumed + RING) issue_next();
     };
 
     Frag<DK> f[NB];
@@ -490,21 +584,21 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         }
         // query rows from the ring (lane (g, i): row i, dims 8g + 32ks .. +8)
         for (int s = 0; s < comp.nq; ++s) {
-            wait_tile(consumed, consumed);
+            wait_tile(0);
             const lds_char* qt = smem + (consumed % RING) * TILE_BYTES;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int r = 16 * row_block<NB>(wv, j);
                 if (r / kSlotRows == s) {
 #pragma unroll
-                    for (int ks = 0; ks < G::KS; ++ks) f[j].q[ks] = lds_b128(qt + (r % kSlotRows) * G::ROWB + off.k[ks]);
+                    for (int ks = 0; ks < G::KS; ++ks) f[j].q[ks] = lds_b128(qt + (r % kSlotRows) * G::ROWB + (off.k0 ^ (ks << 6)));
                 }
             }
-            ++consumed;
+            consume();
         }
         // windowed classes: continue from the band pass's partial state
         for (int s = 0; s < comp.no; ++s) {
-            wait_tile(consumed, consumed);
+            wait_tile(0);
             const lds_char* ot = smem + (consumed % RING) * TILE_BYTES;
             const float* ml = reinterpret_cast<const float*>(side + (consumed % RING) * 1024);
 #pragma unroll
@@ -513,46 +607,57 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
                 if (r / kSlotRows == s)
                     f[j].init_partial_lds(ot + (r % kSlotRows) * G::ROWB, ml + (r % kSlotRows) * 2, rs[j] + i < it.R1);
             }
-            ++consumed;
+            consume();
         }
 
         // k-steps outermost: 4 x NB independent accumulation chains sit
         // between two MFMAs of the same chain, so no MFMA waits for the
         // result of the one before it
-        auto qk = [&](int seq, floatx4 (&sc)[NB][4]) {
-            const lds_char* kt = smem + (seq % RING) * TILE_BYTES;
+        // `act` (a Mask<bits>): the row blocks whose MFMAs run
+        auto qk = [&](auto act, int sl, floatx4 (&sc)[NB][4]) {
+            constexpr int ACT = decltype(act)::value;
+            const lds_char* kt = smem + sl * TILE_BYTES;
+            const int kb0 = off.kbase();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int j = 0; j < NB; ++j) sc[j][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NB; ++j)
+                    if ((ACT >> j) & 1) sc[j][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < G::KS; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const bf16x8 kf = lds_b128(kt + off.k[ks] + kb * 16 * G::ROWB);
+                    const bf16x8 kf = lds_b128(kt + (kb0 ^ (ks << 6)) + kb * 16 * G::ROWB);
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) sc[j][kb] = mfma16(kf, f[j].q[ks], sc[j][kb]);
+                    for (int j = 0; j < NB; ++j)
+                        if ((ACT >> j) & 1) sc[j][kb] = mfma16(kf, f[j].q[ks], sc[j][kb]);
                 }
             }
         };
-        auto pv = [&](int seq, const bf16x8 (&pb)[NB][2]) {
-            const lds_char* vt = smem + (seq % RING) * TILE_BYTES + kTileA * G::ROWB;
+        auto pv = [&](auto act, int sl, const bf16x8 (&pb)[NB][2]) {
+            constexpr int ACT = decltype(act)::value;
+            const lds_char* vt = smem + sl * TILE_BYTES + kTileA * G::ROWB;
+            const int vb0 = off.vbase();
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                 for (int db = 0; db < G::DB; ++db) {
-                    const lds_char* vp = vt + off.v[db] + hh * 32 * G::ROWB;
+                    const lds_char* vp = vt + (vb0 ^ (db << 5)) + hh * 32 * G::ROWB;
                     const shortx4 x0 = lds_tr(vp);
                     const shortx4 x1 = lds_tr(vp + 16 * G::ROWB);
                     typedef short shortx8 __attribute__((ext_vector_type(8)));
                     const shortx8 v8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
                     const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) f[j].acc[db] = mfma16(vf, pb[j][hh], f[j].acc[db]);
+                    for (int j = 0; j < NB; ++j)
+                        if ((ACT >> j) & 1) f[j].acc[db] = mfma16(vf, pb[j][hh], f[j].acc[db]);
                 }
             }
         };
+        constexpr Mask<(1 << NB) - 1> all;
 
+        floatx4 sc[NB][4];
+        int tt = 0;
         // Tiles wholly below the chunk's first row are visible to every row
         // of the chunk and need no mask.  With two blocks per wave they run
         // software-pipelined (the QK^T MFMAs of tile t+1 are issued before
@@ -560,22 +665,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         // second set of scores and rely on the MFMAs of one block running
         // while the softmax of another is computed.
         const int nfull = BAND ? 0 : min(it.R0 / kTileA, comp.ntile - 1);
-        floatx4 sc[NB][4];
         bool have_scores = false;
-        int tt = 0;
         if constexpr (NB == 2 && !BAND) {
             if (nfull > 0) {
-                wait_tile(consumed, consumed);
-                qk(consumed, sc);
+                wait_tile(0);
+                qk(all, consumed % RING, sc);
                 for (; tt < nfull; ++tt) {
-                    wait_tile(consumed + 1, consumed);  // tile `consumed` still feeds P V
+                    wait_tile(1);  // the current tile still feeds P V
                     floatx4 nx[NB][4];
-                    qk(consumed + 1, nx);
+                    qk(all, (consumed + 1) % RING, nx);
                     bf16x8 pb[NB][2];
 #pragma unroll
                     for (int j = 0; j < NB; ++j) softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
-                    pv(consumed, pb);
-                    ++consumed;
+                    pv(all, consumed % RING, pb);
+                    consume();
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -586,21 +689,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         }
         for (; tt < comp.ntile; ++tt) {
             const int k0 = it.kbeg + tt * kTileA;
-            // a band item's block rows rs .. rs+15 see keys rs-W+1 .. rs+15
-            bool skip = false;
-            if (BAND) {
-                skip = true;
+            // a wave whose blocks see no key of the tile skips it: causal
+            // rows rs .. rs+15 see keys up to rs+15, a band item's rows only
+            // from rs-W+1
+            bool skip = true;
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    skip &= !(has[j] && k0 <= rs[j] + 15 && k0 + kTileA - 1 >= rs[j] - it.W + 1);
-            }
+            for (int j = 0; j < NB; ++j)
+                skip &= !(has[j] && k0 <= rs[j] + 15 && (!BAND || k0 + kTileA - 1 >= rs[j] - it.W + 1));
             if (!have_scores) {
-                wait_tile(consumed, consumed);
-                if (!skip) qk(consumed, sc);
+                wait_tile(0);
+                if (!skip) qk(all, consumed % RING, sc);
             }
             have_scores = false;
-            if (skip) {  // neither block sees this tile (the wave still keeps the ring in step)
-                ++consumed;
+            if (skip) {  // (the wave still keeps the ring in step)
+                consume();
                 continue;
             }
             bf16x8 pb[NB][2];
@@ -617,12 +719,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
                             softmax64<DK, true>(f[j], sc[j], rs[j] + i, rs[j] + i - it.W + 1, k0, a.scale_log2, pb[j]);
                     }
                 } else if (has[j] && k0 <= rs[j] + 15) {
-                    if (k0 + kTileA - 1 <= rs[j]) softmax64<DK, false>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
+                    if (k0 + kTileA - 1 <= rs[j]) softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
                     else softmax64<DK, true>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
                 }
             }
-            pv(consumed, pb);
-            ++consumed;
+            pv(all, consumed % RING, pb);
+            consume();
         }
         if (BAND) {  // partial state for the dilated pass: o in `out`, (m, l) in the workspace
 #pragma unroll

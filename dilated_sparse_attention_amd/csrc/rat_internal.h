@@ -85,7 +85,7 @@ struct AttnArgs {
     int nclass;
     int nblocks;
     AttnClass cls[kAttnMaxClasses];
-    int16_t heads[kAttnMaxHeads];
+    int heads[kAttnMaxHeads];  // 32-bit: scalar loads have no 16-bit form
 };
 
 // dilated states, every head: persistent kernel, `grid` workgroups (nblocks = items)
