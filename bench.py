@@ -10,7 +10,8 @@ do not find their data in the 256 MB Infinity Cache.  ``value`` is prefill
 tokens per second per layer, B*T / step time.
 
 Per-kernel durations come from HIP events recorded on the stream the
-kernels are launched on (torch's current stream).  The JSON line also
+kernels are launched on (torch's current stream), around a run of
+back-to-back launches of that one kernel.  The JSON line also
 carries the roofline of the dominant kernel, the oracle timed on the host
 cores on a bounded sample (``cpu_baseline``) and, under ``extra``, the other
 workloads: long prefill with a window (both recurrence readings), the 7.6B
@@ -71,26 +72,6 @@ def load_traffic(kernel):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
-class Timer:
-    """Events around the launches of each kernel on the current stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def mark(self, name, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        out = fn()
-        ev1.record()
-        self.pairs.setdefault(name, []).append((ev0, ev1))
-        return out
-
-    def mean_ms(self, name):
-        return sum(a.elapsed_time(b) for a, b in self.pairs[name]) / len(self.pairs[name])
-
-
 def attn_pairs(T, D, W):
     """(dilated pairs, local pairs) of one head: closed forms of the index-set
     sizes summed over the T queries."""
@@ -129,17 +110,11 @@ def run_prefill(torch, rat, w, steps, warmup, mode=0, nsets=3):
         sets.append((x, ks, vs, out))
     D, W = list(w.D), list(w.W)
 
-    def step(i, timer=None):
+    def step(i):
         x, ks, vs, out = sets[i % nsets]
-        scan = lambda: rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)  # noqa: E731
-        attn = lambda: rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None,  # noqa: E731
-                                                x["v"] if need_raw else None, D=D, W=W, out=out)
-        if timer is None:
-            scan()
-            attn()
-        else:
-            timer.mark("scan", scan)
-            timer.mark("attn", attn)
+        rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)
+        rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None, x["v"] if need_raw else None,
+                                 D=D, W=W, out=out)
 
     for i in range(warmup):
         step(i)
@@ -154,12 +129,25 @@ def run_prefill(torch, rat, w, steps, warmup, mode=0, nsets=3):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / steps
-    # per-kernel durations in a second timed pass (events between launches)
-    timer = Timer(torch)
-    for i in range(steps):
-        step(i, timer)
-    torch.cuda.synchronize()
-    scan_ms, attn_ms = timer.mean_ms("scan"), timer.mean_ms("attn")
+    # per-kernel durations: each kernel launched `steps` times back to back
+    # over the rotating sets, between two events on the launch stream (an
+    # event pair around every single launch would add its own gap to each)
+    def kernel_ms(which):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            x, ks, vs, out = sets[i % nsets]
+            if which == "scan":
+                rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)
+            else:
+                rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None, x["v"] if need_raw else None,
+                                         D=D, W=W, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    scan_ms, attn_ms = kernel_ms("scan"), kernel_ms("attn")
     del sets
     torch.cuda.empty_cache()
     return ms_step, wall, scan_ms, attn_ms
@@ -185,11 +173,14 @@ def run_decode(torch, rat, w, steps, warmup, nsets=3):
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(steps):
-        timer.mark("decode", lambda: call(i))
+        call(i)
+    e1.record()
     torch.cuda.synchronize()
-    ms = timer.mean_ms("decode")
+    ms = e0.elapsed_time(e1) / steps
     nd = [(w.T + Dh - 1) // Dh for Dh in w.D]
     nw = [min(Wh, w.T) for Wh in w.W]
     s = 2

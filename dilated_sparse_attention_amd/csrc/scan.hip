@@ -21,11 +21,12 @@
 //     state; the last state with the gate product forms the segment's
 //     affine map h -> A*h + B per channel (the raw inputs stay in
 //     registers);
-//   * one wave turns the 32 segment maps into exclusive prefixes (and the
-//     chunk's map, which it publishes) while another finds the chunk's
-//     carry-in by a decoupled look-back over the chunks before it (Merrill
-//     & Garland's single-pass scan), through 64-bit words that carry
-//     (value, epoch tag) and so need no memory fence;
+//   * two waves (half of the channels each) turn the 32 segment maps into
+//     exclusive prefixes (and the chunk's map, which they publish) while
+//     another finds the chunk's carry-in by a decoupled look-back over the
+//     chunks before it (Merrill & Garland's single-pass scan), through
+//     64-bit words that carry (value, epoch tag) and so need no memory
+//     fence;
 //   * pass 2 runs the recurrence again from the segment's carry-in (gates
 //     evaluated again) and stores the states.
 //   Chunk order comes from a ticket counter so that every chunk a
@@ -90,6 +91,8 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
     constexpr int TPL = kScanTpl;           // tokens per segment
     constexpr int CT = NSEG * TPL;          // tokens per chunk
     constexpr int C0 = BW / kWave;          // channels per lane of the single-wave steps
+    constexpr int PW = C0 > 1 ? 2 : 1;      // waves of the segment prefix step
+    constexpr int CP = BW / (PW * kWave);   // channels per lane there
     static_assert(CT == kScanChunk && BW == ScanBlock<E>::value, "geometry shared with the host plan");
     // segment maps (A, K, V) per channel; then their exclusive prefixes
     __shared__ float s_seg[NSEG][3][BW];
@@ -265,17 +268,18 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             s_carry[0][lane * C0 + j] = inK[j];
             s_carry[1][lane * C0 + j] = inV[j];
         }
-    } else if (w == 1) {
-        // meanwhile: exclusive prefix maps of the segments (in place), the
-        // chunk's map and its publication (the aggregate, or at once the
-        // inclusive prefix when a restart makes the map ignore its carry-in)
+    } else if (w <= PW) {
+        // meanwhile, waves 1 .. PW (a share of the channels each): exclusive
+        // prefix maps of the segments (in place), the chunk's map and its
+        // publication (the aggregate, or at once the inclusive prefix when a
+        // restart makes the map ignore its carry-in)
         bool closed = true;
-        float cA[C0], cK[C0], cV[C0];
+        float cA[CP], cK[CP], cV[CP];
 #pragma unroll
-        for (int j = 0; j < C0; ++j) {
-            const int ch = lane * C0 + j;
+        for (int j = 0; j < CP; ++j) {
+            const int ch = ((w - 1) * kWave + lane) * CP + j;
             float pA = 1.f, pK = 0.f, pV = 0.f;
-#pragma unroll 4
+#pragma unroll 8
             for (int s2 = 0; s2 < NSEG; ++s2) {
                 const float sa = s_seg[s2][0][ch], sk = s_seg[s2][1][ch], sv = s_seg[s2][2][ch];
                 s_seg[s2][0][ch] = pA;
@@ -289,20 +293,28 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             s_tot[0][ch] = pA; s_tot[1][ch] = pK; s_tot[2][ch] = pV;
             closed &= pA == 0.f;
         }
+        // the successors' look-back reads the words of C0 adjacent channels
+        // per lane and needs them all of one kind: decide over that group
+        // (adjacent lanes here when CP < C0)
+        if (CP < C0) {
+#pragma unroll
+            for (int m = CP; m < C0; m *= 2) closed &= __shfl_xor((int)closed, m / CP) != 0;
+        }
         if (has_next) {
+            const int ch0p = ((w - 1) * kWave + lane) * CP;
             if (closed) {
 #pragma unroll
-                for (int j = 0; j < C0; ++j) {
-                    store_tagged(ic_out + lane * C0 + j, cK[j], tag);
-                    store_tagged(ic_out + BW + lane * C0 + j, cV[j], tag);
+                for (int j = 0; j < CP; ++j) {
+                    store_tagged(ic_out + ch0p + j, cK[j], tag);
+                    store_tagged(ic_out + BW + ch0p + j, cV[j], tag);
                 }
             } else {
                 uint64_t* ag = a.agg + slot * (3 * BW);
 #pragma unroll
-                for (int j = 0; j < C0; ++j) {
-                    store_tagged(ag + lane * C0 + j, cA[j], tag);
-                    store_tagged(ag + BW + lane * C0 + j, cK[j], tag);
-                    store_tagged(ag + 2 * BW + lane * C0 + j, cV[j], tag);
+                for (int j = 0; j < CP; ++j) {
+                    store_tagged(ag + ch0p + j, cA[j], tag);
+                    store_tagged(ag + BW + ch0p + j, cK[j], tag);
+                    store_tagged(ag + 2 * BW + ch0p + j, cV[j], tag);
                 }
             }
         }
