@@ -40,6 +40,14 @@ __device__ __forceinline__ void forget_gate(float logit, float& g, float& gbar)
     gbar = pos ? es : s;
 }
 
+// The forget gate alone, g = 1/(1 + 2^(-l log2 e)): exactly 0 at l = -inf
+// and 1 at l = +inf.  With h = x + g (h - x) -- the same recurrence as
+// g h + (1 - g) x -- the complement is never formed.
+__device__ __forceinline__ float gate(float logit)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-logit * kLog2e));
+}
+
 // Relaxed agent-scope atomics: each 64-bit word carries (value bits, tag) and
 // validates itself, so no fence is needed between producer and consumer.
 __device__ __forceinline__ void store_tagged(uint64_t* p, float v, uint32_t tag)

@@ -32,8 +32,10 @@
 //   Chunk order comes from a ticket counter so that every chunk a
 //   workgroup waits for belongs to a workgroup that is already running;
 //   the same 64-bit atomic returns the call's epoch.
+//   The update is written h = x + g (h - x): one exp and one reciprocal
+//   per element give g, and 1 - g is never formed.
 //   RESTART (state cleared where t mod L == 0) is the same recurrence with
-//   g forced to 0 at those positions; a chunk that starts at a restart
+//   the state before those positions set to 0; a chunk that starts at a restart
 //   needs no carry, and a map with A == 0 is published as an inclusive
 //   prefix at once and ends the look-back of its successors.
 //
@@ -128,15 +130,25 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
     const size_t rowbase = (size_t)b * a.T * a.N + ch0;
 
     u32x4 rk[TPL], rv[TPL], rg[TPL];
+    if (tb + CT <= a.T && cblk + BW <= a.N) {  // the whole chunk exists (uniform)
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        if (cvalid && t0 + i < a.T) {
+        for (int i = 0; i < TPL; ++i) {
             const size_t o = rowbase + (size_t)(t0 + i) * a.N;
             rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + o));
             rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + o));
             rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + o));
-        } else {
-            rk[i] = rv[i] = rg[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            if (cvalid && t0 + i < a.T) {
+                const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+                rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + o));
+                rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + o));
+                rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + o));
+            } else {
+                rk[i] = rv[i] = rg[i] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
     // RESTART positions (t mod L == 0) of this segment, as a bit mask
@@ -156,13 +168,17 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
         const bool restart = (rmask >> i) & 1u;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            float g, gb;
-            forget_gate(R16::get(rg[i], j), g, gb);
-            if (restart) g = 0.f;
+            const float g = gate(R16::get(rg[i], j));
+            if (restart) {  // the state before this token is cleared: the map forgets its input
+                A[j] = 0.f;
+                K[j] = 0.f;
+                V[j] = 0.f;
+            }
             if (live) {
+                const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
                 A[j] *= g;
-                K[j] = fmaf(g, K[j], gb * R16::get(rk[i], j));
-                V[j] = fmaf(g, V[j], gb * R16::get(rv[i], j));
+                K[j] = fmaf(g, K[j] - xk, xk);
+                V[j] = fmaf(g, V[j] - xv, xv);
             }
         }
     }
@@ -354,11 +370,14 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
         float ok[CPL], ov[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            float g, gb;
-            forget_gate(R16::get(rg[i], j), g, gb);
-            if (restart) g = 0.f;
-            ck[j] = fmaf(g, ck[j], gb * R16::get(rk[i], j));
-            cv[j] = fmaf(g, cv[j], gb * R16::get(rv[i], j));
+            const float g = gate(R16::get(rg[i], j));
+            if (restart) {  // cleared state before this token
+                ck[j] = 0.f;
+                cv[j] = 0.f;
+            }
+            const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
+            ck[j] = fmaf(g, ck[j] - xk, xk);
+            cv[j] = fmaf(g, cv[j] - xv, xv);
             ok[j] = ck[j];
             ov[j] = cv[j];
         }
