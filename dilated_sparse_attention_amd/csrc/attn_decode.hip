@@ -55,10 +55,42 @@ template <> struct Row8<float> {  // 8 fp32 = 32 bytes
     }
 };
 
-constexpr int kDecUnroll = 4;
+// A row slice of 8 elements as loaded (one or two 16-byte words), unpacked
+// to fp32 where it is used.  Cache rows are read once per call: the loads
+// are non-temporal (streamed past the caches that later reads would use).
+template <typename E> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    u32x4 w;
+    __device__ __forceinline__ void load(const uint16_t* p)
+    {
+        w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    __device__ __forceinline__ float operator[](int j) const { return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]); }
+};
+template <> struct Raw8<float> {
+    floatx4 a, b;
+    __device__ __forceinline__ void load(const float* p)
+    {
+        a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+    }
+    __device__ __forceinline__ float operator[](int j) const { return j < 4 ? a[j] : b[j - 4]; }
+};
+
+#ifndef RAT_DEC_UNROLL
+#define RAT_DEC_UNROLL 4
+#endif
+// keys per lane group in flight per iteration; waves per SIMD the register
+// budget must allow (six: every (b, h) of the 2.6B-scale decode batch runs
+// in one round of workgroups)
+constexpr int kDecUnroll = RAT_DEC_UNROLL;
+#ifndef RAT_DEC_OCC
+#define RAT_DEC_OCC 6
+#endif
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(RAT_DEC_OCC)))
+void decode_kernel(DecodeArgs a)
 {
     constexpr int LPK = DK / 8;          // lanes per key row
     constexpr int KPI = kWave / LPK;     // keys per wave step
@@ -99,7 +131,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(DecodeArgs a)
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
     for (int k0 = w_begin; k0 < w_end; k0 += KPI * kDecUnroll) {
-        float kx[kDecUnroll][8], vx[kDecUnroll][8];
+        Raw8<E> kx[kDecUnroll], vx[kDecUnroll];
         bool ok[kDecUnroll];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
@@ -108,8 +140,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(DecodeArgs a)
             const int kk = ok[u] ? key : w_begin;
             const E* kr = kk < nd ? kd + (size_t)kk * DK : kw + (size_t)(kk - nd) * DK;
             const E* vr = kk < nd ? vd + (size_t)kk * DK : vw + (size_t)(kk - nd) * DK;
-            Row8<E>::load(kr, kx[u]);
-            Row8<E>::load(vr, vx[u]);
+            kx[u].load(kr);
+            vx[u].load(vr);
         }
         float s[kDecUnroll];
 #pragma unroll
