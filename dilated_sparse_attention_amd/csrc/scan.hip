@@ -381,12 +381,13 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
             ok[j] = ck[j];
             ov[j] = cv[j];
         }
-        // ordinary (cacheable) stores: the attention reads the states right
-        // after, and part of them is still in the Infinity Cache then
+        // non-temporal stores: measured, they leave the attention that reads
+        // the states next faster than cacheable ones do (the scan itself
+        // runs as fast either way)
         if (cvalid && t0 + i < a.T) {
             const size_t o = rowbase + (size_t)(t0 + i) * a.N;
-            *reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o) = R16::pack(ok);
-            *reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o) = R16::pack(ov);
+            __builtin_nontemporal_store(R16::pack(ok), reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o));
+            __builtin_nontemporal_store(R16::pack(ov), reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o));
         }
         // the last position's states in fp32, for a decode loop to continue from
         if (a.fin && cvalid && t0 + i == a.T - 1) {
@@ -495,8 +496,10 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
 // (two 64-token tiles) of one 64-channel block plus the 64 tokens before
 // them, copied into LDS 16 bytes per lane.  Wave w owns tokens 16w .. 16w+15
 // of the chunk, lane = channel: a forward recurrence from zero over its
-// tokens, the in-tile carry from the waves before it through LDS, then a
-// reverse pass over the previous tile gives each token its suffix
+// tokens, and a reverse one over the same 16 offsets of the previous tile.
+// Through LDS each wave then takes the in-tile carry from the waves before
+// it and the previous tile's suffix from the waves after it, which gives
+// every token its suffix
 // X_j = sum_{s=j+1}^{63} (prod_{r=s+1}^{63} g_r)(1-g_s) x_s, and
 // h_t = H_t + P_t * X_j with H_t, P_t the in-tile state and gate product.
 // The previous tile is re-read once per chunk (1.5x input bytes); two
@@ -515,7 +518,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
     static_assert(NIN % kScanWaves == 0 && NOUT % kScanWaves == 0 && NROW % RPG == 0, "even copies");
     static_assert(kSlideBW == kWave, "one channel per lane");
     extern __shared__ __attribute__((aligned(1024))) char s_tile[];  // [3][NROW][ROWB]: k, v, logits
-    __shared__ float s_map[kScanWaves][3][kSlideBW];
+    __shared__ float s_map[kScanWaves][3][kSlideBW];  // forward segment maps (A, K, V)
+    __shared__ float s_rev[kScanWaves][3][kSlideBW];  // previous-tile segments (Q, Sk, Sv)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -547,25 +551,48 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
     };
 
     // forward: local recurrence over this wave's tokens from a zero state
+    // (h = x + g (h - x))
     const int rw = kSlideHalo + w * TPW;  // LDS row of the wave's first token
     float A = 1.f, K = 0.f, V = 0.f;
     float hk[TPW], hv[TPW], pg[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-        float g, gb;
-        forget_gate(at(2, rw + i), g, gb);
+        const float g = gate(at(2, rw + i));
+        const float xk = at(0, rw + i), xv = at(1, rw + i);
         A *= g;
-        K = fmaf(g, K, gb * at(0, rw + i));
-        V = fmaf(g, V, gb * at(1, rw + i));
+        K = fmaf(g, K - xk, xk);
+        V = fmaf(g, V - xv, xv);
         hk[i] = K; hv[i] = V; pg[i] = A;
+    }
+    // reverse over the same offsets of the previous tile (LDS rows
+    // 64 tl + 16 wt ..): lk / lv[i] = the segment's suffix after offset
+    // 16 wt + i, weighted to the segment's end; (Q, Sk, Sv) = the whole
+    // segment's gate product and suffix
+    const int tl = w / 4, wt = w % 4;
+    const bool has_prev = tb + 64 * tl > 0;
+    const int pr = 64 * tl + TPW * wt;
+    float lk[TPW], lv[TPW];
+    float Q = 1.f, Sk = 0.f, Sv = 0.f;
+#pragma unroll
+    for (int i = TPW - 1; i >= 0; --i) {
+        lk[i] = Sk;
+        lv[i] = Sv;
+        float g, gb;
+        forget_gate(at(2, pr + i), g, gb);
+        const float qg = Q * gb;
+        Sk = fmaf(qg, at(0, pr + i), Sk);
+        Sv = fmaf(qg, at(1, pr + i), Sv);
+        Q *= g;
     }
     s_map[w][0][lane] = A;
     s_map[w][1][lane] = K;
     s_map[w][2][lane] = V;
+    s_rev[w][0][lane] = Q;
+    s_rev[w][1][lane] = Sk;
+    s_rev[w][2][lane] = Sv;
     __syncthreads();
 
     // in-tile carry: the waves of this tile before this one
-    const int tl = w / 4, wt = w % 4;
     float cA = 1.f, cK = 0.f, cV = 0.f;
     for (int ww = 4 * tl; ww < w; ++ww) {
         const float sa = s_map[ww][0][lane];
@@ -573,35 +600,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
         cV = fmaf(sa, cV, s_map[ww][2][lane]);
         cA *= sa;
     }
-
-    // reverse over the previous tile (LDS rows 64 tl .. 64 tl + 63): the
-    // suffix X_j of offset j = 16 wt + i, then h = H + P (carry + A X_j)
-    float Xk = 0.f, Xv = 0.f, Q = 1.f;
-    const bool has_prev = tb + 64 * tl > 0;
-    const int pr = 64 * tl;
-    if (has_prev) {
-        for (int s2 = 63; s2 >= 16 * wt + TPW; --s2) {
-            float g, gb;
-            forget_gate(at(2, pr + s2), g, gb);
-            const float qg = Q * gb;
-            Xk = fmaf(qg, at(0, pr + s2), Xk);
-            Xv = fmaf(qg, at(1, pr + s2), Xv);
-            Q *= g;
-        }
+    // the previous tile's segments after this one: suffix Z and gate product G
+    float G = 1.f, Zk = 0.f, Zv = 0.f;
+    for (int ww = 4 * tl + 3; ww > w; --ww) {
+        Zk = fmaf(s_rev[ww][1][lane], G, Zk);
+        Zv = fmaf(s_rev[ww][2][lane], G, Zv);
+        G *= s_rev[ww][0][lane];
     }
+    // X_j = G * l_j + Z over the window's part in the previous tile, then
+    // h = H + P (carry + A X_j)
 #pragma unroll
-    for (int i = TPW - 1; i >= 0; --i) {
-        hk[i] = fmaf(pg[i], fmaf(cA, Xk, cK), hk[i]);
-        hv[i] = fmaf(pg[i], fmaf(cA, Xv, cV), hv[i]);
-        if (has_prev) {
-            const int s2 = 16 * wt + i;
-            float g, gb;
-            forget_gate(at(2, pr + s2), g, gb);
-            const float qg = Q * gb;
-            Xk = fmaf(qg, at(0, pr + s2), Xk);
-            Xv = fmaf(qg, at(1, pr + s2), Xv);
-            Q *= g;
-        }
+    for (int i = 0; i < TPW; ++i) {
+        const float xk = has_prev ? fmaf(G, lk[i], Zk) : 0.f;
+        const float xv = has_prev ? fmaf(G, lv[i], Zv) : 0.f;
+        hk[i] = fmaf(pg[i], fmaf(cA, xk, cK), hk[i]);
+        hv[i] = fmaf(pg[i], fmaf(cA, xv, cV), hv[i]);
     }
     __syncthreads();  // every wave is done reading the inputs
 
