@@ -106,3 +106,29 @@ def attn_masked(q, ks, vs, kr, vr, D, W, scale):
             p = p / p.sum(axis=1, keepdims=True)
             out[b, :, h] = p @ vals
     return out
+
+
+def chunk_mask(T, D):
+    """Boolean [T, T] mask of the chunk grid: key s is a chunk end
+    (s mod D == D - 1) strictly before t, or t itself."""
+    t = np.arange(T)[:, None]
+    s = np.arange(T)[None, :]
+    return ((s % D == D - 1) & (s < t)) | (s == t)
+
+
+def chunk_attn_masked(q, ks, vs, D, scale):
+    """Chunk-grid attention as one dense masked softmax per (b, h)."""
+    q = np.asarray(q, np.float64)
+    B, T, H, d = q.shape
+    out = np.zeros_like(q)
+    D = np.broadcast_to(np.asarray(D), (H,))
+    for h in range(H):
+        mask = chunk_mask(T, int(D[h]))
+        for b in range(B):
+            z = scale * (q[b, :, h] @ ks[b, :, h].T)
+            z = np.where(mask, z, -np.inf)
+            z = z - z.max(axis=1, keepdims=True)
+            p = np.exp(z)
+            p = p / p.sum(axis=1, keepdims=True)
+            out[b, :, h] = p @ vs[b, :, h]
+    return out

@@ -36,6 +36,12 @@
  *     recurrent states at t, t-D, t-2D, ... (>= 0) and to the raw keys and
  *     values at t, t-1, ..., t-W+1 (>= 0), all in ONE softmax with logits
  *     scale * <q_t, key>.  No de-duplication between the two lists.
+ *   - Chunk grid (the absolute reading, after the RAT page: "RAT:
+ *     Bridging RNN Efficiency and Attention Accuracy via Chunk-based
+ *     Sequence Modeling", Abstract -- the input is split into chunks and
+ *     attention runs across chunks): with chunks of D tokens, query t
+ *     attends to the states that end a chunk before it, at positions
+ *     p = cD - 1 < t (c >= 1), and to its own state at t; no raw window.
  *   - Decode at context length T: the single query is position T-1; its
  *     dilated cache entry i holds position ((T-1) mod D) + i*D for
  *     i = 0 .. ceil(T/D)-1, and ring slots 0 .. min(W,T)-1 are valid.
@@ -356,6 +362,73 @@ int oracle_attn_decode(const double* q, const double* kd, const double* vd, int 
         free(kp);
         free(vp);
         free(z);
+    }
+    return bad ? -4 : 0;
+}
+
+/* Chunk-grid index set of query t [RAT abstract: attention across chunks]:
+ * the chunk-end positions cD - 1 < t in increasing order, then t itself.
+ * Returns the count; pos may be NULL (count only). */
+long oracle_chunk_index_set(int t, int D, int* pos)
+{
+    if (t < 0 || D < 1) return -1;
+    long n = 0;
+    for (int p = D - 1; p < t; p += D) {
+        if (pos) pos[n] = p;
+        ++n;
+    }
+    if (pos) pos[n] = t;
+    return n + 1;
+}
+
+/* Chunk-grid prefill attention for a list of query rows (b, t, h): one
+ * softmax over the chunk-end states before t and the own state at t.
+ * k_state, v_state, q: [B,T,H,d]; out_rows [n, d]. */
+int oracle_chunk_attn_prefill_rows(const double* q, const double* k_state, const double* v_state,
+                                   const int* rows, int n, double* out_rows,
+                                   int B, int T, int H, int d, const int* D, double scale)
+{
+    if (!q || !k_state || !v_state || !rows || !out_rows || !D) return -1;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n < 0) return -2;
+    int max_keys = 0;
+    for (int h = 0; h < H; ++h) {
+        if (D[h] < 1) return -3;
+        int nk = (T - 1) / D[h] + 2;
+        if (nk > max_keys) max_keys = nk;
+    }
+    for (int i = 0; i < n; ++i) {
+        int b = rows[3 * i], t = rows[3 * i + 1], h = rows[3 * i + 2];
+        if (b < 0 || b >= B || t < 0 || t >= T || h < 0 || h >= H) return -2;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        const double** kp = (const double**)malloc(sizeof(double*) * max_keys);
+        const double** vp = (const double**)malloc(sizeof(double*) * max_keys);
+        double* z = (double*)malloc(sizeof(double) * max_keys);
+        int* pos = (int*)malloc(sizeof(int) * max_keys);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!kp || !vp || !z || !pos || !tmp) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int i = 0; i < n; ++i) {
+                int b = rows[3 * i], t = rows[3 * i + 1], h = rows[3 * i + 2];
+                int nk = (int)oracle_chunk_index_set(t, D[h], pos);
+                for (int j = 0; j < nk; ++j) {
+                    kp[j] = k_state + idx4(b, pos[j], h, 0, T, H, d);
+                    vp[j] = v_state + idx4(b, pos[j], h, 0, T, H, d);
+                }
+                softmax_rows(q + idx4(b, t, h, 0, T, H, d), kp, vp, nk, d, scale, z, tmp);
+                for (int c = 0; c < d; ++c) out_rows[(size_t)i * d + c] = tmp[c];
+            }
+        }
+        free(kp);
+        free(vp);
+        free(z);
+        free(pos);
+        free(tmp);
     }
     return bad ? -4 : 0;
 }

@@ -93,6 +93,9 @@ class Oracle:
                                                  i, i, i, i, ip, ip, d]
         lib.oracle_attn_decode.argtypes = [dp, dp, dp, i, dp, dp, i, dp, i, i, i, i, ip, ip, d]
         lib.oracle_count_pairs.argtypes = [i, i, i, lp, lp]
+        lib.oracle_chunk_index_set.argtypes = [i, i, ip]
+        lib.oracle_chunk_index_set.restype = ctypes.c_long
+        lib.oracle_chunk_attn_prefill_rows.argtypes = [dp, dp, dp, ip, i, dp, i, i, i, i, ip, d]
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -162,6 +165,34 @@ class Oracle:
                                                  float(scale)), "oracle_attn_prefill_rows")
         return out
 
+    def chunk_index_set(self, t, D):
+        """Chunk-grid keys of query t: chunk-end positions before t, then t."""
+        n = int(self.lib.oracle_chunk_index_set(int(t), int(D), None))
+        if n < 0:
+            raise ValueError("oracle_chunk_index_set rejected its arguments")
+        pos = np.empty(n, dtype=np.int32)
+        self.lib.oracle_chunk_index_set(int(t), int(D), _iptr(pos))
+        return pos
+
+    def chunk_attn_prefill_rows(self, q, k_state, v_state, rows, D, scale):
+        """Chunk-grid prefill attention for sampled rows [(b, t, h), ...] -> [n, d]."""
+        q, ks, vs = _f64(q), _f64(k_state), _f64(v_state)
+        B, T, H, d = q.shape
+        Da, _ = _heads(D, 0, H)
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+        out = np.empty((r.shape[0], d), dtype=np.float64)
+        _check(self.lib.oracle_chunk_attn_prefill_rows(_ptr(q), _ptr(ks), _ptr(vs), _iptr(r),
+                                                       r.shape[0], _ptr(out), B, T, H, d,
+                                                       _iptr(Da), float(scale)),
+               "oracle_chunk_attn_prefill_rows")
+        return out
+
+    def chunk_attn_prefill(self, q, k_state, v_state, D, scale):
+        """Chunk-grid prefill attention, every row -> [B,T,H,d]."""
+        B, T, H, d = q.shape
+        rows = np.array([(b, t, h) for b in range(B) for t in range(T) for h in range(H)], np.int32)
+        return self.chunk_attn_prefill_rows(q, k_state, v_state, rows, D, scale).reshape(B, T, H, d)
+
     def attn_decode(self, q, kd, vd, kw, vw, T, D, W, scale):
         """Decode output [B,H,d] at context length T."""
         q, kd, vd = _f64(q), _f64(kd), _f64(vd)
@@ -217,3 +248,15 @@ def attn_prefill_rows(q, k_state, v_state, k_raw, v_raw, rows, D, W, scale):
 
 def attn_decode(q, kd, vd, kw, vw, T, D, W, scale):
     return default().attn_decode(q, kd, vd, kw, vw, T, D, W, scale)
+
+
+def chunk_index_set(t, D):
+    return default().chunk_index_set(t, D)
+
+
+def chunk_attn_prefill_rows(q, k_state, v_state, rows, D, scale):
+    return default().chunk_attn_prefill_rows(q, k_state, v_state, rows, D, scale)
+
+
+def chunk_attn_prefill(q, k_state, v_state, D, scale):
+    return default().chunk_attn_prefill(q, k_state, v_state, D, scale)

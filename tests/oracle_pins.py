@@ -346,4 +346,64 @@ def pin_decode_ring_order(o):
     np.testing.assert_array_equal(got, base)
 
 
+# ---------------------------------------------------------------- chunk grid
+# The absolute reading of the dilated pattern, after the RAT page ("RAT:
+# Bridging RNN Efficiency and Attention Accuracy via Chunk-based Sequence
+# Modeling", Abstract: chunks, attention across chunks): query t sees the
+# states ending a chunk of D tokens before t, and its own state.
+def pin_chunk_index_sets_by_hand(o):
+    assert o.chunk_index_set(9, 4).tolist() == [3, 7, 9]
+    assert o.chunk_index_set(3, 4).tolist() == [3]       # its own state ends the chunk
+    assert o.chunk_index_set(4, 4).tolist() == [3, 4]
+    assert o.chunk_index_set(0, 1).tolist() == [0]
+    assert o.chunk_index_set(5, 1).tolist() == [0, 1, 2, 3, 4, 5]
+    for D in (1, 2, 3, 16, 64):
+        for t in range(0, 200, 7):
+            got = o.chunk_index_set(t, D).tolist()
+            want = sorted({p for p in range(t) if p % D == D - 1} | {t})
+            assert got == want, (t, D)
+            assert len(got) == t // D + 1  # as many keys as the relative reading
+
+
+def pin_chunk_attn_dense_is_sdpa(o):
+    """D = 1: every earlier position ends a chunk -- dense causal attention."""
+    q, ks, vs, _ = _inputs(21, 2, 41, 2, 8)
+    scale = 1 / math.sqrt(8)
+    out = o.chunk_attn_prefill(q, ks, vs, 1, scale)
+    for b in range(2):
+        for h in range(2):
+            want = _sdpa_causal(q[b, :, h], ks[b, :, h], vs[b, :, h], scale)
+            np.testing.assert_allclose(out[b, :, h], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_chunk_attn_chunk_ends(o):
+    """Queries that end a chunk (t mod D = D - 1) see exactly the chunk ends
+    up to t: causal attention over q[D-1::D], states[D-1::D]."""
+    q, ks, vs, _ = _inputs(22, 1, 61, 2, 8)
+    for D in (2, 5, 16):
+        out = o.chunk_attn_prefill(q, ks, vs, D, 0.3)
+        for h in range(2):
+            want = _sdpa_causal(q[0, D - 1::D, h], ks[0, D - 1::D, h], vs[0, D - 1::D, h], 0.3)
+            np.testing.assert_allclose(out[0, D - 1::D, h], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_chunk_attn_own_state_only(o):
+    """Before the first chunk end (t < D) a query has one key, its own
+    state: the output IS that state's value."""
+    q, ks, vs, _ = _inputs(23, 2, 30, 2, 8)
+    for D in (8, 30, 1000):
+        out = o.chunk_attn_prefill(q, ks, vs, D, 0.5)
+        n = min(D, 30)
+        assert np.array_equal(out[:, :n], vs[:, :n])
+
+
+def pin_chunk_attn_masked_matrix(o):
+    """Brute force on tiny T: one dense masked softmax per head (mixed D)."""
+    q, ks, vs, _ = _inputs(24, 2, 67, 4, 8)
+    D = [1, 3, 8, 20]
+    out = o.chunk_attn_prefill(q, ks, vs, D, 0.35)
+    want = brute.chunk_attn_masked(q, ks, vs, D, 0.35)
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,9 @@ MUTANTS = {
     "decode_count_floor": ("int nd = (T - 1) / D[h] + 1;\n                    int nw",
                            "int nd = T / D[h];\n                    int nw"),
     "decode_ring_short": ("for (int j = 0; j < nw; ++j) {", "for (int j = 0; j + 1 < nw; ++j) {"),
+    "chunk_end_off_by_one": ("for (int p = D - 1; p < t; p += D) {", "for (int p = D; p < t; p += D) {"),
+    "chunk_end_not_strict": ("for (int p = D - 1; p < t; p += D) {", "for (int p = D - 1; p <= t; p += D) {"),
+    "chunk_own_state_dropped": ("    if (pos) pos[n] = t;\n    return n + 1;", "    return n;"),
     "count_window_short": ("for (int w = 0; w < W && t - w >= 0; ++w) {\n        if (loc)",
                            "for (int w = 1; w < W && t - w >= 0; ++w) {\n        if (loc)"),
 }
