@@ -15,7 +15,9 @@ back-to-back launches of that one kernel.  The JSON line also
 carries the roofline of the dominant kernel, the oracle timed on the host
 cores on a bounded sample (``cpu_baseline``) and, under ``extra``, the other
 workloads: long prefill with a window (both recurrence readings), the 7.6B
-hybrid prefill and the 2.6B decode at D = 64 and D = 16.
+hybrid prefill, the 2.6B decode at D = 64 and D = 16, the chunk-grid
+attention on the 1.5B-scale prefill shape and the decode-loop step (the
+recurrence update fused with decode attention) on the 2.6B decode shape.
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 # kernel names as the profiler lists them (bf16, d = 128, full recurrence)
 SCAN_KERNEL = "rat::scan_full_kernel<unsigned short>"
-ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false>"
+ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false, false>"
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
@@ -190,6 +192,98 @@ def run_decode(torch, rat, w, steps, warmup, nsets=3):
     return ms, nbytes
 
 
+def chunk_units(w):
+    """Algorithmic bytes / FLOPs of chunk-grid attention: q, every own state
+    (k and v) and the output once, the chunk-end states once; query t scores
+    its floor(t / D) chunk ends and its own state."""
+    E = w.B * w.T * w.H * w.d
+    s = 2
+    ends = sum(w.T // Dh for Dh in w.D) * w.B * w.d  # chunk-end rows (p = cD - 1 <= T - 1), all heads
+    nbytes = 4 * E * s + 2 * ends * s
+    pairs = sum(sum(t // Dh + 1 for t in range(w.T)) for Dh in w.D)
+    return nbytes, 4 * w.d * pairs * w.B
+
+
+def run_chunk(torch, rat, w, steps, warmup, nsets=3):
+    """Chunk-grid attention over the recurrence states of the prefill
+    workload `w` (the states come from the scan kernel, outside the timed
+    region); back-to-back launches over rotating sets."""
+    from dilated_sparse_attention_amd import inputs
+
+    sets = []
+    for i in range(nsets):
+        x = inputs.make_prefill(w, seed=i, device="cuda")
+        ks, vs = rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=w.modes[0])
+        sets.append((x["q"], ks, vs, torch.empty_like(x["q"])))
+        del x
+    D = list(w.D)
+    call = lambda i: rat.chunk_attn_prefill(*sets[i % nsets][:3], D=D, out=sets[i % nsets][3])  # noqa: E731
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del sets
+    torch.cuda.empty_cache()
+    return ms
+
+
+def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
+    """One decode-loop step (recurrence update, history and ring writes,
+    decode attention) at context length w.T for the whole batch: the state
+    history holds every position (n_cap = D ceil(T / D) rows per head)."""
+    from dilated_sparse_attention_amd import inputs
+
+    D, W = list(w.D), list(w.W)
+    n_cap = max(Dh * ((w.T + Dh - 1) // Dh) for Dh in D)
+    sets = []
+    for i in range(nsets):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(100 + i)
+        mk = lambda *shape: torch.randn(shape, generator=g, device="cuda").to(w.dtype)  # noqa: E731
+        x = {n: mk(w.B, w.H, w.d) for n in ("q", "k", "v", "gate")}
+        x["state"] = torch.randn((w.B, w.H, 2, w.d), generator=g, device="cuda")
+        x["kc"], x["vc"] = mk(w.B, w.H, n_cap, w.d), mk(w.B, w.H, n_cap, w.d)
+        x["kw"], x["vw"] = mk(w.B, w.H, w.w_cap, w.d), mk(w.B, w.H, w.w_cap, w.d)
+        x["out"] = torch.empty_like(x["q"])
+        sets.append(x)
+    ws_bytes = rat.decode_workspace_bytes(w.B, w.H, w.d, w.T, D, W)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        x = sets[i % nsets]
+        rat.decode_step(x["q"], x["k"], x["v"], x["gate"], x["state"], x["kc"], x["vc"], x["kw"], x["vw"], w.T,
+                        D, W, out=x["out"], workspace=ws if ws_bytes else None)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # bytes: q, k, v, gate read; state read and written (fp32); the state
+    # row and the raw token written; the residue's history rows and the ring
+    # read; the output written
+    s = 2
+    E = w.B * w.H * w.d
+    rows = sum((w.T - 1) // Dh + 1 + min(Wh, w.T) for Dh, Wh in zip(D, W)) * w.B * w.d
+    nbytes = 4 * E * s + 2 * (2 * E * 4) + 4 * E * s + 2 * rows * s + E * s
+    del sets
+    torch.cuda.empty_cache()
+    return ms, nbytes
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, min_s=12.0, max_reps=100):
     """The fp64 oracle on the host cores, timed on the headline workload
@@ -286,6 +380,29 @@ def main():
                               "GBps": dbytes / (dms / 1e3) / 1e9,
                               "hbm_frac": dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS,
                               "config": dw.describe()}
+
+        cw = inputs.PREFILL_1P5B
+        key = "chunk_grid_" + cw.name
+        if args.only is None or args.only == key:
+            progress("chunk grid", cw.name)
+            cms = run_chunk(torch, rat, cw, max(5, args.steps), 3)
+            cb, cf = chunk_units(cw)
+            extra[key] = {"attn_ms": cms, "attn_GBps": cb / (cms / 1e3) / 1e9,
+                          "hbm_frac": cb / (cms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "attn_TFLOPs": cf / (cms / 1e3) / 1e12,
+                          "mfma_frac": cf / (cms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "algorithmic_bytes": cb, "algorithmic_flops": cf,
+                          "config": dict(cw.describe(), attention="chunk grid: chunk-end states + own state")}
+        sw = inputs.DECODE_2P6B_D64
+        key = "decode_step_" + sw.name
+        if args.only is None or args.only == key:
+            progress("decode step", sw.name)
+            sms, sbytes = run_decode_step(torch, rat, sw, max(5, args.steps), 3)
+            extra[key] = {"decode_tokens_per_s": sw.B / (sms / 1e3), "step_ms": sms,
+                          "GBps": sbytes / (sms / 1e3) / 1e9, "hbm_frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes": sbytes,
+                          "config": dict(sw.describe(), history_rows_per_head=max(
+                              Dh * ((sw.T + Dh - 1) // Dh) for Dh in sw.D))}
 
     if ms is None:  # a profiling run of one extra workload
         print(json.dumps({"extra": extra}))

@@ -44,6 +44,13 @@ bool size_ok(int64_t a, int64_t b, int64_t c, int64_t d)
     return n2 * d < kMaxElems;
 }
 
+// Decode caches: the kernels address them with 64-bit offsets, so only one
+// head's rows (cap x d) and the B x H x d query rows need 32-bit indices.
+bool caches_ok(int B, int H, int d, int nd_cap, int w_cap)
+{
+    return size_ok(B, H, d, 1) && (int64_t)nd_cap * d < kMaxElems && (int64_t)std::max(w_cap, 1) * d < kMaxElems;
+}
+
 struct ScanPlan {
     int chunk, nblk, nseq, nchunk, nwg;
     size_t agg_off, incl_off, bytes;
@@ -189,43 +196,20 @@ size_t rat_attn_prefill_workspace_bytes(int B, int T, int H, int d, const int* D
     return (size_t)B * T * H * 2 * sizeof(float);
 }
 
-int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
-                             const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
-                             float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+namespace {
+
+// bf16 prefill attention, relative dilation (chunk = 0) or chunk grid
+// (chunk = 1: every head's W is 1 over the states, passed as k_raw / v_raw).
+// Heads with W > 0 first get their raw-key band (one workgroup per 256
+// contiguous queries), which leaves a partial softmax state per query in
+// `out` and the workspace; then every head runs the persistent dilated
+// kernel (items = (b, h, r, 256-row chunk)), which continues from those
+// states.  Heads are grouped into (D, W) classes; classes with the longest
+// single items come first, each class's levels most expensive first.
+int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, const void* k_raw,
+                      const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
+                      bool any_w, float scale, int chunk, void* workspace, size_t workspace_bytes, hipStream_t s)
 {
-    if (!q || !k_state || !v_state || !out) return RAT_ERR_NULL;
-    if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
-    bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
-    if (hc != RAT_OK) return hc;
-    if (any_w && (!k_raw || !v_raw)) return RAT_ERR_NULL;
-    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return RAT_ERR_SHAPE;
-    const void* ins[5] = {q, k_state, v_state, k_raw, v_raw};
-    for (const void* in : ins)
-        if (in && in == out) return RAT_ERR_ALIAS;
-    for (const void* p : ins)
-        if (p && !aligned16(p)) return RAT_ERR_ALIGN;
-    if (!aligned16(out)) return RAT_ERR_ALIGN;
-    hipStream_t s = (hipStream_t)stream;
-
-    if (dtype == RAT_DTYPE_F32) {
-        AttnF32Args a;
-        memset(&a, 0, sizeof(a));
-        a.q = (const float*)q; a.ks = (const float*)k_state; a.vs = (const float*)v_state;
-        a.kr = (const float*)k_raw; a.vr = (const float*)v_raw; a.out = (float*)out;
-        a.B = B; a.T = T; a.H = H; a.d = d; a.scale = scale;
-        for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
-        return hip_status(launch_attn_prefill_f32(a, s));
-    }
-
-    // Heads with W > 0 first get their raw-key band (one workgroup per 256
-    // contiguous queries), which leaves a partial softmax state per query
-    // in `out` and the workspace; then every head runs the persistent
-    // dilated kernel (items = (b, h, r, 256-row chunk)), which continues
-    // from those states.  Heads are grouped into (D, W) classes; classes
-    // with the longest single items come first, each class's levels most
-    // expensive first.
     if (any_w) {
         const size_t need = (size_t)B * T * H * 2 * sizeof(float);
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RAT_ERR_WORKSPACE;
@@ -254,6 +238,7 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
     dil.B = B; dil.T = T; dil.H = H;
     dil.scale_log2 = scale * 1.4426950408889634f;
     band = dil;
+    dil.chunk = chunk;
     int64_t items = 0, blocks = 0;
     int hoff = 0;
     for (const Cls& c : cls) {
@@ -284,6 +269,77 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
     }
     const int grid = std::min(dil.nblocks, device_cu_count());
     return hip_status(launch_attn_dilated_bf16(dil, d, grid, s));
+}
+
+}  // namespace
+
+int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
+                             const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
+                             float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k_state || !v_state || !out) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!k_raw || !v_raw)) return RAT_ERR_NULL;
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[5] = {q, k_state, v_state, k_raw, v_raw};
+    for (const void* in : ins)
+        if (in && in == out) return RAT_ERR_ALIAS;
+    for (const void* p : ins)
+        if (p && !aligned16(p)) return RAT_ERR_ALIGN;
+    if (!aligned16(out)) return RAT_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (dtype == RAT_DTYPE_F32) {
+        AttnF32Args a;
+        memset(&a, 0, sizeof(a));
+        a.q = (const float*)q; a.ks = (const float*)k_state; a.vs = (const float*)v_state;
+        a.kr = (const float*)k_raw; a.vr = (const float*)v_raw; a.out = (float*)out;
+        a.B = B; a.T = T; a.H = H; a.d = d; a.scale = scale;
+        for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+        return hip_status(launch_attn_prefill_f32(a, s));
+    }
+
+    return attn_prefill_bf16(q, k_state, v_state, k_raw, v_raw, out, B, T, H, d, D, W, any_w, scale, 0, workspace,
+                             workspace_bytes, s);
+}
+
+int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out, int B, int T, int H,
+                           int d, const int* D, float scale, rat_dtype dtype, void* stream)
+{
+    if (!q || !k_state || !v_state || !out || !D) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
+    if (H > kAttnMaxHeads) return RAT_ERR_UNSUPPORTED;
+    int W0[kAttnMaxHeads];
+    for (int h = 0; h < H; ++h) {
+        if (D[h] < 1) return RAT_ERR_SHAPE;
+        W0[h] = 0;
+    }
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[3] = {q, k_state, v_state};
+    for (const void* in : ins)
+        if (in == out) return RAT_ERR_ALIAS;
+    for (const void* p : ins)
+        if (!aligned16(p)) return RAT_ERR_ALIGN;
+    if (!aligned16(out)) return RAT_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == RAT_DTYPE_F32) {
+        AttnF32Args a;
+        memset(&a, 0, sizeof(a));
+        a.q = (const float*)q; a.ks = (const float*)k_state; a.vs = (const float*)v_state;
+        a.out = (float*)out;
+        a.B = B; a.T = T; a.H = H; a.d = d; a.scale = scale; a.chunk = 1;
+        for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = 0; }
+        return hip_status(launch_attn_prefill_f32(a, s));
+    }
+    // dilated items whose keys are the chunk ends (residue D - 1) strictly
+    // before each query, their softmax started from the query's own state
+    return attn_prefill_bf16(q, k_state, v_state, nullptr, nullptr, out, B, T, H, d, D, W0, false, scale, 1,
+                             nullptr, 0, s);
 }
 
 namespace {
@@ -324,7 +380,7 @@ int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int n
         if ((T - 1) / D[h] + 1 > nd_cap) return RAT_ERR_SHAPE;
         if (std::min(W[h], T) > w_cap) return RAT_ERR_SHAPE;
     }
-    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, H, nd_cap, d) || !size_ok(B, H, std::max(w_cap, 1), d))
+    if (!dtype_ok(dtype) || !d_ok(d) || !caches_ok(B, H, d, nd_cap, w_cap))
         return RAT_ERR_UNSUPPORTED;
     if (!(scale == scale)) return RAT_ERR_SHAPE;
     const void* ins[5] = {q, kd, vd, kw, vw};
@@ -363,7 +419,7 @@ int rat_decode_step(const void* q, const void* k_new, const void* v_new, const v
         if (p / D[h] >= n_cap / D[h]) return RAT_ERR_SHAPE;  // history rows of the residue
         if (W[h] > w_cap) return RAT_ERR_SHAPE;               // ring slot p mod W
     }
-    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, H, n_cap, d) || !size_ok(B, H, std::max(w_cap, 1), d))
+    if (!dtype_ok(dtype) || !d_ok(d) || !caches_ok(B, H, d, n_cap, w_cap))
         return RAT_ERR_UNSUPPORTED;
     if (!(scale == scale)) return RAT_ERR_SHAPE;
     const void* ins[5] = {q, k_new, v_new, gate_new, state};

@@ -145,6 +145,38 @@ struct Frag {
         }
     }
 
+    // Chunk grid: the softmax starts from the query's own state.  krow /
+    // vrow: the block's first row in the K / V half of an own-state slot
+    // (query i's own key and value at row i of the block); koff0: the
+    // lane's K-fragment offset of k-step 0.  Score in the log2 domain.
+    __device__ __forceinline__ void init_own_lds(const lds_char* krow, int koff0, const lds_char* vrow, float c)
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int g = lane >> 4, i = lane & 15;
+        float dot = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < Geo<DK>::KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (koff0 ^ (ks << 6)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{q[ks][2 * e], q[ks][2 * e + 1]},
+                                                      bf16x2{kf[2 * e], kf[2 * e + 1]}, dot, false);
+        }
+        // the four lane groups hold the dims of one query: sum them
+        auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+        dot = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+        dot = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+        m = dot * c;
+        l = g == 0 ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < Geo<DK>::DB; ++db) {
+            const int dim = 16 * db + 4 * g;
+            const u32x2 o = *reinterpret_cast<const u32x2*>(vrow + swz<DK>(i, dim >> 3) + (dim & 7) * 2);
+            acc[db] = floatx4{bf16_lo(o[0]), bf16_hi(o[0]), bf16_lo(o[1]), bf16_hi(o[1])};
+        }
+    }
+
     __device__ __forceinline__ float total_l() const
     {
         float t = l + __shfl_xor(l, 16);
@@ -187,6 +219,8 @@ constexpr int kRingA = 4;    // LDS ring depth
 struct ItemA {
     int b, h, D, W, r, R0, R1;
     int kbeg;  // first key (0, or the start of a band item's key range)
+    int kres;  // residue of the key rows: r, or D - 1 on the chunk grid (0 for a band item)
+    int nkey;  // key rows the item's queries can see: R1, or R1 - 1 on the chunk grid
     bool valid;
 };
 
@@ -194,7 +228,7 @@ struct ItemA {
 // 256-row chunk index) most expensive first, then head fastest, residue,
 // batch -- consecutive items read the same positions of different heads,
 // i.e. whole contiguous token rows.
-template <bool BAND>
+template <bool BAND, bool CHUNK>
 __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 {
     ItemA it;
@@ -215,6 +249,8 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
         it.R0 = (local / k.per_level) * kAttnRowsA;
         it.R1 = min(it.R0 + kAttnRowsA, a.T);
         it.kbeg = max(0, it.R0 - k.W + 1) & ~(kTileA - 1);
+        it.kres = 0;
+        it.nkey = it.R1;
         it.valid = it.R0 < a.T;
         return it;
     }
@@ -229,6 +265,10 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
     it.R0 = level * kAttnRowsA;
     it.R1 = min(it.R0 + kAttnRowsA, M);
     it.kbeg = 0;
+    // chunk grid: query row i (position r + iD) sees the chunk ends
+    // jD + D - 1 with j < i, all of which exist
+    it.kres = CHUNK ? k.D - 1 : it.r;
+    it.nkey = CHUNK ? it.R1 - 1 : it.R1;
     it.valid = it.R0 < M;
     return it;
 }
@@ -239,10 +279,11 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 // The DMA issue cursor and the compute cursor are two copies.
 constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
 
-template <bool BAND>
+template <bool BAND, bool CHUNK>
 struct CursorA {
-    int round, t, nq, no, ntile;
+    int round, t, nq, no, nown, ntile;
     int rowidx;   // (b T + r) H + h: first row of the item in units of head rows
+    int krowidx;  // the same for its key rows (residue kres)
     int dstride;  // min(D, T) H: head rows between consecutive rows of the item
     ItemA it;
 
@@ -255,13 +296,16 @@ struct CursorA {
     __device__ __forceinline__ void seek(const AttnArgs& a, int rnd)
     {
         for (round = rnd; round * (int)gridDim.x < a.nblocks; ++round) {
-            it = decode_item_a<BAND>(a, item_of(round));
+            it = decode_item_a<BAND, CHUNK>(a, item_of(round));
             if (it.valid) {
                 t = 0;
                 nq = (it.R1 - it.R0 + kSlotRows - 1) / kSlotRows;
                 no = (!BAND && it.W > 0) ? nq : 0;
-                ntile = (it.R1 - it.kbeg + kTileA - 1) / kTileA;
+                // chunk grid: the item's own states, 64 query rows per step
+                nown = CHUNK ? (it.R1 - it.R0 + kTileA - 1) / kTileA : 0;
+                ntile = max(0, (CHUNK ? it.nkey : it.R1) - it.kbeg + kTileA - 1) / kTileA;
                 rowidx = (it.b * a.T + it.r) * a.H + it.h;
+                krowidx = CHUNK ? (it.b * a.T + it.kres) * a.H + it.h : rowidx;
                 // a residue of D >= T holds one row: min(D, T) keeps byte
                 // strides below 2^32 without changing any address
                 dstride = min(it.D, a.T) * a.H;
@@ -272,7 +316,7 @@ struct CursorA {
     }
     __device__ __forceinline__ void advance(const AttnArgs& a)
     {
-        if (++t == nq + no + ntile) seek(a, round + 1);
+        if (++t == nq + no + (CHUNK ? nown : 0) + ntile) seek(a, round + 1);
     }
 };
 
@@ -325,8 +369,8 @@ struct DmaLane {
 // PER_WAVE row copies of RPI rows each; partial-output steps add one copy
 // of their (m, l) words into `side` on waves 0-3).  Rows past the item's
 // last row R1 - 1 are clamped to it.
-template <int DK, int NW, bool BAND>
-__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND>& c, uint64_t src_q,
+template <int DK, int NW, bool BAND, bool CHUNK>
+__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK>& c, uint64_t src_q,
                                              uint64_t src_out, uint64_t src_kv, const DmaLane<DK>& dl, uint32_t buf,
                                              uint32_t side)
 {
@@ -336,21 +380,27 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BA
     static_assert(PER_WAVE * G::RPI <= kTileA && kTileA % (PER_WAVE * G::RPI) == 0, "a wave copies K or V rows only");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
-    const int kt = c.t - c.nq - c.no;  // key tile index, < 0 for query / partial steps
+    const int ko = c.t - c.nq - c.no;  // own-state step, then key tile; < 0 for query / partial steps
+    const bool own = CHUNK && ko >= 0 && ko < c.nown;
+    const int kt = CHUNK && ko >= 0 ? ko - c.nown : ko;  // key tile index (< 0 also for own-state steps)
     // first row of the wave's share of the slot, and the tensor it comes from
     int row0;
     uint64_t tsrc;
-    if (kt < 0) {  // query rows, or partial outputs, R0 + 128 s + 16 PER_WAVE wv ...
+    if (ko < 0) {  // query rows, or partial outputs, R0 + 128 s + 16 PER_WAVE wv ...
         const int s = c.t < c.nq ? c.t : c.t - c.nq;
         row0 = c.it.R0 + s * kSlotRows + wv * PER_WAVE * G::RPI;
         tsrc = c.t < c.nq ? src_q : src_out;
+    } else if (own) {  // K rows (waves 0 .. NW/2-1) or V rows of the own states, R0 + 64 ko ...
+        row0 = c.it.R0 + ko * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
+        tsrc = src_kv;
     } else {       // K rows (waves 0 .. NW/2-1) or V rows of key tile kt
         row0 = c.it.kbeg + kt * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
         tsrc = src_kv;
     }
-    const uint32_t item_el = (uint32_t)c.rowidx * DK;
+    const bool keys = CHUNK && ko >= 0 && !own;  // a chunk-grid key tile: rows of residue kres
+    const uint32_t item_el = (uint32_t)(keys ? c.krowidx : c.rowidx) * DK;
     const uint32_t dp2 = (uint32_t)c.dstride * (2 * DK);  // bytes between rows r and r + 1 of the item
-    const int last = c.it.R1 - 1;
+    const int last = (CHUNK && ko >= 0 && !own ? c.it.nkey : c.it.R1) - 1;
     const uint32_t slot = buf + wv * PER_WAVE * 1024;  // LDS byte address of the wave's first copy
     if (row0 + PER_WAVE * G::RPI - 1 <= last) {
         // every row of the wave's share exists: copy j starts RPI rows after
@@ -379,7 +429,7 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BA
             dma16_s(base, voff, slot + j * 1024);
         }
     }
-    if (kt < 0 && c.t >= c.nq && wv < 4) {
+    if (ko < 0 && c.t >= c.nq && wv < 4) {
         // (m, l) of the slot's 128 rows: 64 words per wave on waves 0-3, lane l -> word l
         const int w = wv * kWave + lane;
         const int row = min(c.it.R0 + (c.t - c.nq) * kSlotRows + (w >> 1), c.it.R1 - 1);
@@ -510,7 +560,9 @@ __device__ __forceinline__ int row_block(int wv, int j)
     return j == 0 ? wv : j == 1 ? 15 - wv : j == 2 ? 7 - wv : 8 + wv;
 }
 
-template <int DK, int NW, int RING, bool BAND>
+// CHUNK: the chunk grid (keys of residue D - 1 strictly before the query,
+// the softmax started from the query's own state)
+template <int DK, int NW, int RING, bool BAND, bool CHUNK>
 __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
@@ -528,13 +580,15 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int i = lane & 15;
     const int pitch = a.H * DK;
+    // keys strictly before the query (chunk grid) or up to it
+    constexpr int sh = CHUNK ? 1 : 0;
 
     LaneOffsets<DK> off;
     off.init();
     DmaLane<DK> dl;
     dl.init();
     const DmaSrc dsrc = dma_sources<NW, BAND>(a, wv);
-    CursorA<BAND> issue, comp;
+    CursorA<BAND, CHUNK> issue, comp;
     issue.seek(a, 0);
     comp = issue;
     // ring steps issued and consumed; step n lives in slot n mod RING (a
@@ -545,7 +599,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     const uint32_t side_lds = smem_lds + (uint32_t)(side - smem);
     auto issue_next = [&]() {
         const int sl = issued % RING;
-        issue_step_a<DK, NW, BAND>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
+        issue_step_a<DK, NW, BAND, CHUNK>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
                                    side_lds + sl * 1024);
         ++issued;
         issue.advance(a);
@@ -606,6 +660,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
                 const int r = 16 * row_block<NB>(wv, j);
                 if (r / kSlotRows == s)
                     f[j].init_partial_lds(ot + (r % kSlotRows) * G::ROWB, ml + (r % kSlotRows) * 2, rs[j] + i < it.R1);
+            }
+            consume();
+        }
+        // chunk grid: each query's softmax starts from its own state (64
+        // query rows per ring step)
+        for (int u = 0; CHUNK && u < comp.nown; ++u) {
+            wait_tile(0);
+            const lds_char* sl = smem + (consumed % RING) * TILE_BYTES;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int r = 16 * row_block<NB>(wv, j);
+                if (r / kTileA == u)
+                    f[j].init_own_lds(sl + (r % kTileA) * G::ROWB, off.k0, sl + (kTileA + r % kTileA) * G::ROWB,
+                                      a.scale_log2);
             }
             consume();
         }
@@ -695,7 +763,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             bool skip = true;
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                skip &= !(has[j] && k0 <= rs[j] + 15 && (!BAND || k0 + kTileA - 1 >= rs[j] - it.W + 1));
+                skip &= !(has[j] && k0 <= rs[j] + 15 - sh && (!BAND || k0 + kTileA - 1 >= rs[j] - it.W + 1));
             if (!have_scores) {
                 wait_tile(0);
                 if (!skip) qk(all, consumed % RING, sc);
@@ -718,9 +786,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
                         else
                             softmax64<DK, true>(f[j], sc[j], rs[j] + i, rs[j] + i - it.W + 1, k0, a.scale_log2, pb[j]);
                     }
-                } else if (has[j] && k0 <= rs[j] + 15) {
-                    if (k0 + kTileA - 1 <= rs[j]) softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
-                    else softmax64<DK, true>(f[j], sc[j], rs[j] + i, 0, k0, a.scale_log2, pb[j]);
+                } else if (has[j] && k0 <= rs[j] + 15 - sh) {
+                    // key row j is visible to query row i when j <= i - sh
+                    if (k0 + kTileA - 1 <= rs[j] - sh) softmax64<DK, false>(f[j], sc[j], 0, 0, 0, a.scale_log2, pb[j]);
+                    else softmax64<DK, true>(f[j], sc[j], rs[j] + i - sh, 0, k0, a.scale_log2, pb[j]);
                 }
             }
             pv(all, consumed % RING, pb);
@@ -767,7 +836,7 @@ static void set_lds(K kernel, size_t lds, bool& done)
 #endif
 constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated kernel
 
-template <bool BAND>
+template <bool BAND, bool CHUNK>
 static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, hipStream_t stream)
 {
     static bool s[2][2] = {{false, false}, {false, false}};
@@ -775,35 +844,42 @@ static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, 
     if (ring5) {  // deeper prefetch: five ring slots (no side buffers)
         const size_t lds = attn_lds_bytes_a5(d);
         if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND>, lds, s[0][0]);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK>, lds, s[0][0]);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK>), dim3(grid), block, lds, stream, a);
         } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND>, lds, s[0][1]);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK>, lds, s[0][1]);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK>), dim3(grid), block, lds, stream, a);
         }
         return hipGetLastError();
     }
-    const size_t lds = attn_lds_bytes_a(d);
-    if (d == 128) {
-        set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND>, lds, s[1][0]);
-        hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND>), dim3(grid), block, lds, stream, a);
+    if constexpr (CHUNK) {
+        return hipErrorInvalidValue;  // the chunk grid has no windowed classes
     } else {
-        set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND>, lds, s[1][1]);
-        hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND>), dim3(grid), block, lds, stream, a);
+        const size_t lds = attn_lds_bytes_a(d);
+        if (d == 128) {
+            set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false>, lds, s[1][0]);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false>), dim3(grid), block, lds,
+                               stream, a);
+        } else {
+            set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false>, lds, s[1][1]);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false>), dim3(grid), block, lds,
+                               stream, a);
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
     bool windowed = false;
     for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
-    return launch_path_a<false>(a, d, grid, !windowed, stream);
+    if (a.chunk) return launch_path_a<false, true>(a, d, grid, true, stream);  // no windowed classes
+    return launch_path_a<false, false>(a, d, grid, !windowed, stream);
 }
 
 hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
-    return launch_path_a<true>(a, d, grid, true, stream);
+    return launch_path_a<true, false>(a, d, grid, true, stream);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -835,8 +911,13 @@ __global__ __launch_bounds__(kWave) void attn_prefill_f32_kernel(AttnF32Args a)
         l = l * al + p;
         m = mn;
     };
-    for (int s = t; s >= 0; s -= D) visit(a.ks, a.vs, s);
-    for (int w = 0; w < W && t - w >= 0; ++w) visit(a.kr, a.vr, t - w);
+    if (a.chunk) {  // chunk-end states before t, then the own state
+        for (int s = D - 1; s < t; s += D) visit(a.ks, a.vs, s);
+        visit(a.ks, a.vs, t);
+    } else {
+        for (int s = t; s >= 0; s -= D) visit(a.ks, a.vs, s);
+        for (int w = 0; w < W && t - w >= 0; ++w) visit(a.kr, a.vr, t - w);
+    }
     if (lane < d) a.out[base + t * pitch + lane] = o0 / l;
     if (lane + kWave < d) a.out[base + t * pitch + lane + kWave] = o1 / l;
 }

@@ -82,6 +82,7 @@ struct AttnArgs {
     float* ml;         // [B][T][H][2] partial (m, l) of the band pass (heads with W > 0)
     int B, T, H;
     float scale_log2;  // softmax scale * log2(e)
+    int chunk;         // 1: chunk grid -- keys are the chunk-end states (residue D-1), strictly before the query
     int nclass;
     int nblocks;
     AttnClass cls[kAttnMaxClasses];
@@ -104,7 +105,7 @@ struct AttnF32Args {
     float* out;
     int B, T, H, d;
     float scale;
-    const int* dummy;
+    int chunk;  // 1: chunk grid (chunk-end states before t, then the own state)
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
 };

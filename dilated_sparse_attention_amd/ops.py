@@ -26,6 +26,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 
 # every symbol include/rat.h declares
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
+           "rat_chunk_attn_prefill",
            "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_status_string",
            "rat_last_hip_error")
 
@@ -62,6 +63,8 @@ def load_library(path: str = LIBRARY):
     lib.rat_attn_prefill_workspace_bytes.restype = sz
     lib.rat_dilated_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
     lib.rat_dilated_attn_prefill.restype = i
+    lib.rat_chunk_attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, ip, f, i, vp]
+    lib.rat_chunk_attn_prefill.restype = i
     lib.rat_decode_workspace_bytes.argtypes = [i, i, i, i, ip, ip]
     lib.rat_decode_workspace_bytes.restype = sz
     lib.rat_dilated_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
@@ -194,6 +197,22 @@ def dilated_attn_prefill(q, k_state, v_state, k_raw=None, v_raw=None, D=1, W=0, 
                                       _ptr(out), B, T, H, d, Dh, Wh, scale, _DTYPES[q.dtype], _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream())
     _raise("rat_dilated_attn_prefill", rc, lib)
+    return out
+
+
+def chunk_attn_prefill(q, k_state, v_state, D=1, scale=None, out=None):
+    """Chunk-grid causal attention: each query sees the states that end a
+    chunk of D tokens before it, and its own state."""
+    lib = load_library()
+    B, T, H, d = q.shape
+    for name, t in (("q", q), ("k_state", k_state), ("v_state", v_state)):
+        _check_tensor(name, t, q.dtype, q.shape)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib.rat_chunk_attn_prefill(_ptr(q), _ptr(k_state), _ptr(v_state), _ptr(out), B, T, H, d, _heads(D, H),
+                                    scale, _DTYPES[q.dtype], _stream())
+    _raise("rat_chunk_attn_prefill", rc, lib)
     return out
 
 

@@ -26,7 +26,8 @@
  *  - dtype: RAT_DTYPE_F32 (float) or RAT_DTYPE_BF16 (bfloat16, round to
  *    nearest even on output).  All arithmetic is fp32.
  *  - Supported head size d: 64 or 128.  Every pointer must be 16-byte
- *    aligned.  B*T*H*d (and B*H*N*d for caches) must be below 2^31.
+ *    aligned.  B*T*H*d must be below 2^31; for decode caches, B*H*d and
+ *    N*d (one head's rows) must be, the whole cache need not.
  *  - Every call only enqueues work on `stream` (a hipStream_t, may be NULL
  *    for the default stream) and returns without synchronising.
  *  - All validation happens on the host before any HIP call: on an error
@@ -117,6 +118,24 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
                              int B, int T, int H, int d, const int* D, const int* W,
                              float scale, rat_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2, prefill, on the chunk grid -- the absolute reading of the
+ * dilated pattern, after the RAT page ("RAT: Bridging RNN Efficiency and
+ * Attention Accuracy via Chunk-based Sequence Modeling", Abstract: the
+ * sequence is split into chunks and attention runs across chunks): with
+ * chunks of D[h] tokens, the query at position t attends in one softmax to
+ * the recurrent states that end a chunk before it (positions c*D[h] - 1 < t)
+ * and to its own state at t.  A decode cache under this reading holds the
+ * chunk ends plus the current state, which rat_dilated_attn_decode reads
+ * as its dilated cache unchanged (ceil(T/D) entries).
+ *   q, k_state, v_state, out : [B,T,H,d];
+ *   D : host int[H], D[h] >= 1 (D[h] = 1 is dense causal attention);
+ *       at most 8 distinct values.
+ * No raw local window, no workspace.  Errors: RAT_ERR_NULL, _SHAPE,
+ * _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
+int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out,
+                           int B, int T, int H, int d, const int* D, float scale, rat_dtype dtype,
+                           void* stream);
 
 /* Bytes of device workspace rat_dilated_attn_decode needs (0 when none; it
  * holds split-key partial softmax states when B*H is small). 256-byte

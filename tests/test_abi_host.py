@@ -133,6 +133,27 @@ def test_attn_workspace_sizes(lib):
     assert lib.rat_attn_prefill_workspace_bytes(1, 64, 2, 128, heads([4, 4]), heads([0, 8]), 0) == 0  # fp32
 
 
+def chunk(lib, q=P[0], ks=P[1], vs=P[2], out=P[5], B=1, T=64, H=2, d=128, D=(4, 16), scale=0.1, dtype=1):
+    Dh = None if D is None else heads(D)
+    return lib.rat_chunk_attn_prefill(q, ks, vs, out, B, T, H, d, Dh, scale, dtype, None)
+
+
+def test_chunk_attn_validation(lib):
+    assert chunk(lib, q=None) == NULL
+    assert chunk(lib, vs=None) == NULL
+    assert chunk(lib, D=None) == NULL
+    assert chunk(lib, T=0) == SHAPE
+    assert chunk(lib, D=(0, 4)) == SHAPE
+    assert chunk(lib, d=32) == UNSUP
+    assert chunk(lib, dtype=3) == UNSUP
+    assert chunk(lib, scale=float("nan")) == SHAPE
+    assert chunk(lib, out=P[1]) == ALIAS
+    assert chunk(lib, ks=MIS) == ALIGN
+    assert chunk(lib, H=300, D=[4] * 300) == UNSUP
+    many = [(i % 9) + 1 for i in range(16)]
+    assert chunk(lib, H=16, D=many) == UNSUP  # more than 8 dilation classes
+
+
 def decode(lib, q=P[0], kd=P[1], vd=P[2], nd_cap=512, kw=P[3], vw=P[4], w_cap=64, out=P[5], B=4, T=32768,
            H=2, d=128, D=(64, 64), W=(64, 64), scale=0.1, dtype=1, ws=P[6], wsb=1 << 30):
     return lib.rat_dilated_attn_decode(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, heads(D), heads(W),
@@ -154,6 +175,10 @@ def test_decode_validation(lib):
     assert need > 0
     assert decode(lib, B=1, H=1, T=1 << 20, D=(1,), W=(0,), nd_cap=1 << 20, w_cap=0, ws=None) == WSPACE
     assert lib.rat_decode_workspace_bytes(64, 20, 128, 32768, heads([64] * 20), heads([64] * 20)) == 0
+    # a cache of more than 2^31 elements passes the size checks (64-bit
+    # cache offsets): the misaligned query is the first error found
+    assert decode(lib, q=MIS, B=64, H=20, D=[64] * 20, W=[64] * 20, nd_cap=1 << 15) == ALIGN
+    assert decode(lib, nd_cap=1 << 24) == UNSUP  # one head's rows exceed 2^31 elements
 
 
 def step(lib, q=P[0], kn=P[1], vn=P[2], gn=P[3], st=P[4], kc=P[5], vc=P[6], n_cap=1024, kw=P[7],
@@ -176,3 +201,5 @@ def test_decode_step_validation(lib):
     assert step(lib, kc=P[1]) == ALIAS
     assert step(lib, vc=P[5]) == ALIAS
     assert step(lib, st=MIS) == ALIGN
+    # the full-position history of a 64 x 20-head batch at T = 32768 (> 2^31 elements)
+    assert step(lib, st=MIS, B=64, H=20, n_cap=1 << 15, T=32768, D=[64] * 20, W=[64] * 20) == ALIGN

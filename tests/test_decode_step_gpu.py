@@ -111,3 +111,65 @@ def test_scan_final_state(mode, L):
     err = np.abs(got - ref)
     assert np.isfinite(got).all()
     assert (err <= FP32_RTOL * np.abs(ref) + FP32_ATOL).all(), f"max err {err.max():.3g}"
+
+
+@pytest.mark.slow
+def test_decode_step_full_size():
+    """One decode-loop step on the 2.6B decode shape (B=64, T=32768, H=20,
+    d=128, D=64, W=64) in the benchmark's launch configuration, with a state
+    history that holds every position (n_cap = 32768 rows per head, more
+    than 2^31 elements per cache).  Sampled heads are checked: the running
+    state against the oracle's recurrence continued by one token, the written
+    history row and ring slot, untouched neighbours, and the output against
+    the oracle's decode over the residue's history rows and the ring."""
+    w = inputs.DECODE_2P6B_D64
+    B, T, H, d = w.B, w.T, w.H, w.d
+    D, W = list(w.D), list(w.W)
+    Dh, Wh = D[0], W[0]
+    n_cap = Dh * ((T + Dh - 1) // Dh)
+    p = T - 1
+    P = 6  # prefix tokens whose recurrence gives the running state
+    x = inputs.make_random_prefill(B, P + 1, H, d, torch.bfloat16, seed=21, gate_mean=1.5)
+    wk, wv = oracle.scan(x["k"], x["v"], x["gate"], P + 1, 0)
+    state = torch.from_numpy(np.stack([wk[:, P - 1], wv[:, P - 1]], axis=2)).float().cuda()  # [B,H,2,d]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(22)
+    mk = lambda *s: torch.randn(s, generator=gen, device="cuda").to(torch.bfloat16)  # noqa: E731
+    q = mk(B, H, d)
+    kc, vc = mk(B, H, n_cap, d), mk(B, H, n_cap, d)
+    kw, vw = mk(B, H, Wh, d), mk(B, H, Wh, d)
+    k_new, v_new, g_new = (x[n][:, P].contiguous().cuda() for n in ("k", "v", "gate"))
+    mcap = n_cap // Dh
+    r, j = p % Dh, p // Dh
+    row = r * mcap + j  # the last row of the cache here (r = D - 1, j = mcap - 1)
+    others = [row - 1, row - mcap, 0]  # same residue, same slot of another residue, first row
+    samples = [(0, 0), (B - 1, H - 1), (17, 5), (40, 11), (63, 0)]
+    before = {(b, h): (kc[b, h, others].cpu(), kw[b, h].cpu(), vw[b, h].cpu(),
+                       kc[b, h, r * mcap:row].cpu(), vc[b, h, r * mcap:row].cpu())
+              for b, h in samples}
+    announce("decode step full size", w.name, "n_cap", n_cap)
+    out = rat.decode_step(q, k_new, v_new, g_new, state, kc, vc, kw, vw, T, D, W)
+    torch.cuda.synchronize()
+    for b, h in samples:
+        want_state = np.stack([wk[b, P, h], wv[b, P, h]])
+        got_state = state[b, h].cpu().double().numpy()
+        assert (np.abs(got_state - want_state) <= 1e-3 * np.abs(want_state) + 1e-5).all(), (b, h)
+        other0, kw0, vw0, khist, vhist = before[(b, h)]
+        # the new history row is the state rounded to bf16; its neighbours are untouched
+        new_k = torch.from_numpy(want_state[0]).to(torch.bfloat16)
+        assert (kc[b, h, row].cpu().float() - new_k.float()).abs().max() <= 2 ** -7 * new_k.float().abs().max()
+        assert torch.equal(kc[b, h, others].cpu(), other0)
+        # the ring holds the raw token in slot p mod W
+        kw1 = kw0.clone()
+        kw1[p % Wh] = x["k"][b, P, h]
+        assert torch.equal(kw[b, h].cpu(), kw1)
+        vw1 = vw0.clone()
+        vw1[p % Wh] = x["v"][b, P, h]
+        assert torch.equal(vw[b, h].cpu(), vw1)
+        # output: the oracle's decode over this residue's rows 0 .. j (the
+        # last one the oracle's new state in bf16) and the ring
+        kd = torch.cat([khist, new_k[None]], 0)[None, None]
+        vd = torch.cat([vhist, torch.from_numpy(want_state[1]).to(torch.bfloat16)[None]], 0)[None, None]
+        want = oracle.attn_decode(q[b, h][None, None].cpu(), kd, vd, kw1[None, None], vw1[None, None], T,
+                                  [Dh], [Wh], w.scale)
+        assert_parity(out[b, h][None, None], want, torch.bfloat16, f"decode step b{b} h{h}")
