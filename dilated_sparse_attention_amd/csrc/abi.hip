@@ -92,6 +92,43 @@ bool scan_uses_workspace(int T, int L, rat_recur_mode mode)
     return L >= T || mode == RAT_RECUR_RESTART;
 }
 
+// The scan after validation (workspace already checked).  hist: write the
+// states as a per-residue history instead of [B][T][H][d].
+int run_scan(const void* k, const void* v, const void* g, void* ks, void* vs, int B, int T, int H, int d, int L,
+             rat_recur_mode mode, rat_dtype dtype, void* workspace, float* final_state, const StateHist* hist,
+             hipStream_t s)
+{
+    const bool bf16 = dtype == RAT_DTYPE_BF16;
+    if (scan_uses_workspace(T, L, mode)) {
+        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        ScanFullArgs a;
+        memset(&a, 0, sizeof(a));
+        a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs;
+        a.T = T; a.N = H * d; a.nblk = p.nblk; a.nseq = p.nseq; a.nchunk = p.nchunk;
+        a.L = L >= T ? 0 : L; a.nwg = p.nwg;
+        char* ws = static_cast<char*>(workspace);
+        a.hdr = reinterpret_cast<ScanHeader*>(ws);
+        a.agg = reinterpret_cast<uint64_t*>(ws + p.agg_off);
+        a.incl = reinterpret_cast<uint64_t*>(ws + p.incl_off);
+        a.fin = final_state;
+        a.d = d;
+        if (hist) a.hist = *hist;
+        return hip_status(launch_scan_full(a, bf16, hist != nullptr, s));
+    }
+    ScanSlideArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs;
+    a.B = B; a.T = T; a.N = H * d; a.L = L;
+    if (hist) a.hist = *hist;
+    if (bf16 && L == 64 && a.N % 64 == 0) return hip_status(launch_scan_slide64(a, hist != nullptr, s));
+    const int ntiles = (T + L - 1) / L;
+    // spans of at least 256 tokens: one halo tile per span
+    a.tiles_per_span = std::max(1, (256 + L - 1) / L);
+    const int nspans = (ntiles + a.tiles_per_span - 1) / a.tiles_per_span;
+    const int cgroups = (a.N + 63) / 64;
+    return hip_status(launch_scan_sliding(a, nspans * B * cgroups, bf16, hist != nullptr, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,34 +179,12 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void
             if (p == final_state) return RAT_ERR_ALIAS;
         if (!aligned16(final_state)) return RAT_ERR_ALIGN;
     }
-    hipStream_t s = (hipStream_t)stream;
-    const bool bf16 = dtype == RAT_DTYPE_BF16;
-
     if (scan_uses_workspace(T, L, mode)) {
         const ScanPlan p = scan_plan(B, T, H, d, dtype);
         if (!workspace || workspace_bytes < p.bytes || ((uintptr_t)workspace & 255u)) return RAT_ERR_WORKSPACE;
-        ScanFullArgs a;
-        a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state;
-        a.T = T; a.N = H * d; a.nblk = p.nblk; a.nseq = p.nseq; a.nchunk = p.nchunk;
-        a.L = L >= T ? 0 : L; a.nwg = p.nwg;
-        char* ws = static_cast<char*>(workspace);
-        a.hdr = reinterpret_cast<ScanHeader*>(ws);
-        a.agg = reinterpret_cast<uint64_t*>(ws + p.agg_off);
-        a.incl = reinterpret_cast<uint64_t*>(ws + p.incl_off);
-        a.fin = final_state;
-        a.d = d;
-        return hip_status(launch_scan_full(a, bf16, s));
     }
-    ScanSlideArgs a;
-    a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state;
-    a.B = B; a.T = T; a.N = H * d; a.L = L;
-    if (bf16 && L == 64 && a.N % 64 == 0) return hip_status(launch_scan_slide64(a, s));
-    const int ntiles = (T + L - 1) / L;
-    // spans of at least 256 tokens: one halo tile per span
-    a.tiles_per_span = std::max(1, (256 + L - 1) / L);
-    const int nspans = (ntiles + a.tiles_per_span - 1) / a.tiles_per_span;
-    const int cgroups = (a.N + 63) / 64;
-    return hip_status(launch_scan_sliding(a, nspans * B * cgroups, bf16, s));
+    return run_scan(k, v, gate_logits, k_state, v_state, B, T, H, d, L, mode, dtype, workspace, final_state,
+                    nullptr, (hipStream_t)stream);
 }
 
 namespace {
@@ -208,7 +223,8 @@ namespace {
 // single items come first, each class's levels most expensive first.
 int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, const void* k_raw,
                       const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
-                      bool any_w, float scale, int chunk, void* workspace, size_t workspace_bytes, hipStream_t s)
+                      bool any_w, float scale, int chunk, int n_cap, void* workspace, size_t workspace_bytes,
+                      hipStream_t s)
 {
     if (any_w) {
         const size_t need = (size_t)B * T * H * 2 * sizeof(float);
@@ -239,6 +255,7 @@ int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, c
     dil.scale_log2 = scale * 1.4426950408889634f;
     band = dil;
     dil.chunk = chunk;
+    dil.n_cap = n_cap;  // states as a per-residue history (0: [B][T][H][d])
     int64_t items = 0, blocks = 0;
     int hoff = 0;
     for (const Cls& c : cls) {
@@ -303,8 +320,8 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
         return hip_status(launch_attn_prefill_f32(a, s));
     }
 
-    return attn_prefill_bf16(q, k_state, v_state, k_raw, v_raw, out, B, T, H, d, D, W, any_w, scale, 0, workspace,
-                             workspace_bytes, s);
+    return attn_prefill_bf16(q, k_state, v_state, k_raw, v_raw, out, B, T, H, d, D, W, any_w, scale, 0, 0,
+                             workspace, workspace_bytes, s);
 }
 
 int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out, int B, int T, int H,
@@ -338,7 +355,7 @@ int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_sta
     }
     // dilated items whose keys are the chunk ends (residue D - 1) strictly
     // before each query, their softmax started from the query's own state
-    return attn_prefill_bf16(q, k_state, v_state, nullptr, nullptr, out, B, T, H, d, D, W0, false, scale, 1,
+    return attn_prefill_bf16(q, k_state, v_state, nullptr, nullptr, out, B, T, H, d, D, W0, false, scale, 1, 0,
                              nullptr, 0, s);
 }
 
@@ -364,6 +381,92 @@ size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, cons
     const int ns = decode_nsplit(B, H, T, D, W);
     if (ns == 1) return 0;
     return (size_t)B * H * ns * (d + 2) * sizeof(float);
+}
+
+constexpr bool kLayerPrefillEnabled = false;
+
+int rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits, void* out, void* kc,
+                      void* vc, int n_cap, void* kw, void* vw, int w_cap, float* final_state, int B, int T, int H,
+                      int d, int L, rat_recur_mode mode, const int* D, const int* W, float scale, rat_dtype dtype,
+                      void* scan_workspace, size_t scan_workspace_bytes, void* attn_workspace,
+                      size_t attn_workspace_bytes, void* stream)
+{
+    if (!q || !k || !v || !gate_logits || !out || !kc || !vc) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1 || n_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
+    if (mode != RAT_RECUR_RESTART && mode != RAT_RECUR_SLIDING) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
+    for (int h = 0; h < H; ++h) {
+        if ((T - 1) / D[h] >= n_cap / D[h]) return RAT_ERR_SHAPE;  // history rows of position T-1
+        if (W[h] > w_cap) return RAT_ERR_SHAPE;                   // ring slots p mod W
+    }
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d) || !size_ok(B, H, n_cap, d) ||
+        !size_ok(B, H, std::max(w_cap, 1), d))
+        return RAT_ERR_UNSUPPORTED;
+    if (mode == RAT_RECUR_SLIDING && L < T && L > 64) return RAT_ERR_UNSUPPORTED;
+    if (final_state && !scan_uses_workspace(T, L, mode)) return RAT_ERR_UNSUPPORTED;  // SLIDING: no single state
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[4] = {q, k, v, gate_logits};
+    const void* outs[6] = {out, kc, vc, kw, vw, final_state};
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i]) continue;
+        for (const void* in : ins)
+            if (outs[i] == in) return RAT_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return RAT_ERR_ALIAS;
+    }
+    for (const void* x : ins)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (x && !aligned16(x)) return RAT_ERR_ALIGN;
+    if (scan_uses_workspace(T, L, mode)) {
+        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        if (!scan_workspace || scan_workspace_bytes < p.bytes || ((uintptr_t)scan_workspace & 255u))
+            return RAT_ERR_WORKSPACE;
+    }
+    const bool bf16 = dtype == RAT_DTYPE_BF16;
+    if (bf16 && any_w) {
+        const size_t need = (size_t)B * T * H * 2 * sizeof(float);
+        if (!attn_workspace || attn_workspace_bytes < need || !aligned16(attn_workspace)) return RAT_ERR_WORKSPACE;
+    }
+    // The launch path below (history-writing scan instances, the history
+    // instances of the dilated kernel, the ring fill) is switched off: a run
+    // of it faulted the device, and reading the code and checking every
+    // address it forms on the host has not yet shown the cause.
+    if (!kLayerPrefillEnabled) return RAT_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+
+    // 1. the recurrence, its states written straight into the history
+    StateHist hist;
+    memset(&hist, 0, sizeof(hist));
+    hist.n_cap = n_cap; hist.d = d; hist.H = H;
+    for (int h = 0; h < H; ++h) hist.D[h] = D[h];
+    int rc = run_scan(k, v, gate_logits, kc, vc, B, T, H, d, L, mode, dtype, scan_workspace, final_state, &hist, s);
+    if (rc != RAT_OK) return rc;
+    // 2. the raw ring of the last W tokens
+    if (any_w) {
+        RingFillArgs r;
+        memset(&r, 0, sizeof(r));
+        r.k = k; r.v = v; r.kw = kw; r.vw = vw;
+        r.B = B; r.T = T; r.H = H; r.d = d; r.w_cap = w_cap;
+        for (int h = 0; h < H; ++h) r.W[h] = W[h];
+        rc = hip_status(launch_ring_fill(r, bf16, s));
+        if (rc != RAT_OK) return rc;
+    }
+    // 3. dilated (+ local window) attention over the history
+    if (!bf16) {
+        AttnF32Args a;
+        memset(&a, 0, sizeof(a));
+        a.q = (const float*)q; a.ks = (const float*)kc; a.vs = (const float*)vc;
+        a.kr = (const float*)k; a.vr = (const float*)v; a.out = (float*)out;
+        a.B = B; a.T = T; a.H = H; a.d = d; a.scale = scale; a.n_cap = n_cap;
+        for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+        return hip_status(launch_attn_prefill_f32(a, s));
+    }
+    return attn_prefill_bf16(q, kc, vc, k, v, out, B, T, H, d, D, W, any_w, scale, 0, n_cap, attn_workspace,
+                             attn_workspace_bytes, s);
 }
 
 int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,

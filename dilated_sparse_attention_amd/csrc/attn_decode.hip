@@ -290,6 +290,43 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a)
     }
 }
 
+// Raw ring after a prefill: slot s of head h holds the latest position
+// p < T with p mod W[h] = s (so positions T - W[h] .. T-1); slots with no
+// such position, and slots at or past W[h], are left alone.  One thread per
+// 16 bytes of a row.
+template <typename E>
+__global__ __launch_bounds__(256) void ring_fill_kernel(RingFillArgs a)
+{
+    constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte vector
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int vpr = a.d / EPV;           // vectors per row
+    if (idx >= (size_t)a.B * a.H * a.w_cap * vpr) return;
+    const int c = (int)(idx % vpr) * EPV;
+    const size_t row = idx / vpr;        // (b H + h) w_cap + slot
+    const int slot = (int)(row % a.w_cap);
+    const size_t bh = row / a.w_cap;
+    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+    const int W = a.W[h];
+    if (slot >= W) return;
+    const int p = (a.T - 1) - ((a.T - 1 - slot) % W + W) % W;  // latest position of the slot
+    if (p < 0) return;
+    const size_t src = (((size_t)b * a.T + p) * a.H + h) * a.d + c;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + row * a.d + c) =
+        *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + src);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + row * a.d + c) =
+        *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + src);
+}
+
+hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream)
+{
+    const size_t n = (size_t)a.B * a.H * a.w_cap * (a.d / (bf16 ? 8 : 4));
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(ring_fill_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(ring_fill_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream)
 {
     const size_t n = (size_t)a.B * a.H * a.d;

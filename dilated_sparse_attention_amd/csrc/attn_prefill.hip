@@ -279,11 +279,12 @@ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
 // The DMA issue cursor and the compute cursor are two copies.
 constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
 
-template <bool BAND, bool CHUNK>
+template <bool BAND, bool CHUNK, bool HIST>
 struct CursorA {
     int round, t, nq, no, nown, ntile;
     int rowidx;   // (b T + r) H + h: first row of the item in units of head rows
-    int krowidx;  // the same for its key rows (residue kres)
+    int krowidx;  // the same for its key rows (residue kres); with HIST the first
+                  // history row of the residue, (b H + h) n_cap + r n_cap / D
     int dstride;  // min(D, T) H: head rows between consecutive rows of the item
     ItemA it;
 
@@ -305,7 +306,9 @@ struct CursorA {
                 nown = CHUNK ? (it.R1 - it.R0 + kTileA - 1) / kTileA : 0;
                 ntile = max(0, (CHUNK ? it.nkey : it.R1) - it.kbeg + kTileA - 1) / kTileA;
                 rowidx = (it.b * a.T + it.r) * a.H + it.h;
-                krowidx = CHUNK ? (it.b * a.T + it.kres) * a.H + it.h : rowidx;
+                krowidx = HIST    ? (it.b * a.H + it.h) * a.n_cap + it.r * (a.n_cap / it.D)
+                          : CHUNK ? (it.b * a.T + it.kres) * a.H + it.h
+                                  : rowidx;
                 // a residue of D >= T holds one row: min(D, T) keeps byte
                 // strides below 2^32 without changing any address
                 dstride = min(it.D, a.T) * a.H;
@@ -369,8 +372,8 @@ struct DmaLane {
 // PER_WAVE row copies of RPI rows each; partial-output steps add one copy
 // of their (m, l) words into `side` on waves 0-3).  Rows past the item's
 // last row R1 - 1 are clamped to it.
-template <int DK, int NW, bool BAND, bool CHUNK>
-__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK>& c, uint64_t src_q,
+template <int DK, int NW, bool BAND, bool CHUNK, bool HIST>
+__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK, HIST>& c, uint64_t src_q,
                                              uint64_t src_out, uint64_t src_kv, const DmaLane<DK>& dl, uint32_t buf,
                                              uint32_t side)
 {
@@ -397,9 +400,12 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BA
         row0 = c.it.kbeg + kt * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
         tsrc = src_kv;
     }
-    const bool keys = CHUNK && ko >= 0 && !own;  // a chunk-grid key tile: rows of residue kres
+    // a key tile read elsewhere than the query rows: the chunk ends
+    // (residue kres), or the residue's contiguous rows of a state history
+    const bool keys = (CHUNK || HIST) && ko >= 0 && !own;
     const uint32_t item_el = (uint32_t)(keys ? c.krowidx : c.rowidx) * DK;
-    const uint32_t dp2 = (uint32_t)c.dstride * (2 * DK);  // bytes between rows r and r + 1 of the item
+    // bytes between rows r and r + 1 of the item
+    const uint32_t dp2 = (HIST && keys ? 1u : (uint32_t)c.dstride) * (2 * DK);
     const int last = (CHUNK && ko >= 0 && !own ? c.it.nkey : c.it.R1) - 1;
     const uint32_t slot = buf + wv * PER_WAVE * 1024;  // LDS byte address of the wave's first copy
     if (row0 + PER_WAVE * G::RPI - 1 <= last) {
@@ -561,8 +567,9 @@ __device__ __forceinline__ int row_block(int wv, int j)
 }
 
 // CHUNK: the chunk grid (keys of residue D - 1 strictly before the query,
-// the softmax started from the query's own state)
-template <int DK, int NW, int RING, bool BAND, bool CHUNK>
+// the softmax started from the query's own state).  HIST: the states are a
+// per-residue history ([B][H][n_cap][d], a residue's rows contiguous).
+template <int DK, int NW, int RING, bool BAND, bool CHUNK, bool HIST>
 __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
@@ -588,7 +595,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     DmaLane<DK> dl;
     dl.init();
     const DmaSrc dsrc = dma_sources<NW, BAND>(a, wv);
-    CursorA<BAND, CHUNK> issue, comp;
+    CursorA<BAND, CHUNK, HIST> issue, comp;
     issue.seek(a, 0);
     comp = issue;
     // ring steps issued and consumed; step n lives in slot n mod RING (a
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     const uint32_t side_lds = smem_lds + (uint32_t)(side - smem);
     auto issue_next = [&]() {
         const int sl = issued % RING;
-        issue_step_a<DK, NW, BAND, CHUNK>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
+        issue_step_a<DK, NW, BAND, CHUNK, HIST>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
                                    side_lds + sl * 1024);
         ++issued;
         issue.advance(a);
@@ -836,7 +843,7 @@ static void set_lds(K kernel, size_t lds, bool& done)
 #endif
 constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated kernel
 
-template <bool BAND, bool CHUNK>
+template <bool BAND, bool CHUNK, bool HIST>
 static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, hipStream_t stream)
 {
     static bool s[2][2] = {{false, false}, {false, false}};
@@ -844,11 +851,11 @@ static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, 
     if (ring5) {  // deeper prefetch: five ring slots (no side buffers)
         const size_t lds = attn_lds_bytes_a5(d);
         if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK>, lds, s[0][0]);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK, HIST>, lds, s[0][0]);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK, HIST>), dim3(grid), block, lds, stream, a);
         } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK>, lds, s[0][1]);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK>), dim3(grid), block, lds, stream, a);
+            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK, HIST>, lds, s[0][1]);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK, HIST>), dim3(grid), block, lds, stream, a);
         }
         return hipGetLastError();
     }
@@ -857,12 +864,12 @@ static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, 
     } else {
         const size_t lds = attn_lds_bytes_a(d);
         if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false>, lds, s[1][0]);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false>), dim3(grid), block, lds,
+            set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false, HIST>, lds, s[1][0]);
+            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false, HIST>), dim3(grid), block, lds,
                                stream, a);
         } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false>, lds, s[1][1]);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false>), dim3(grid), block, lds,
+            set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false, HIST>, lds, s[1][1]);
+            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false, HIST>), dim3(grid), block, lds,
                                stream, a);
         }
         return hipGetLastError();
@@ -873,13 +880,14 @@ hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStrea
 {
     bool windowed = false;
     for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
-    if (a.chunk) return launch_path_a<false, true>(a, d, grid, true, stream);  // no windowed classes
-    return launch_path_a<false, false>(a, d, grid, !windowed, stream);
+    if (a.chunk) return launch_path_a<false, true, false>(a, d, grid, true, stream);  // no windowed classes
+    if (a.n_cap > 0) return launch_path_a<false, false, true>(a, d, grid, !windowed, stream);
+    return launch_path_a<false, false, false>(a, d, grid, !windowed, stream);
 }
 
 hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
-    return launch_path_a<true, false>(a, d, grid, true, stream);
+    return launch_path_a<true, false, false>(a, d, grid, true, stream);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -897,26 +905,30 @@ __global__ __launch_bounds__(kWave) void attn_prefill_f32_kernel(AttnF32Args a)
     const float q0 = lane < d ? a.q[base + t * pitch + lane] : 0.f;
     const float q1 = lane + kWave < d ? a.q[base + t * pitch + lane + kWave] : 0.f;
     float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    auto visit = [&](const float* kbase, const float* vbase, int s) {
-        const float* kr = kbase + base + s * pitch;
+    // row s of a state tensor: [B][T][H][d], or a per-residue history
+    const size_t hbase = (size_t)bh * a.n_cap * d;
+    const int mcap = a.n_cap > 0 ? a.n_cap / D : 0;
+    auto srow = [&](int s) -> size_t { return a.n_cap > 0 ? hbase + (size_t)((s % D) * mcap + s / D) * d : base + s * pitch; };
+    auto visit = [&](const float* kbase, const float* vbase, size_t row) {
+        const float* kr = kbase + row;
         float dot = (lane < d ? q0 * kr[lane] : 0.f) + (lane + kWave < d ? q1 * kr[lane + kWave] : 0.f);
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
         const float z = dot * a.scale;
         const float mn = fmaxf(m, z);
         const float al = expf(m - mn), p = expf(z - mn);
-        const float* vr = vbase + base + s * pitch;
+        const float* vr = vbase + row;
         o0 = o0 * al + p * (lane < d ? vr[lane] : 0.f);
         o1 = o1 * al + p * (lane + kWave < d ? vr[lane + kWave] : 0.f);
         l = l * al + p;
         m = mn;
     };
     if (a.chunk) {  // chunk-end states before t, then the own state
-        for (int s = D - 1; s < t; s += D) visit(a.ks, a.vs, s);
-        visit(a.ks, a.vs, t);
+        for (int s = D - 1; s < t; s += D) visit(a.ks, a.vs, srow(s));
+        visit(a.ks, a.vs, srow(t));
     } else {
-        for (int s = t; s >= 0; s -= D) visit(a.ks, a.vs, s);
-        for (int w = 0; w < W && t - w >= 0; ++w) visit(a.kr, a.vr, t - w);
+        for (int s = t; s >= 0; s -= D) visit(a.ks, a.vs, srow(s));
+        for (int w = 0; w < W && t - w >= 0; ++w) visit(a.kr, a.vr, base + (size_t)(t - w) * pitch);
     }
     if (lane < d) a.out[base + t * pitch + lane] = o0 / l;
     if (lane + kWave < d) a.out[base + t * pitch + lane + kWave] = o1 / l;

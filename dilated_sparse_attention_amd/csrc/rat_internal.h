@@ -6,6 +6,18 @@
 
 namespace rat {
 
+constexpr int kAttnMaxHeads = 256;
+
+// Per-residue state history (the decode cache): the state of head h at
+// position p is row (p mod D[h]) * (n_cap / D[h]) + p / D[h] of that head's
+// [n_cap][d] block, heads [B][H] outermost.  The rows of one residue are
+// contiguous and in position order.
+struct StateHist {
+    int n_cap;  // rows per head
+    int d, H;
+    int D[kAttnMaxHeads];
+};
+
 // ---------------------------------------------------------------- scan
 // Tile of the full / RESTART scan: a workgroup of kScanWaves waves covers
 // one block of channels (128 bf16 / 64 fp32: a 256-byte row segment) x
@@ -42,6 +54,7 @@ struct ScanFullArgs {
     ScanHeader* hdr;
     float* fin;      // optional fp32 states at t = T-1, [B][H][2][d] (NULL: none)
     int d;           // head size (for `fin`)
+    StateHist hist;  // state layout of the history-writing instances
 };
 
 struct ScanSlideArgs {
@@ -51,16 +64,17 @@ struct ScanSlideArgs {
     void* ks;
     void* vs;
     int B, T, N, L, tiles_per_span;
+    StateHist hist;  // state layout of the history-writing instances
 };
 
-hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, hipStream_t stream);
+// hist: write the states as a StateHist instead of [B][T][H][d]
+hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, hipStream_t stream);
+hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, bool hist, hipStream_t stream);
 // SLIDING with L = 64 in bf16 (N a multiple of 64)
-hipError_t launch_scan_slide64(const ScanSlideArgs& a, hipStream_t stream);
+hipError_t launch_scan_slide64(const ScanSlideArgs& a, bool hist, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnMaxClasses = 8;
-constexpr int kAttnMaxHeads = 256;
 constexpr int kAttnRowsA = 256;   // query rows of one residue per path-A item / band block
 
 struct AttnClass {
@@ -83,6 +97,7 @@ struct AttnArgs {
     int B, T, H;
     float scale_log2;  // softmax scale * log2(e)
     int chunk;         // 1: chunk grid -- keys are the chunk-end states (residue D-1), strictly before the query
+    int n_cap;         // > 0: ks / vs are a StateHist with n_cap rows per head (relative dilation only)
     int nclass;
     int nblocks;
     AttnClass cls[kAttnMaxClasses];
@@ -106,6 +121,7 @@ struct AttnF32Args {
     int B, T, H, d;
     float scale;
     int chunk;  // 1: chunk grid (chunk-end states before t, then the own state)
+    int n_cap;  // > 0: ks / vs are a StateHist with n_cap rows per head
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
 };
@@ -148,5 +164,17 @@ struct StepArgs {
     int slot_w[kAttnMaxHeads];  // ring slot of the new position, -1 without a window
 };
 hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream);
+
+// Raw ring of a prefill: positions max(0, T - W[h]) .. T-1 of k, v
+// ([B][T][H][d]) into slots p mod W[h] of kw, vw ([B][H][w_cap][d]).
+struct RingFillArgs {
+    const void* k;
+    const void* v;
+    void* kw;
+    void* vw;
+    int B, T, H, d, w_cap;
+    int W[kAttnMaxHeads];
+};
+hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace rat

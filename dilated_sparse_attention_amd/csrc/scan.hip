@@ -81,7 +81,28 @@ template <> struct Row16<float> {
     }
 };
 
-template <typename E>
+// Row of position t in a StateHist head with dilation D and mcap = n_cap / D
+// rows per residue, walked token by token without a division.
+struct HistRow {
+    int res, q, D, mcap;
+    __device__ __forceinline__ void init(int t, int D_, int n_cap)
+    {
+        D = D_;
+        mcap = n_cap / D_;
+        q = t / D_;
+        res = t - q * D_;
+    }
+    __device__ __forceinline__ int row() const { return res * mcap + q; }
+    __device__ __forceinline__ void next()
+    {
+        if (++res == D) {
+            res = 0;
+            ++q;
+        }
+    }
+};
+
+template <typename E, bool HIST>
 __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs a)
 {
     typedef Row16<E> R16;
@@ -355,6 +376,13 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
     // evaluated again; the empty asm hides the logits' identity from
     // common-subexpression elimination, which would keep pass 1's gates in
     // 8 more registers per token)
+    HistRow hr;
+    size_t hbase = 0;
+    if (HIST) {  // the lane's head, its history block and the row of t0
+        const int hh = ch0 / a.d;
+        hr.init(t0, a.hist.D[cvalid ? hh : 0], a.hist.n_cap);
+        hbase = ((size_t)b * a.hist.H + hh) * a.hist.n_cap * a.d + (ch0 - hh * a.d);
+    }
     float ck[CPL], cv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -385,10 +413,11 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs
         // the states next faster than cacheable ones do (the scan itself
         // runs as fast either way)
         if (cvalid && t0 + i < a.T) {
-            const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+            const size_t o = HIST ? hbase + (size_t)hr.row() * a.d : rowbase + (size_t)(t0 + i) * a.N;
             __builtin_nontemporal_store(R16::pack(ok), reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o));
             __builtin_nontemporal_store(R16::pack(ov), reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o));
         }
+        if (HIST) hr.next();
         // the last position's states in fp32, for a decode loop to continue from
         if (a.fin && cvalid && t0 + i == a.T - 1) {
 #pragma unroll
@@ -414,7 +443,7 @@ template <> __device__ __forceinline__ void store1<uint16_t>(uint16_t* p, float 
 
 // One wave = 64 channels (one per lane) x a span of `tiles_per_span` tiles
 // of L tokens; the tile before the span is re-read to seed the suffix sums.
-template <typename E>
+template <typename E, bool HIST>
 __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
 {
     __shared__ float s_x[2][kSlideMaxL][kWave];  // suffix sums X_j (k, v) of the previous tile
@@ -435,6 +464,14 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
     const E* gp = static_cast<const E*>(a.g) + base;
     E* ksp = static_cast<E*>(a.ks) + base;
     E* vsp = static_cast<E*>(a.vs) + base;
+    int hD = 1;
+    if (HIST) {  // the lane's head and its history block
+        const int hh = (cvalid ? c : 0) / a.hist.d;
+        hD = a.hist.D[hh];
+        const size_t hb = ((size_t)b * a.hist.H + hh) * a.hist.n_cap * a.hist.d + ((cvalid ? c : 0) - hh * a.hist.d);
+        ksp = static_cast<E*>(a.ks) + hb;
+        vsp = static_cast<E*>(a.vs) + hb;
+    }
 
     for (int j = 0; j < L; ++j) { s_x[0][j][lane] = 0.f; s_x[1][j][lane] = 0.f; }
 
@@ -456,6 +493,8 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
         if (m >= tile_first) {
             // forward: in-tile recurrence plus the previous tile's suffix
             float P = 1.f, Hk = 0.f, Hv = 0.f;
+            HistRow hr;
+            if (HIST) hr.init(ts, hD, a.hist.n_cap);
 #pragma unroll
             for (int j = 0; j < kSlideMaxL; ++j) {
                 if (j < n) {
@@ -465,10 +504,11 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
                     Hk = fmaf(g, Hk, gb * rk[j]);
                     Hv = fmaf(g, Hv, gb * rv[j]);
                     if (cvalid) {
-                        const size_t o = (size_t)(ts + j) * a.N;
+                        const size_t o = HIST ? (size_t)hr.row() * a.hist.d : (size_t)(ts + j) * a.N;
                         store1<E>(ksp + o, fmaf(P, s_x[0][j][lane], Hk));
                         store1<E>(vsp + o, fmaf(P, s_x[1][j][lane], Hv));
                     }
+                    if (HIST) hr.next();
                 }
             }
         }
@@ -506,6 +546,7 @@ __global__ __launch_bounds__(kWave) void scan_sliding_kernel(ScanSlideArgs a)
 // workgroups fit on a compute unit.
 constexpr int kSlideCT = 128, kSlideHalo = 64, kSlideBW = 64;
 
+template <bool HIST>
 __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArgs a)
 {
     constexpr int ROWB = kSlideBW * 2;           // bytes of a 64-channel bf16 row
@@ -520,6 +561,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
     extern __shared__ __attribute__((aligned(1024))) char s_tile[];  // [3][NROW][ROWB]: k, v, logits
     __shared__ float s_map[kScanWaves][3][kSlideBW];  // forward segment maps (A, K, V)
     __shared__ float s_rev[kScanWaves][3][kSlideBW];  // previous-tile segments (Q, Sk, Sv)
+    __shared__ int s_hrow[HIST ? kSlideCT : 1];         // history row of each token of the chunk
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -530,6 +572,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
     const int tb = chunk * kSlideCT;             // first token of the chunk
     const int r0 = tb - kSlideHalo;              // token of LDS row 0
     const size_t rowbase = (size_t)b * a.T * a.N + (size_t)blk * kSlideBW;
+    size_t hbase = 0;  // the block's channels in its head's history (one head: d is 64 or 128)
+    if (HIST) {
+        const int hh = blk * kSlideBW / a.hist.d;
+        hbase = ((size_t)b * a.hist.H + hh) * a.hist.n_cap * a.hist.d + (blk * kSlideBW - hh * a.hist.d);
+        if (threadIdx.x < kSlideCT) {
+            const int D = a.hist.D[hh], t = tb + threadIdx.x;
+            s_hrow[threadIdx.x] = (t % D) * (a.hist.n_cap / D) + t / D;
+        }
+    }
 
     {
         const uint16_t* src[3] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
@@ -635,44 +686,51 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
             const int tensor = row / kSlideCT, tok = row % kSlideCT;
             const u32x4 val = *reinterpret_cast<const u32x4*>(
                 s_tile + (tensor * NROW + kSlideHalo + tok) * ROWB + (lane % LPR) * 16);
-            if (tb + tok < a.T)
-                *reinterpret_cast<u32x4*>(dst[tensor] + rowbase + (size_t)(tb + tok) * a.N + (lane % LPR) * 8) = val;
+            if (tb + tok < a.T) {
+                const size_t o = HIST ? hbase + (size_t)s_hrow[tok] * a.hist.d : rowbase + (size_t)(tb + tok) * a.N;
+                *reinterpret_cast<u32x4*>(dst[tensor] + o + (lane % LPR) * 8) = val;
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------- launches
-hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, hipStream_t stream)
+hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, hipStream_t stream)
 {
-    if (bf16)
-        hipLaunchKernelGGL((scan_full_kernel<uint16_t>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((scan_full_kernel<float>), dim3(a.nwg), dim3(kScanThreads), 0, stream, a);
+    const dim3 grid(a.nwg), block(kScanThreads);
+    if (bf16 && hist) hipLaunchKernelGGL((scan_full_kernel<uint16_t, true>), grid, block, 0, stream, a);
+    else if (bf16) hipLaunchKernelGGL((scan_full_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    else if (hist) hipLaunchKernelGGL((scan_full_kernel<float, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((scan_full_kernel<float, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, hipStream_t stream)
+hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, bool hist, hipStream_t stream)
 {
-    if (bf16)
-        hipLaunchKernelGGL((scan_sliding_kernel<uint16_t>), dim3(nblocks), dim3(kWave), 0, stream, a);
-    else
-        hipLaunchKernelGGL((scan_sliding_kernel<float>), dim3(nblocks), dim3(kWave), 0, stream, a);
+    const dim3 grid(nblocks), block(kWave);
+    if (bf16 && hist) hipLaunchKernelGGL((scan_sliding_kernel<uint16_t, true>), grid, block, 0, stream, a);
+    else if (bf16) hipLaunchKernelGGL((scan_sliding_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    else if (hist) hipLaunchKernelGGL((scan_sliding_kernel<float, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((scan_sliding_kernel<float, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace rat
 
 namespace rat {
-hipError_t launch_scan_slide64(const ScanSlideArgs& a, hipStream_t stream)
+hipError_t launch_scan_slide64(const ScanSlideArgs& a, bool hist, hipStream_t stream)
 {
-    static bool attr = false;
+    static bool attr[2] = {false, false};
     const size_t lds = 3 * (size_t)(kSlideCT + kSlideHalo) * kSlideBW * 2;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void*)scan_slide64_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        attr = true;
+    const void* fn = hist ? (const void*)scan_slide64_kernel<true> : (const void*)scan_slide64_kernel<false>;
+    if (!attr[hist]) {
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        attr[hist] = true;
     }
     const int nchunk = (a.T + kSlideCT - 1) / kSlideCT;
-    hipLaunchKernelGGL(scan_slide64_kernel, dim3(nchunk * a.B * (a.N / kSlideBW)), dim3(kScanThreads), lds, stream, a);
+    const dim3 grid(nchunk * a.B * (a.N / kSlideBW)), block(kScanThreads);
+    if (hist) hipLaunchKernelGGL(scan_slide64_kernel<true>, grid, block, lds, stream, a);
+    else hipLaunchKernelGGL(scan_slide64_kernel<false>, grid, block, lds, stream, a);
     return hipGetLastError();
 }
 }  // namespace rat

@@ -27,7 +27,8 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 # every symbol include/rat.h declares
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
            "rat_chunk_attn_prefill",
-           "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_status_string",
+           "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_layer_prefill",
+           "rat_status_string",
            "rat_last_hip_error")
 
 
@@ -72,6 +73,9 @@ def load_library(path: str = LIBRARY):
     lib.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, ip, ip, f, i, vp, sz,
                                     vp]
     lib.rat_decode_step.restype = i
+    lib.rat_layer_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, ip, ip, f, i,
+                                      vp, sz, vp, sz, vp]
+    lib.rat_layer_prefill.restype = i
     lib.rat_status_string.argtypes = [i]
     lib.rat_status_string.restype = ctypes.c_char_p
     lib.rat_last_hip_error.argtypes = []
@@ -252,6 +256,65 @@ def rat_layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=No
     need_raw = any(int(w) > 0 for w in (W if hasattr(W, "__len__") else [W]))
     return dilated_attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None,
                                 D=D, W=W, scale=scale)
+
+
+def history_rows(T, D):
+    """Rows per head a state history needs to hold positions 0 .. T-1 for
+    every head's dilation: the smallest n with (T-1) // D[h] < n // D[h]."""
+    return max(Dh * ((T - 1) // Dh + 1) for Dh in D)
+
+
+def layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None, n_cap=None, w_cap=None,
+                  final_state=True, out=None, kc=None, vc=None, kw=None, vw=None):
+    """The whole prefill (recurrence, then dilated + local attention) in one
+    library call, emitting the decode caches: the per-residue state history
+    (kc, vc: [B,H,n_cap,d]), the raw ring of the last W tokens (kw, vw:
+    [B,H,w_cap,d]) and the fp32 states at T-1.  ``n_cap`` defaults to the
+    rows positions 0 .. T-1 need.  Returns (out, kc, vc, kw, vw, state);
+    kw / vw are None when every W is 0, state None when not asked for."""
+    lib = load_library()
+    B, T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate_logits", gate_logits)):
+        _check_tensor(name, t, q.dtype, q.shape)
+    L = T if L is None else int(L)
+    Dl = list(D) if hasattr(D, "__len__") else [int(D)] * H
+    Wl = list(W) if hasattr(W, "__len__") else [int(W)] * H
+    Dh, Wh = _heads(Dl, H), _heads(Wl, H)
+    n_cap = history_rows(T, Dl) if n_cap is None else int(n_cap)
+    if kc is None:
+        kc = torch.empty((B, H, n_cap, d), dtype=q.dtype, device=q.device)
+    if vc is None:
+        vc = torch.empty_like(kc)
+    _check_tensor("kc", kc, q.dtype, (B, H, n_cap, d))
+    _check_tensor("vc", vc, q.dtype, (B, H, n_cap, d))
+    any_w = any(int(x) > 0 for x in Wl)
+    w_cap = (max(int(x) for x in Wl) if any_w else 0) if w_cap is None else int(w_cap)
+    if any_w and kw is None:
+        kw = torch.zeros((B, H, w_cap, d), dtype=q.dtype, device=q.device)
+    if any_w and vw is None:
+        vw = torch.zeros_like(kw)
+    if kw is not None:
+        _check_tensor("kw", kw, q.dtype, (B, H, w_cap, d))
+        _check_tensor("vw", vw, q.dtype, (B, H, w_cap, d))
+    if final_state is True:
+        final_state = torch.empty((B, H, 2, d), dtype=torch.float32, device=q.device)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _check_tensor("final_state", final_state, torch.float32, (B, H, 2, d))
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sbytes = lib.rat_scan_workspace_bytes(B, T, H, d, L, mode, _DTYPES[q.dtype])
+    sws = scan_workspace(sbytes, q.device) if sbytes else None
+    abytes = lib.rat_attn_prefill_workspace_bytes(B, T, H, d, Dh, Wh, _DTYPES[q.dtype])
+    aws = attn_workspace(abytes, q.device) if abytes else None
+    rc = lib.rat_layer_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_logits), _ptr(out), _ptr(kc), _ptr(vc), n_cap,
+                               _ptr(kw), _ptr(vw), w_cap, _ptr(final_state), B, T, H, d, L, mode, Dh, Wh, scale,
+                               _DTYPES[q.dtype], _ptr(sws), 0 if sws is None else sws.numel(), _ptr(aws),
+                               0 if aws is None else aws.numel(), _stream())
+    _raise("rat_layer_prefill", rc, lib)
+    return out, kc, vc, kw, vw, final_state
 
 
 def decode_step(q, k_new, v_new, gate_new, state, kc, vc, kw, vw, T, D, W, L=None, scale=None, out=None,

@@ -186,6 +186,41 @@ int rat_decode_step(const void* q, const void* k_new, const void* v_new, const v
                     float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* The whole prefill of the layer in one call, handing a decode loop its
+ * caches: the recurrence of rat_scan_prefill (Deep Dive 2.1), then the
+ * attention of rat_dilated_attn_prefill (RAT+ Abstract; Deep Dive 1 and 6),
+ * with the states written once, straight into the per-residue history that
+ * rat_decode_step reads and extends (the decode cache of the RAT+ Abstract).
+ *   q, k, v, gate_logits : [B,T,H,d] inputs; out : [B,T,H,d], equal to
+ *            rat_dilated_attn_prefill over rat_scan_prefill's states with
+ *            k_raw = k, v_raw = v;
+ *   kc, vc : [B,H,n_cap,d] state history, layout as for rat_decode_step:
+ *            position p of head h at row (p mod D[h]) * (n_cap / D[h]) +
+ *            p / D[h]; rows of positions 0 .. T-1 are written, others left
+ *            alone.  (T-1) / D[h] < n_cap / D[h] for every h; B*H*n_cap*d
+ *            must be below 2^31.  A decode loop can continue at T+1 when
+ *            T / D[h] < n_cap / D[h] as well;
+ *   kw, vw : [B,H,w_cap,d] ring, slot p mod W[h] holding raw k, v of the
+ *            last W[h] positions p < T (slots with no such position, and
+ *            slots >= W[h], left alone); w_cap >= W[h]; may be NULL iff
+ *            every W[h] == 0;
+ *   final_state : optional fp32 [B,H,2,d], as in rat_scan_prefill (not for
+ *            SLIDING with L < T);
+ *   L, mode : as rat_scan_prefill;  D, W, scale : as rat_dilated_attn_prefill;
+ *   scan_workspace : rat_scan_workspace_bytes(...) bytes, the same
+ *            zero-filled-once buffer rules as rat_scan_prefill;
+ *   attn_workspace : rat_attn_prefill_workspace_bytes(...) bytes.
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP.
+ * In this build the call validates its arguments and then returns
+ * RAT_ERR_UNSUPPORTED without launching anything: its launch path is
+ * switched off until a device fault seen in it is explained. */
+int rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits,
+                      void* out, void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
+                      float* final_state, int B, int T, int H, int d, int L, rat_recur_mode mode,
+                      const int* D, const int* W, float scale, rat_dtype dtype,
+                      void* scan_workspace, size_t scan_workspace_bytes,
+                      void* attn_workspace, size_t attn_workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* rat_status_string(int status);
 

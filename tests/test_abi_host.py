@@ -203,3 +203,35 @@ def test_decode_step_validation(lib):
     assert step(lib, st=MIS) == ALIGN
     # the full-position history of a 64 x 20-head batch at T = 32768 (> 2^31 elements)
     assert step(lib, st=MIS, B=64, H=20, n_cap=1 << 15, T=32768, D=[64] * 20, W=[64] * 20) == ALIGN
+
+
+def layer(lib, q=P[0], k=P[1], v=P[2], g=P[3], out=P[4], kc=P[5], vc=P[6], n_cap=1024, kw=P[7],
+          vw=ctypes.c_void_p(0x10000 + 0x100000 * 9), w_cap=64, fin=None, B=1, T=1000, H=2, d=128, L=1000,
+          mode=0, D=(64, 16), W=(64, 0), scale=0.1, dtype=1, sws=ctypes.c_void_p(0x10000 + 0x100000 * 10),
+          swsb=1 << 30, aws=ctypes.c_void_p(0x10000 + 0x100000 * 11), awsb=1 << 30):
+    return lib.rat_layer_prefill(q, k, v, g, out, kc, vc, n_cap, kw, vw, w_cap, fin, B, T, H, d, L, mode,
+                                 heads(D), heads(W), scale, dtype, sws, swsb, aws, awsb, None)
+
+
+def test_layer_prefill_validation(lib):
+    assert layer(lib, kc=None) == NULL
+    assert layer(lib, kw=None) == NULL                 # head 0 has a window
+    assert layer(lib, n_cap=0) == SHAPE
+    # position 999 of the D = 64 head is row 15 of its residue: 16 rows per residue needed
+    assert layer(lib, n_cap=64 * 15) == SHAPE
+    assert layer(lib, w_cap=63) == SHAPE               # ring slots p mod 64
+    assert layer(lib, mode=5) == SHAPE
+    assert layer(lib, d=32) == UNSUP
+    assert layer(lib, B=64, H=20, D=[64] * 20, W=[64] * 20, n_cap=1 << 15) == UNSUP  # history >= 2^31 elements
+    assert layer(lib, mode=1, L=64, fin=ctypes.c_void_p(0x10000 + 0x100000 * 12)) == UNSUP  # SLIDING: no state
+    assert layer(lib, mode=1, L=100) == UNSUP          # SLIDING window above 64
+    assert layer(lib, out=P[0]) == ALIAS
+    assert layer(lib, kc=P[1]) == ALIAS
+    assert layer(lib, vw=P[5]) == ALIAS                # two outputs share memory
+    assert layer(lib, fin=P[6]) == ALIAS
+    assert layer(lib, vc=MIS) == ALIGN
+    assert layer(lib, sws=None) == WSPACE              # the full recurrence needs its workspace
+    assert layer(lib, sws=ctypes.c_void_p(0x10040)) == WSPACE
+    assert layer(lib, aws=None) == WSPACE              # a windowed head needs the attention workspace
+    # valid arguments: the launch path is switched off in this build
+    assert layer(lib) == UNSUP
