@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 # kernel names as the profiler lists them (bf16, d = 128, full recurrence)
-SCAN_KERNEL = "rat::scan_full_kernel<unsigned short>"
-ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false, false>"
+SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, false>"
+ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false, false, false>"
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
