@@ -433,6 +433,140 @@ int oracle_chunk_attn_prefill_rows(const double* q, const double* k_state, const
     return bad ? -4 : 0;
 }
 
+/* Backward of the layer: the gradient of a scalar loss through the forward
+ * above (recurrence of Deep Dive S2.1, then the one-softmax attention of
+ * Deep Dive S1 / RAT+ abstract), by the chain rule applied to those
+ * definitions.  This is what the training of Deep Dive S2.2 (Active
+ * Recurrence Learning: half of a batch at D = 1, half at D = 64, recurrence
+ * over the full sequence) differentiates.  Full recurrence (L >= T) and
+ * RESTART only; a SLIDING window returns -5.
+ *
+ * Given dout = dLoss/dout [B,T,H,d]:
+ *   attention, per query t with keys/values (kappa_j, nu_j), j over the
+ *   dilated states then the raw window, z_j = scale <q_t, kappa_j>,
+ *   p_j = softmax(z)_j:
+ *     dp_j = <dout_t, nu_j>,  delta = sum_j p_j dp_j,
+ *     ds_j = p_j (dp_j - delta),
+ *     dq_t += scale sum_j ds_j kappa_j,
+ *     dkappa_j += scale ds_j q_t,   dnu_j += p_j dout_t;
+ *   recurrence h_t = g_t h_{t-1} + (1 - g_t) x_t (h_{t-1} := 0 at t = 0 and
+ *   at RESTART positions), walked backwards with lambda_t = dLoss/dh_t:
+ *     lambda_t = dh_t + g_{t+1} lambda_{t+1}  (no carry into t when t + 1
+ *                is a restart position, nor past the end),
+ *     dx_t += (1 - g_t) lambda_t,
+ *     dlogit_t = g_t (1 - g_t) sum_{x in k, v} lambda_t (h_{t-1} - x_t)
+ *   (the gate is shared by keys and values; dsigma/dl = sigma (1 - sigma)).
+ * Outputs dq, dk, dv, dlogit: [B,T,H,d]; dk and dv sum the state path and
+ * the raw-window path. */
+int oracle_layer_backward(const double* q, const double* k, const double* v, const double* logit,
+                          const double* dout, double* dq, double* dk, double* dv, double* dlogit,
+                          int B, int T, int H, int d, int L, int mode, const int* D, const int* W,
+                          double scale)
+{
+    if (!q || !k || !v || !logit || !dout || !dq || !dk || !dv || !dlogit || !D || !W) return -1;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return -2;
+    if (mode != ORACLE_MODE_RESTART && mode != ORACLE_MODE_SLIDING) return -3;
+    const int full = (L >= T);
+    if (!full && mode == ORACLE_MODE_SLIDING) return -5;
+    int need_raw, max_keys;
+    if (check_heads(H, D, W, &need_raw, &max_keys, T)) return -3;
+    const size_t n = (size_t)B * T * H * d;
+    double* ks = (double*)malloc(sizeof(double) * n);
+    double* vs = (double*)malloc(sizeof(double) * n);
+    double* dks = (double*)calloc(n, sizeof(double));  /* dLoss/d state (from attention) */
+    double* dvs = (double*)calloc(n, sizeof(double));
+    if (!ks || !vs || !dks || !dvs) {
+        free(ks); free(vs); free(dks); free(dvs);
+        return -4;
+    }
+    oracle_scan(k, v, logit, ks, vs, B, T, H, d, L, mode);
+    for (size_t i = 0; i < n; ++i) { dq[i] = 0.0; dk[i] = 0.0; dv[i] = 0.0; dlogit[i] = 0.0; }
+    int bad = 0;
+    /* attention: the accumulations of one (b, h) touch only that head */
+#pragma omp parallel
+    {
+        const double** kp = (const double**)malloc(sizeof(double*) * max_keys);
+        const double** vp = (const double**)malloc(sizeof(double*) * max_keys);
+        double** dkp = (double**)malloc(sizeof(double*) * max_keys);
+        double** dvp = (double**)malloc(sizeof(double*) * max_keys);
+        double* z = (double*)malloc(sizeof(double) * max_keys);
+        double* p = (double*)malloc(sizeof(double) * max_keys);
+        if (!kp || !vp || !dkp || !dvp || !z || !p) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic)
+            for (int b = 0; b < B; ++b)
+                for (int h = 0; h < H; ++h)
+                    for (int t = 0; t < T; ++t) {
+                        int nk = 0;
+                        for (int s = t; s >= 0; s -= D[h]) {
+                            size_t o = idx4(b, s, h, 0, T, H, d);
+                            kp[nk] = ks + o; vp[nk] = vs + o; dkp[nk] = dks + o; dvp[nk] = dvs + o;
+                            ++nk;
+                        }
+                        for (int w = 0; w < W[h] && t - w >= 0; ++w) {
+                            size_t o = idx4(b, t - w, h, 0, T, H, d);
+                            kp[nk] = k + o; vp[nk] = v + o; dkp[nk] = dk + o; dvp[nk] = dv + o;
+                            ++nk;
+                        }
+                        const double* qt = q + idx4(b, t, h, 0, T, H, d);
+                        const double* go = dout + idx4(b, t, h, 0, T, H, d);
+                        double* gq = dq + idx4(b, t, h, 0, T, H, d);
+                        double m = -INFINITY;
+                        for (int j = 0; j < nk; ++j) {
+                            double dot = 0.0;
+                            for (int c = 0; c < d; ++c) dot += qt[c] * kp[j][c];
+                            z[j] = dot * scale;
+                            if (z[j] > m) m = z[j];
+                        }
+                        double den = 0.0;
+                        for (int j = 0; j < nk; ++j) { p[j] = exp(z[j] - m); den += p[j]; }
+                        double delta = 0.0;
+                        for (int j = 0; j < nk; ++j) {
+                            p[j] /= den;
+                            double dp = 0.0;
+                            for (int c = 0; c < d; ++c) dp += go[c] * vp[j][c];
+                            z[j] = dp;  /* reuse: dp_j */
+                            delta += p[j] * dp;
+                        }
+                        for (int j = 0; j < nk; ++j) {
+                            double ds = p[j] * (z[j] - delta);
+                            for (int c = 0; c < d; ++c) {
+                                gq[c] += scale * ds * kp[j][c];
+                                dkp[j][c] += scale * ds * qt[c];
+                                dvp[j][c] += p[j] * go[c];
+                            }
+                        }
+                    }
+        }
+        free(kp); free(vp); free(dkp); free(dvp); free(z); free(p);
+    }
+    /* recurrence, backwards in time, one channel at a time */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < d; ++c) {
+                double lk = 0.0, lv = 0.0;  /* carry g_{t+1} lambda_{t+1} into t */
+                for (int t = T - 1; t >= 0; --t) {
+                    size_t i = idx4(b, t, h, c, T, H, d);
+                    double g, gb;
+                    gate_pair(logit[i], &g, &gb);
+                    const int cut = (t == 0) || (!full && t % L == 0);  /* h_{t-1} replaced by 0 */
+                    double hk_prev = cut ? 0.0 : ks[idx4(b, t - 1, h, c, T, H, d)];
+                    double hv_prev = cut ? 0.0 : vs[idx4(b, t - 1, h, c, T, H, d)];
+                    double lamk = dks[i] + lk, lamv = dvs[i] + lv;
+                    dk[i] += gb * lamk;
+                    dv[i] += gb * lamv;
+                    dlogit[i] = g * gb * (lamk * (hk_prev - k[i]) + lamv * (hv_prev - v[i]));
+                    lk = cut ? 0.0 : g * lamk;
+                    lv = cut ? 0.0 : g * lamv;
+                }
+            }
+    free(ks); free(vs); free(dks); free(dvs);
+    return bad ? -4 : 0;
+}
+
 /* Counting mode for the FLOP / KV-size invariants [Deep Dive S3.1 table:
  * attention FLOPs T/D]: totals over all T queries of one head. */
 int oracle_count_pairs(int T, int D, int W, long long* n_dil_total, long long* n_loc_total)

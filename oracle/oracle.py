@@ -96,6 +96,8 @@ class Oracle:
         lib.oracle_chunk_index_set.argtypes = [i, i, ip]
         lib.oracle_chunk_index_set.restype = ctypes.c_long
         lib.oracle_chunk_attn_prefill_rows.argtypes = [dp, dp, dp, ip, i, dp, i, i, i, i, ip, d]
+        lib.oracle_layer_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                              i, i, i, i, i, i, ip, ip, d]
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -208,6 +210,19 @@ class Oracle:
                "oracle_attn_decode")
         return out
 
+    def layer_backward(self, q, k, v, logit, dout, L, mode, D, W, scale):
+        """Gradients (dq, dk, dv, dlogit), each [B,T,H,d], of <dout, out>
+        through the recurrence (full or RESTART) and the attention."""
+        q, k, v, logit, dout = (_f64(x) for x in (q, k, v, logit, dout))
+        B, T, H, d = q.shape
+        Da, Wa = _heads(D, W, H)
+        dq, dk, dv, dl = (np.empty_like(q) for _ in range(4))
+        _check(self.lib.oracle_layer_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(dout),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), B, T, H, d,
+                                              int(L), int(mode), _iptr(Da), _iptr(Wa), float(scale)),
+               "oracle_layer_backward")
+        return dq, dk, dv, dl
+
 
 _default = None
 
@@ -260,3 +275,7 @@ def chunk_attn_prefill_rows(q, k_state, v_state, rows, D, scale):
 
 def chunk_attn_prefill(q, k_state, v_state, D, scale):
     return default().chunk_attn_prefill(q, k_state, v_state, D, scale)
+
+
+def layer_backward(q, k, v, logit, dout, L, mode, D, W, scale):
+    return default().layer_backward(q, k, v, logit, dout, L, mode, D, W, scale)

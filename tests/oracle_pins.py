@@ -406,4 +406,69 @@ def pin_chunk_attn_masked_matrix(o):
     np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------- backward
+def _layer_loss(o, q, k, v, lg, dout, L, mode, D, W, scale):
+    """<dout, out> of the oracle's forward (recurrence, then attention)."""
+    ks, vs = o.scan(k, v, lg, L, mode)
+    need_raw = any(w > 0 for w in W)
+    out = o.attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None, D, W, scale)
+    return float(np.sum(dout * out))
+
+
+def pin_backward_finite_differences(o):
+    """The backward against central differences of the (separately pinned)
+    forward, element by element, for the full recurrence and RESTART, dense,
+    dilated and windowed heads together: every input of every tensor."""
+    eps = 1e-5
+    for (T, L, D, W) in [(10, 10, [1, 3], [0, 2]), (11, 4, [2, 1], [3, 0]), (9, 9, [4, 20], [1, 0])]:
+        q, k, v, lg = _inputs(40 + T, 1, T, 2, 3, gate_mean=0.5)
+        dout = _rng(41 + T).standard_normal(q.shape)
+        args = (L, 0, D, W, 0.7)
+        grads = o.layer_backward(q, k, v, lg, dout, *args)
+        for which, (x, g) in enumerate(zip((q, k, v, lg), grads)):
+            fd = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                saved = x[idx]
+                x[idx] = saved + eps
+                up = _layer_loss(o, q, k, v, lg, dout, *args)
+                x[idx] = saved - eps
+                dn = _layer_loss(o, q, k, v, lg, dout, *args)
+                x[idx] = saved
+                fd[idx] = (up - dn) / (2 * eps)
+            np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=f"input {which} T={T} L={L}")
+
+
+def pin_backward_own_state_only(o):
+    """D >= T and no window: each query's only key is its own state, so
+    out_t = v_state_t, dq = 0, the keys get no gradient, and the value
+    gradient is the reverse recurrence of dout: with a constant gate g,
+    dL/dv_state_t = sum_{s >= t} g^(s-t) dout_s and dv_t = (1 - g) times it."""
+    B, T, H, d = 2, 12, 2, 5
+    q, k, v, _ = _inputs(45, B, T, H, d)
+    lg = np.full(q.shape, 0.8)
+    dout = _rng(46).standard_normal(q.shape)
+    dq, dk, dv, dl = o.layer_backward(q, k, v, lg, dout, T, 0, [T, 50], [0, 0], 0.5)
+    assert np.array_equal(dq, np.zeros_like(dq))
+    assert np.array_equal(dk, np.zeros_like(dk))
+    g = 1.0 / (1.0 + math.exp(-0.8))
+    lam = np.zeros_like(dout)
+    for t in range(T):
+        for s in range(t, T):
+            lam[:, t] += g ** (s - t) * dout[:, s]
+    np.testing.assert_allclose(dv, (1 - g) * lam, rtol=1e-12, atol=1e-14)
+    _, vs = o.scan(k, v, lg, T, 0)
+    prev = np.concatenate([np.zeros_like(vs[:, :1]), vs[:, :-1]], axis=1)
+    np.testing.assert_allclose(dl, g * (1 - g) * lam * (prev - v), rtol=1e-11, atol=1e-13)
+
+
+def pin_backward_rejects_sliding(o):
+    """A SLIDING window below T has no backward here: the call is refused."""
+    q, k, v, lg = _inputs(47, 1, 8, 1, 2)
+    try:
+        o.layer_backward(q, k, v, lg, q, 4, 1, [1], [0], 1.0)
+    except ValueError:
+        return
+    raise AssertionError("SLIDING backward was accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

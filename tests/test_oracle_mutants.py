@@ -45,6 +45,14 @@ MUTANTS = {
     "chunk_end_off_by_one": ("for (int p = D - 1; p < t; p += D) {", "for (int p = D; p < t; p += D) {"),
     "chunk_end_not_strict": ("for (int p = D - 1; p < t; p += D) {", "for (int p = D - 1; p <= t; p += D) {"),
     "chunk_own_state_dropped": ("    if (pos) pos[n] = t;\n    return n + 1;", "    return n;"),
+    "bwd_delta_dropped": ("double ds = p[j] * (z[j] - delta);", "double ds = p[j] * z[j];"),
+    "bwd_gate_derivative_sign": ("dlogit[i] = g * gb * (", "dlogit[i] = -g * gb * ("),
+    "bwd_restart_carry_kept": ("lk = cut ? 0.0 : g * lamk;", "lk = g * lamk;"),
+    "bwd_input_grad_ungated": ("dk[i] += gb * lamk;", "dk[i] += lamk;"),
+    "bwd_raw_path_to_states": ("kp[nk] = k + o; vp[nk] = v + o; dkp[nk] = dk + o; dvp[nk] = dv + o;",
+                               "kp[nk] = k + o; vp[nk] = v + o; dkp[nk] = dks + o; dvp[nk] = dvs + o;"),
+    "bwd_prev_state_off_by_one": ("double hv_prev = cut ? 0.0 : vs[idx4(b, t - 1, h, c, T, H, d)];",
+                                  "double hv_prev = cut ? 0.0 : vs[idx4(b, t, h, c, T, H, d)];"),
     "count_window_short": ("for (int w = 0; w < W && t - w >= 0; ++w) {\n        if (loc)",
                            "for (int w = 1; w < W && t - w >= 0; ++w) {\n        if (loc)"),
 }
