@@ -7,4 +7,4 @@ library; the first call does, and raises if it has not been built.
 """
 from .ops import (RESTART, SLIDING, RatError, attn_prefill_workspace_bytes, chunk_attn_prefill,  # noqa: F401
                   decode_step, decode_workspace_bytes, dilated_attn_decode, dilated_attn_prefill, history_rows,
-                  layer_prefill, load_library, rat_layer_prefill, scan_prefill, scan_workspace_bytes)
+                  layer_backward, layer_prefill, load_library, rat_layer_prefill, scan_prefill, scan_workspace_bytes)

@@ -129,6 +129,29 @@ int run_scan(const void* k, const void* v, const void* g, void* ks, void* vs, in
     return hip_status(launch_scan_sliding(a, nspans * B * cgroups, bf16, hist != nullptr, s));
 }
 
+
+// Workspace of the backward: per query row (lse, delta), the state
+// gradients, the per-chunk maps and carries; every part 256-byte aligned.
+struct BwdPlan {
+    int nchunk;
+    size_t off_lse, off_delta, off_dks, off_dvs, off_maps, off_carry, bytes;
+};
+
+BwdPlan bwd_plan(int B, int T, int H, int d)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    BwdPlan p;
+    p.nchunk = (T + kBwdChunk - 1) / kBwdChunk;
+    const size_t rows = (size_t)B * T * H, elems = rows * d, cells = (size_t)p.nchunk * B * H * d;
+    p.off_lse = 0;
+    p.off_delta = up(p.off_lse + rows * 4);
+    p.off_dks = up(p.off_delta + rows * 4);
+    p.off_dvs = up(p.off_dks + elems * 4);
+    p.off_maps = up(p.off_dvs + elems * 4);
+    p.off_carry = up(p.off_maps + cells * 5 * 4);
+    p.bytes = up(p.off_carry + cells * 4 * 4);
+    return p;
+}
 }  // namespace
 
 extern "C" {
@@ -467,6 +490,63 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
     }
     return attn_prefill_bf16(q, kc, vc, k, v, out, B, T, H, d, D, W, any_w, scale, 0, n_cap, attn_workspace,
                              attn_workspace_bytes, s);
+}
+
+size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || !size_ok(B, T, H, d)) return 0;
+    return bwd_plan(B, T, H, d).bytes;
+}
+
+int rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits, const void* k_state,
+                       const void* v_state, const void* dout, float* dq, float* dk, float* dv, float* dgate, int B,
+                       int T, int H, int d, int L, rat_recur_mode mode, const int* D, const int* W, float scale,
+                       rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const void* ins[7] = {q, k, v, gate_logits, k_state, v_state, dout};
+    const void* outs[4] = {dq, dk, dv, dgate};
+    for (const void* x : ins)
+        if (!x) return RAT_ERR_NULL;
+    for (const void* x : outs)
+        if (!x) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return RAT_ERR_SHAPE;
+    if (mode != RAT_RECUR_RESTART && mode != RAT_RECUR_SLIDING) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
+    if (mode == RAT_RECUR_SLIDING && L < T) return RAT_ERR_UNSUPPORTED;  // no backward of a sliding window
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    for (int i = 0; i < 4; ++i) {
+        for (const void* x : ins)
+            if (outs[i] == x) return RAT_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return RAT_ERR_ALIAS;
+    }
+    for (const void* x : ins)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    const BwdPlan p = bwd_plan(B, T, H, d);
+    if (!workspace || workspace_bytes < p.bytes || ((uintptr_t)workspace & 255u)) return RAT_ERR_WORKSPACE;
+
+    BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k; a.v = v; a.g = gate_logits; a.ks = k_state; a.vs = v_state; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dgate;
+    char* ws = static_cast<char*>(workspace);
+    a.lse = reinterpret_cast<float*>(ws + p.off_lse);
+    a.delta = reinterpret_cast<float*>(ws + p.off_delta);
+    a.dks = reinterpret_cast<float*>(ws + p.off_dks);
+    a.dvs = reinterpret_cast<float*>(ws + p.off_dvs);
+    a.maps = reinterpret_cast<float*>(ws + p.off_maps);
+    a.carry = reinterpret_cast<float*>(ws + p.off_carry);
+    a.B = B; a.T = T; a.H = H; a.d = d;
+    a.L = L >= T ? 0 : L;
+    a.nchunk = p.nchunk;
+    a.scale = scale;
+    for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+    return hip_status(launch_backward(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 
 int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,

@@ -177,4 +177,34 @@ struct RingFillArgs {
 };
 hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream);
 
+// ---------------------------------------------------------------- backward
+constexpr int kBwdChunk = 16;  // tokens per chunk of the reverse recurrence
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;     // gate logits
+    const void* ks;
+    const void* vs;    // forward states
+    const void* dout;  // [B][T][H][d] in the layer's dtype
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dg;         // [B][T][H][d] fp32 gradients
+    float* lse;
+    float* delta;      // [B][T][H] per query row
+    float* dks;
+    float* dvs;        // [B][T][H][d] gradients of the states
+    float* maps;       // [nchunk][B][H d][5] per-chunk maps
+    float* carry;      // [nchunk][B][H d][4] state before / carry into each chunk
+    int B, T, H, d;
+    int L;             // RESTART period, 0 for the full recurrence
+    int nchunk;        // ceil(T / kBwdChunk)
+    float scale;
+    int D[kAttnMaxHeads];
+    int W[kAttnMaxHeads];
+};
+hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+
 }  // namespace rat

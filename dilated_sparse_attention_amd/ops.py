@@ -28,6 +28,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
            "rat_chunk_attn_prefill",
            "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_layer_prefill",
+           "rat_layer_backward_workspace_bytes", "rat_layer_backward",
            "rat_status_string",
            "rat_last_hip_error")
 
@@ -76,6 +77,11 @@ def load_library(path: str = LIBRARY):
     lib.rat_layer_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, ip, ip, f, i,
                                       vp, sz, vp, sz, vp]
     lib.rat_layer_prefill.restype = i
+    lib.rat_layer_backward_workspace_bytes.argtypes = [i, i, i, i]
+    lib.rat_layer_backward_workspace_bytes.restype = sz
+    lib.rat_layer_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, ip, ip, f, i,
+                                       vp, sz, vp]
+    lib.rat_layer_backward.restype = i
     lib.rat_status_string.argtypes = [i]
     lib.rat_status_string.restype = ctypes.c_char_p
     lib.rat_last_hip_error.argtypes = []
@@ -315,6 +321,33 @@ def layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None, 
                                0 if aws is None else aws.numel(), _stream())
     _raise("rat_layer_prefill", rc, lib)
     return out, kc, vc, kw, vw, final_state
+
+
+def layer_backward(q, k, v, gate_logits, k_state, v_state, dout, D, W, L=None, mode=RESTART, scale=None,
+                   grads=None, workspace=None):
+    """Gradients (dq, dk, dv, dgate), fp32 [B,T,H,d], of a loss with
+    incoming gradient ``dout`` through the layer's forward (the states it
+    produced are passed in).  Full recurrence or RESTART."""
+    lib = load_library()
+    B, T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate_logits", gate_logits), ("k_state", k_state),
+                    ("v_state", v_state), ("dout", dout)):
+        _check_tensor(name, t, q.dtype, q.shape)
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(4))
+    for name, t in zip(("dq", "dk", "dv", "dgate"), grads):
+        _check_tensor(name, t, torch.float32, q.shape)
+    L = T if L is None else int(L)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = lib.rat_layer_backward_workspace_bytes(B, T, H, d)
+    if workspace is None:
+        workspace = attn_workspace(nbytes, q.device)
+    rc = lib.rat_layer_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_logits), _ptr(k_state), _ptr(v_state),
+                                _ptr(dout), *(_ptr(g) for g in grads), B, T, H, d, L, mode,
+                                _heads(D, H), _heads(W, H), scale, _DTYPES[q.dtype], _ptr(workspace),
+                                workspace.numel(), _stream())
+    _raise("rat_layer_backward", rc, lib)
+    return grads
 
 
 def decode_step(q, k_new, v_new, gate_new, state, kc, vc, kw, vw, T, D, W, L=None, scale=None, out=None,

@@ -221,6 +221,40 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
                       void* scan_workspace, size_t scan_workspace_bytes,
                       void* attn_workspace, size_t attn_workspace_bytes, void* stream);
 
+/* Bytes of device workspace rat_layer_backward needs: per query row the
+ * log-sum-exp and dout.out, the fp32 gradients of the states, and per
+ * 16-token chunk of every channel its recurrence maps and carries.
+ * 256-byte aligned; no initialisation. */
+size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d);
+
+/* Backward of the layer (the training of Deep Dive 2.2, Active Recurrence
+ * Learning, differentiates the forward of rat_scan_prefill and
+ * rat_dilated_attn_prefill; there the recurrence runs over the full
+ * sequence): given dout = dLoss/dout, the gradients of the loss with
+ * respect to q, k, v and the gate logits, by the chain rule through the
+ * one-softmax attention (states at t, t-D, ... and raw tokens t .. t-W+1)
+ * and then through the recurrence h_t = g_t h_{t-1} + (1 - g_t) x_t walked
+ * backwards (dk and dv sum the state path and the raw-window path).
+ *   q, k, v, gate_logits : [B,T,H,d] forward inputs;
+ *   k_state, v_state     : [B,T,H,d] forward states (rat_scan_prefill);
+ *   dout                 : [B,T,H,d] incoming gradient;  all in `dtype`.
+ *                          The softmax is recomputed in fp32, and the
+ *                          row term <dout_t, out_t> is formed from it, so
+ *                          the forward output is not an input;
+ *   dq, dk, dv, dgate    : [B,T,H,d] fp32 outputs;
+ *   L, mode              : the forward's recurrence; the full recurrence
+ *                          (L >= T) and RESTART only -- a SLIDING window
+ *                          below T returns RAT_ERR_UNSUPPORTED;
+ *   D, W, scale          : as rat_dilated_attn_prefill;
+ *   workspace            : rat_layer_backward_workspace_bytes(...) bytes.
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
+int rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits,
+                       const void* k_state, const void* v_state, const void* dout,
+                       float* dq, float* dk, float* dv, float* dgate,
+                       int B, int T, int H, int d, int L, rat_recur_mode mode,
+                       const int* D, const int* W, float scale, rat_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* rat_status_string(int status);
 

@@ -235,3 +235,36 @@ def test_layer_prefill_validation(lib):
     assert layer(lib, aws=None) == WSPACE              # a windowed head needs the attention workspace
     # valid arguments: the launch path is switched off in this build
     assert layer(lib) == UNSUP
+
+
+def backward(lib, q=P[0], k=P[1], v=P[2], g=P[3], ks=P[4], vs=P[5], dout=P[7],
+             dq=ctypes.c_void_p(0x10000 + 0x100000 * 9), dk=ctypes.c_void_p(0x10000 + 0x100000 * 10),
+             dv=ctypes.c_void_p(0x10000 + 0x100000 * 11), dg=ctypes.c_void_p(0x10000 + 0x100000 * 12),
+             B=1, T=100, H=2, d=128, L=100, mode=0, D=(1, 64), W=(0, 8), scale=0.1, dtype=1,
+             ws=ctypes.c_void_p(0x10000 + 0x100000 * 13), wsb=1 << 30):
+    return lib.rat_layer_backward(q, k, v, g, ks, vs, dout, dq, dk, dv, dg, B, T, H, d, L, mode,
+                                  heads(D), heads(W), scale, dtype, ws, wsb, None)
+
+
+def test_backward_validation(lib):
+    assert backward(lib, dout=None) == NULL
+    assert backward(lib, dg=None) == NULL
+    assert backward(lib, T=0) == SHAPE
+    assert backward(lib, D=(0, 1)) == SHAPE
+    assert backward(lib, d=96) == UNSUP
+    assert backward(lib, mode=1, L=64) == UNSUP      # no backward of a sliding window
+    assert backward(lib, dq=P[0]) == ALIAS
+    assert backward(lib, dv=ctypes.c_void_p(0x10000 + 0x100000 * 9)) == ALIAS  # two gradients share memory
+    assert backward(lib, ks=MIS) == ALIGN
+    assert backward(lib, ws=None) == WSPACE
+    assert backward(lib, wsb=1024) == WSPACE
+
+
+def test_backward_workspace_size(lib):
+    B, T, H, d = 2, 100, 3, 64
+    rows, elems = B * T * H, B * T * H * d
+    cells = ((T + 15) // 16) * B * H * d
+    need = lib.rat_layer_backward_workspace_bytes(B, T, H, d)
+    assert need >= 4 * (2 * rows + 2 * elems + 9 * cells)
+    assert need < 4 * (2 * rows + 2 * elems + 9 * cells) + 6 * 256
+    assert lib.rat_layer_backward_workspace_bytes(0, T, H, d) == 0
