@@ -16,8 +16,10 @@ carries the roofline of the dominant kernel, the oracle timed on the host
 cores on a bounded sample (``cpu_baseline``) and, under ``extra``, the other
 workloads: long prefill with a window (both recurrence readings), the 7.6B
 hybrid prefill, the 2.6B decode at D = 64 and D = 16, the chunk-grid
-attention on the 1.5B-scale prefill shape and the decode-loop step (the
-recurrence update fused with decode attention) on the 2.6B decode shape.
+attention on the 1.5B-scale prefill shape, the decode-loop step (the
+recurrence update fused with decode attention) on the 2.6B decode shape,
+and the layer backward of Active Recurrence Learning training (half of the
+1.5B-scale batch at D = 1, half at D = 64).
 """
 from __future__ import annotations
 
@@ -284,6 +286,56 @@ def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
     return ms, nbytes
 
 
+def run_backward_arl(torch, rat, w, steps, warmup):
+    """The training step's backward of Active Recurrence Learning on the
+    prefill workload `w`: half of the batch at D = 1, half at D = 64, full
+    recurrence; one layer_backward call per half (the forward's states come
+    from the scan kernel, outside the timed region)."""
+    from dilated_sparse_attention_amd import inputs
+
+    x = inputs.make_prefill(w, seed=7, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(w.dtype)
+    half = w.B // 2
+    parts = []
+    for b0, Dv in ((0, 1), (half, 64)):
+        xs = {n: t[b0:b0 + half].contiguous() for n, t in x.items()}
+        ks, vs = rat.scan_prefill(xs["k"], xs["v"], xs["gate"])
+        grads = tuple(torch.empty(xs["q"].shape, dtype=torch.float32, device="cuda") for _ in range(4))
+        ws = torch.empty(rat.ops.load_library().rat_layer_backward_workspace_bytes(half, w.T, w.H, w.d),
+                         dtype=torch.uint8, device="cuda")
+        parts.append((xs, ks, vs, dout[b0:b0 + half].contiguous(), [Dv] * w.H, grads, ws))
+    del x
+
+    def step():
+        for xs, ks, vs, do, D, grads, ws in parts:
+            rat.layer_backward(xs["q"], xs["k"], xs["v"], xs["gate"], ks, vs, do, D, [0] * w.H, grads=grads,
+                               workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # algorithmic units: per visible (query, key) pair five length-d
+    # contractions (scores, dout.v, and the three gradient products); bytes:
+    # the seven inputs once and the four fp32 gradients once
+    pairs = half * sum(attn_pairs(w.T, Dv, 0)[0] * w.H for Dv in (1, 64))
+    flops = 10 * w.d * pairs
+    E = w.B * w.T * w.H * w.d
+    nbytes = 7 * E * 2 + 4 * E * 4
+    del parts
+    torch.cuda.empty_cache()
+    return ms, flops, nbytes
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, min_s=12.0, max_reps=100):
     """The fp64 oracle on the host cores, timed on the headline workload
@@ -403,6 +455,19 @@ def main():
                           "algorithmic_bytes": sbytes,
                           "config": dict(sw.describe(), history_rows_per_head=max(
                               Dh * ((sw.T + Dh - 1) // Dh) for Dh in sw.D))}
+
+        bw = inputs.PREFILL_1P5B
+        key = "backward_arl_" + bw.name
+        if args.only is None or args.only == key:
+            progress("backward (ARL halves D=1 / D=64)", bw.name)
+            bms, bflops, bbytes = run_backward_arl(torch, rat, bw, max(3, args.steps // 4), 1)
+            extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bms / 1e3), "ms_per_step": bms,
+                          "TFLOPs": bflops / (bms / 1e3) / 1e12,
+                          "mfma_frac": bflops / (bms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "GBps": bbytes / (bms / 1e3) / 1e9, "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                          "config": dict(bw.describe(), D="half the batch at 1, half at 64", W=0,
+                                         recurrence="full")}
 
     if ms is None:  # a profiling run of one extra workload
         print(json.dumps({"extra": extra}))

@@ -545,7 +545,20 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
     a.L = L >= T ? 0 : L;
     a.nchunk = p.nchunk;
     a.scale = scale;
-    for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+    a.mfma = dtype == RAT_DTYPE_BF16 ? 1 : 0;
+    int64_t items = 0;
+    for (int h = 0; h < H; ++h) {
+        a.D[h] = D[h];
+        a.W[h] = W[h];
+        a.mitem[h] = (int)items;
+        if (a.mfma && W[h] == 0) {
+            // B x min(D, T) residues x blocks of 64 rows of the longest residue
+            const int64_t nb = ((T + D[h] - 1) / D[h] + 63) / 64;
+            items += (int64_t)B * std::min(D[h], T) * nb;
+        }
+        if (items >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
+    }
+    a.mitem[H] = (int)items;
     return hip_status(launch_backward(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 

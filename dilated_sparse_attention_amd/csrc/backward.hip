@@ -25,6 +25,11 @@
 //   bwd_key_kernel    one wave per key row: the state key's gradients from
 //                     the queries t = s, s + D, ... and the raw key's from
 //                     t = s .. s + W - 1;
+//   bwd_q_mfma / bwd_kv_mfma  the same for bf16 heads without a raw window,
+//                     on MFMA: a residue is a dense causal problem over the
+//                     states r, r + D, ..., so a workgroup takes 64 rows of
+//                     one residue (queries for dq, keys for dk / dv) and
+//                     walks the other side's 64-row tiles through LDS;
 //   bwd_scan_*        the reverse recurrence in chunks of kBwdChunk tokens:
 //                     per-chunk affine maps (forward state map and backward
 //                     carry map), a sequential pass over the chunks of each
@@ -32,6 +37,7 @@
 //                     from the chunk's start state and walked backwards.
 #include "rat_device.h"
 #include "rat_internal.h"
+#include "rat_mfma.h"
 
 namespace rat {
 
@@ -42,74 +48,133 @@ template <> __device__ __forceinline__ float ldx<uint16_t>(const void* p, size_t
 }
 template <> __device__ __forceinline__ float ldx<float>(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
 
-__device__ __forceinline__ float wave_sum(float x)
+// Sums over the 64 lanes of N values at once (the shuffle chains of the N
+// values interleave).
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&x)[N])
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], o);
 }
 
-// A row of d <= 128 channels across one wave: lane holds channels lane and
-// lane + 64 (zero past d).
-template <typename E>
-struct Row2 {
+// A row of d <= 128 channels across one wave: lane holds channels 2 lane and
+// 2 lane + 1 (zero past d), one 4- or 8-byte load.
+template <typename E> struct Row2;
+template <> struct Row2<uint16_t> {
     float a, b;
     __device__ __forceinline__ void load(const void* p, size_t row, int d, int lane)
     {
-        a = lane < d ? ldx<E>(p, row + lane) : 0.f;
-        b = lane + kWave < d ? ldx<E>(p, row + lane + kWave) : 0.f;
+        if (2 * lane < d) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + row + 2 * lane);
+            a = bf16_lo(w);
+            b = bf16_hi(w);
+        } else {
+            a = b = 0.f;
+        }
     }
-    __device__ __forceinline__ float dot(const Row2& o) const { return wave_sum(a * o.a + b * o.b); }
 };
+template <> struct Row2<float> {
+    float a, b;
+    __device__ __forceinline__ void load(const void* p, size_t row, int d, int lane)
+    {
+        if (2 * lane < d) {
+            const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + row + 2 * lane);
+            a = w.x;
+            b = w.y;
+        } else {
+            a = b = 0.f;
+        }
+    }
+};
+template <typename E>
+__device__ __forceinline__ float part(const Row2<E>& x, const Row2<E>& y) { return fmaf(x.a, y.a, x.b * y.b); }
+
+constexpr int kBwdGroup = 4;  // keys (or queries) per step of a row's loop: loads issued together
 
 // ---------------------------------------------------------------- attention
 template <typename E>
 __global__ __launch_bounds__(kWave) void bwd_query_kernel(BwdArgs a)
 {
+    constexpr int G = kBwdGroup;
     const int lane = threadIdx.x;
     const int t = blockIdx.x % a.T;
     const int bh = blockIdx.x / a.T;
     const int h = bh % a.H, b = bh / a.H;
     const int d = a.d, D = a.D[h], W = a.W[h];
+    if (a.mfma && W == 0) return;  // the MFMA kernels take this head
     const size_t pitch = (size_t)a.H * d;
     const size_t base = ((size_t)b * a.T * a.H + h) * d;  // row 0 of (b, h)
     const size_t rt = base + (size_t)t * pitch;
     Row2<E> q, go;
     q.load(a.q, rt, d, lane);
     go.load(a.dout, rt, d, lane);
+    // key j: the state at t - jD (j < nd), then the raw token at t - (j - nd)
+    const int nd = t / D + 1, nk = nd + min(W, t + 1);
+    auto load_key = [&](int j, Row2<E>& kk, Row2<E>& vv) {
+        if (j < nd) {
+            const size_t r = base + (size_t)(t - j * D) * pitch;
+            kk.load(a.ks, r, d, lane);
+            vv.load(a.vs, r, d, lane);
+        } else if (j < nk) {
+            const size_t r = base + (size_t)(t - (j - nd)) * pitch;
+            kk.load(a.k, r, d, lane);
+            vv.load(a.v, r, d, lane);
+        } else {
+            kk.a = kk.b = vv.a = vv.b = 0.f;
+        }
+    };
     // pass 1: log-sum-exp of the logits and delta = sum_j p_j dp_j
     float m = -INFINITY, l = 0.f, u = 0.f;  // u: sum_j e^{z_j - m} dp_j
-    auto stat = [&](const void* kp, const void* vp, size_t row) {
-        Row2<E> kk, vv;
-        kk.load(kp, row, d, lane);
-        vv.load(vp, row, d, lane);
-        const float z = q.dot(kk) * a.scale;
-        const float dp = go.dot(vv);
-        const float mn = fmaxf(m, z);
-        const float r = __expf(m - mn), e = __expf(z - mn);
-        l = fmaf(l, r, e);
-        u = fmaf(u, r, e * dp);
-        m = mn;
-    };
-    for (int s = t; s >= 0; s -= D) stat(a.ks, a.vs, base + (size_t)s * pitch);
-    for (int w = 0; w < W && t - w >= 0; ++w) stat(a.k, a.v, base + (size_t)(t - w) * pitch);
+    for (int j0 = 0; j0 < nk; j0 += G) {
+        Row2<E> kk[G], vv[G];
+        float x[2 * G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) load_key(j0 + i, kk[i], vv[i]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            x[2 * i] = part(q, kk[i]);
+            x[2 * i + 1] = part(go, vv[i]);
+        }
+        wave_sum_n(x);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            if (j0 + i < nk) {
+                const float z = x[2 * i] * a.scale;
+                const float mn = fmaxf(m, z);
+                const float r = __expf(m - mn), e = __expf(z - mn);
+                l = fmaf(l, r, e);
+                u = fmaf(u, r, e * x[2 * i + 1]);
+                m = mn;
+            }
+        }
+    }
     const float lse = m + __logf(l);
     const float delta = u / l;
     // pass 2: dq = scale sum_j p_j (dp_j - delta) kappa_j
     float ga = 0.f, gb = 0.f;
-    auto grad = [&](const void* kp, const void* vp, size_t row) {
-        Row2<E> kk, vv;
-        kk.load(kp, row, d, lane);
-        vv.load(vp, row, d, lane);
-        const float p = __expf(q.dot(kk) * a.scale - lse);
-        const float ds = p * (go.dot(vv) - delta) * a.scale;
-        ga = fmaf(ds, kk.a, ga);
-        gb = fmaf(ds, kk.b, gb);
-    };
-    for (int s = t; s >= 0; s -= D) grad(a.ks, a.vs, base + (size_t)s * pitch);
-    for (int w = 0; w < W && t - w >= 0; ++w) grad(a.k, a.v, base + (size_t)(t - w) * pitch);
-    if (lane < d) a.dq[rt + lane] = ga;
-    if (lane + kWave < d) a.dq[rt + lane + kWave] = gb;
+    for (int j0 = 0; j0 < nk; j0 += G) {
+        Row2<E> kk[G], vv[G];
+        float x[2 * G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) load_key(j0 + i, kk[i], vv[i]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            x[2 * i] = part(q, kk[i]);
+            x[2 * i + 1] = part(go, vv[i]);
+        }
+        wave_sum_n(x);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            // keys past the list are zero rows: their ds multiplies a zero row
+            const float p = __expf(x[2 * i] * a.scale - lse);
+            const float ds = p * (x[2 * i + 1] - delta) * a.scale;
+            ga = fmaf(ds, kk[i].a, ga);
+            gb = fmaf(ds, kk[i].b, gb);
+        }
+    }
+    if (2 * lane < d) *reinterpret_cast<float2*>(a.dq + rt + 2 * lane) = float2{ga, gb};
     if (lane == 0) {
         const size_t r = ((size_t)b * a.T + t) * a.H + h;
         a.lse[r] = lse;
@@ -120,6 +185,7 @@ __global__ __launch_bounds__(kWave) void bwd_query_kernel(BwdArgs a)
 template <typename E>
 __global__ __launch_bounds__(kWave) void bwd_key_kernel(BwdArgs a)
 {
+    constexpr int G = kBwdGroup;
     const int lane = threadIdx.x;
     const int s = blockIdx.x % a.T;
     const int bh = blockIdx.x / a.T;
@@ -128,38 +194,353 @@ __global__ __launch_bounds__(kWave) void bwd_key_kernel(BwdArgs a)
     const size_t pitch = (size_t)a.H * d;
     const size_t base = ((size_t)b * a.T * a.H + h) * d;
     const size_t rs = base + (size_t)s * pitch;
-    // one key row against the queries that see it
-    auto key_grads = [&](const void* kp, const void* vp, int t0, int t1, int step, float* dk_out, float* dv_out) {
+    // one key row against the nq queries t = s + j step that see it
+    auto key_grads = [&](const void* kp, const void* vp, int nq, int step, float* dk_out, float* dv_out) {
         Row2<E> kk, vv;
         kk.load(kp, rs, d, lane);
         vv.load(vp, rs, d, lane);
         float ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
-        for (int t = t0; t <= t1; t += step) {
-            const size_t rt = base + (size_t)t * pitch;
-            const size_t r = ((size_t)b * a.T + t) * a.H + h;
-            Row2<E> q, go;
-            q.load(a.q, rt, d, lane);
-            go.load(a.dout, rt, d, lane);
-            const float p = __expf(q.dot(kk) * a.scale - a.lse[r]);
-            const float ds = p * (go.dot(vv) - a.delta[r]) * a.scale;
-            ka = fmaf(ds, q.a, ka);
-            kb = fmaf(ds, q.b, kb);
-            va = fmaf(p, go.a, va);
-            vb = fmaf(p, go.b, vb);
+        for (int j0 = 0; j0 < nq; j0 += G) {
+            Row2<E> q[G], go[G];
+            float lse[G], dl[G], x[2 * G];
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                if (j0 + i < nq) {
+                    const int t = s + (j0 + i) * step;
+                    const size_t rt = base + (size_t)t * pitch;
+                    const size_t r = ((size_t)b * a.T + t) * a.H + h;
+                    q[i].load(a.q, rt, d, lane);
+                    go[i].load(a.dout, rt, d, lane);
+                    lse[i] = a.lse[r];
+                    dl[i] = a.delta[r];
+                } else {
+                    q[i].a = q[i].b = go[i].a = go[i].b = 0.f;
+                    lse[i] = INFINITY;  // p = 0
+                    dl[i] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                x[2 * i] = part(q[i], kk);
+                x[2 * i + 1] = part(go[i], vv);
+            }
+            wave_sum_n(x);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float p = __expf(x[2 * i] * a.scale - lse[i]);
+                const float ds = p * (x[2 * i + 1] - dl[i]) * a.scale;
+                ka = fmaf(ds, q[i].a, ka);
+                kb = fmaf(ds, q[i].b, kb);
+                va = fmaf(p, go[i].a, va);
+                vb = fmaf(p, go[i].b, vb);
+            }
         }
-        if (lane < d) {
-            dk_out[rs + lane] = ka;
-            dv_out[rs + lane] = va;
-        }
-        if (lane + kWave < d) {
-            dk_out[rs + lane + kWave] = kb;
-            dv_out[rs + lane + kWave] = vb;
+        if (2 * lane < d) {
+            *reinterpret_cast<float2*>(dk_out + rs + 2 * lane) = float2{ka, kb};
+            *reinterpret_cast<float2*>(dv_out + rs + 2 * lane) = float2{va, vb};
         }
     };
-    // the state at s: queries s, s + D, ... (< T)
-    key_grads(a.ks, a.vs, s, a.T - 1, D, a.dks, a.dvs);
-    // the raw token at s: queries s .. s + W - 1 (an empty range writes zeros)
-    key_grads(a.k, a.v, s, min(s + W - 1, a.T - 1), 1, a.dk, a.dv);
+    // the state at s: queries s, s + D, ... (< T); the MFMA kernels take
+    // heads without a raw window
+    if (!(a.mfma && W == 0)) key_grads(a.ks, a.vs, (a.T - 1 - s) / D + 1, D, a.dks, a.dvs);
+    // the raw token at s: queries s .. s + W - 1 (< T); none writes zeros
+    key_grads(a.k, a.v, min(W, a.T - s), 1, a.dk, a.dv);
+}
+
+
+// ---------------------------------------------------------------- MFMA path
+// Work item: (head h with W = 0, batch b, residue r, block of 64 rows of
+// that residue); items of head h start at a.mitem[h].
+constexpr int kBwdRows = 64;
+
+struct BwdItem {
+    int b, h, r, blk, M, D;
+    bool valid;
+};
+
+__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int item)
+{
+    BwdItem it;
+    int h = 0;
+    while (h + 1 < a.H && item >= a.mitem[h + 1]) ++h;
+    it.h = h;
+    it.D = a.D[h];
+    const int Dr = min(it.D, a.T);
+    const int nb = ((a.T + it.D - 1) / it.D + kBwdRows - 1) / kBwdRows;  // blocks of the longest residue
+    const int local = item - a.mitem[h];
+    it.blk = local % nb;
+    const int rest = local / nb;
+    it.r = rest % Dr;
+    it.b = rest / Dr;
+    it.M = (a.T - it.r + it.D - 1) / it.D;
+    it.valid = item < a.mitem[h + 1] && it.blk * kBwdRows < it.M;
+    return it;
+}
+
+// element offset of row `row` of residue r of (b, h) in a [B][T][H][DK] tensor
+template <int DK>
+__device__ __forceinline__ size_t res_row(const BwdArgs& a, const BwdItem& it, int row)
+{
+    return (((size_t)it.b * a.T + (it.r + (size_t)row * it.D)) * a.H + it.h) * DK;
+}
+
+// 64 rows (row0 ..) of a residue into a swizzled LDS tile; rows past M are zero
+template <int DK>
+__device__ __forceinline__ void load_rows(lds_char* tile, const void* src, const BwdArgs& a, const BwdItem& it,
+                                          int row0)
+{
+    constexpr int CH = Geo<DK>::CH;
+    for (int idx = threadIdx.x; idx < kBwdRows * CH; idx += 4 * kWave) {
+        const int row = idx / CH, c = idx % CH;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row0 + row < it.M)
+            val = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + res_row<DK>(a, it, row0 + row) + c * 8);
+        *reinterpret_cast<u32x4*>(tile + swz<DK>(row, c)) = val;
+    }
+}
+
+// B-operand fragments of one row (lane (g, i): the row of i, dims 8g + 32ks)
+template <int DK>
+__device__ __forceinline__ void load_frag(bf16x8 (&f)[Geo<DK>::KS], const void* src, size_t row_el, bool valid)
+{
+    const int g = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
+    for (int ks = 0; ks < Geo<DK>::KS; ++ks)
+        f[ks] = valid ? *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(src) + row_el + 8 * g + 32 * ks)
+                      : bf16x8{};
+}
+
+// A-operand offset of the transposing reads (lane (g, i): rows 4g .. 4g+3
+// of a 16-row group, dims 4 (i % 4) ..; XOR in the dim block as db << 5)
+template <int DK>
+__device__ __forceinline__ int tr_offset()
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4, i = lane & 15;
+    const int dim = 4 * (i & 3);
+    return swz<DK>(4 * g + (i >> 2), dim >> 3) + (dim & 7) * 2;
+}
+
+// A operand (rows = dims 16 db .. of a 16-dim block, k = the 32 rows of
+// half hh of a 64-row tile in the order {4g + j, 16 + 4g + j})
+template <int DK>
+__device__ __forceinline__ bf16x8 tr_frag(const lds_char* tile, int off, int db, int hh)
+{
+    const lds_char* p = tile + (off ^ (db << 5)) + hh * 32 * Geo<DK>::ROWB;
+    const shortx4 x0 = lds_tr(p);
+    const shortx4 x1 = lds_tr(p + 16 * Geo<DK>::ROWB);
+    typedef short shortx8 __attribute__((ext_vector_type(8)));
+    const shortx8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// dS enters the MFMA products as a pair of bf16 values, hi = bf16(x) and
+// lo = bf16(x - hi) (about 16 mantissa bits together): its terms have both
+// signs and sum to zero over a query's keys, so a single bf16 rounding of
+// each would dominate sums that cancel.
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int e)
+{
+    const __bf16 h = (__bf16)x;
+    hi[e] = h;
+    lo[e] = (__bf16)(x - (float)h);
+}
+
+// dq (and each query row's log-sum-exp and delta): wave w owns queries
+// 16w .. 16w+15 of the block; lane (g, i) query i.  Scores are S^T = K Q^T
+// (lane: keys 16kb + 4g + j of its query), dP^T = V dO^T, and
+// dQ^T += K^T dS^T with dS^T packed to bf16 as the B operand.
+template <int DK>
+__global__ __launch_bounds__(4 * kWave) void bwd_q_mfma(BwdArgs a)
+{
+    typedef Geo<DK> G;
+    __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
+    __shared__ __attribute__((aligned(1024))) char vt[kBwdRows * G::ROWB];
+    const BwdItem it = bwd_item(a, blockIdx.x);
+    if (!it.valid) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int g = lane >> 4, i = lane & 15;
+    const float c = a.scale * kLog2e;
+    const int qr = it.blk * kBwdRows + 16 * wv + i;
+    const bool qvalid = qr < it.M;
+    const size_t qe = qvalid ? res_row<DK>(a, it, qr) : 0;
+    bf16x8 qf[G::KS], gf[G::KS];
+    load_frag<DK>(qf, a.q, qe, qvalid);
+    load_frag<DK>(gf, a.dout, qe, qvalid);
+    const int ntile = it.blk + 1;  // key tiles up to the block's last query
+    auto scores = [&](floatx4 (&st)[4], floatx4 (&dpt)[4]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            st[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            dpt[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                st[kb] = mfma16(lds_b128(kt + swz<DK>(16 * kb + i, g + 4 * ks)), qf[ks], st[kb]);
+                dpt[kb] = mfma16(lds_b128(vt + swz<DK>(16 * kb + i, g + 4 * ks)), gf[ks], dpt[kb]);
+            }
+        }
+    };
+    // sweep 1: per lane group, (max, sum of e^(z - max), sum of e^(z - max) dp) over its keys
+    float m = -INFINITY, l = 0.f, u = 0.f;
+    for (int t = 0; t < ntile; ++t) {
+        __syncthreads();
+        load_rows<DK>(kt, a.ks, a, it, t * kBwdRows);
+        load_rows<DK>(vt, a.vs, a, it, t * kBwdRows);
+        __syncthreads();
+        floatx4 st[4], dpt[4];
+        scores(st, dpt);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
+                if (kr <= qr) {
+                    const float z = st[kb][j] * c;
+                    const float mn = fmaxf(m, z);
+                    const float sc = __builtin_amdgcn_exp2f(m - mn), e = __builtin_amdgcn_exp2f(z - mn);
+                    l = fmaf(l, sc, e);
+                    u = fmaf(u, sc, e * dpt[kb][j]);
+                    m = mn;
+                }
+            }
+    }
+    // combine the four lane groups of the query
+    float mall = m;
+    mall = fmaxf(mall, __shfl_xor(mall, 16));
+    mall = fmaxf(mall, __shfl_xor(mall, 32));
+    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mall);
+    float lall = l * w, uall = u * w;
+    lall += __shfl_xor(lall, 16);
+    lall += __shfl_xor(lall, 32);
+    uall += __shfl_xor(uall, 16);
+    uall += __shfl_xor(uall, 32);
+    const float lse2 = mall + __log2f(lall);  // log2-domain log-sum-exp
+    const float delta = uall / lall;
+    // sweep 2: dQ^T
+    const int toff = tr_offset<DK>();
+    floatx4 dqt[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) dqt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < ntile; ++t) {
+        __syncthreads();
+        load_rows<DK>(kt, a.ks, a, it, t * kBwdRows);
+        load_rows<DK>(vt, a.vs, a, it, t * kBwdRows);
+        __syncthreads();
+        floatx4 st[4], dpt[4];
+        scores(st, dpt);
+        bf16x8 sh[2], sl[2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
+                const float p = kr <= qr ? __builtin_amdgcn_exp2f(fmaf(st[kb][j], c, -lse2)) : 0.f;
+                split_bf16(p * (dpt[kb][j] - delta) * a.scale, sh[kb >> 1], sl[kb >> 1], 4 * (kb & 1) + j);
+            }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                const bf16x8 kf = tr_frag<DK>(kt, toff, db, hh);
+                dqt[db] = mfma16(kf, sh[hh], dqt[db]);
+                dqt[db] = mfma16(kf, sl[hh], dqt[db]);
+            }
+    }
+    if (qvalid) {
+        const size_t o = qe;  // same [B][T][H][DK] position, fp32
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+            *reinterpret_cast<floatx4*>(a.dq + o + 16 * db + 4 * g) = dqt[db];
+        if (g == 0) {
+            const size_t rrow = ((size_t)it.b * a.T + it.r + (size_t)qr * it.D) * a.H + it.h;
+            a.lse[rrow] = lse2 * 0.6931471805599453f;  // natural log
+            a.delta[rrow] = delta;
+        }
+    }
+}
+
+// dk, dv of the states: wave w owns keys 16w .. 16w+15 of the block; lane
+// (g, i) key i.  Scores S = Q K^T (lane: queries 16qb + 4g + j of its key),
+// dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS with P and dS packed to
+// bf16 as B operands.
+template <int DK>
+__global__ __launch_bounds__(4 * kWave) void bwd_kv_mfma(BwdArgs a)
+{
+    typedef Geo<DK> G;
+    __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
+    __shared__ __attribute__((aligned(1024))) char gt[kBwdRows * G::ROWB];
+    __shared__ float s_lse2[kBwdRows], s_dl[kBwdRows];
+    const BwdItem it = bwd_item(a, blockIdx.x);
+    if (!it.valid) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int g = lane >> 4, i = lane & 15;
+    const float c = a.scale * kLog2e;
+    const int kr = it.blk * kBwdRows + 16 * wv + i;
+    const bool kvalid = kr < it.M;
+    const size_t ke = kvalid ? res_row<DK>(a, it, kr) : 0;
+    bf16x8 kf[G::KS], vf[G::KS];
+    load_frag<DK>(kf, a.ks, ke, kvalid);
+    load_frag<DK>(vf, a.vs, ke, kvalid);
+    const int toff = tr_offset<DK>();
+    floatx4 dkt[G::DB], dvt[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        dkt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dvt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int ntile = (it.M + kBwdRows - 1) / kBwdRows;
+    for (int t = it.blk; t < ntile; ++t) {  // query tiles from the block's own on
+        __syncthreads();
+        load_rows<DK>(qt, a.q, a, it, t * kBwdRows);
+        load_rows<DK>(gt, a.dout, a, it, t * kBwdRows);
+        if (threadIdx.x < kBwdRows) {
+            const int q = t * kBwdRows + threadIdx.x;
+            if (q < it.M) {
+                const size_t rrow = ((size_t)it.b * a.T + it.r + (size_t)q * it.D) * a.H + it.h;
+                s_lse2[threadIdx.x] = a.lse[rrow] * kLog2e;
+                s_dl[threadIdx.x] = a.delta[rrow];
+            } else {
+                s_lse2[threadIdx.x] = INFINITY;  // p = 0
+                s_dl[threadIdx.x] = 0.f;
+            }
+        }
+        __syncthreads();
+        bf16x8 pb[2], sh[2], sl[2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            floatx4 sv = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                sv = mfma16(lds_b128(qt + swz<DK>(16 * qb + i, g + 4 * ks)), kf[ks], sv);
+                dp = mfma16(lds_b128(gt + swz<DK>(16 * qb + i, g + 4 * ks)), vf[ks], dp);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ql = 16 * qb + 4 * g + j;
+                const int q = t * kBwdRows + ql;
+                const float p = q >= kr ? __builtin_amdgcn_exp2f(fmaf(sv[j], c, -s_lse2[ql])) : 0.f;
+                pb[qb >> 1][4 * (qb & 1) + j] = (__bf16)p;
+                split_bf16(p * (dp[j] - s_dl[ql]) * a.scale, sh[qb >> 1], sl[qb >> 1], 4 * (qb & 1) + j);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                dvt[db] = mfma16(tr_frag<DK>(gt, toff, db, hh), pb[hh], dvt[db]);
+                const bf16x8 qf = tr_frag<DK>(qt, toff, db, hh);
+                dkt[db] = mfma16(qf, sh[hh], dkt[db]);
+                dkt[db] = mfma16(qf, sl[hh], dkt[db]);
+            }
+    }
+    if (kvalid) {
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) {
+            *reinterpret_cast<floatx4*>(a.dks + ke + 16 * db + 4 * g) = dkt[db];
+            *reinterpret_cast<floatx4*>(a.dvs + ke + 16 * db + 4 * g) = dvt[db];
+        }
+    }
 }
 
 // ---------------------------------------------------------------- recurrence
@@ -300,7 +681,16 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
     const unsigned cells = (unsigned)(((size_t)a.nchunk * a.B * N + 255) / 256);
     const unsigned chans = (unsigned)(((size_t)a.B * N + 255) / 256);
     if (bf16) {
+        const unsigned items = (unsigned)a.mitem[a.H];
+        if (a.mfma && items > 0) {
+            if (a.d == 128) hipLaunchKernelGGL(bwd_q_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
+            else hipLaunchKernelGGL(bwd_q_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
+        }
         hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
+        if (a.mfma && items > 0) {
+            if (a.d == 128) hipLaunchKernelGGL(bwd_kv_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
+            else hipLaunchKernelGGL(bwd_kv_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
+        }
         hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);

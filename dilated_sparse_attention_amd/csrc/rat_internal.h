@@ -202,8 +202,10 @@ struct BwdArgs {
     int L;             // RESTART period, 0 for the full recurrence
     int nchunk;        // ceil(T / kBwdChunk)
     float scale;
+    int mfma;          // bf16: heads without a raw window run on the MFMA kernels
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
+    int mitem[kAttnMaxHeads + 1];  // first MFMA work item of each head; [H] = total
 };
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
 
