@@ -546,6 +546,7 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
     a.nchunk = p.nchunk;
     a.scale = scale;
     a.mfma = dtype == RAT_DTYPE_BF16 ? 1 : 0;
+    a.raw = (any_w || !a.mfma) ? 1 : 0;
     int64_t items = 0;
     for (int h = 0; h < H; ++h) {
         a.D[h] = D[h];

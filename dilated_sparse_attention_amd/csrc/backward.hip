@@ -299,6 +299,37 @@ __device__ __forceinline__ void load_rows(lds_char* tile, const void* src, const
     }
 }
 
+// The same 64 rows staged through registers, so that the next tile's loads
+// are in flight while the current one is computed: load, then (after the
+// barrier that frees the tile) store.
+template <int DK>
+struct TileRegs {
+    static constexpr int N = kBwdRows * Geo<DK>::CH / (4 * kWave);  // 16-byte chunks per thread
+    u32x4 v[N];
+    __device__ __forceinline__ void load(const void* src, const BwdArgs& a, const BwdItem& it, int row0)
+    {
+        constexpr int CH = Geo<DK>::CH;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int idx = threadIdx.x + n * 4 * kWave;
+            const int row = idx / CH, c = idx % CH;
+            v[n] = u32x4{0u, 0u, 0u, 0u};
+            if (row0 + row < it.M)
+                v[n] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + res_row<DK>(a, it, row0 + row) +
+                                                       c * 8);
+        }
+    }
+    __device__ __forceinline__ void store(lds_char* tile) const
+    {
+        constexpr int CH = Geo<DK>::CH;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int idx = threadIdx.x + n * 4 * kWave;
+            *reinterpret_cast<u32x4*>(tile + swz<DK>(idx / CH, idx % CH)) = v[n];
+        }
+    }
+};
+
 // B-operand fragments of one row (lane (g, i): the row of i, dims 8g + 32ks)
 template <int DK>
 __device__ __forceinline__ void load_frag(bf16x8 (&f)[Geo<DK>::KS], const void* src, size_t row_el, bool valid)
@@ -350,7 +381,7 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
 // (lane: keys 16kb + 4g + j of its query), dP^T = V dO^T, and
 // dQ^T += K^T dS^T with dS^T packed to bf16 as the B operand.
 template <int DK>
-__global__ __launch_bounds__(4 * kWave) void bwd_q_mfma(BwdArgs a)
+__global__ __launch_bounds__(4 * kWave, 2) void bwd_q_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
@@ -380,13 +411,25 @@ __global__ __launch_bounds__(4 * kWave) void bwd_q_mfma(BwdArgs a)
             }
         }
     };
+    // key / value tiles t = 0 .. 2 ntile - 1 (both sweeps) through registers
+    TileRegs<DK> rk, rv;
+    rk.load(a.ks, a, it, 0);
+    rv.load(a.vs, a, it, 0);
+    auto next_tile = [&](int t) {  // tile t into LDS, tile t + 1 into registers
+        __syncthreads();
+        rk.store(kt);
+        rv.store(vt);
+        __syncthreads();
+        const int tn = (t + 1) % ntile;
+        if (t + 1 < 2 * ntile) {
+            rk.load(a.ks, a, it, tn * kBwdRows);
+            rv.load(a.vs, a, it, tn * kBwdRows);
+        }
+    };
     // sweep 1: per lane group, (max, sum of e^(z - max), sum of e^(z - max) dp) over its keys
     float m = -INFINITY, l = 0.f, u = 0.f;
     for (int t = 0; t < ntile; ++t) {
-        __syncthreads();
-        load_rows<DK>(kt, a.ks, a, it, t * kBwdRows);
-        load_rows<DK>(vt, a.vs, a, it, t * kBwdRows);
-        __syncthreads();
+        next_tile(t);
         floatx4 st[4], dpt[4];
         scores(st, dpt);
 #pragma unroll
@@ -422,10 +465,7 @@ __global__ __launch_bounds__(4 * kWave) void bwd_q_mfma(BwdArgs a)
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) dqt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < ntile; ++t) {
-        __syncthreads();
-        load_rows<DK>(kt, a.ks, a, it, t * kBwdRows);
-        load_rows<DK>(vt, a.vs, a, it, t * kBwdRows);
-        __syncthreads();
+        next_tile(ntile + t);
         floatx4 st[4], dpt[4];
         scores(st, dpt);
         bf16x8 sh[2], sl[2];
@@ -464,7 +504,7 @@ __global__ __launch_bounds__(4 * kWave) void bwd_q_mfma(BwdArgs a)
 // dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS with P and dS packed to
 // bf16 as B operands.
 template <int DK>
-__global__ __launch_bounds__(4 * kWave) void bwd_kv_mfma(BwdArgs a)
+__global__ __launch_bounds__(4 * kWave, 2) void bwd_kv_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
@@ -490,22 +530,32 @@ __global__ __launch_bounds__(4 * kWave) void bwd_kv_mfma(BwdArgs a)
         dvt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const int ntile = (it.M + kBwdRows - 1) / kBwdRows;
-    for (int t = it.blk; t < ntile; ++t) {  // query tiles from the block's own on
+    // query tiles from the block's own on, staged through registers
+    TileRegs<DK> rq, rg;
+    float rl = INFINITY, rd = 0.f;  // the tile's (lse, delta) of row threadIdx.x (< 64)
+    auto fetch = [&](int t) {
+        rq.load(a.q, a, it, t * kBwdRows);
+        rg.load(a.dout, a, it, t * kBwdRows);
+        const int q = t * kBwdRows + threadIdx.x;
+        rl = INFINITY;  // rows past the residue: p = 0
+        rd = 0.f;
+        if (threadIdx.x < kBwdRows && q < it.M) {
+            const size_t rrow = ((size_t)it.b * a.T + it.r + (size_t)q * it.D) * a.H + it.h;
+            rl = a.lse[rrow] * kLog2e;
+            rd = a.delta[rrow];
+        }
+    };
+    fetch(it.blk);
+    for (int t = it.blk; t < ntile; ++t) {
         __syncthreads();
-        load_rows<DK>(qt, a.q, a, it, t * kBwdRows);
-        load_rows<DK>(gt, a.dout, a, it, t * kBwdRows);
+        rq.store(qt);
+        rg.store(gt);
         if (threadIdx.x < kBwdRows) {
-            const int q = t * kBwdRows + threadIdx.x;
-            if (q < it.M) {
-                const size_t rrow = ((size_t)it.b * a.T + it.r + (size_t)q * it.D) * a.H + it.h;
-                s_lse2[threadIdx.x] = a.lse[rrow] * kLog2e;
-                s_dl[threadIdx.x] = a.delta[rrow];
-            } else {
-                s_lse2[threadIdx.x] = INFINITY;  // p = 0
-                s_dl[threadIdx.x] = 0.f;
-            }
+            s_lse2[threadIdx.x] = rl;
+            s_dl[threadIdx.x] = rd;
         }
         __syncthreads();
+        if (t + 1 < ntile) fetch(t + 1);
         bf16x8 pb[2], sh[2], sl[2];
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
@@ -607,28 +657,58 @@ __global__ __launch_bounds__(256) void bwd_scan_carry_kernel(BwdArgs a)
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)a.B * N) return;
     const size_t stride = (size_t)a.B * N;  // between chunks
+    const float* __restrict__ maps = a.maps;
+    float* __restrict__ carry = a.carry;
+    // U chunks' maps are loaded before any of them is combined: the chain
+    // is one fma per chunk, the loads are what take time
+    constexpr int U = 8;
     float hk = 0.f, hv = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-        const size_t cell = (size_t)c * stride + idx;
-        a.carry[cell * 4 + 0] = hk;
-        a.carry[cell * 4 + 1] = hv;
-        const float* m = a.maps + cell * 5;
-        hk = fmaf(m[0], hk, m[1]);
-        hv = fmaf(m[0], hv, m[2]);
+    for (int c0 = 0; c0 < a.nchunk; c0 += U) {
+        float A[U], K[U], V[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t cell = (size_t)min(c0 + u, a.nchunk - 1) * stride + idx;
+            A[u] = maps[cell * 5 + 0];
+            K[u] = maps[cell * 5 + 1];
+            V[u] = maps[cell * 5 + 2];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u < a.nchunk) {
+                const size_t cell = (size_t)(c0 + u) * stride + idx;
+                carry[cell * 4 + 0] = hk;
+                carry[cell * 4 + 1] = hv;
+                hk = fmaf(A[u], hk, K[u]);
+                hv = fmaf(A[u], hv, V[u]);
+            }
+        }
     }
     float mk = 0.f, mv = 0.f;
-    for (int c = a.nchunk - 1; c >= 0; --c) {
-        const size_t cell = (size_t)c * stride + idx;
-        a.carry[cell * 4 + 2] = mk;
-        a.carry[cell * 4 + 3] = mv;
-        const float* m = a.maps + cell * 5;
-        mk = fmaf(m[0], mk, m[3]);
-        mv = fmaf(m[0], mv, m[4]);
+    for (int c0 = a.nchunk - 1; c0 >= 0; c0 -= U) {
+        float A[U], Bk[U], Bv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t cell = (size_t)max(c0 - u, 0) * stride + idx;
+            A[u] = maps[cell * 5 + 0];
+            Bk[u] = maps[cell * 5 + 3];
+            Bv[u] = maps[cell * 5 + 4];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 - u >= 0) {
+                const size_t cell = (size_t)(c0 - u) * stride + idx;
+                carry[cell * 4 + 2] = mk;
+                carry[cell * 4 + 3] = mv;
+                mk = fmaf(A[u], mk, Bk[u]);
+                mv = fmaf(A[u], mv, Bv[u]);
+            }
+        }
     }
 }
 
 // Per chunk: the fp32 states again from the chunk's start state, then the
-// chunk walked backwards.  dk / dv already hold the raw-window gradients.
+// chunk walked backwards.  With a raw window somewhere, dk / dv already hold
+// the raw-window gradients and are added to; otherwise they are written.
 template <typename E>
 __global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdArgs a)
 {
@@ -664,8 +744,8 @@ __global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdArgs a)
             forget_gate(ldx<E>(a.g, x), g, gb);
             const bool cut = restart_at(a, t);
             const float lk = a.dks[x] + mk, lv = a.dvs[x] + mv;
-            a.dk[x] = fmaf(gb, lk, a.dk[x]);
-            a.dv[x] = fmaf(gb, lv, a.dv[x]);
+            a.dk[x] = a.raw ? fmaf(gb, lk, a.dk[x]) : gb * lk;
+            a.dv[x] = a.raw ? fmaf(gb, lv, a.dv[x]) : gb * lv;
             const float pk = (cut || t == 0) ? 0.f : hk[i], pv = (cut || t == 0) ? 0.f : hv[i];
             a.dg[x] = g * gb * (lk * (pk - ldx<E>(a.k, x)) + lv * (pv - ldx<E>(a.v, x)));
             mk = cut ? 0.f : g * lk;
@@ -686,12 +766,14 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
             if (a.d == 128) hipLaunchKernelGGL(bwd_q_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
             else hipLaunchKernelGGL(bwd_q_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
         }
-        hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
+        // the per-row kernels: heads with a raw window (and the raw-window
+        // gradients, zero for the other heads); none when no head has one
+        if (a.raw) hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         if (a.mfma && items > 0) {
             if (a.d == 128) hipLaunchKernelGGL(bwd_kv_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
             else hipLaunchKernelGGL(bwd_kv_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
         }
-        hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
+        if (a.raw) hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_apply_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);

@@ -203,6 +203,7 @@ struct BwdArgs {
     int nchunk;        // ceil(T / kBwdChunk)
     float scale;
     int mfma;          // bf16: heads without a raw window run on the MFMA kernels
+    int raw;           // some head has a raw window (the per-row kernels run); always 1 for fp32
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
     int mitem[kAttnMaxHeads + 1];  // first MFMA work item of each head; [H] = total
