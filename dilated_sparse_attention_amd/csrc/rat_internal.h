@@ -23,9 +23,13 @@ struct StateHist {
 // one block of channels (128 bf16 / 64 fp32: a 256-byte row segment) x
 // kScanChunk tokens; each lane holds 16 bytes of a row (8 bf16 / 4 fp32
 // channels) for kScanTpl consecutive tokens.
-constexpr int kScanWaves = 8;
+constexpr int kScanWaves = 8;  // the SLIDING L = 64 kernel's workgroup
+#ifndef RAT_SCAN_FULL_WAVES
+#define RAT_SCAN_FULL_WAVES 8
+#endif
+constexpr int kScanFullWaves = RAT_SCAN_FULL_WAVES;  // the full / RESTART kernel's workgroup
 constexpr int kScanTpl = 4;
-constexpr int kScanChunk = kScanWaves * 4 * kScanTpl;  // 4 token segments per wave
+constexpr int kScanChunk = kScanFullWaves * 4 * kScanTpl;  // 4 token segments per wave
 template <typename E> struct ScanBlock { static constexpr int value = 256 / sizeof(E); };
 
 struct ScanHeader {

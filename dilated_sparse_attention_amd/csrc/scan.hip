@@ -103,14 +103,14 @@ struct HistRow {
 };
 
 template <typename E, bool HIST>
-__global__ __launch_bounds__(kScanThreads, 4) void scan_full_kernel(ScanFullArgs a)
+__global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(ScanFullArgs a)
 {
     typedef Row16<E> R16;
     constexpr int CPL = R16::CPL;           // channels per lane
     constexpr int LPR = 16;                 // lanes per token row of the block
     constexpr int BW = LPR * CPL;           // channels per block
     constexpr int GPW = kWave / LPR;        // token segments per wave
-    constexpr int NSEG = kScanWaves * GPW;  // segments per chunk
+    constexpr int NSEG = kScanFullWaves * GPW;  // segments per chunk
     constexpr int TPL = kScanTpl;           // tokens per segment
     constexpr int CT = NSEG * TPL;          // tokens per chunk
     constexpr int C0 = BW / kWave;          // channels per lane of the single-wave steps
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
 // ---------------------------------------------------------------- launches
 hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, hipStream_t stream)
 {
-    const dim3 grid(a.nwg), block(kScanThreads);
+    const dim3 grid(a.nwg), block(kScanFullWaves * kWave);
     if (bf16 && hist) hipLaunchKernelGGL((scan_full_kernel<uint16_t, true>), grid, block, 0, stream, a);
     else if (bf16) hipLaunchKernelGGL((scan_full_kernel<uint16_t, false>), grid, block, 0, stream, a);
     else if (hist) hipLaunchKernelGGL((scan_full_kernel<float, true>), grid, block, 0, stream, a);
