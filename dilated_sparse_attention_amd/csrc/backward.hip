@@ -250,7 +250,9 @@ __global__ __launch_bounds__(kWave) void bwd_key_kernel(BwdArgs a)
 
 // ---------------------------------------------------------------- MFMA path
 // Work item: (head h with W = 0, batch b, residue r, block of 64 rows of
-// that residue); items of head h start at a.mitem[h].
+// that residue); items of head h start at a.mitem[h].  Within a head the
+// block index is outermost, in the order that puts the largest blocks first
+// (dq: a block's work grows with its index; dk / dv: it shrinks).
 constexpr int kBwdRows = 64;
 
 struct BwdItem {
@@ -258,6 +260,7 @@ struct BwdItem {
     bool valid;
 };
 
+template <bool LAST_FIRST>
 __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int item)
 {
     BwdItem it;
@@ -268,8 +271,8 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int item)
     const int Dr = min(it.D, a.T);
     const int nb = ((a.T + it.D - 1) / it.D + kBwdRows - 1) / kBwdRows;  // blocks of the longest residue
     const int local = item - a.mitem[h];
-    it.blk = local % nb;
-    const int rest = local / nb;
+    const int level = local / (a.B * Dr), rest = local % (a.B * Dr);
+    it.blk = LAST_FIRST ? nb - 1 - level : level;
     it.r = rest % Dr;
     it.b = rest / Dr;
     it.M = (a.T - it.r + it.D - 1) / it.D;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_q_mfma(BwdArgs a)
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char vt[kBwdRows * G::ROWB];
-    const BwdItem it = bwd_item(a, blockIdx.x);
+    const BwdItem it = bwd_item<true>(a, blockIdx.x);
     if (!it.valid) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_kv_mfma(BwdArgs a)
     __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char gt[kBwdRows * G::ROWB];
     __shared__ float s_lse2[kBwdRows], s_dl[kBwdRows];
-    const BwdItem it = bwd_item(a, blockIdx.x);
+    const BwdItem it = bwd_item<false>(a, blockIdx.x);
     if (!it.valid) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -650,59 +653,85 @@ __global__ __launch_bounds__(256) void bwd_scan_maps_kernel(BwdArgs a)
 }
 
 // Per (b, channel), over its chunks: the state before each chunk (forward)
-// and the carry into each chunk's last token (backward).
+// and the carry into each chunk's last token (backward).  A workgroup takes
+// 16 channels x 16 runs of consecutive chunks: each thread composes the maps
+// of its run, the runs' carries are chained through LDS, then each thread
+// walks its run again writing the per-chunk carries.
+constexpr int kCarryRuns = 16;
 __global__ __launch_bounds__(256) void bwd_scan_carry_kernel(BwdArgs a)
 {
+    __shared__ float s_run[kCarryRuns][16][5];   // run maps (A, K, V, Bk, Bv)
+    __shared__ float s_in[kCarryRuns][16][4];    // state before / carry into each run
     const size_t N = (size_t)a.H * a.d;
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)a.B * N) return;
+    const int ch = threadIdx.x % 16, run = threadIdx.x / 16;
+    const size_t idx = (size_t)blockIdx.x * 16 + ch;  // (b, channel)
+    const bool valid = idx < (size_t)a.B * N;
     const size_t stride = (size_t)a.B * N;  // between chunks
     const float* __restrict__ maps = a.maps;
     float* __restrict__ carry = a.carry;
-    // U chunks' maps are loaded before any of them is combined: the chain
-    // is one fma per chunk, the loads are what take time
-    constexpr int U = 8;
-    float hk = 0.f, hv = 0.f;
-    for (int c0 = 0; c0 < a.nchunk; c0 += U) {
-        float A[U], K[U], V[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t cell = (size_t)min(c0 + u, a.nchunk - 1) * stride + idx;
-            A[u] = maps[cell * 5 + 0];
-            K[u] = maps[cell * 5 + 1];
-            V[u] = maps[cell * 5 + 2];
+    const int per = (a.nchunk + kCarryRuns - 1) / kCarryRuns;
+    const int c0 = run * per, c1 = min(c0 + per, a.nchunk);
+    // compose the run: forward h -> A h + (K, V) over c0 .. c1 - 1, backward
+    // mu -> A mu + (Bk, Bv) over c1 - 1 .. c0 (the same A)
+    float A = 1.f, K = 0.f, V = 0.f, Bk = 0.f, Bv = 0.f;
+    if (valid) {
+        for (int c = c0; c < c1; ++c) {
+            const float* m = maps + ((size_t)c * stride + idx) * 5;
+            K = fmaf(m[0], K, m[1]);
+            V = fmaf(m[0], V, m[2]);
+            A *= m[0];
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (c0 + u < a.nchunk) {
-                const size_t cell = (size_t)(c0 + u) * stride + idx;
-                carry[cell * 4 + 0] = hk;
-                carry[cell * 4 + 1] = hv;
-                hk = fmaf(A[u], hk, K[u]);
-                hv = fmaf(A[u], hv, V[u]);
-            }
+        // the carry out of chunk c0 weighs chunk c's own term by the gates
+        // of the chunks before it in the run: Bk = sum_c (prod_{c0 <= c' < c} A_c') Bk_c
+        float Ar = 1.f;
+        for (int c = c0; c < c1; ++c) {
+            const float* m = maps + ((size_t)c * stride + idx) * 5;
+            Bk = fmaf(Ar, m[3], Bk);
+            Bv = fmaf(Ar, m[4], Bv);
+            Ar *= m[0];
         }
     }
-    float mk = 0.f, mv = 0.f;
-    for (int c0 = a.nchunk - 1; c0 >= 0; c0 -= U) {
-        float A[U], Bk[U], Bv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t cell = (size_t)max(c0 - u, 0) * stride + idx;
-            A[u] = maps[cell * 5 + 0];
-            Bk[u] = maps[cell * 5 + 3];
-            Bv[u] = maps[cell * 5 + 4];
+    s_run[run][ch][0] = A;
+    s_run[run][ch][1] = K;
+    s_run[run][ch][2] = V;
+    s_run[run][ch][3] = Bk;
+    s_run[run][ch][4] = Bv;
+    __syncthreads();
+    if (run == 0) {  // chain the runs of this channel
+        float hk = 0.f, hv = 0.f;
+        for (int r = 0; r < kCarryRuns; ++r) {
+            s_in[r][ch][0] = hk;
+            s_in[r][ch][1] = hv;
+            hk = fmaf(s_run[r][ch][0], hk, s_run[r][ch][1]);
+            hv = fmaf(s_run[r][ch][0], hv, s_run[r][ch][2]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (c0 - u >= 0) {
-                const size_t cell = (size_t)(c0 - u) * stride + idx;
-                carry[cell * 4 + 2] = mk;
-                carry[cell * 4 + 3] = mv;
-                mk = fmaf(A[u], mk, Bk[u]);
-                mv = fmaf(A[u], mv, Bv[u]);
-            }
+        float mk = 0.f, mv = 0.f;
+        for (int r = kCarryRuns - 1; r >= 0; --r) {
+            s_in[r][ch][2] = mk;
+            s_in[r][ch][3] = mv;
+            mk = fmaf(s_run[r][ch][0], mk, s_run[r][ch][3]);
+            mv = fmaf(s_run[r][ch][0], mv, s_run[r][ch][4]);
         }
+    }
+    __syncthreads();
+    if (!valid) return;
+    float hk = s_in[run][ch][0], hv = s_in[run][ch][1];
+    for (int c = c0; c < c1; ++c) {
+        const size_t cell = (size_t)c * stride + idx;
+        const float* m = maps + cell * 5;
+        carry[cell * 4 + 0] = hk;
+        carry[cell * 4 + 1] = hv;
+        hk = fmaf(m[0], hk, m[1]);
+        hv = fmaf(m[0], hv, m[2]);
+    }
+    float mk = s_in[run][ch][2], mv = s_in[run][ch][3];
+    for (int c = c1 - 1; c >= c0; --c) {
+        const size_t cell = (size_t)c * stride + idx;
+        const float* m = maps + cell * 5;
+        carry[cell * 4 + 2] = mk;
+        carry[cell * 4 + 3] = mv;
+        mk = fmaf(m[0], mk, m[3]);
+        mv = fmaf(m[0], mv, m[4]);
     }
 }
 
@@ -759,7 +788,7 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
     const unsigned rows = (unsigned)((size_t)a.B * a.H * a.T);
     const size_t N = (size_t)a.H * a.d;
     const unsigned cells = (unsigned)(((size_t)a.nchunk * a.B * N + 255) / 256);
-    const unsigned chans = (unsigned)(((size_t)a.B * N + 255) / 256);
+    const unsigned chans = (unsigned)(((size_t)a.B * N + 15) / 16);  // 16 channels per carry workgroup
     if (bf16) {
         const unsigned items = (unsigned)a.mitem[a.H];
         if (a.mfma && items > 0) {
