@@ -5,6 +5,7 @@ The hot path lives in the HIP library ``librat.so`` (C ABI in
 seeded synthetic workloads.  Importing the package does not load the
 library; the first call does, and raises if it has not been built.
 """
-from .ops import (RESTART, SLIDING, RatError, attn_prefill_workspace_bytes, chunk_attn_prefill,  # noqa: F401
+from .ops import (RESTART, SLIDING, RatError, attn_prefill_workspace_bytes, build_decode_caches,  # noqa: F401
+                  chunk_attn_prefill,
                   decode_step, decode_workspace_bytes, dilated_attn_decode, dilated_attn_prefill, history_rows,
                   layer_backward, layer_prefill, load_library, rat_layer_prefill, scan_prefill, scan_workspace_bytes)

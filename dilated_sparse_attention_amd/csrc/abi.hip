@@ -492,6 +492,43 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
                              attn_workspace_bytes, s);
 }
 
+int rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v, void* kc,
+                            void* vc, int n_cap, void* kw, void* vw, int w_cap, int B, int T, int H, int d,
+                            const int* D, const int* W, rat_dtype dtype, void* stream)
+{
+    if (!k_state || !v_state || !kc || !vc) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const int hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!k || !v || !kw || !vw)) return RAT_ERR_NULL;
+    for (int h = 0; h < H; ++h) {
+        if ((T - 1) / D[h] >= n_cap / D[h]) return RAT_ERR_SHAPE;  // history rows of position T-1
+        if (W[h] > w_cap) return RAT_ERR_SHAPE;                   // ring slots p mod W
+    }
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d) || !caches_ok(B, H, d, n_cap, w_cap))
+        return RAT_ERR_UNSUPPORTED;
+    const void* ins[4] = {k_state, v_state, k, v};
+    const void* outs[4] = {kc, vc, kw, vw};
+    for (int i = 0; i < 4; ++i) {
+        if (!outs[i]) continue;
+        for (const void* x : ins)
+            if (x && x == outs[i]) return RAT_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return RAT_ERR_ALIAS;
+    }
+    for (const void* x : ins)
+        if (x && !aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (x && !aligned16(x)) return RAT_ERR_ALIGN;
+    CacheArgs a;
+    memset(&a, 0, sizeof(a));
+    a.ks = k_state; a.vs = v_state; a.k = k; a.v = v; a.kc = kc; a.vc = vc; a.kw = kw; a.vw = vw;
+    a.B = B; a.T = T; a.H = H; a.d = d; a.n_cap = n_cap; a.w_cap = w_cap;
+    for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
+    return hip_status(launch_cache_build(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
+}
+
 size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d)
 {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || !size_ok(B, T, H, d)) return 0;

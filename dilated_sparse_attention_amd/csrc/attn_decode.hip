@@ -327,6 +327,43 @@ hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream
     return hipGetLastError();
 }
 
+// One thread per 16 bytes of a prefill row (b, p, h): the state row into
+// the history, and for the last W[h] positions the raw row into the ring.
+template <typename E>
+__global__ __launch_bounds__(256) void cache_build_kernel(CacheArgs a)
+{
+    constexpr int EPV = 16 / sizeof(E);
+    const int vpr = a.d / EPV;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)a.B * a.T * a.H * vpr) return;
+    const int c = (int)(idx % vpr) * EPV;
+    const size_t row = idx / vpr;  // (b T + p) H + h
+    const int h = (int)(row % a.H);
+    const size_t bp = row / a.H;
+    const int p = (int)(bp % a.T), b = (int)(bp / a.T);
+    const int D = a.D[h], W = a.W[h];
+    const size_t src = row * a.d + c;
+    const size_t bh = (size_t)b * a.H + h;
+    const size_t dst = (bh * a.n_cap + (size_t)(p % D) * (a.n_cap / D) + p / D) * a.d + c;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kc) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.ks) + src);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vc) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.vs) + src);
+    if (W > 0 && p >= a.T - W) {
+        const size_t dw = (bh * a.w_cap + (size_t)(p % W)) * a.d + c;
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + dw) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + src);
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + dw) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + src);
+    }
+}
+
+hipError_t launch_cache_build(const CacheArgs& a, bool bf16, hipStream_t stream)
+{
+    const size_t n = (size_t)a.B * a.T * a.H * (a.d / (bf16 ? 8 : 4));
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(cache_build_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(cache_build_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream)
 {
     const size_t n = (size_t)a.B * a.H * a.d;

@@ -181,6 +181,25 @@ struct RingFillArgs {
 };
 hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream);
 
+// Decode caches from a prefill's states: state (b, p, h) of [B][T][H][d]
+// into row (p mod D[h]) (n_cap / D[h]) + p / D[h] of head (b, h)'s history
+// [B][H][n_cap][d]; raw k, v of the last W[h] positions into ring slot
+// p mod W[h] of [B][H][w_cap][d].
+struct CacheArgs {
+    const void* ks;
+    const void* vs;
+    const void* k;
+    const void* v;
+    void* kc;
+    void* vc;
+    void* kw;
+    void* vw;
+    int B, T, H, d, n_cap, w_cap;
+    int D[kAttnMaxHeads];
+    int W[kAttnMaxHeads];
+};
+hipError_t launch_cache_build(const CacheArgs& a, bool bf16, hipStream_t stream);
+
 // ---------------------------------------------------------------- backward
 constexpr int kBwdChunk = 16;  // tokens per chunk of the reverse recurrence
 

@@ -28,7 +28,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
            "rat_chunk_attn_prefill",
            "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_layer_prefill",
-           "rat_layer_backward_workspace_bytes", "rat_layer_backward",
+           "rat_layer_backward_workspace_bytes", "rat_layer_backward", "rat_build_decode_caches",
            "rat_status_string",
            "rat_last_hip_error")
 
@@ -77,6 +77,8 @@ def load_library(path: str = LIBRARY):
     lib.rat_layer_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, ip, ip, f, i,
                                       vp, sz, vp, sz, vp]
     lib.rat_layer_prefill.restype = i
+    lib.rat_build_decode_caches.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, ip, ip, i, vp]
+    lib.rat_build_decode_caches.restype = i
     lib.rat_layer_backward_workspace_bytes.argtypes = [i, i, i, i]
     lib.rat_layer_backward_workspace_bytes.restype = sz
     lib.rat_layer_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, ip, ip, f, i,
@@ -321,6 +323,37 @@ def layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None, 
                                0 if aws is None else aws.numel(), _stream())
     _raise("rat_layer_prefill", rc, lib)
     return out, kc, vc, kw, vw, final_state
+
+
+def build_decode_caches(k_state, v_state, k, v, D, W, n_cap=None, w_cap=None, kc=None, vc=None, kw=None, vw=None):
+    """Decode caches of a finished prefill: the per-residue state history
+    (kc, vc: [B,H,n_cap,d]) and the raw ring of the last W tokens (kw, vw:
+    [B,H,w_cap,d]), as decode_step reads and extends them.  Returns
+    (kc, vc, kw, vw); kw / vw are None when every W is 0."""
+    lib = load_library()
+    B, T, H, d = k_state.shape
+    for name, t in (("k_state", k_state), ("v_state", v_state), ("k", k), ("v", v)):
+        _check_tensor(name, t, k_state.dtype, k_state.shape)
+    Dl = list(D) if hasattr(D, "__len__") else [int(D)] * H
+    Wl = list(W) if hasattr(W, "__len__") else [int(W)] * H
+    n_cap = history_rows(T, Dl) if n_cap is None else int(n_cap)
+    kc = torch.empty((B, H, n_cap, d), dtype=k_state.dtype, device=k_state.device) if kc is None else kc
+    vc = torch.empty_like(kc) if vc is None else vc
+    _check_tensor("kc", kc, k_state.dtype, (B, H, n_cap, d))
+    _check_tensor("vc", vc, k_state.dtype, (B, H, n_cap, d))
+    any_w = any(int(x) > 0 for x in Wl)
+    w_cap = (max(int(x) for x in Wl) if any_w else 0) if w_cap is None else int(w_cap)
+    if any_w and kw is None:
+        kw = torch.zeros((B, H, w_cap, d), dtype=k_state.dtype, device=k_state.device)
+        vw = torch.zeros_like(kw)
+    if kw is not None:
+        _check_tensor("kw", kw, k_state.dtype, (B, H, w_cap, d))
+        _check_tensor("vw", vw, k_state.dtype, (B, H, w_cap, d))
+    rc = lib.rat_build_decode_caches(_ptr(k_state), _ptr(v_state), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), n_cap,
+                                     _ptr(kw), _ptr(vw), w_cap, B, T, H, d, _heads(Dl, H), _heads(Wl, H),
+                                     _DTYPES[k_state.dtype], _stream())
+    _raise("rat_build_decode_caches", rc, lib)
+    return kc, vc, kw, vw
 
 
 def layer_backward(q, k, v, gate_logits, k_state, v_state, dout, D, W, L=None, mode=RESTART, scale=None,

@@ -221,6 +221,25 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
                       void* scan_workspace, size_t scan_workspace_bytes,
                       void* attn_workspace, size_t attn_workspace_bytes, void* stream);
 
+/* The decode caches of a finished prefill, for a decode loop to continue
+ * from (the decode cache of the RAT+ Abstract, kept per residue as
+ * rat_decode_step reads and extends it): copies the states rat_scan_prefill
+ * wrote and the raw tokens of the last W[h] positions.
+ *   k_state, v_state : [B,T,H,d] prefill states;  k, v : [B,T,H,d] raw
+ *            inputs (may be NULL iff every W[h] == 0);
+ *   kc, vc : [B,H,n_cap,d] history: position p of head h to row
+ *            (p mod D[h]) * (n_cap / D[h]) + p / D[h] for p < T, other rows
+ *            left alone; (T-1) / D[h] < n_cap / D[h];
+ *   kw, vw : [B,H,w_cap,d] ring: position p of the last W[h] to slot
+ *            p mod W[h], other slots left alone; w_cap >= W[h]; may be NULL
+ *            iff every W[h] == 0.
+ * The fp32 running state for the loop is rat_scan_prefill's final_state.
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
+int rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v,
+                            void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
+                            int B, int T, int H, int d, const int* D, const int* W, rat_dtype dtype,
+                            void* stream);
+
 /* Bytes of device workspace rat_layer_backward needs: per query row the
  * log-sum-exp and dout.out, the fp32 gradients of the states, and per
  * 16-token chunk of every channel its recurrence maps and carries.

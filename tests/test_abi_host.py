@@ -268,3 +268,20 @@ def test_backward_workspace_size(lib):
     assert need >= 4 * (2 * rows + 2 * elems + 9 * cells)
     assert need < 4 * (2 * rows + 2 * elems + 9 * cells) + 6 * 256
     assert lib.rat_layer_backward_workspace_bytes(0, T, H, d) == 0
+
+
+def caches(lib, ks=P[0], vs=P[1], k=P[2], v=P[3], kc=P[4], vc=P[5], n_cap=1024, kw=P[6], vw=P[7], w_cap=64,
+           B=1, T=1000, H=2, d=128, D=(64, 16), W=(64, 0), dtype=1):
+    return lib.rat_build_decode_caches(ks, vs, k, v, kc, vc, n_cap, kw, vw, w_cap, B, T, H, d, heads(D), heads(W),
+                                       dtype, None)
+
+
+def test_build_decode_caches_validation(lib):
+    assert caches(lib, kc=None) == NULL
+    assert caches(lib, kw=None) == NULL           # head 0 has a window
+    assert caches(lib, n_cap=64 * 15) == SHAPE    # position 999 of D = 64 needs 16 rows per residue
+    assert caches(lib, w_cap=63) == SHAPE
+    assert caches(lib, d=48) == UNSUP
+    assert caches(lib, kc=P[0]) == ALIAS
+    assert caches(lib, vw=P[6]) == ALIAS
+    assert caches(lib, vc=MIS) == ALIGN

@@ -173,3 +173,59 @@ def test_decode_step_full_size():
         want = oracle.attn_decode(q[b, h][None, None].cpu(), kd, vd, kw1[None, None], vw1[None, None], T,
                                   [Dh], [Wh], w.scale)
         assert_parity(out[b, h][None, None], want, torch.bfloat16, f"decode step b{b} h{h}")
+
+
+@pytest.mark.parametrize("case", [
+    # (B, T0, steps, H, d, D, W, L)
+    (2, 300, 12, 3, 128, [1, 16, 64], [0, 8, 64], None),
+    (1, 257, 10, 2, 64, [5, 1], [3, 0], 64),   # RESTART every 64 positions
+])
+def test_prefill_caches_then_decode(case):
+    """The library builds the decode caches from its own prefill
+    (build_decode_caches): the history rows and ring slots are exact copies
+    of the states and raw tokens (rows and slots it must not write keep a
+    sentinel), and a decode loop continued from them matches the oracle's
+    prefill rows at the later positions."""
+    B, T0, steps, H, d, D, W, L = case
+    Tt = T0 + steps
+    Lr = Tt if L is None else L
+    x = inputs.make_random_prefill(B, Tt, H, d, torch.bfloat16, seed=12, gate_mean=1.5)
+    q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
+    pre = [t[:, :T0].contiguous() for t in (k, v, g)]
+    state = torch.empty((B, H, 2, d), dtype=torch.float32, device="cuda")
+    announce("prefill caches", case)
+    ks, vs = rat.scan_prefill(*pre, L=min(Lr, T0), final_state=state)
+    n_cap = rat.history_rows(Tt, D) + max(D)
+    w_cap = max(W) + 2
+    kc = torch.full((B, H, n_cap, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, 7.0)
+    kw = torch.full((B, H, w_cap, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    vw = torch.full_like(kw, 7.0)
+    rat.build_decode_caches(ks, vs, pre[0], pre[1], D, W, n_cap=n_cap, w_cap=w_cap, kc=kc, vc=vc, kw=kw, vw=vw)
+    torch.cuda.synchronize()
+    kc_h, vc_h, kw_h, vw_h = kc.cpu(), vc.cpu(), kw.cpu(), vw.cpu()
+    ks_h, vs_h = ks.cpu(), vs.cpu()
+    for h, (Dh, Wh) in enumerate(zip(D, W)):
+        p = np.arange(T0)
+        rows = (p % Dh) * (n_cap // Dh) + p // Dh
+        assert torch.equal(kc_h[:, h, rows], ks_h[:, :, h]) and torch.equal(vc_h[:, h, rows], vs_h[:, :, h]), h
+        rest = np.setdiff1d(np.arange(n_cap), rows)
+        assert (kc_h[:, h, rest] == 7.0).all() and (vc_h[:, h, rest] == 7.0).all(), h
+        for s in range(w_cap):
+            last = [t for t in range(max(0, T0 - Wh), T0) if Wh > 0 and t % Wh == s]
+            if last:
+                assert torch.equal(kw_h[:, h, s], x["k"][:, last[0], h]) and torch.equal(vw_h[:, h, s], x["v"][:, last[0], h])
+            else:
+                assert (kw_h[:, h, s] == 7.0).all() and (vw_h[:, h, s] == 7.0).all(), (h, s)
+    wk, wv = oracle.scan(x["k"], x["v"], x["gate"], Lr, 0)
+    rows = np.array([(b, t, h) for t in range(T0, Tt) for b in range(B) for h in range(H)], np.int32)
+    want = oracle.attn_prefill_rows(x["q"], wk, wv, x["k"], x["v"], rows, D, W, 1 / math.sqrt(d))
+    want = want.reshape(steps, B, H, d)
+    got = []
+    for T in range(T0 + 1, Tt + 1):
+        t = T - 1
+        out = rat.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                              g[:, t].contiguous(), state, kc, vc, kw, vw, T, D, W, L=Lr)
+        got.append(out.clone())
+    torch.cuda.synchronize()
+    assert_parity(torch.stack(got), want, torch.bfloat16, "decode after the library's caches")
