@@ -590,8 +590,8 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
         a.W[h] = W[h];
         a.mitem[h] = (int)items;
         if (a.mfma && W[h] == 0) {
-            // B x min(D, T) residues x blocks of 64 rows of the longest residue
-            const int64_t nb = ((T + D[h] - 1) / D[h] + 63) / 64;
+            // B x min(D, T) residues x blocks of 16 kBwdWaves rows of the longest residue
+            const int64_t nb = ((T + D[h] - 1) / D[h] + 16 * kBwdWaves - 1) / (16 * kBwdWaves);
             items += (int64_t)B * std::min(D[h], T) * nb;
         }
         if (items >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;

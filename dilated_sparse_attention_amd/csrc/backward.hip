@@ -253,7 +253,9 @@ __global__ __launch_bounds__(kWave) void bwd_key_kernel(BwdArgs a)
 // that residue); items of head h start at a.mitem[h].  Within a head the
 // block index is outermost, in the order that puts the largest blocks first
 // (dq: a block's work grows with its index; dk / dv: it shrinks).
-constexpr int kBwdRows = 64;
+constexpr int kBwdRows = 64;  // rows of the other side's tiles
+constexpr int kBwdThreads = kBwdWaves * kWave;
+constexpr int kBwdOwn = 16 * kBwdWaves;  // rows a workgroup owns (16 per wave)
 
 struct BwdItem {
     int b, h, r, blk, M, D;
@@ -269,14 +271,14 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int item)
     it.h = h;
     it.D = a.D[h];
     const int Dr = min(it.D, a.T);
-    const int nb = ((a.T + it.D - 1) / it.D + kBwdRows - 1) / kBwdRows;  // blocks of the longest residue
+    const int nb = ((a.T + it.D - 1) / it.D + kBwdOwn - 1) / kBwdOwn;  // blocks of the longest residue
     const int local = item - a.mitem[h];
     const int level = local / (a.B * Dr), rest = local % (a.B * Dr);
     it.blk = LAST_FIRST ? nb - 1 - level : level;
     it.r = rest % Dr;
     it.b = rest / Dr;
     it.M = (a.T - it.r + it.D - 1) / it.D;
-    it.valid = item < a.mitem[h + 1] && it.blk * kBwdRows < it.M;
+    it.valid = item < a.mitem[h + 1] && it.blk * kBwdOwn < it.M;
     return it;
 }
 
@@ -293,7 +295,7 @@ __device__ __forceinline__ void load_rows(lds_char* tile, const void* src, const
                                           int row0)
 {
     constexpr int CH = Geo<DK>::CH;
-    for (int idx = threadIdx.x; idx < kBwdRows * CH; idx += 4 * kWave) {
+    for (int idx = threadIdx.x; idx < kBwdRows * CH; idx += kBwdThreads) {
         const int row = idx / CH, c = idx % CH;
         u32x4 val = {0u, 0u, 0u, 0u};
         if (row0 + row < it.M)
@@ -307,14 +309,15 @@ __device__ __forceinline__ void load_rows(lds_char* tile, const void* src, const
 // barrier that frees the tile) store.
 template <int DK>
 struct TileRegs {
-    static constexpr int N = kBwdRows * Geo<DK>::CH / (4 * kWave);  // 16-byte chunks per thread
+    static constexpr int N = kBwdRows * Geo<DK>::CH / kBwdThreads;  // 16-byte chunks per thread
+    static_assert(N * kBwdThreads == kBwdRows * Geo<DK>::CH, "whole tile per pass");
     u32x4 v[N];
     __device__ __forceinline__ void load(const void* src, const BwdArgs& a, const BwdItem& it, int row0)
     {
         constexpr int CH = Geo<DK>::CH;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const int idx = threadIdx.x + n * 4 * kWave;
+            const int idx = threadIdx.x + n * kBwdThreads;
             const int row = idx / CH, c = idx % CH;
             v[n] = u32x4{0u, 0u, 0u, 0u};
             if (row0 + row < it.M)
@@ -327,7 +330,7 @@ struct TileRegs {
         constexpr int CH = Geo<DK>::CH;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const int idx = threadIdx.x + n * 4 * kWave;
+            const int idx = threadIdx.x + n * kBwdThreads;
             *reinterpret_cast<u32x4*>(tile + swz<DK>(idx / CH, idx % CH)) = v[n];
         }
     }
@@ -384,7 +387,7 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
 // (lane: keys 16kb + 4g + j of its query), dP^T = V dO^T, and
 // dQ^T += K^T dS^T with dS^T packed to bf16 as the B operand.
 template <int DK>
-__global__ __launch_bounds__(4 * kWave, 2) void bwd_q_mfma(BwdArgs a)
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
@@ -395,13 +398,14 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_q_mfma(BwdArgs a)
     const int wv = threadIdx.x / kWave;
     const int g = lane >> 4, i = lane & 15;
     const float c = a.scale * kLog2e;
-    const int qr = it.blk * kBwdRows + 16 * wv + i;
+    const int qr = it.blk * kBwdOwn + 16 * wv + i;
     const bool qvalid = qr < it.M;
     const size_t qe = qvalid ? res_row<DK>(a, it, qr) : 0;
     bf16x8 qf[G::KS], gf[G::KS];
     load_frag<DK>(qf, a.q, qe, qvalid);
     load_frag<DK>(gf, a.dout, qe, qvalid);
-    const int ntile = it.blk + 1;  // key tiles up to the block's last query
+    // key tiles up to the block's last query
+    const int ntile = (min(it.M, (it.blk + 1) * kBwdOwn) - 1) / kBwdRows + 1;
     auto scores = [&](floatx4 (&st)[4], floatx4 (&dpt)[4]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_q_mfma(BwdArgs a)
 // dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS with P and dS packed to
 // bf16 as B operands.
 template <int DK>
-__global__ __launch_bounds__(4 * kWave, 2) void bwd_kv_mfma(BwdArgs a)
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_kv_mfma(BwdArgs a)
     const int wv = threadIdx.x / kWave;
     const int g = lane >> 4, i = lane & 15;
     const float c = a.scale * kLog2e;
-    const int kr = it.blk * kBwdRows + 16 * wv + i;
+    const int kr = it.blk * kBwdOwn + 16 * wv + i;
     const bool kvalid = kr < it.M;
     const size_t ke = kvalid ? res_row<DK>(a, it, kr) : 0;
     bf16x8 kf[G::KS], vf[G::KS];
@@ -548,8 +552,9 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_kv_mfma(BwdArgs a)
             rd = a.delta[rrow];
         }
     };
-    fetch(it.blk);
-    for (int t = it.blk; t < ntile; ++t) {
+    const int t0 = it.blk * kBwdOwn / kBwdRows;  // the tile holding the block's first key
+    fetch(t0);
+    for (int t = t0; t < ntile; ++t) {
         __syncthreads();
         rq.store(qt);
         rg.store(gt);
@@ -792,15 +797,15 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
     if (bf16) {
         const unsigned items = (unsigned)a.mitem[a.H];
         if (a.mfma && items > 0) {
-            if (a.d == 128) hipLaunchKernelGGL(bwd_q_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
-            else hipLaunchKernelGGL(bwd_q_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
+            if (a.d == 128) hipLaunchKernelGGL(bwd_q_mfma<128>, dim3(items), dim3(kBwdThreads), 0, stream, a);
+            else hipLaunchKernelGGL(bwd_q_mfma<64>, dim3(items), dim3(kBwdThreads), 0, stream, a);
         }
         // the per-row kernels: heads with a raw window (and the raw-window
         // gradients, zero for the other heads); none when no head has one
         if (a.raw) hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         if (a.mfma && items > 0) {
-            if (a.d == 128) hipLaunchKernelGGL(bwd_kv_mfma<128>, dim3(items), dim3(4 * kWave), 0, stream, a);
-            else hipLaunchKernelGGL(bwd_kv_mfma<64>, dim3(items), dim3(4 * kWave), 0, stream, a);
+            if (a.d == 128) hipLaunchKernelGGL(bwd_kv_mfma<128>, dim3(items), dim3(kBwdThreads), 0, stream, a);
+            else hipLaunchKernelGGL(bwd_kv_mfma<64>, dim3(items), dim3(kBwdThreads), 0, stream, a);
         }
         if (a.raw) hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);

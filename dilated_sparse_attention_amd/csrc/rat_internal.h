@@ -202,6 +202,10 @@ hipError_t launch_cache_build(const CacheArgs& a, bool bf16, hipStream_t stream)
 
 // ---------------------------------------------------------------- backward
 constexpr int kBwdChunk = 16;  // tokens per chunk of the reverse recurrence
+#ifndef RAT_BWD_WAVES
+#define RAT_BWD_WAVES 4
+#endif
+constexpr int kBwdWaves = RAT_BWD_WAVES;  // waves of an MFMA backward workgroup (16 owned rows each)
 
 struct BwdArgs {
     const void* q;
