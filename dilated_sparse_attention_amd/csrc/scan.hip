@@ -51,6 +51,9 @@
 
 namespace rat {
 
+// A compile-time bool for the two forms of a kernel's inner loops.
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 constexpr int kScanThreads = kScanWaves * kWave;
 constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before the watchdog fires
 #ifndef RAT_SCAN_LOOKBACK
@@ -178,31 +181,44 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
         for (int t = ((t0 + a.L - 1) / a.L) * a.L; t < t0 + TPL; t += a.L) rmask |= 1u << (t - t0);
     }
 
+    // Both passes come in two forms.  The fast one serves a wave whose
+    // segments all lie inside the sequence and hold no RESTART position
+    // (every wave of a whole chunk of the full recurrence): with no per-token
+    // liveness or restart test, the gates of all tokens and channels form
+    // straight-line code the compiler can interleave.  The general form
+    // handles the ragged end and the restarts.
+    const bool fast = tb + CT <= a.T && cblk + BW <= a.N && !__any(rmask != 0u);
+
     // pass 1: the segment's map h -> A h + (K, V), its recurrence from a
     // zero state (the raw inputs stay in registers for pass 2)
     float A[CPL], K[CPL], V[CPL];
+    auto pass1 = [&](auto fast_form) {
+        constexpr bool FAST = decltype(fast_form)::value;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) { A[j] = 1.f; K[j] = 0.f; V[j] = 0.f; }
+        for (int j = 0; j < CPL; ++j) { A[j] = 1.f; K[j] = 0.f; V[j] = 0.f; }
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        const bool live = t0 + i < a.T;
-        const bool restart = (rmask >> i) & 1u;
+        for (int i = 0; i < TPL; ++i) {
+            const bool live = FAST || t0 + i < a.T;
+            const bool restart = !FAST && ((rmask >> i) & 1u);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const float g = gate(R16::get(rg[i], j));
-            if (restart) {  // the state before this token is cleared: the map forgets its input
-                A[j] = 0.f;
-                K[j] = 0.f;
-                V[j] = 0.f;
-            }
-            if (live) {
-                const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
-                A[j] *= g;
-                K[j] = fmaf(g, K[j] - xk, xk);
-                V[j] = fmaf(g, V[j] - xv, xv);
+            for (int j = 0; j < CPL; ++j) {
+                const float g = gate(R16::get(rg[i], j));
+                if (restart) {  // the state before this token is cleared: the map forgets its input
+                    A[j] = 0.f;
+                    K[j] = 0.f;
+                    V[j] = 0.f;
+                }
+                if (live) {
+                    const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
+                    A[j] *= g;
+                    K[j] = fmaf(g, K[j] - xk, xk);
+                    V[j] = fmaf(g, V[j] - xv, xv);
+                }
             }
         }
-    }
+    };
+    if (fast) pass1(BoolC<true>{});
+    else pass1(BoolC<false>{});
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         s_seg[seg][0][c * CPL + j] = A[j];
@@ -391,44 +407,62 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
         ck[j] = fmaf(pa, s_carry[0][ch], s_seg[seg][1][ch]);
         cv[j] = fmaf(pa, s_carry[1][ch], s_seg[seg][2][ch]);
     }
+    // the last position's states in fp32, for a decode loop to continue from
+    // (a lane's CPL channels lie in one head: d is a multiple of 64)
+    float* fin = nullptr;
+    if (a.fin && cvalid) {
+        const int hh = ch0 / a.d;
+        fin = a.fin + ((size_t)(b * (a.N / a.d) + hh) * 2) * a.d + (ch0 - hh * a.d);
+    }
+    auto pass2 = [&](auto fast_form) {
+        constexpr bool FAST = decltype(fast_form)::value;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-        asm volatile("" : "+v"(rg[i]));
-        const bool restart = (rmask >> i) & 1u;
-        float ok[CPL], ov[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const float g = gate(R16::get(rg[i], j));
-            if (restart) {  // cleared state before this token
-                ck[j] = 0.f;
-                cv[j] = 0.f;
-            }
-            const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
-            ck[j] = fmaf(g, ck[j] - xk, xk);
-            cv[j] = fmaf(g, cv[j] - xv, xv);
-            ok[j] = ck[j];
-            ov[j] = cv[j];
-        }
-        // non-temporal stores: measured, they leave the attention that reads
-        // the states next faster than cacheable ones do (the scan itself
-        // runs as fast either way)
-        if (cvalid && t0 + i < a.T) {
-            const size_t o = HIST ? hbase + (size_t)hr.row() * a.d : rowbase + (size_t)(t0 + i) * a.N;
-            __builtin_nontemporal_store(R16::pack(ok), reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o));
-            __builtin_nontemporal_store(R16::pack(ov), reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o));
-        }
-        if (HIST) hr.next();
-        // the last position's states in fp32, for a decode loop to continue from
-        if (a.fin && cvalid && t0 + i == a.T - 1) {
+        for (int i = 0; i < TPL; ++i) {
+            asm volatile("" : "+v"(rg[i]));
+            const bool restart = !FAST && ((rmask >> i) & 1u);
+            float ok[CPL], ov[CPL];
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int ch = ch0 + j, hh = ch / a.d, cc = ch - hh * a.d;
-                float* f = a.fin + ((size_t)(b * (a.N / a.d) + hh) * 2) * a.d + cc;
-                f[0] = ok[j];
-                f[a.d] = ov[j];
+                const float g = gate(R16::get(rg[i], j));
+                if (restart) {  // cleared state before this token
+                    ck[j] = 0.f;
+                    cv[j] = 0.f;
+                }
+                const float xk = R16::get(rk[i], j), xv = R16::get(rv[i], j);
+                ck[j] = fmaf(g, ck[j] - xk, xk);
+                cv[j] = fmaf(g, cv[j] - xv, xv);
+                ok[j] = ck[j];
+                ov[j] = cv[j];
+            }
+            // non-temporal stores: measured, they leave the attention that
+            // reads the states next faster than cacheable ones do (the scan
+            // itself runs as fast either way)
+            if (FAST || (cvalid && t0 + i < a.T)) {
+                const size_t o = HIST ? hbase + (size_t)hr.row() * a.d : rowbase + (size_t)(t0 + i) * a.N;
+                __builtin_nontemporal_store(R16::pack(ok), reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o));
+                __builtin_nontemporal_store(R16::pack(ov), reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o));
+            }
+            if (HIST) hr.next();
+            if (!FAST && fin && t0 + i == a.T - 1) {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    fin[j] = ok[j];
+                    fin[a.d + j] = ov[j];
+                }
             }
         }
-    }
+        // fast form: every token of the segment is live, so the state after
+        // the loop is that of its last token
+        if (FAST && fin && t0 + TPL == a.T) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                fin[j] = ck[j];
+                fin[a.d + j] = cv[j];
+            }
+        }
+    };
+    if (fast) pass2(BoolC<true>{});
+    else pass2(BoolC<false>{});
 }
 
 // ---------------------------------------------------------------- SLIDING
