@@ -336,6 +336,29 @@ def run_backward_arl(torch, rat, w, steps, warmup):
     return ms, flops, nbytes
 
 
+def run_copy_reference(torch, nbytes, steps, nsets=3):
+    """A plain device-to-device copy moving ``nbytes`` (half read, half
+    written), over rotating buffer sets that together exceed the caches: the
+    rate the HBM delivers in practice, reported beside the spec peak."""
+    n = nbytes // 2
+    bufs = [(torch.ones(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(nsets)]
+    for i in range(2 * nsets):
+        bufs[i % nsets][1].copy_(bufs[i % nsets][0])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        bufs[i % nsets][1].copy_(bufs[i % nsets][0])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del bufs
+    torch.cuda.empty_cache()
+    return ms
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, min_s=12.0, max_reps=100):
     """The fp64 oracle on the host cores, timed on the headline workload
@@ -480,10 +503,18 @@ def main():
     else:
         dom, dom_bytes, dom_ms, dom_kernel = "attn", attn_bytes, attn_ms, ATTN_KERNEL
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    progress("device copy of", dom_bytes, "bytes (achievable HBM rate)")
+    copy_ms = run_copy_reference(torch, dom_bytes, 20)
+    copy_gbs = dom_bytes / (copy_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom_kernel),
                 "kernel": dom_kernel, "algorithmic_bytes_per_launch": dom_bytes,
-                "kernel_ms": round(dom_ms, 4)}
+                "kernel_ms": round(dom_ms, 4),
+                "copy_reference": {"GBps": round(copy_gbs, 1), "ms": round(copy_ms, 4),
+                                   "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                                   "kernel_frac_of_copy": round(achieved / copy_gbs, 4),
+                                   "what": "torch copy_ of the same byte count (half read, half written), "
+                                           "3 rotating buffer sets"}}
     line = {
         "metric": "prefill tokens/s per layer and decode tokens/s at D=16/64; % HBM / MFMA peak",
         "value": w.B * w.T / (ms / 1e3),
