@@ -433,26 +433,36 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
             rv.load(a.vs, a, it, tn * kBwdRows);
         }
     };
-    // sweep 1: per lane group, (max, sum of e^(z - max), sum of e^(z - max) dp) over its keys
+    // sweep 1: per lane group, (max, sum of e^(z - max), sum of e^(z - max) dp)
+    // over its keys, rescaled once per tile: the tile's 16 scores of the lane
+    // (-inf past the query) give the new max first
     float m = -INFINITY, l = 0.f, u = 0.f;
     for (int t = 0; t < ntile; ++t) {
         next_tile(t);
         floatx4 st[4], dpt[4];
         scores(st, dpt);
+        float tm = m;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
-                if (kr <= qr) {
-                    const float z = st[kb][j] * c;
-                    const float mn = fmaxf(m, z);
-                    const float sc = __builtin_amdgcn_exp2f(m - mn), e = __builtin_amdgcn_exp2f(z - mn);
-                    l = fmaf(l, sc, e);
-                    u = fmaf(u, sc, e * dpt[kb][j]);
-                    m = mn;
-                }
+                st[kb][j] = kr <= qr ? st[kb][j] * c : -INFINITY;
+                tm = fmaxf(tm, st[kb][j]);
             }
+        const float ts = tm == -INFINITY ? 0.f : tm;  // no visible key yet: every term is 0
+        const float sc = __builtin_amdgcn_exp2f(m - ts);
+        l *= sc;
+        u *= sc;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(st[kb][j] - ts);
+                l += e;
+                u = fmaf(e, dpt[kb][j], u);
+            }
+        m = tm;
     }
     // combine the four lane groups of the query
     float mall = m;
