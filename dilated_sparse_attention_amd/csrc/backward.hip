@@ -262,6 +262,19 @@ struct BwdItem {
     bool valid;
 };
 
+// The dispatcher deals workgroups to the chip's 8 XCDs in turn (workgroup i
+// to XCD i mod 8), and each XCD has its own L2.  Workgroup i runs item
+// xcd_item(i): XCD x takes one contiguous eighth of the item list, in order,
+// so the workgroups resident on an XCD share one or two heads' tiles instead
+// of every head's.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int wg, int n)
+{
+    const int per = n / kXcds, extra = n % kXcds;  // XCD x runs per + (x < extra) items
+    const int x = wg % kXcds, k = wg / kXcds;
+    return x * per + min(x, extra) + k;
+}
+
 template <bool LAST_FIRST>
 __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int item)
 {
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char vt[kBwdRows * G::ROWB];
-    const BwdItem it = bwd_item<true>(a, blockIdx.x);
+    const BwdItem it = bwd_item<true>(a, xcd_item(blockIdx.x, gridDim.x));
     if (!it.valid) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
     __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char gt[kBwdRows * G::ROWB];
     __shared__ float s_lse2[kBwdRows], s_dl[kBwdRows];
-    const BwdItem it = bwd_item<false>(a, blockIdx.x);
+    const BwdItem it = bwd_item<false>(a, xcd_item(blockIdx.x, gridDim.x));
     if (!it.valid) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
