@@ -151,13 +151,15 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     const int ch0 = cblk + c * CPL;
     const bool cvalid = ch0 < a.N;
     const int t0 = tb + seg * TPL;
-    const size_t rowbase = (size_t)b * a.T * a.N + ch0;
+    // element offset of the lane's first token row; token t0 + i is i N further
+    // (one 64-bit offset per lane, the i N terms uniform)
+    const size_t obase = ((size_t)b * a.T + t0) * a.N + ch0;
 
     u32x4 rk[TPL], rv[TPL], rg[TPL];
     if (tb + CT <= a.T && cblk + BW <= a.N) {  // the whole chunk exists (uniform)
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+            const size_t o = obase + (size_t)i * a.N;
             rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + o));
             rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + o));
             rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + o));
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             if (cvalid && t0 + i < a.T) {
-                const size_t o = rowbase + (size_t)(t0 + i) * a.N;
+                const size_t o = obase + (size_t)i * a.N;
                 rk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + o));
                 rv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + o));
                 rg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + o));
@@ -407,6 +409,12 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
         ck[j] = fmaf(pa, s_carry[0][ch], s_seg[seg][1][ch]);
         cv[j] = fmaf(pa, s_carry[1][ch], s_seg[seg][2][ch]);
     }
+    // the store offset, formed again from the lane index: the empty asm hides
+    // that it equals the loads' offset, so no 64-bit address stays live (and
+    // spills) across the passes
+    int lane2 = lane;
+    asm volatile("" : "+v"(lane2));
+    const size_t sbase = ((size_t)b * a.T + tb + (w * GPW + lane2 / LPR) * TPL) * a.N + cblk + (lane2 % LPR) * CPL;
     // the last position's states in fp32, for a decode loop to continue from
     // (a lane's CPL channels lie in one head: d is a multiple of 64)
     float* fin = nullptr;
@@ -438,7 +446,7 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
             // reads the states next faster than cacheable ones do (the scan
             // itself runs as fast either way)
             if (FAST || (cvalid && t0 + i < a.T)) {
-                const size_t o = HIST ? hbase + (size_t)hr.row() * a.d : rowbase + (size_t)(t0 + i) * a.N;
+                const size_t o = HIST ? hbase + (size_t)hr.row() * a.d : sbase + (size_t)i * a.N;
                 __builtin_nontemporal_store(R16::pack(ok), reinterpret_cast<u32x4*>(static_cast<E*>(a.ks) + o));
                 __builtin_nontemporal_store(R16::pack(ov), reinterpret_cast<u32x4*>(static_cast<E*>(a.vs) + o));
             }
