@@ -601,8 +601,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
     static_assert(NIN % kScanWaves == 0 && NOUT % kScanWaves == 0 && NROW % RPG == 0, "even copies");
     static_assert(kSlideBW == kWave, "one channel per lane");
     extern __shared__ __attribute__((aligned(1024))) char s_tile[];  // [3][NROW][ROWB]: k, v, logits
-    __shared__ float s_map[kScanWaves][3][kSlideBW];  // forward segment maps (A, K, V)
-    __shared__ float s_rev[kScanWaves][3][kSlideBW];  // previous-tile segments (Q, Sk, Sv)
+    // forward segment maps (A, K, V) and previous-tile segments (Q, Sk, Sv):
+    // 12 KiB over the first k rows of the tile, written once every wave has
+    // read its inputs there.  Separate arrays would take the workgroup to
+    // 84 KiB, and two would no longer fit a CU's 160 KiB of LDS.
+    typedef float SegMaps[3][kSlideBW];
+    SegMaps* s_map = reinterpret_cast<SegMaps*>(s_tile);
+    SegMaps* s_rev = reinterpret_cast<SegMaps*>(s_tile + sizeof(SegMaps) * kScanWaves);
+    static_assert(2 * sizeof(SegMaps) * kScanWaves <= (size_t)NROW * ROWB, "segment maps fit the k rows");
     __shared__ int s_hrow[HIST ? kSlideCT : 1];         // history row of each token of the chunk
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -677,6 +683,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
         Sv = fmaf(qg, at(1, pr + i), Sv);
         Q *= g;
     }
+    __syncthreads();  // every wave is done reading the k rows the maps overwrite
     s_map[w][0][lane] = A;
     s_map[w][1][lane] = K;
     s_map[w][2][lane] = V;
