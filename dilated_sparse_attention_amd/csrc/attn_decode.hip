@@ -246,47 +246,53 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// One thread per (b, h, channel): h = g * h_prev + (1 - g) * x for keys and
-// values (the recurrence of "RAT+ Deep Dive" section 2.1, one token), kept
-// in fp32 in `state`, stored in the element type into the state history
-// and, with the raw token, into the window ring.
-template <typename E> __device__ __forceinline__ float ld1(const void* p, size_t i);
-template <> __device__ __forceinline__ float ld1<uint16_t>(const void* p, size_t i)
-{
-    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
-}
-template <> __device__ __forceinline__ float ld1<float>(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
-template <typename E> __device__ __forceinline__ void st1(void* p, size_t i, float x);
-template <> __device__ __forceinline__ void st1<uint16_t>(void* p, size_t i, float x)
-{
-    static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-template <> __device__ __forceinline__ void st1<float>(void* p, size_t i, float x) { static_cast<float*>(p)[i] = x; }
-
+// One thread per 16 bytes of a (b, h) row (CPL = 16 / sizeof(E) channels):
+// h = g * h_prev + (1 - g) * x for keys and values (the recurrence of "RAT+
+// Deep Dive" section 2.1, one token), kept in fp32 in `state`, stored in the
+// element type into the state history and, with the raw token, into the
+// window ring.
 template <typename E>
 __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a)
 {
+    typedef Row16<E> R16;
+    constexpr int CPL = R16::CPL;
+    const int vpr = a.d / CPL;  // 16-byte vectors per row
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.B * a.H * a.d) return;
-    const int c = (int)(idx % a.d);
-    const size_t bh = idx / a.d;
+    if (idx >= (size_t)a.B * a.H * vpr) return;
+    const int c = (int)(idx % vpr) * CPL;
+    const size_t bh = idx / vpr;
     const int h = (int)(bh % a.H);
-    float g, gb;
-    forget_gate(ld1<E>(a.g_new, idx), g, gb);
-    if (a.restart) g = 0.f;
-    const float xk = ld1<E>(a.k_new, idx), xv = ld1<E>(a.v_new, idx);
+    const size_t e = bh * a.d + c;  // the (b, h, c) element of a [B][H][d] row
+    const u32x4 rg = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g_new) + e);
+    const u32x4 rk = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k_new) + e);
+    const u32x4 rv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v_new) + e);
     float* st = a.state + bh * 2 * a.d + c;
-    const float hk = fmaf(g, st[0], gb * xk);
-    const float hv = fmaf(g, st[a.d], gb * xv);
-    st[0] = hk;
-    st[a.d] = hv;
+    float sk[CPL], sv[CPL], hk[CPL], hv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; j += 4) {
+        *reinterpret_cast<float4*>(sk + j) = *reinterpret_cast<const float4*>(st + j);
+        *reinterpret_cast<float4*>(sv + j) = *reinterpret_cast<const float4*>(st + a.d + j);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        float g, gb;
+        forget_gate(R16::get(rg, j), g, gb);
+        if (a.restart) g = 0.f;
+        hk[j] = fmaf(g, sk[j], gb * R16::get(rk, j));
+        hv[j] = fmaf(g, sv[j], gb * R16::get(rv, j));
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; j += 4) {
+        *reinterpret_cast<float4*>(st + j) = *reinterpret_cast<const float4*>(hk + j);
+        *reinterpret_cast<float4*>(st + a.d + j) = *reinterpret_cast<const float4*>(hv + j);
+    }
     const size_t rc = (bh * a.n_cap + a.slot_c[h]) * a.d + c;
-    st1<E>(a.kc, rc, hk);
-    st1<E>(a.vc, rc, hv);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kc) + rc) = R16::pack(hk);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vc) + rc) = R16::pack(hv);
     if (a.slot_w[h] >= 0) {
         const size_t rw = (bh * a.w_cap + a.slot_w[h]) * a.d + c;
-        st1<E>(a.kw, rw, xk);
-        st1<E>(a.vw, rw, xv);
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + rw) = rk;
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + rw) = rv;
     }
 }
 
@@ -366,7 +372,7 @@ hipError_t launch_cache_build(const CacheArgs& a, bool bf16, hipStream_t stream)
 
 hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream)
 {
-    const size_t n = (size_t)a.B * a.H * a.d;
+    const size_t n = (size_t)a.B * a.H * (a.d / (bf16 ? 8 : 4));  // one thread per 16 bytes of a row
     const unsigned blocks = (unsigned)((n + 255) / 256);
     if (bf16) hipLaunchKernelGGL(decode_step_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);

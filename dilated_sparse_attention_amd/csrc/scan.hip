@@ -61,29 +61,6 @@ constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before th
 #endif
 constexpr int kLookbackWindow = RAT_SCAN_LOOKBACK;  // predecessors examined per round
 
-// 16 bytes of one token row: CPL = 16 / sizeof(E) adjacent channels.
-template <typename E> struct Row16;
-template <> struct Row16<uint16_t> {
-    static constexpr int CPL = 8;
-    static __device__ __forceinline__ float get(const u32x4& r, int j)
-    {
-        return (j & 1) ? bf16_hi(r[j >> 1]) : bf16_lo(r[j >> 1]);
-    }
-    static __device__ __forceinline__ u32x4 pack(const float (&x)[8])
-    {
-        return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7])};
-    }
-};
-template <> struct Row16<float> {
-    static constexpr int CPL = 4;
-    static __device__ __forceinline__ float get(const u32x4& r, int j) { return __uint_as_float(r[j]); }
-    static __device__ __forceinline__ u32x4 pack(const float (&x)[4])
-    {
-        return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-    }
-};
-
 // Row of position t in a StateHist head with dilation D and mcap = n_cap / D
 // rows per residue, walked token by token without a division.
 struct HistRow {
