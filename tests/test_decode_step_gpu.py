@@ -54,23 +54,30 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}T{c[1]}+{c[2]}H{c[3]}d{c[4]}D{c[5]}W{c[6]}L{c[7]}")
-def test_decode_loop(case):
+# every case in bf16; the first and the RESTART one also in fp32 (the step
+# kernel's 4-channel vectors and the fp32 decode kernel)
+LOOP_CASES = [(c, torch.bfloat16) for c in CASES] + [(CASES[0], torch.float32), (CASES[2], torch.float32)]
+
+
+@pytest.mark.parametrize("case,dtype", LOOP_CASES,
+                         ids=lambda c: f"B{c[0]}T{c[1]}+{c[2]}H{c[3]}d{c[4]}D{c[5]}W{c[6]}L{c[7]}"
+                         if isinstance(c, tuple) else str(c)[6:])
+def test_decode_loop(case, dtype):
     B, T0, steps, H, d, D, W, L = case
     Tt = T0 + steps
     Lr = Tt if L is None else L
-    x = inputs.make_random_prefill(B, Tt, H, d, torch.bfloat16, seed=3, gate_mean=1.5)
+    x = inputs.make_random_prefill(B, Tt, H, d, dtype, seed=3, gate_mean=1.5)
     q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
     n_cap = max(Dh * ((Tt + Dh - 1) // Dh) for Dh in D) + 16
     w_cap = max(W) + 3
     state = torch.zeros((B, H, 2, d), dtype=torch.float32, device="cuda")
     if T0 > 0:
-        announce("decode loop prefill", case)
+        announce("decode loop prefill", case, dtype)
         ks, vs = rat.scan_prefill(k[:, :T0].contiguous(), v[:, :T0].contiguous(), g[:, :T0].contiguous(),
                                   L=min(Lr, T0) if Lr < T0 else T0, final_state=state)
         kc, vc = _history(ks, vs, T0, D, n_cap)
     else:
-        kc = torch.zeros((B, H, n_cap, d), dtype=torch.bfloat16, device="cuda")
+        kc = torch.zeros((B, H, n_cap, d), dtype=dtype, device="cuda")
         vc = torch.zeros_like(kc)
     kw, vw = _ring(k, v, T0, W, w_cap)
 
@@ -87,7 +94,7 @@ def test_decode_loop(case):
                               g[:, t].contiguous(), state, kc, vc, kw, vw, T, D, W, L=Lr)
         got.append(out.clone())
     torch.cuda.synchronize()
-    assert_parity(torch.stack(got), want, torch.bfloat16, "decode loop outputs")
+    assert_parity(torch.stack(got), want, dtype, "decode loop outputs")
     # the running state is the fp32 recurrence of every token so far
     st = state.cpu().double().numpy()
     ref = np.stack([wk[:, Tt - 1], wv[:, Tt - 1]], axis=2)  # [B,H,2,d]
