@@ -63,7 +63,7 @@ def progress(*parts):
 def load_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when it is absent or was taken from other kernel sources."""
-    path = os.path.join(PROFILES, "hbm_traffic.json")
+    path = os.path.join(PROFILES, "scan_full_attn_dilated_prefill_1p5b_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
