@@ -4,6 +4,8 @@
         --title TITLE --command CMD [--match SUBSTR ...]
     python -m dilated_sparse_attention_amd.profiling traffic \\
         --fetch COUNTER_CSV --write COUNTER_CSV --command CMD
+    python -m dilated_sparse_attention_amd.profiling counters COUNTER_CSV ... \\
+        --title TITLE --command CMD
 
 ``stats`` turns ``rocprofv3 --kernel-trace --stats --output-format csv``
 output (``*_kernel_stats.csv``) into a markdown table.  ``traffic`` reads two
@@ -11,7 +13,10 @@ output (``*_kernel_stats.csv``) into a markdown table.  ``traffic`` reads two
 with ``WRITE_SIZE`` (KiB per dispatch), and scales both by what the counters
 read for a plain elementwise kernel of known size (``torch.neg`` over 1 GiB of
 float32 into another 1 GiB, run by ``bench.py --copy-calibration``), giving
-HBM bytes per launch for every kernel of this library.
+HBM bytes per launch for every kernel of this library.  ``counters`` reads
+``rocprofv3 --pmc`` passes of SQ counters (one CSV per pass, each pass with
+``SQ_WAVES``) and tabulates, per kernel of this library, the instructions a
+wave issues and the share of its cycles spent issuing or waiting.
 """
 from __future__ import annotations
 
@@ -116,6 +121,43 @@ def traffic(fetch_csv, write_csv, command):
     }
 
 
+def _all_counter_means(paths):
+    """{kernel: {counter: mean over dispatches}} over several pmc passes."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Kernel_Name"].startswith("void rat::"):
+                    acc[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters_table(paths, title, command):
+    means = _all_counter_means(paths)
+    out = [f"# {title}", "", "Commands (one rocprofv3 pass per counter set):", "", "```", command, "```", "",
+           f"Kernel sources hash: `{kernel_sources_hash()}`", "",
+           "Per wave: instructions issued (SQ_INSTS_* / SQ_WAVES). Issue and wait shares: SQ_ACTIVE_INST_ANY "
+           "and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES (wave-cycles). LDS conflicts: SQ_LDS_BANK_CONFLICT cycles "
+           "per LDS instruction.", "",
+           "| kernel | waves | VALU/wave | MFMA/wave | LDS/wave | SALU/wave | VMEM/wave | issuing | waiting | "
+           "waiting on LDS | LDS conflict cyc/instr |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+
+    def ratio(d, a, b):
+        return d[a] / d[b] if a in d and d.get(b) else float("nan")
+
+    for k in sorted(means):
+        d = means[k]
+        out.append(f"| `{k}` | {d.get('SQ_WAVES', float('nan')):.0f} | {ratio(d, 'SQ_INSTS_VALU', 'SQ_WAVES'):.0f} | "
+                   f"{ratio(d, 'SQ_INSTS_MFMA', 'SQ_WAVES'):.0f} | {ratio(d, 'SQ_INSTS_LDS', 'SQ_WAVES'):.0f} | "
+                   f"{ratio(d, 'SQ_INSTS_SALU', 'SQ_WAVES'):.0f} | {ratio(d, 'SQ_INSTS_VMEM', 'SQ_WAVES'):.0f} | "
+                   f"{ratio(d, 'SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES'):.2f} | "
+                   f"{ratio(d, 'SQ_WAIT_INST_ANY', 'SQ_WAVE_CYCLES'):.2f} | "
+                   f"{ratio(d, 'SQ_WAIT_INST_LDS', 'SQ_WAVE_CYCLES'):.2f} | "
+                   f"{ratio(d, 'SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS'):.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -128,9 +170,15 @@ def main(argv=None):
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
     a = p.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_table(a.csv, a.title, a.command, a.match))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters_table(a.csv, a.title, a.command))
     else:
         sys.stdout.write(json.dumps(traffic(a.fetch, a.write, a.command), indent=1) + "\n")
 
