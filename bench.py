@@ -236,6 +236,47 @@ def run_chunk(torch, rat, w, steps, warmup, nsets=3):
     return ms
 
 
+def run_decode_caches(torch, rat, w, steps, warmup, nsets=3):
+    """The decode caches of a finished prefill of workload `w`: its states
+    copied into the per-residue history and its last W raw tokens into the
+    ring (the states come from the scan kernel, outside the timed region);
+    back-to-back launches over rotating sets.  Algorithmic bytes: the
+    states read and the history written once, the ring's raw rows read and
+    written once."""
+    from dilated_sparse_attention_amd import inputs
+
+    sets = []
+    D, W = list(w.D), list(w.W)
+    n_cap = rat.history_rows(w.T, D)
+    w_cap = max(W)
+    for i in range(nsets):
+        x = inputs.make_prefill(w, seed=i, device="cuda")
+        ks, vs = rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=w.modes[0])
+        kc = torch.empty((w.B, w.H, n_cap, w.d), dtype=ks.dtype, device="cuda")
+        kw = torch.empty((w.B, w.H, w_cap, w.d), dtype=ks.dtype, device="cuda") if w_cap > 0 else None
+        sets.append((ks, vs, x["k"], x["v"], kc, torch.empty_like(kc), kw, None if kw is None else torch.empty_like(kw)))
+        del x
+    def call(i):
+        ks, vs, k, v, kc, vc, kw, vw = sets[i % nsets]
+        rat.build_decode_caches(ks, vs, k, v, D, W, n_cap=n_cap, w_cap=w_cap, kc=kc, vc=vc, kw=kw, vw=vw)
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del sets
+    torch.cuda.empty_cache()
+    s = 2
+    nbytes = 2 * 2 * w.B * w.T * w.H * w.d * s + 2 * 2 * w.B * w.d * s * sum(min(Wh, w.T) for Wh in W)
+    return ms, nbytes
+
+
 def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
     """One decode-loop step (recurrence update, history and ring writes,
     decode attention) at context length w.T for the whole batch: the state
@@ -478,6 +519,15 @@ def main():
                           "algorithmic_bytes": sbytes,
                           "config": dict(sw.describe(), history_rows_per_head=max(
                               Dh * ((sw.T + Dh - 1) // Dh) for Dh in sw.D))}
+
+        cw = inputs.PREFILL_LONG
+        key = "decode_caches_" + cw.name
+        if args.only is None or args.only == key:
+            progress("decode caches from a prefill", cw.name)
+            cms, cbytes = run_decode_caches(torch, rat, cw, max(5, args.steps), 3)
+            extra[key] = {"caches_ms": cms, "GBps": cbytes / (cms / 1e3) / 1e9,
+                          "hbm_frac": cbytes / (cms / 1e3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": cbytes,
+                          "config": dict(cw.describe(), caches="per-residue state history + raw ring of the last W")}
 
         bw = inputs.PREFILL_1P5B
         key = "backward_arl_" + bw.name
