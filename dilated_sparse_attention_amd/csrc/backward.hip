@@ -655,27 +655,41 @@ __global__ __launch_bounds__(256) void bwd_scan_maps_kernel(BwdArgs a)
     ChunkPos p;
     if (!chunk_pos(a, p)) return;
     const size_t N = (size_t)a.H * a.d;
-    const int t0 = p.c * kBwdChunk, t1 = min(t0 + kBwdChunk, a.T);
+    const int t0 = p.c * kBwdChunk, n = min(kBwdChunk, a.T - t0);
+    const size_t x0 = ((size_t)p.b * a.T + t0) * N + p.n;
     float A = 1.f, K = 0.f, V = 0.f;
-    for (int t = t0; t < t1; ++t) {
-        const size_t i = ((size_t)p.b * a.T + t) * N + p.n;
-        float g, gb;
-        forget_gate(ldx<E>(a.g, i), g, gb);
-        if (restart_at(a, t)) { A = 0.f; K = 0.f; V = 0.f; }
-        A *= g;
-        K = fmaf(g, K, gb * ldx<E>(a.k, i));
-        V = fmaf(g, V, gb * ldx<E>(a.v, i));
-    }
     float Bk = 0.f, Bv = 0.f;  // carry out of the chunk's first token with a zero carry in
-    for (int t = t1 - 1; t >= t0; --t) {
-        const size_t i = ((size_t)p.b * a.T + t) * N + p.n;
-        float g, gb;
-        forget_gate(ldx<E>(a.g, i), g, gb);
-        const float lk = a.dks[i] + Bk, lv = a.dvs[i] + Bv;
-        const bool cut = restart_at(a, t);
-        Bk = cut ? 0.f : g * lk;
-        Bv = cut ? 0.f : g * lv;
-    }
+    // a whole chunk takes the form without the per-token bound, whose loads
+    // can all be in flight at once; the last, ragged chunk the guarded form
+    auto walk = [&](auto whole) {
+        constexpr bool FULL = decltype(whole)::value;
+#pragma unroll
+        for (int i = 0; i < kBwdChunk; ++i) {
+            if (FULL || i < n) {
+                const size_t x = x0 + (size_t)i * N;
+                float g, gb;
+                forget_gate(ldx<E>(a.g, x), g, gb);
+                if (restart_at(a, t0 + i)) { A = 0.f; K = 0.f; V = 0.f; }
+                A *= g;
+                K = fmaf(g, K, gb * ldx<E>(a.k, x));
+                V = fmaf(g, V, gb * ldx<E>(a.v, x));
+            }
+        }
+#pragma unroll
+        for (int i = kBwdChunk - 1; i >= 0; --i) {
+            if (FULL || i < n) {
+                const size_t x = x0 + (size_t)i * N;
+                float g, gb;
+                forget_gate(ldx<E>(a.g, x), g, gb);
+                const float lk = a.dks[x] + Bk, lv = a.dvs[x] + Bv;
+                const bool cut = restart_at(a, t0 + i);
+                Bk = cut ? 0.f : g * lk;
+                Bv = cut ? 0.f : g * lv;
+            }
+        }
+    };
+    if (n == kBwdChunk) walk(BoolC<true>{});
+    else walk(BoolC<false>{});
     float* m = a.maps + p.cell * 5;
     m[0] = A; m[1] = K; m[2] = V; m[3] = Bk; m[4] = Bv;
 }

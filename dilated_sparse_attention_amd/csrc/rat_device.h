@@ -113,4 +113,7 @@ template <> struct Row16<float> {
     }
 };
 
+// A compile-time bool for the two forms of a kernel's inner loops.
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 }  // namespace rat

@@ -51,9 +51,6 @@
 
 namespace rat {
 
-// A compile-time bool for the two forms of a kernel's inner loops.
-template <bool B> struct BoolC { static constexpr bool value = B; };
-
 constexpr int kScanThreads = kScanWaves * kWave;
 constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before the watchdog fires
 #ifndef RAT_SCAN_LOOKBACK
