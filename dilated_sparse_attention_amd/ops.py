@@ -52,8 +52,8 @@ def load_library(path: str = LIBRARY):
     if _lib is not None and path == LIBRARY:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with `python -m dilated_sparse_attention_amd.build` "
-                           "(or __graft_entry__.build()); there is no CPU fallback")
+        raise RuntimeError(f"{path} is missing: build it with `python -m dilated_sparse_attention_amd.build`; "
+                           "there is no CPU fallback")
     lib = ctypes.CDLL(path)
     vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     ip = ctypes.POINTER(ctypes.c_int)
