@@ -17,7 +17,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-int hip_status(hipError_t e)
+rat_status hip_status(hipError_t e)
 {
     if (e == hipSuccess) return RAT_OK;
     g_last_hip_error = (int)e;
@@ -94,7 +94,7 @@ bool scan_uses_workspace(int T, int L, rat_recur_mode mode)
 
 // The scan after validation (workspace already checked).  hist: write the
 // states as a per-residue history instead of [B][T][H][d].
-int run_scan(const void* k, const void* v, const void* g, void* ks, void* vs, int B, int T, int H, int d, int L,
+rat_status run_scan(const void* k, const void* v, const void* g, void* ks, void* vs, int B, int T, int H, int d, int L,
              rat_recur_mode mode, rat_dtype dtype, void* workspace, float* final_state, const StateHist* hist,
              hipStream_t s)
 {
@@ -156,7 +156,7 @@ BwdPlan bwd_plan(int B, int T, int H, int d)
 
 extern "C" {
 
-const char* rat_status_string(int s)
+const char* rat_status_string(rat_status s)
 {
     switch (s) {
     case RAT_OK: return "ok";
@@ -180,7 +180,7 @@ size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L, rat_recur_mod
     return scan_plan(B, T, H, d, dtype).bytes;
 }
 
-int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void* k_state, void* v_state,
+rat_status rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void* k_state, void* v_state,
                      int B, int T, int H, int d, int L, rat_recur_mode mode, rat_dtype dtype,
                      void* workspace, size_t workspace_bytes, float* final_state, void* stream)
 {
@@ -212,7 +212,7 @@ int rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void
 
 namespace {
 
-int check_heads(int H, const int* D, const int* W, bool* any_w)
+rat_status check_heads(int H, const int* D, const int* W, bool* any_w)
 {
     if (!D || !W) return RAT_ERR_NULL;
     if (H > kAttnMaxHeads) return RAT_ERR_UNSUPPORTED;
@@ -244,7 +244,7 @@ namespace {
 // kernel (items = (b, h, r, 256-row chunk)), which continues from those
 // states.  Heads are grouped into (D, W) classes; classes with the longest
 // single items come first, each class's levels most expensive first.
-int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, const void* k_raw,
+rat_status attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, const void* k_raw,
                       const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
                       bool any_w, float scale, int chunk, int n_cap, void* workspace, size_t workspace_bytes,
                       hipStream_t s)
@@ -304,7 +304,7 @@ int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, c
     dil.nblocks = (int)items;
     band.nblocks = (int)blocks;
     if (band.nblocks > 0) {
-        const int rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, device_cu_count()), s));
+        const rat_status rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, device_cu_count()), s));
         if (rc != RAT_OK) return rc;
     }
     const int grid = std::min(dil.nblocks, device_cu_count());
@@ -313,14 +313,14 @@ int attn_prefill_bf16(const void* q, const void* k_state, const void* v_state, c
 
 }  // namespace
 
-int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
+rat_status rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state, const void* k_raw,
                              const void* v_raw, void* out, int B, int T, int H, int d, const int* D, const int* W,
                              float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!q || !k_state || !v_state || !out) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (any_w && (!k_raw || !v_raw)) return RAT_ERR_NULL;
     if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
@@ -347,7 +347,7 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
                              workspace, workspace_bytes, s);
 }
 
-int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out, int B, int T, int H,
+rat_status rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out, int B, int T, int H,
                            int d, const int* D, float scale, rat_dtype dtype, void* stream)
 {
     if (!q || !k_state || !v_state || !out || !D) return RAT_ERR_NULL;
@@ -408,7 +408,7 @@ size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, cons
 
 constexpr bool kLayerPrefillEnabled = false;
 
-int rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits, void* out, void* kc,
+rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits, void* out, void* kc,
                       void* vc, int n_cap, void* kw, void* vw, int w_cap, float* final_state, int B, int T, int H,
                       int d, int L, rat_recur_mode mode, const int* D, const int* W, float scale, rat_dtype dtype,
                       void* scan_workspace, size_t scan_workspace_bytes, void* attn_workspace,
@@ -418,7 +418,7 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1 || n_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
     if (mode != RAT_RECUR_RESTART && mode != RAT_RECUR_SLIDING) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
     for (int h = 0; h < H; ++h) {
@@ -466,7 +466,7 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
     memset(&hist, 0, sizeof(hist));
     hist.n_cap = n_cap; hist.d = d; hist.H = H;
     for (int h = 0; h < H; ++h) hist.D[h] = D[h];
-    int rc = run_scan(k, v, gate_logits, kc, vc, B, T, H, d, L, mode, dtype, scan_workspace, final_state, &hist, s);
+    rat_status rc = run_scan(k, v, gate_logits, kc, vc, B, T, H, d, L, mode, dtype, scan_workspace, final_state, &hist, s);
     if (rc != RAT_OK) return rc;
     // 2. the raw ring of the last W tokens
     if (any_w) {
@@ -492,14 +492,14 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
                              attn_workspace_bytes, s);
 }
 
-int rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v, void* kc,
+rat_status rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v, void* kc,
                             void* vc, int n_cap, void* kw, void* vw, int w_cap, int B, int T, int H, int d,
                             const int* D, const int* W, rat_dtype dtype, void* stream)
 {
     if (!k_state || !v_state || !kc || !vc) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (any_w && (!k || !v || !kw || !vw)) return RAT_ERR_NULL;
     for (int h = 0; h < H; ++h) {
@@ -535,7 +535,7 @@ size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d)
     return bwd_plan(B, T, H, d).bytes;
 }
 
-int rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits, const void* k_state,
+rat_status rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits, const void* k_state,
                        const void* v_state, const void* dout, float* dq, float* dk, float* dv, float* dgate, int B,
                        int T, int H, int d, int L, rat_recur_mode mode, const int* D, const int* W, float scale,
                        rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
@@ -549,7 +549,7 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return RAT_ERR_SHAPE;
     if (mode != RAT_RECUR_RESTART && mode != RAT_RECUR_SLIDING) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
     if (mode == RAT_RECUR_SLIDING && L < T) return RAT_ERR_UNSUPPORTED;  // no backward of a sliding window
@@ -600,14 +600,14 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
     return hip_status(launch_backward(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 
-int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
+rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
                             int w_cap, void* out, int B, int T, int H, int d, const int* D, const int* W, float scale,
                             rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!q || !kd || !vd || !out) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || nd_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
     for (int h = 0; h < H; ++h) {
@@ -637,7 +637,7 @@ int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int n
     return hip_status(launch_decode(a, d, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 
-int rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new, float* state,
+rat_status rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new, float* state,
                     void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap, void* out, int B, int T, int H,
                     int d, int L, const int* D, const int* W, float scale, rat_dtype dtype, void* workspace,
                     size_t workspace_bytes, void* stream)
@@ -645,7 +645,7 @@ int rat_decode_step(const void* q, const void* k_new, const void* v_new, const v
     if (!q || !k_new || !v_new || !gate_new || !state || !kc || !vc || !out) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n_cap <= 0 || w_cap < 0 || L < 1) return RAT_ERR_SHAPE;
     bool any_w = false;
-    const int hc = check_heads(H, D, W, &any_w);
+    const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
     const int p = T - 1;  // position of the new token
@@ -691,7 +691,7 @@ int rat_decode_step(const void* q, const void* k_new, const void* v_new, const v
         a.D[h] = D[h]; a.W[h] = W[h];
         a.dil_off[h] = (p % D[h]) * mcap;
     }
-    const int rc = hip_status(launch_decode_step(st, bf16, s));
+    const rat_status rc = hip_status(launch_decode_step(st, bf16, s));
     if (rc != RAT_OK) return rc;
     return hip_status(launch_decode(a, d, bf16, s));
 }

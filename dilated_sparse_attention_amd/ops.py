@@ -134,10 +134,20 @@ def scan_workspace_bytes(B, T, H, d, L, mode=RESTART, dtype=torch.bfloat16):
 _workspaces = {}
 
 
+def _ws_key(device):
+    """Cached workspaces are kept per (device, stream): calls in flight on
+    two streams must not share one (the scan's carries and tickets assume
+    one call at a time per workspace)."""
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    return idx, torch.cuda.current_stream(idx).cuda_stream
+
+
 def scan_workspace(nbytes, device):
     """A zero-filled scan workspace of at least ``nbytes`` on ``device``,
-    kept per device and reused (the library keeps it consistent itself)."""
-    key = torch.device(device).index
+    kept per (device, current stream) and reused (the library keeps it
+    consistent itself)."""
+    key = _ws_key(device)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -182,8 +192,9 @@ _attn_workspaces = {}
 
 def attn_workspace(nbytes, device):
     """Scratch for the local-window pass of prefill attention (no
-    initialisation needed), kept per device and grown on demand."""
-    key = torch.device(device).index
+    initialisation needed), kept per (device, current stream) and grown on
+    demand."""
+    key = _ws_key(device)
     ws = _attn_workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -258,8 +269,10 @@ def dilated_attn_decode(q, kd, vd, kw, vw, T, D, W, scale=None, out=None, worksp
     return out
 
 
-def rat_layer_prefill(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None):
-    """The whole prefill hot path: recurrence, then dilated attention."""
+def prefill_two_calls(q, k, v, gate_logits, D, W, L=None, mode=RESTART, scale=None):
+    """The whole prefill hot path as two library calls: rat_scan_prefill,
+    then rat_dilated_attn_prefill over its states (the one-call C entry
+    point that also emits decode caches is ``layer_prefill``)."""
     ks, vs = scan_prefill(k, v, gate_logits, L=L, mode=mode)
     need_raw = any(int(w) > 0 for w in (W if hasattr(W, "__len__") else [W]))
     return dilated_attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None,

@@ -89,7 +89,7 @@ size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L,
  *                       available for SLIDING with L < T (RAT_ERR_UNSUPPORTED).
  * Errors: RAT_ERR_NULL, _SHAPE (B,T,H,d,L < 1), _UNSUPPORTED (d, dtype,
  * SLIDING with 64 < L < T, sizes), _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
-int rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
+rat_status rat_scan_prefill(const void* k, const void* v, const void* gate_logits,
                      void* k_state, void* v_state,
                      int B, int T, int H, int d, int L, rat_recur_mode mode,
                      rat_dtype dtype, void* workspace, size_t workspace_bytes,
@@ -113,7 +113,7 @@ size_t rat_attn_prefill_workspace_bytes(int B, int T, int H, int d, const int* D
  *   workspace : at least rat_attn_prefill_workspace_bytes(...) bytes, may
  *          be NULL when that is 0.  Calls in flight must not share it.
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
-int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state,
+rat_status rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_state,
                              const void* k_raw, const void* v_raw, void* out,
                              int B, int T, int H, int d, const int* D, const int* W,
                              float scale, rat_dtype dtype,
@@ -133,7 +133,7 @@ int rat_dilated_attn_prefill(const void* q, const void* k_state, const void* v_s
  *       at most 8 distinct values.
  * No raw local window, no workspace.  Errors: RAT_ERR_NULL, _SHAPE,
  * _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
-int rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out,
+rat_status rat_chunk_attn_prefill(const void* q, const void* k_state, const void* v_state, void* out,
                            int B, int T, int H, int d, const int* D, float scale, rat_dtype dtype,
                            void* stream);
 
@@ -153,7 +153,7 @@ size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, cons
  *              slots 0 .. min(W[h],T)-1, in any order; may be NULL iff every
  *              W[h] == 0; w_cap >= min(W[h], T).
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
-int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap,
+rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap,
                             const void* kw, const void* vw, int w_cap, void* out,
                             int B, int T, int H, int d, const int* D, const int* W,
                             float scale, rat_dtype dtype,
@@ -180,7 +180,7 @@ int rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int n
  *            residue rows and ring slots above.
  *   workspace: rat_decode_workspace_bytes(B, H, d, T, D, W) bytes.
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
-int rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new,
+rat_status rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new,
                     float* state, void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
                     void* out, int B, int T, int H, int d, int L, const int* D, const int* W,
                     float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes,
@@ -214,7 +214,7 @@ int rat_decode_step(const void* q, const void* k_new, const void* v_new, const v
  * In this build the call validates its arguments and then returns
  * RAT_ERR_UNSUPPORTED without launching anything: its launch path is
  * switched off until a device fault seen in it is explained. */
-int rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits,
+rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits,
                       void* out, void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
                       float* final_state, int B, int T, int H, int d, int L, rat_recur_mode mode,
                       const int* D, const int* W, float scale, rat_dtype dtype,
@@ -235,7 +235,7 @@ int rat_layer_prefill(const void* q, const void* k, const void* v, const void* g
  *            iff every W[h] == 0.
  * The fp32 running state for the loop is rat_scan_prefill's final_state.
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _HIP. */
-int rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v,
+rat_status rat_build_decode_caches(const void* k_state, const void* v_state, const void* k, const void* v,
                             void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
                             int B, int T, int H, int d, const int* D, const int* W, rat_dtype dtype,
                             void* stream);
@@ -267,7 +267,7 @@ size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d);
  *   D, W, scale          : as rat_dilated_attn_prefill;
  *   workspace            : rat_layer_backward_workspace_bytes(...) bytes.
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
-int rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits,
+rat_status rat_layer_backward(const void* q, const void* k, const void* v, const void* gate_logits,
                        const void* k_state, const void* v_state, const void* dout,
                        float* dq, float* dk, float* dv, float* dgate,
                        int B, int T, int H, int d, int L, rat_recur_mode mode,
@@ -275,7 +275,7 @@ int rat_layer_backward(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
-const char* rat_status_string(int status);
+const char* rat_status_string(rat_status status);
 
 /* hipError_t of the calling thread's last RAT_ERR_HIP (0 if none). */
 int rat_last_hip_error(void);

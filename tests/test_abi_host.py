@@ -285,3 +285,32 @@ def test_build_decode_caches_validation(lib):
     assert caches(lib, kc=P[0]) == ALIAS
     assert caches(lib, vw=P[6]) == ALIAS
     assert caches(lib, vc=MIS) == ALIGN
+
+
+def test_cached_workspaces_are_per_stream(monkeypatch):
+    """The binding's cached scan / attention workspaces are keyed by
+    (device, stream): calls in flight on two streams never share one."""
+    import torch
+
+    class Stream:
+        def __init__(self, handle):
+            self.cuda_stream = handle
+
+    current = {"s": Stream(11)}
+    monkeypatch.setattr(ops.torch.cuda, "current_stream", lambda device=None: current["s"])
+    monkeypatch.setattr(ops.torch.cuda, "current_device", lambda: 0)
+    real_zeros, real_empty = torch.zeros, torch.empty
+    monkeypatch.setattr(ops.torch, "zeros", lambda *a, **k: real_zeros(*a, **dict(k, device="cpu")))
+    monkeypatch.setattr(ops.torch, "empty", lambda *a, **k: real_empty(*a, **dict(k, device="cpu")))
+    monkeypatch.setattr(ops, "_workspaces", {})
+    monkeypatch.setattr(ops, "_attn_workspaces", {})
+    for get in (ops.scan_workspace, ops.attn_workspace):
+        current["s"] = Stream(11)
+        a = get(4096, "cuda:0")
+        assert get(1024, "cuda:0") is a                 # same stream: reused
+        current["s"] = Stream(12)
+        b = get(4096, "cuda:0")
+        assert b is not a and b.data_ptr() != a.data_ptr()  # another stream: its own buffer
+        current["s"] = Stream(11)
+        assert get(4096, "cuda:0") is a
+        assert get(1 << 16, "cuda:0").numel() >= 1 << 16  # grown on demand

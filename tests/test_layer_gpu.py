@@ -30,7 +30,7 @@ def test_layer_end_to_end(w, B, T):
     L = min(w.L, T) if w.L < w.T else T
     for mode in w.modes:
         announce("layer", w.name, "B", B, "T", T, "mode", mode)
-        out = rat.rat_layer_prefill(q, k, v, g, D=list(w.D), W=list(w.W), L=L, mode=mode)
+        out = rat.prefill_two_calls(q, k, v, g, D=list(w.D), W=list(w.W), L=L, mode=mode)
         torch.cuda.synchronize()
         ks, vs = oracle.scan(x["k"], x["v"], x["gate"], L, mode)
         want = oracle.attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None, x["v"] if need_raw else None,
