@@ -600,9 +600,13 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
     return hip_status(launch_backward(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 
-rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
-                            int w_cap, void* out, int B, int T, int H, int d, const int* D, const int* W, float scale,
-                            rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+namespace {
+
+// Validation shared by the decode entry points; on success *ns holds the
+// key-range splits and *need the bytes of split partials they use.
+rat_status check_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
+                        int w_cap, void* out, int B, int T, int H, int d, const int* D, const int* W, float scale,
+                        rat_dtype dtype, int* ns, size_t* need)
 {
     if (!q || !kd || !vd || !out) return RAT_ERR_NULL;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || nd_cap <= 0 || w_cap < 0) return RAT_ERR_SHAPE;
@@ -623,18 +627,62 @@ rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd
     for (const void* p : ins)
         if (p && !aligned16(p)) return RAT_ERR_ALIGN;
     if (!aligned16(out)) return RAT_ERR_ALIGN;
-    const int ns = decode_nsplit(B, H, T, D, W);
-    const size_t need = ns == 1 ? 0 : (size_t)B * H * ns * (d + 2) * sizeof(float);
-    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) return RAT_ERR_WORKSPACE;
+    *ns = decode_nsplit(B, H, T, D, W);
+    *need = *ns == 1 ? 0 : (size_t)B * H * *ns * (d + 2) * sizeof(float);
+    return RAT_OK;
+}
 
+rat_status launch_decode_checked(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw,
+                                 const void* vw, int w_cap, void* out, int B, int T, int H, int d, const int* D,
+                                 const int* W, float scale, rat_dtype dtype, int ns, float* part, hipStream_t s)
+{
     DecodeArgs a;
     memset(&a, 0, sizeof(a));
     a.q = q; a.kd = kd; a.vd = vd; a.kw = kw ? kw : kd; a.vw = vw ? vw : vd; a.out = out;
-    a.part = static_cast<float*>(workspace);
+    a.part = part;
     a.B = B; a.H = H; a.T = T; a.nd_cap = nd_cap; a.w_cap = w_cap; a.nsplit = ns;
     a.scale_log2 = scale * 1.4426950408889634f;
     for (int h = 0; h < H; ++h) { a.D[h] = D[h]; a.W[h] = W[h]; }
-    return hip_status(launch_decode(a, d, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
+    return hip_status(launch_decode(a, d, dtype == RAT_DTYPE_BF16, s));
+}
+
+}  // namespace
+
+rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw, const void* vw,
+                            int w_cap, void* out, int B, int T, int H, int d, const int* D, const int* W, float scale,
+                            rat_dtype dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int ns = 1;
+    size_t need = 0;
+    const rat_status rc = check_decode(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, D, W, scale, dtype, &ns,
+                                       &need);
+    if (rc != RAT_OK) return rc;
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) return RAT_ERR_WORKSPACE;
+    return launch_decode_checked(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, D, W, scale, dtype, ns,
+                                 static_cast<float*>(workspace), (hipStream_t)stream);
+}
+
+size_t rat_decode_static_scratch_bytes(void) { return kDecodeScratchBytes; }
+
+rat_status rat_dilated_attn_decode_static(const void* q, const void* kd, const void* vd, int nd_cap, const void* kw,
+                                          const void* vw, int w_cap, void* out, int B, int T, int H, int d,
+                                          const int* D, const int* W, float scale, rat_dtype dtype, void* stream)
+{
+    int ns = 1;
+    size_t need = 0;
+    const rat_status rc = check_decode(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, D, W, scale, dtype, &ns,
+                                       &need);
+    if (rc != RAT_OK) return rc;
+    if (need > kDecodeScratchBytes) return RAT_ERR_WORKSPACE;
+    float* part = nullptr;
+    if (need > 0) {
+        void* p = nullptr;
+        const hipError_t e = decode_scratch(&p);
+        if (e != hipSuccess) return hip_status(e);
+        part = static_cast<float*>(p);
+    }
+    return launch_decode_checked(q, kd, vd, nd_cap, kw, vw, w_cap, out, B, T, H, d, D, W, scale, dtype, ns, part,
+                                 (hipStream_t)stream);
 }
 
 rat_status rat_decode_step(const void* q, const void* k_new, const void* v_new, const void* gate_new, float* state,

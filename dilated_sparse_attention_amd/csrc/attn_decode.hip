@@ -13,6 +13,8 @@
 // every key group keeps its own online-softmax state, merged across lane
 // groups and waves at the end.  Long caches with few (b, h) pairs are split
 // over several workgroups whose partial states a second kernel merges.
+#include <mutex>
+
 #include "rat_device.h"
 #include "rat_internal.h"
 
@@ -377,6 +379,32 @@ hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream)
     if (bf16) hipLaunchKernelGGL(decode_step_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+// The scratch of rat_dilated_attn_decode_static: split partials
+// [B*H][nsplit][d + 2] in fp32.  Host code never uses the array's name as an
+// address (on the host it is a stand-in, not device memory): kernels get
+// the pointer hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* cached[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        cached[dev] = p;
+    }
+    *ptr = cached[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream)

@@ -151,6 +151,13 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, hipStream_t stream);
 
+// Split partials of the decode entry point that allocates nothing: a
+// file-scope device array of kDecodeScratchBytes per GPU, held until the
+// process ends.  decode_scratch returns its address on the current device
+// (looked up once per device, with that device current).
+constexpr size_t kDecodeScratchBytes = (size_t)1 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Recurrence step of the decode loop: the new token's state from the
 // running fp32 state, written to the state history and the raw ring.
 struct StepArgs {

@@ -28,6 +28,7 @@ STATUS = {0: "RAT_OK", 1: "RAT_ERR_NULL", 2: "RAT_ERR_SHAPE", 3: "RAT_ERR_UNSUPP
 EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_workspace_bytes", "rat_dilated_attn_prefill",
            "rat_chunk_attn_prefill",
            "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_layer_prefill",
+           "rat_decode_static_scratch_bytes", "rat_dilated_attn_decode_static",
            "rat_layer_backward_workspace_bytes", "rat_layer_backward", "rat_build_decode_caches",
            "rat_status_string",
            "rat_last_hip_error")
@@ -71,6 +72,10 @@ def load_library(path: str = LIBRARY):
     lib.rat_decode_workspace_bytes.restype = sz
     lib.rat_dilated_attn_decode.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp, sz, vp]
     lib.rat_dilated_attn_decode.restype = i
+    lib.rat_decode_static_scratch_bytes.argtypes = []
+    lib.rat_decode_static_scratch_bytes.restype = sz
+    lib.rat_dilated_attn_decode_static.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp]
+    lib.rat_dilated_attn_decode_static.restype = i
     lib.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, ip, ip, f, i, vp, sz,
                                     vp]
     lib.rat_decode_step.restype = i
@@ -266,6 +271,28 @@ def dilated_attn_decode(q, kd, vd, kw, vw, T, D, W, scale=None, out=None, worksp
                                      _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                      _stream())
     _raise("rat_dilated_attn_decode", rc, lib)
+    return out
+
+
+def dilated_attn_decode_static(q, kd, vd, kw, vw, T, D, W, scale=None, out=None):
+    """dilated_attn_decode without a workspace: the library keeps the split
+    partials in its own static per-GPU scratch (calls overlapping on one GPU
+    race; see rat_dilated_attn_decode_static)."""
+    lib = load_library()
+    B, H, d = q.shape
+    _check_tensor("q", q, q.dtype)
+    _check_tensor("kd", kd, q.dtype)
+    _check_tensor("vd", vd, q.dtype, kd.shape)
+    _check_tensor("kw", kw, q.dtype)
+    _check_tensor("vw", vw, q.dtype, None if kw is None else kw.shape)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    w_cap = 0 if kw is None else kw.shape[2]
+    rc = lib.rat_dilated_attn_decode_static(_ptr(q), _ptr(kd), _ptr(vd), kd.shape[2], _ptr(kw), _ptr(vw), w_cap,
+                                            _ptr(out), B, int(T), H, d, _heads(D, H), _heads(W, H), scale,
+                                            _DTYPES[q.dtype], _stream())
+    _raise("rat_dilated_attn_decode_static", rc, lib)
     return out
 
 

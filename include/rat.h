@@ -159,6 +159,24 @@ rat_status rat_dilated_attn_decode(const void* q, const void* kd, const void* vd
                             float scale, rat_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * attention of rat_dilated_attn_decode, same arguments and results, without
+ * a workspace.  Its split-key partials live in a static scratch array of
+ * rat_decode_static_scratch_bytes() bytes (1 MiB) that the library defines
+ * once per GPU and holds until the process ends; the call allocates and
+ * frees nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (two streams, two threads) race: order
+ * them.  Nothing in the array needs to start at zero.  The partials need
+ * B*H*nsplit*(d+2)*4 bytes with B*H*nsplit below 1024, so every valid call
+ * fits; a call that would not returns RAT_ERR_WORKSPACE before launching.
+ * Errors: as rat_dilated_attn_decode (RAT_ERR_WORKSPACE only as above). */
+size_t rat_decode_static_scratch_bytes(void);
+rat_status rat_dilated_attn_decode_static(const void* q, const void* kd, const void* vd, int nd_cap,
+                                          const void* kw, const void* vw, int w_cap, void* out,
+                                          int B, int T, int H, int d, const int* D, const int* W,
+                                          float scale, rat_dtype dtype, void* stream);
+
 /* One step of a decode loop (the recurrence of Deep Dive 2.1 for one new
  * token, then the decode attention above): the token at position T-1 of a
  * T-token context arrives with its query q, raw key / value k_new, v_new

@@ -314,3 +314,26 @@ def test_cached_workspaces_are_per_stream(monkeypatch):
         current["s"] = Stream(11)
         assert get(4096, "cuda:0") is a
         assert get(1 << 16, "cuda:0").numel() >= 1 << 16  # grown on demand
+
+
+def test_static_decode_validation(lib):
+    """The decode entry point without a workspace validates like the one
+    with: errors before any HIP call (the fake pointers are never touched)."""
+    assert lib.rat_decode_static_scratch_bytes() == 1 << 20
+    D, W = heads([4, 4]), heads([0, 8])
+
+    def call(q=P[0], kd=P[1], vd=P[2], nd=64, kw=P[3], vw=P[4], wc=8, out=P[5], B=1, T=100, H=2, d=64, Dh=D, Wh=W,
+             scale=0.125, dtype=1):
+        return lib.rat_dilated_attn_decode_static(q, kd, vd, nd, kw, vw, wc, out, B, T, H, d, Dh, Wh, scale, dtype,
+                                                  None)
+
+    assert call(q=None) == NULL
+    assert call(kw=None) == NULL
+    assert call(B=0) == SHAPE
+    assert call(nd=10) == SHAPE      # ceil(100 / 4) = 25 entries needed
+    assert call(wc=4) == SHAPE       # min(W, T) = 8 ring slots needed
+    assert call(d=96) == UNSUP
+    assert call(dtype=5) == UNSUP
+    assert call(out=P[0]) == ALIAS
+    assert call(q=MIS) == ALIGN
+    assert call(scale=float("nan")) == SHAPE
