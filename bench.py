@@ -38,6 +38,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, false>"
 ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false, false, false>"
 
+# launches timed per kernel (each between its own pair of HIP events)
+MIN_TIMED = 50
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -45,10 +48,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-extra", action="store_true", help="only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--launches", type=int, default=50,
+                   help="launches timed per kernel, each between its own HIP events (profiled runs use fewer)")
     p.add_argument("--only", default=None, help="run one workload of --list by name (profiling)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -58,6 +63,44 @@ def parse():
 # ------------------------------------------------------------------ helpers
 def progress(*parts):
     print("[bench]", *parts, file=sys.stderr, flush=True)
+
+
+def time_launches(torch, fn, n, warmup):
+    """Per-launch durations (ms) of ``fn(i)``: ``warmup`` untimed calls, then
+    ``n`` calls, each between its own pair of HIP events recorded on the
+    launch stream; returns median, p10, p90 and mean."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        fn(i)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    def pct(p):
+        x = p * (len(ms) - 1)
+        lo = int(x)
+        hi = min(lo + 1, len(ms) - 1)
+        return ms[lo] + (ms[hi] - ms[lo]) * (x - lo)
+
+    return {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9), "mean": sum(ms) / len(ms), "n": len(ms)}
+
+
+def stats_fields(prefix, st, nbytes=None, flops=None):
+    """JSON fields of one kernel's launch statistics, its rates at the median."""
+    out = {f"{prefix}_ms": st["median"], f"{prefix}_ms_p10": st["p10"], f"{prefix}_ms_p90": st["p90"],
+           f"{prefix}_ms_mean": st["mean"], f"{prefix}_launches_timed": st["n"]}
+    sec = st["median"] / 1e3
+    if nbytes is not None:
+        out[f"{prefix}_GBps"] = nbytes / sec / 1e9
+        out[f"{prefix}_hbm_frac"] = nbytes / sec / 1e9 / HBM_PEAK_GBS
+    if flops is not None:
+        out[f"{prefix}_TFLOPs"] = flops / sec / 1e12
+        out[f"{prefix}_mfma_frac"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    return out
 
 
 def load_traffic(kernel):
@@ -133,28 +176,21 @@ def run_prefill(torch, rat, w, steps, warmup, mode=0, nsets=3):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / steps
-    # per-kernel durations: each kernel launched `steps` times back to back
-    # over the rotating sets, between two events on the launch stream (an
-    # event pair around every single launch would add its own gap to each)
-    def kernel_ms(which):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            x, ks, vs, out = sets[i % nsets]
-            if which == "scan":
-                rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)
-            else:
-                rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None, x["v"] if need_raw else None,
-                                         D=D, W=W, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
 
-    scan_ms, attn_ms = kernel_ms("scan"), kernel_ms("attn")
+    def launch(which, i):
+        x, ks, vs, out = sets[i % nsets]
+        if which == "scan":
+            rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=ks, v_state=vs)
+        else:
+            rat.dilated_attn_prefill(x["q"], ks, vs, x["k"] if need_raw else None, x["v"] if need_raw else None,
+                                     D=D, W=W, out=out)
+
+    n = max(steps, MIN_TIMED)
+    scan_st = time_launches(torch, lambda i: launch("scan", i), n, warmup)
+    attn_st = time_launches(torch, lambda i: launch("attn", i), n, warmup)
     del sets
     torch.cuda.empty_cache()
-    return ms_step, wall, scan_ms, attn_ms
+    return ms_step, wall, scan_st, attn_st
 
 
 def run_decode(torch, rat, w, steps, warmup, nsets=3):
@@ -174,24 +210,14 @@ def run_decode(torch, rat, w, steps, warmup, nsets=3):
         rat.dilated_attn_decode(x["q"], x["kd"], x["vd"], x["kw"], x["vw"], w.T, D, W, out=x["out"],
                                 workspace=ws if ws_bytes else None)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = time_launches(torch, call, max(steps, MIN_TIMED), warmup)
     nd = [(w.T + Dh - 1) // Dh for Dh in w.D]
     nw = [min(Wh, w.T) for Wh in w.W]
     s = 2
     nbytes = w.B * sum((a + b) * 2 * w.d * s for a, b in zip(nd, nw)) + 2 * w.B * w.H * w.d * s
     del sets
     torch.cuda.empty_cache()
-    return ms, nbytes
+    return st, nbytes
 
 
 def chunk_units(w):
@@ -209,7 +235,7 @@ def chunk_units(w):
 def run_chunk(torch, rat, w, steps, warmup, nsets=3):
     """Chunk-grid attention over the recurrence states of the prefill
     workload `w` (the states come from the scan kernel, outside the timed
-    region); back-to-back launches over rotating sets."""
+    region), over rotating sets."""
     from dilated_sparse_attention_amd import inputs
 
     sets = []
@@ -220,29 +246,18 @@ def run_chunk(torch, rat, w, steps, warmup, nsets=3):
         del x
     D = list(w.D)
     call = lambda i: rat.chunk_attn_prefill(*sets[i % nsets][:3], D=D, out=sets[i % nsets][3])  # noqa: E731
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = time_launches(torch, call, max(steps, MIN_TIMED), warmup)
     del sets
     torch.cuda.empty_cache()
-    return ms
+    return st
 
 
 def run_decode_caches(torch, rat, w, steps, warmup, nsets=3):
     """The decode caches of a finished prefill of workload `w`: its states
     copied into the per-residue history and its last W raw tokens into the
-    ring (the states come from the scan kernel, outside the timed region);
-    back-to-back launches over rotating sets.  Algorithmic bytes: the
-    states read and the history written once, the ring's raw rows read and
-    written once."""
+    ring (the states come from the scan kernel, outside the timed region),
+    over rotating sets.  Algorithmic bytes: the states read and the history
+    written once, the ring's raw rows read and written once."""
     from dilated_sparse_attention_amd import inputs
 
     sets = []
@@ -256,33 +271,23 @@ def run_decode_caches(torch, rat, w, steps, warmup, nsets=3):
         kw = torch.empty((w.B, w.H, w_cap, w.d), dtype=ks.dtype, device="cuda") if w_cap > 0 else None
         sets.append((ks, vs, x["k"], x["v"], kc, torch.empty_like(kc), kw, None if kw is None else torch.empty_like(kw)))
         del x
+
     def call(i):
         ks, vs, k, v, kc, vc, kw, vw = sets[i % nsets]
         rat.build_decode_caches(ks, vs, k, v, D, W, n_cap=n_cap, w_cap=w_cap, kc=kc, vc=vc, kw=kw, vw=vw)
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    st = time_launches(torch, call, max(steps, MIN_TIMED), warmup)
     del sets
     torch.cuda.empty_cache()
     s = 2
     nbytes = 2 * 2 * w.B * w.T * w.H * w.d * s + 2 * 2 * w.B * w.d * s * sum(min(Wh, w.T) for Wh in W)
-    return ms, nbytes
+    return st, nbytes
 
 
 def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
     """One decode-loop step (recurrence update, history and ring writes,
     decode attention) at context length w.T for the whole batch: the state
     history holds every position (n_cap = D ceil(T / D) rows per head)."""
-    from dilated_sparse_attention_amd import inputs
-
     D, W = list(w.D), list(w.W)
     n_cap = max(Dh * ((w.T + Dh - 1) // Dh) for Dh in D)
     sets = []
@@ -304,17 +309,7 @@ def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
         rat.decode_step(x["q"], x["k"], x["v"], x["gate"], x["state"], x["kc"], x["vc"], x["kw"], x["vw"], w.T,
                         D, W, out=x["out"], workspace=ws if ws_bytes else None)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = time_launches(torch, call, max(steps, MIN_TIMED), warmup)
     # bytes: q, k, v, gate read; state read and written (fp32); the state
     # row and the raw token written; the residue's history rows and the ring
     # read; the output written
@@ -324,7 +319,7 @@ def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
     nbytes = 4 * E * s + 2 * (2 * E * 4) + 4 * E * s + 2 * rows * s + E * s
     del sets
     torch.cuda.empty_cache()
-    return ms, nbytes
+    return st, nbytes
 
 
 def run_backward_arl(torch, rat, w, steps, warmup):
@@ -349,22 +344,12 @@ def run_backward_arl(torch, rat, w, steps, warmup):
         parts.append((xs, ks, vs, dout[b0:b0 + half].contiguous(), [Dv] * w.H, grads, ws))
     del x
 
-    def step():
+    def step(_):
         for xs, ks, vs, do, D, grads, ws in parts:
             rat.layer_backward(xs["q"], xs["k"], xs["v"], xs["gate"], ks, vs, do, D, [0] * w.H, grads=grads,
                                workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = time_launches(torch, step, max(steps, MIN_TIMED), warmup)
     # algorithmic units: per visible (query, key) pair five length-d
     # contractions (scores, dout.v, and the three gradient products); bytes:
     # the seven inputs once and the four fp32 gradients once
@@ -374,7 +359,7 @@ def run_backward_arl(torch, rat, w, steps, warmup):
     nbytes = 7 * E * 2 + 4 * E * 4
     del parts
     torch.cuda.empty_cache()
-    return ms, flops, nbytes
+    return st, flops, nbytes
 
 
 def run_copy_reference(torch, nbytes, steps, nsets=3):
@@ -384,24 +369,38 @@ def run_copy_reference(torch, nbytes, steps, nsets=3):
     n = nbytes // 2
     bufs = [(torch.ones(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
             for _ in range(nsets)]
-    for i in range(2 * nsets):
-        bufs[i % nsets][1].copy_(bufs[i % nsets][0])
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        bufs[i % nsets][1].copy_(bufs[i % nsets][0])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = time_launches(torch, lambda i: bufs[i % nsets][1].copy_(bufs[i % nsets][0]), max(steps, MIN_TIMED),
+                       2 * nsets)
     del bufs
     torch.cuda.empty_cache()
-    return ms
+    return st
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, min_s=12.0, max_reps=100):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _timed(fn, min_s, max_reps):
+    """Seconds per call of ``fn``: repeated until ``min_s`` seconds have
+    passed (at least once, at most ``max_reps`` times)."""
+    reps, total, out = 0, 0.0, None
+    while (total < min_s and reps < max_reps) or reps == 0:
+        t0 = time.perf_counter()
+        out = fn()
+        total += time.perf_counter() - t0
+        reps += 1
+    return total / reps, reps, out
+
+
+def cpu_baseline(w, min_s=10.0, max_reps=100):
     """The fp64 oracle on the host cores, timed on the headline workload
     itself: one oracle step is the recurrence over every (batch, token, head,
     channel) followed by attention for every query row, from inputs already
@@ -417,24 +416,83 @@ def cpu_baseline(w, min_s=12.0, max_reps=100):
     x = inputs.make_prefill(w, seed=0)
     q, k, v, g = (np.ascontiguousarray(x[n].double().numpy()) for n in ("q", "k", "v", "gate"))
     need_raw = any(wh > 0 for wh in w.W)
-    reps, t_total = 0, 0.0
-    while (t_total < min_s and reps < max_reps) or reps == 0:
-        t0 = time.perf_counter()
+
+    def step():
         ks, vs = orc.scan(k, v, g, w.L, 0)
         orc.attn_prefill(q, ks, vs, k if need_raw else None, v if need_raw else None, w.D, w.W, w.scale)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    per_step = t_total / reps
+
+    per_step, reps, _ = _timed(step, min_s, max_reps)
+    total = per_step * reps
     return {"value": w.B * w.T / per_step, "unit": "tokens/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": (f"fp64 C oracle (OpenMP), the whole {w.name} step (recurrence over all "
                        f"{w.B}x{w.T}x{w.H}x{w.d} elements, then attention for all {w.B * w.T * w.H} query "
-                       f"rows) repeated {reps} times in {t_total:.1f} s: {per_step:.2f} s per step")}
+                       f"rows) repeated {reps} times in {total:.1f} s: {per_step:.2f} s per step")}
+
+
+def cpu_baseline_per_config(budget_s=4.0, sample_rows=1024):
+    """The oracle per workload and per stage (recurrence, attention, decode),
+    on the host cores, each stage timed by repetition for about ``budget_s``
+    seconds.  Stages whose full run would take much longer (the attention of
+    the long and hybrid prefills) are timed on ``sample_rows`` random query
+    rows and scaled to the whole workload by visible (query, key) pairs;
+    those entries say "extrapolated"."""
+    import numpy as np
+
+    from dilated_sparse_attention_amd import inputs
+    from oracle import oracle
+
+    oracle.build(force=False)
+    orc = oracle.default()
+    res = {"cores": orc.num_threads(), "cpu_model": _cpu_model(), "kind": "oracle", "configs": {}}
+    big = {inputs.PREFILL_LONG.name, inputs.PREFILL_7P6B_HYBRID.name}
+    for w in inputs.PREFILL_WORKLOADS:
+        x = inputs.make_prefill(w, seed=0)
+        q, k, v, g = (np.ascontiguousarray(x[n].double().numpy()) for n in ("q", "k", "v", "gate"))
+        del x
+        need_raw = any(wh > 0 for wh in w.W)
+        kr, vr = (k, v) if need_raw else (None, None)
+        entry = {"config": w.describe()}
+        for mode in w.modes:
+            tag = "restart" if mode == 0 else "sliding"
+            t_scan, reps, (ks, vs) = _timed(lambda: orc.scan(k, v, g, w.L, mode), budget_s, 20)
+            entry[f"scan_s_{tag}"] = t_scan
+            if w.name in big:
+                rng = np.random.default_rng(5)
+                rows = np.stack([rng.integers(0, w.B, sample_rows), rng.integers(0, w.T, sample_rows),
+                                 rng.integers(0, w.H, sample_rows)], 1).astype(np.int32)
+                t_rows, _, _ = _timed(lambda: orc.attn_prefill_rows(q, ks, vs, kr, vr, rows, w.D, w.W, w.scale),
+                                      budget_s, 50)
+                pairs_rows = sum(t // w.D[h] + 1 + min(w.W[h], t + 1) for _, t, h in rows.tolist())
+                pairs_all = w.B * sum(sum(attn_pairs(w.T, Dh, Wh)) for Dh, Wh in zip(w.D, w.W))
+                t_attn = t_rows * pairs_all / pairs_rows
+                entry["attn_timing"] = (f"extrapolated: {sample_rows} random query rows in {t_rows:.3f} s, "
+                                        f"scaled by visible pairs ({pairs_all} / {pairs_rows})")
+            else:
+                t_attn, _, _ = _timed(lambda: orc.attn_prefill(q, ks, vs, kr, vr, w.D, w.W, w.scale), budget_s, 20)
+                entry["attn_timing"] = "every query row"
+            entry[f"attn_s_{tag}"] = t_attn
+            entry[f"prefill_tokens_per_s_{tag}"] = w.B * w.T / (t_scan + t_attn)
+            del ks, vs
+        res["configs"][w.name] = entry
+        del q, k, v, g
+    for w in inputs.DECODE_WORKLOADS:
+        x = inputs.make_decode(w, seed=0)
+        a = {n: np.ascontiguousarray(t.double().numpy()) for n, t in x.items()}
+        del x
+        t_dec, _, _ = _timed(lambda: orc.attn_decode(a["q"], a["kd"], a["vd"], a["kw"], a["vw"], w.T, w.D, w.W,
+                                                     w.scale), budget_s, 50)
+        res["configs"][w.name] = {"config": w.describe(), "decode_s": t_dec, "decode_tokens_per_s": w.B / t_dec,
+                                  "attn_timing": "every sequence of the batch"}
+        del a
+    return res
 
 
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    global MIN_TIMED
+    MIN_TIMED = max(1, args.launches)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} is not supported "
@@ -462,61 +520,55 @@ def main():
     w = inputs.PREFILL_1P5B
     if args.only is None or args.only == w.name:
         progress("prefill", w.name)
-        ms, wall, scan_ms, attn_ms = run_prefill(torch, rat, w, args.steps, args.warmup)
+        ms, wall, scan_st, attn_st = run_prefill(torch, rat, w, args.steps, args.warmup)
     else:
-        ms = wall = scan_ms = attn_ms = None
+        ms = wall = scan_st = attn_st = None
     scan_bytes, attn_bytes, attn_flops = prefill_units(w)
 
     extra = {}
     if not args.no_extra:
-        for pw in (inputs.PREFILL_LONG, inputs.PREFILL_7P6B_HYBRID):
+        for pw in (inputs.TINY_FP32, inputs.PREFILL_LONG, inputs.PREFILL_7P6B_HYBRID):
             for mode in pw.modes:
                 key = pw.name + ("" if len(pw.modes) == 1 else ("_restart" if mode == 0 else "_sliding"))
                 if args.only is not None and args.only != key:
                     continue
                 progress("prefill", key)
-                m2, _, s_ms, a_ms = run_prefill(torch, rat, pw, max(3, args.steps // 4), 2, mode=mode)
+                m2, _, s_st, a_st = run_prefill(torch, rat, pw, args.steps, args.warmup, mode=mode)
                 sb, ab, af = prefill_units(pw)
+                a_sec = a_st["median"] / 1e3
                 extra[key] = {
-                    "prefill_tokens_per_s": pw.B * pw.T / (m2 / 1e3), "ms_per_step": m2,
-                    "scan_ms": s_ms, "scan_GBps": sb / (s_ms / 1e3) / 1e9,
-                    "scan_hbm_frac": sb / (s_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                    "attn_ms": a_ms, "attn_GBps": ab / (a_ms / 1e3) / 1e9,
-                    "attn_TFLOPs": af / (a_ms / 1e3) / 1e12,
-                    "attn_mfma_frac": af / (a_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                    "attn_roofline_frac": (max(ab / HBM_PEAK_GBS / 1e9, af / MFMA_BF16_PEAK_TFLOPS / 1e12)
-                                           / (a_ms / 1e3)),
+                    "prefill_tokens_per_s": pw.B * pw.T / ((s_st["median"] + a_st["median"]) / 1e3),
+                    "ms_per_step": m2,
+                    **stats_fields("scan", s_st, nbytes=sb),
+                    **stats_fields("attn", a_st, nbytes=ab, flops=af),
+                    "attn_roofline_frac": (max(ab / HBM_PEAK_GBS / 1e9, af / MFMA_BF16_PEAK_TFLOPS / 1e12) / a_sec),
+                    "scan_algorithmic_bytes": sb, "attn_algorithmic_bytes": ab, "attn_algorithmic_flops": af,
                     "config": pw.describe(), "mode": "restart" if mode == 0 else "sliding"}
         for dw in inputs.DECODE_WORKLOADS:
             if args.only is not None and args.only != dw.name:
                 continue
             progress("decode", dw.name)
-            dms, dbytes = run_decode(torch, rat, dw, max(5, args.steps), 3)
-            extra[dw.name] = {"decode_tokens_per_s": dw.B / (dms / 1e3), "decode_ms": dms,
-                              "GBps": dbytes / (dms / 1e3) / 1e9,
-                              "hbm_frac": dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            dst, dbytes = run_decode(torch, rat, dw, args.steps, args.warmup)
+            extra[dw.name] = {"decode_tokens_per_s": dw.B / (dst["median"] / 1e3),
+                              **stats_fields("decode", dst, nbytes=dbytes), "algorithmic_bytes": dbytes,
                               "config": dw.describe()}
 
         cw = inputs.PREFILL_1P5B
         key = "chunk_grid_" + cw.name
         if args.only is None or args.only == key:
             progress("chunk grid", cw.name)
-            cms = run_chunk(torch, rat, cw, max(5, args.steps), 3)
+            cst = run_chunk(torch, rat, cw, args.steps, args.warmup)
             cb, cf = chunk_units(cw)
-            extra[key] = {"attn_ms": cms, "attn_GBps": cb / (cms / 1e3) / 1e9,
-                          "hbm_frac": cb / (cms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                          "attn_TFLOPs": cf / (cms / 1e3) / 1e12,
-                          "mfma_frac": cf / (cms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            extra[key] = {**stats_fields("attn", cst, nbytes=cb, flops=cf),
                           "algorithmic_bytes": cb, "algorithmic_flops": cf,
                           "config": dict(cw.describe(), attention="chunk grid: chunk-end states + own state")}
         sw = inputs.DECODE_2P6B_D64
         key = "decode_step_" + sw.name
         if args.only is None or args.only == key:
             progress("decode step", sw.name)
-            sms, sbytes = run_decode_step(torch, rat, sw, max(5, args.steps), 3)
-            extra[key] = {"decode_tokens_per_s": sw.B / (sms / 1e3), "step_ms": sms,
-                          "GBps": sbytes / (sms / 1e3) / 1e9, "hbm_frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                          "algorithmic_bytes": sbytes,
+            sst, sbytes = run_decode_step(torch, rat, sw, args.steps, args.warmup)
+            extra[key] = {"decode_tokens_per_s": sw.B / (sst["median"] / 1e3),
+                          **stats_fields("step", sst, nbytes=sbytes), "algorithmic_bytes": sbytes,
                           "config": dict(sw.describe(), history_rows_per_head=max(
                               Dh * ((sw.T + Dh - 1) // Dh) for Dh in sw.D))}
 
@@ -524,20 +576,17 @@ def main():
         key = "decode_caches_" + cw.name
         if args.only is None or args.only == key:
             progress("decode caches from a prefill", cw.name)
-            cms, cbytes = run_decode_caches(torch, rat, cw, max(5, args.steps), 3)
-            extra[key] = {"caches_ms": cms, "GBps": cbytes / (cms / 1e3) / 1e9,
-                          "hbm_frac": cbytes / (cms / 1e3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": cbytes,
+            cst, cbytes = run_decode_caches(torch, rat, cw, args.steps, args.warmup)
+            extra[key] = {**stats_fields("caches", cst, nbytes=cbytes), "algorithmic_bytes": cbytes,
                           "config": dict(cw.describe(), caches="per-residue state history + raw ring of the last W")}
 
         bw = inputs.PREFILL_1P5B
         key = "backward_arl_" + bw.name
         if args.only is None or args.only == key:
             progress("backward (ARL halves D=1 / D=64)", bw.name)
-            bms, bflops, bbytes = run_backward_arl(torch, rat, bw, max(3, args.steps // 4), 1)
-            extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bms / 1e3), "ms_per_step": bms,
-                          "TFLOPs": bflops / (bms / 1e3) / 1e12,
-                          "mfma_frac": bflops / (bms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                          "GBps": bbytes / (bms / 1e3) / 1e9, "hbm_frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            bst, bflops, bbytes = run_backward_arl(torch, rat, bw, args.steps, 2)
+            extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bst["median"] / 1e3),
+                          **stats_fields("backward", bst, nbytes=bbytes, flops=bflops),
                           "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
                           "config": dict(bw.describe(), D="half the batch at 1, half at 64", W=0,
                                          recurrence="full")}
@@ -546,20 +595,25 @@ def main():
         print(json.dumps({"extra": extra}))
         return
 
+    scan_ms, attn_ms = scan_st["median"], attn_st["median"]
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
     attn_gbs = attn_bytes / (attn_ms / 1e3) / 1e9
     if scan_ms >= attn_ms:
-        dom, dom_bytes, dom_ms, dom_kernel = "scan", scan_bytes, scan_ms, SCAN_KERNEL
+        dom_bytes, dom_st, dom_kernel = scan_bytes, scan_st, SCAN_KERNEL
     else:
-        dom, dom_bytes, dom_ms, dom_kernel = "attn", attn_bytes, attn_ms, ATTN_KERNEL
+        dom_bytes, dom_st, dom_kernel = attn_bytes, attn_st, ATTN_KERNEL
+    dom_ms = dom_st["median"]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     progress("device copy of", dom_bytes, "bytes (achievable HBM rate)")
-    copy_ms = run_copy_reference(torch, dom_bytes, 20)
+    copy_st = run_copy_reference(torch, dom_bytes, args.steps)
+    copy_ms = copy_st["median"]
     copy_gbs = dom_bytes / (copy_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom_kernel),
                 "kernel": dom_kernel, "algorithmic_bytes_per_launch": dom_bytes,
-                "kernel_ms": round(dom_ms, 4),
+                "kernel_ms": round(dom_ms, 4), "kernel_ms_p10": round(dom_st["p10"], 4),
+                "kernel_ms_p90": round(dom_st["p90"], 4), "launches_timed": dom_st["n"],
+                "timing": "median of per-launch HIP event pairs on the launch stream",
                 "copy_reference": {"GBps": round(copy_gbs, 1), "ms": round(copy_ms, 4),
                                    "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
                                    "kernel_frac_of_copy": round(achieved / copy_gbs, 4),
@@ -576,12 +630,9 @@ def main():
         "config": w.describe(),
         "roofline": roofline,
         "kernels": {
-            SCAN_KERNEL: {"ms": scan_ms, "GBps": scan_gbs, "hbm_frac": scan_gbs / HBM_PEAK_GBS,
-                                 "algorithmic_bytes": scan_bytes},
-            ATTN_KERNEL: {"ms": attn_ms, "GBps": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS,
-                                    "TFLOPs": attn_flops / (attn_ms / 1e3) / 1e12,
-                                    "mfma_frac": attn_flops / (attn_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                                    "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops},
+            SCAN_KERNEL: {**stats_fields("scan", scan_st, nbytes=scan_bytes), "algorithmic_bytes": scan_bytes},
+            ATTN_KERNEL: {**stats_fields("attn", attn_st, nbytes=attn_bytes, flops=attn_flops),
+                          "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops},
         },
         "wall_s_timed": wall,
         "sources_hash": profiling.kernel_sources_hash(),
@@ -589,8 +640,11 @@ def main():
     if extra:
         line["extra"] = extra
     if not args.no_cpu_baseline:
-        progress("cpu baseline (oracle)")
+        progress("cpu baseline (oracle), headline step")
         line["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_extra:
+            progress("cpu baseline (oracle), per workload and stage")
+            line["cpu_baseline"]["per_config"] = cpu_baseline_per_config()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line))

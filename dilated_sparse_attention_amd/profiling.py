@@ -132,16 +132,34 @@ def _all_counter_means(paths):
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
 
 
-def counters_table(paths, title, command):
+MFMA_FLOP_PER_INSTR = 16384      # v_mfma_f32_16x16x32_bf16, the only MFMA these kernels issue
+MFMA_PEAK_FLOPS = 2.5e15          # MI355X dense bf16 MFMA
+NUM_CU = 256
+
+
+def _avg_duration_ns(stats_csv):
+    """{kernel: average duration in ns} from a rocprofv3 kernel_stats.csv."""
+    out = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            out[short_name(r["Name"])] = float(r["AverageNs"])
+    return out
+
+
+def counters_table(paths, title, command, stats_csv=None):
     means = _all_counter_means(paths)
+    dur = _avg_duration_ns(stats_csv) if stats_csv else {}
     out = [f"# {title}", "", "Commands (one rocprofv3 pass per counter set):", "", "```", command, "```", "",
            f"Kernel sources hash: `{kernel_sources_hash()}`", "",
            "Per wave: instructions issued (SQ_INSTS_* / SQ_WAVES). Issue and wait shares: SQ_ACTIVE_INST_ANY "
            "and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES (wave-cycles). LDS conflicts: SQ_LDS_BANK_CONFLICT cycles "
            "per LDS instruction.", "",
+           "MFMA utilisation: issued MFMA FLOPs (SQ_INSTS_MFMA x 16,384 per v_mfma_f32_16x16x32_bf16) over "
+           "(average kernel duration from the kernel trace x 2.5 PFLOP/s); MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES "
+           "over (GRBM_GUI_ACTIVE x 256 CUs), the share of CU-cycles with the matrix unit busy.", "",
            "| kernel | waves | VALU/wave | MFMA/wave | LDS/wave | SALU/wave | VMEM/wave | issuing | waiting | "
-           "waiting on LDS | LDS conflict cyc/instr |",
-           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+           "waiting on LDS | LDS conflict cyc/instr | avg us | MFMA util | MFMA busy |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
 
     def ratio(d, a, b):
         return d[a] / d[b] if a in d and d.get(b) else float("nan")
@@ -154,7 +172,10 @@ def counters_table(paths, title, command):
                    f"{ratio(d, 'SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES'):.2f} | "
                    f"{ratio(d, 'SQ_WAIT_INST_ANY', 'SQ_WAVE_CYCLES'):.2f} | "
                    f"{ratio(d, 'SQ_WAIT_INST_LDS', 'SQ_WAVE_CYCLES'):.2f} | "
-                   f"{ratio(d, 'SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS'):.2f} |")
+                   f"{ratio(d, 'SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS'):.2f} | "
+                   f"{dur[k] / 1e3 if k in dur else float('nan'):.1f} | "
+                   f"{d['SQ_INSTS_MFMA'] * MFMA_FLOP_PER_INSTR / (dur[k] * 1e-9) / MFMA_PEAK_FLOPS if k in dur and 'SQ_INSTS_MFMA' in d else float('nan'):.3f} | "
+                   f"{ratio(d, 'SQ_VALU_MFMA_BUSY_CYCLES', 'GRBM_GUI_ACTIVE') / NUM_CU:.3f} |")
     return "\n".join(out) + "\n"
 
 
@@ -174,11 +195,12 @@ def main(argv=None):
     c.add_argument("csv", nargs="+")
     c.add_argument("--title", required=True)
     c.add_argument("--command", required=True)
+    c.add_argument("--stats", default=None, help="kernel_stats.csv of the same workload (durations)")
     a = p.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_table(a.csv, a.title, a.command, a.match))
     elif a.cmd == "counters":
-        sys.stdout.write(counters_table(a.csv, a.title, a.command))
+        sys.stdout.write(counters_table(a.csv, a.title, a.command, a.stats))
     else:
         sys.stdout.write(json.dumps(traffic(a.fetch, a.write, a.command), indent=1) + "\n")
 
