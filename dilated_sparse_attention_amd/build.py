@@ -26,6 +26,10 @@ FLAGS = [
     "-shared",
     # keep the compiler from emitting packed fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics stay single atomics: the optimizer's wave-wide
+    # rewrite reads the result back at once, a full memory wait in every
+    # wave that runs the code
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",

@@ -744,4 +744,101 @@ rat_status rat_decode_step(const void* q, const void* k_new, const void* v_new, 
     return hip_status(launch_decode(a, d, bf16, s));
 }
 
+// Longest recurrence window a SLIDING decode step runs over (each step
+// reads the window's L raw rows).
+constexpr int kSlideDecodeMaxL = 1024;
+
+rat_status rat_decode_step_sliding(const void* q, const void* k_new, const void* v_new, const void* gate_new,
+                                   void* rk, void* rv, void* rg, int L, void* kc, void* vc, int n_cap, void* kw,
+                                   void* vw, int w_cap, void* out, int B, int T, int H, int d, const int* D,
+                                   const int* W, float scale, rat_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    if (!q || !k_new || !v_new || !gate_new || !rk || !rv || !rg || !kc || !vc || !out) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || n_cap <= 0 || w_cap < 0 || L < 1) return RAT_ERR_SHAPE;
+    bool any_w = false;
+    const rat_status hc = check_heads(H, D, W, &any_w);
+    if (hc != RAT_OK) return hc;
+    if (any_w && (!kw || !vw)) return RAT_ERR_NULL;
+    const int p = T - 1;  // position of the new token
+    for (int h = 0; h < H; ++h) {
+        if (p / D[h] >= n_cap / D[h]) return RAT_ERR_SHAPE;  // history rows of the residue
+        if (W[h] > w_cap) return RAT_ERR_SHAPE;               // ring slot p mod W
+    }
+    if (L > kSlideDecodeMaxL) return RAT_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !d_ok(d) || !caches_ok(B, H, d, n_cap, w_cap) || !caches_ok(B, H, d, L, 0))
+        return RAT_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return RAT_ERR_SHAPE;
+    const void* ins[4] = {q, k_new, v_new, gate_new};
+    const void* outs[8] = {rk, rv, rg, kc, vc, kw, vw, out};
+    for (int i = 0; i < 8; ++i) {
+        if (!outs[i]) continue;
+        for (const void* in : ins)
+            if (outs[i] == in) return RAT_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return RAT_ERR_ALIAS;
+    }
+    for (const void* x : ins)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (x && !aligned16(x)) return RAT_ERR_ALIGN;
+    const int ns = decode_nsplit(B, H, T, D, W);
+    const size_t need = ns == 1 ? 0 : (size_t)B * H * ns * (d + 2) * sizeof(float);
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) return RAT_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf16 = dtype == RAT_DTYPE_BF16;
+
+    SlideStepArgs st;
+    memset(&st, 0, sizeof(st));
+    st.k_new = k_new; st.v_new = v_new; st.g_new = gate_new;
+    st.rk = rk; st.rv = rv; st.rg = rg;
+    st.kc = kc; st.vc = vc; st.kw = kw; st.vw = vw;
+    st.B = B; st.H = H; st.d = d; st.n_cap = n_cap; st.w_cap = w_cap; st.L = L; st.p = p;
+    for (int h = 0; h < H; ++h) {
+        st.slot_c[h] = (p % D[h]) * (n_cap / D[h]) + p / D[h];
+        st.slot_w[h] = W[h] > 0 ? p % W[h] : -1;
+    }
+    const rat_status rc = hip_status(launch_decode_step_sliding(st, bf16, s));
+    if (rc != RAT_OK) return rc;
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.kd = kc; a.vd = vc; a.kw = kw ? kw : kc; a.vw = vw ? vw : vc; a.out = out;
+    a.part = static_cast<float*>(workspace);
+    a.B = B; a.H = H; a.T = T; a.nd_cap = n_cap; a.w_cap = w_cap; a.nsplit = ns;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    for (int h = 0; h < H; ++h) {
+        a.D[h] = D[h]; a.W[h] = W[h];
+        a.dil_off[h] = (p % D[h]) * (n_cap / D[h]);
+    }
+    return hip_status(launch_decode(a, d, bf16, s));
+}
+
+rat_status rat_sliding_state_from_prefill(const void* k, const void* v, const void* gate_logits, void* rk, void* rv,
+                                          void* rg, int B, int T, int H, int d, int L, rat_dtype dtype,
+                                          void* stream)
+{
+    if (!k || !v || !gate_logits || !rk || !rv || !rg) return RAT_ERR_NULL;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return RAT_ERR_SHAPE;
+    if (L > kSlideDecodeMaxL) return RAT_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d) || !caches_ok(B, H, d, L, 0))
+        return RAT_ERR_UNSUPPORTED;
+    const void* ins[3] = {k, v, gate_logits};
+    const void* outs[3] = {rk, rv, rg};
+    for (int i = 0; i < 3; ++i) {
+        for (const void* in : ins)
+            if (outs[i] == in) return RAT_ERR_ALIAS;
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return RAT_ERR_ALIAS;
+    }
+    for (const void* x : ins)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    for (const void* x : outs)
+        if (!aligned16(x)) return RAT_ERR_ALIGN;
+    SlideFillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k = k; a.v = v; a.g = gate_logits; a.rk = rk; a.rv = rv; a.rg = rg;
+    a.B = B; a.T = T; a.H = H; a.d = d; a.L = L;
+    return hip_status(launch_sliding_fill(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -298,6 +298,115 @@ __global__ __launch_bounds__(256) void decode_step_kernel(StepArgs a)
     }
 }
 
+// One thread per 16 bytes of a (b, h) row: the SLIDING window's state at
+// the new position p is the recurrence h = g h + (1 - g) x run from a zero
+// state over positions max(0, p - L + 1) .. p ("RAT+ Deep Dive" section 2.1:
+// a fixed window that looks back L tokens), i.e. exactly the sum over the
+// window of the gated inputs, each weighted by the gates after it.  The
+// positions before p come from the ring (slot position mod L), the new
+// token from its inputs, which then take its slot (it held p - L, outside
+// the window).  State and raw token are stored as decode_step_kernel does.
+template <typename E>
+__global__ __launch_bounds__(256) void decode_step_sliding_kernel(SlideStepArgs a)
+{
+    typedef Row16<E> R16;
+    constexpr int CPL = R16::CPL;
+    const int vpr = a.d / CPL;  // 16-byte vectors per row
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)a.B * a.H * vpr) return;
+    const int c = (int)(idx % vpr) * CPL;
+    const size_t bh = idx / vpr;
+    const int h = (int)(bh % a.H);
+    const size_t e = bh * a.d + c;  // the (b, h, c) element of a [B][H][d] row
+    const u32x4 ng = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g_new) + e);
+    const u32x4 nk = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k_new) + e);
+    const u32x4 nv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v_new) + e);
+    const size_t ring = bh * a.L * a.d + c;  // slot 0 of this (b, h, c) in the recurrence ring
+    float hk[CPL], hv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) { hk[j] = 0.f; hv[j] = 0.f; }
+    const int first = max(0, a.p - a.L + 1);
+    int slot = first % a.L;
+#pragma unroll 4
+    for (int s = first; s < a.p; ++s) {
+        const size_t o = ring + (size_t)slot * a.d;
+        const u32x4 rgv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.rg) + o);
+        const u32x4 rkv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.rk) + o);
+        const u32x4 rvv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.rv) + o);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            float g, gb;
+            forget_gate(R16::get(rgv, j), g, gb);
+            hk[j] = fmaf(g, hk[j], gb * R16::get(rkv, j));
+            hv[j] = fmaf(g, hv[j], gb * R16::get(rvv, j));
+        }
+        slot = slot + 1 == a.L ? 0 : slot + 1;
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        float g, gb;
+        forget_gate(R16::get(ng, j), g, gb);
+        hk[j] = fmaf(g, hk[j], gb * R16::get(nk, j));
+        hv[j] = fmaf(g, hv[j], gb * R16::get(nv, j));
+    }
+    const size_t on = ring + (size_t)(a.p % a.L) * a.d;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rk) + on) = nk;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rv) + on) = nv;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rg) + on) = ng;
+    const size_t rc = (bh * a.n_cap + a.slot_c[h]) * a.d + c;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kc) + rc) = R16::pack(hk);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vc) + rc) = R16::pack(hv);
+    if (a.slot_w[h] >= 0) {
+        const size_t rw = (bh * a.w_cap + a.slot_w[h]) * a.d + c;
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + rw) = nk;
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + rw) = nv;
+    }
+}
+
+// The recurrence ring of a finished SLIDING prefill: one thread per 16
+// bytes of a ring row; slot s of (b, h) holds the latest position p < T with
+// p mod L = s (positions T - L .. T-1); slots with no such position are left
+// alone.
+template <typename E>
+__global__ __launch_bounds__(256) void sliding_fill_kernel(SlideFillArgs a)
+{
+    constexpr int EPV = 16 / sizeof(E);
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int vpr = a.d / EPV;
+    if (idx >= (size_t)a.B * a.H * a.L * vpr) return;
+    const int c = (int)(idx % vpr) * EPV;
+    const size_t row = idx / vpr;  // (b H + h) L + slot
+    const int slot = (int)(row % a.L);
+    const size_t bh = row / a.L;
+    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+    const int p = (a.T - 1) - ((a.T - 1 - slot) % a.L + a.L) % a.L;  // latest position of the slot
+    if (p < 0) return;
+    const size_t src = (((size_t)b * a.T + p) * a.H + h) * a.d + c;
+    const size_t dst = row * a.d + c;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rk) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + src);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rv) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + src);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.rg) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.g) + src);
+}
+
+hipError_t launch_decode_step_sliding(const SlideStepArgs& a, bool bf16, hipStream_t stream)
+{
+    const size_t n = (size_t)a.B * a.H * (a.d / (bf16 ? 8 : 4));
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(decode_step_sliding_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(decode_step_sliding_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sliding_fill(const SlideFillArgs& a, bool bf16, hipStream_t stream)
+{
+    const size_t n = (size_t)a.B * a.H * a.L * (a.d / (bf16 ? 8 : 4));
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(sliding_fill_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(sliding_fill_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 // Raw ring after a prefill: slot s of head h holds the latest position
 // p < T with p mod W[h] = s (so positions T - W[h] .. T-1); slots with no
 // such position, and slots at or past W[h], are left alone.  One thread per

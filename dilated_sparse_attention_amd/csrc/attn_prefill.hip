@@ -309,17 +309,6 @@ __device__ __forceinline__ DmaSrc dma_sources(const AttnArgs& a, int wv)
     return DmaSrc{q, out, kv};
 }
 
-// global_load_lds_dwordx4 with a scalar base and a 32-bit per-lane byte
-// offset: lane l's 16 bytes at base + voff land at dst + 16 l (M0 = dst).
-__device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t m0)
-{
-    // readfirstlane returns int: widen each half through uint32_t (no sign extension)
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
-    base = ((uint64_t)hi << 32) | lo;
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
-}
-
 // Per-lane constants of the ring DMA: row lq = lane / CH of each RPI-row
 // copy, and the swizzled 16-byte chunk the lane fetches for a copy whose
 // first slot row is a multiple of RPI (the XOR key is linear in the row

@@ -90,6 +90,27 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
+// global_load_lds_dwordx4 with a scalar base and a 32-bit per-lane byte
+// offset: lane l's 16 bytes at base + voff land at dst + 16 l (M0 = dst).
+__device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t m0)
+{
+    // readfirstlane returns int: widen each half through uint32_t (no sign extension)
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+    base = ((uint64_t)hi << 32) | lo;
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads()
+// it does not wait for outstanding global memory operations, so direct
+// global -> LDS copies stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 16 bytes of one token row: CPL = 16 / sizeof(E) adjacent channels.
 template <typename E> struct Row16;
 template <> struct Row16<uint16_t> {

@@ -176,6 +176,42 @@ struct StepArgs {
 };
 hipError_t launch_decode_step(const StepArgs& a, bool bf16, hipStream_t stream);
 
+// Recurrence step of the decode loop under a SLIDING window of L tokens: the
+// new state is the recurrence from a zero state over the last L positions,
+// whose raw key, value and gate logit a ring of L slots keeps (position p in
+// slot p mod L; the new token's slot is written here).
+struct SlideStepArgs {
+    const void* k_new;
+    const void* v_new;
+    const void* g_new;   // [B][H][d]
+    void* rk;
+    void* rv;
+    void* rg;            // [B][H][L][d] raw ring of the recurrence window
+    void* kc;
+    void* vc;            // [B][H][n_cap][d] state history
+    void* kw;
+    void* vw;            // [B][H][w_cap][d] raw ring of the attention window
+    int B, H, d, n_cap, w_cap, L;
+    int p;               // position of the new token (T - 1)
+    int slot_c[kAttnMaxHeads];  // history row of the new position
+    int slot_w[kAttnMaxHeads];  // attention-ring slot of the new position, -1 without a window
+};
+hipError_t launch_decode_step_sliding(const SlideStepArgs& a, bool bf16, hipStream_t stream);
+
+// The SLIDING decode state of a prefill: raw k, v, gate logits of positions
+// max(0, T - L) .. T-1 ([B][T][H][d]) into slot p mod L of rk, rv, rg
+// ([B][H][L][d]).
+struct SlideFillArgs {
+    const void* k;
+    const void* v;
+    const void* g;
+    void* rk;
+    void* rv;
+    void* rg;
+    int B, T, H, d, L;
+};
+hipError_t launch_sliding_fill(const SlideFillArgs& a, bool bf16, hipStream_t stream);
+
 // Raw ring of a prefill: positions max(0, T - W[h]) .. T-1 of k, v
 // ([B][T][H][d]) into slots p mod W[h] of kw, vw ([B][H][w_cap][d]).
 struct RingFillArgs {

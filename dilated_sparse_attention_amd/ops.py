@@ -29,6 +29,7 @@ EXPORTS = ("rat_scan_workspace_bytes", "rat_scan_prefill", "rat_attn_prefill_wor
            "rat_chunk_attn_prefill",
            "rat_decode_workspace_bytes", "rat_decode_step", "rat_dilated_attn_decode", "rat_layer_prefill",
            "rat_decode_static_scratch_bytes", "rat_dilated_attn_decode_static",
+           "rat_decode_step_sliding", "rat_sliding_state_from_prefill",
            "rat_layer_backward_workspace_bytes", "rat_layer_backward", "rat_build_decode_caches",
            "rat_status_string",
            "rat_last_hip_error")
@@ -76,6 +77,11 @@ def load_library(path: str = LIBRARY):
     lib.rat_decode_static_scratch_bytes.restype = sz
     lib.rat_dilated_attn_decode_static.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip, ip, f, i, vp]
     lib.rat_dilated_attn_decode_static.restype = i
+    lib.rat_decode_step_sliding.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, vp, i, vp, i, i, i, i, ip,
+                                            ip, f, i, vp, sz, vp]
+    lib.rat_decode_step_sliding.restype = i
+    lib.rat_sliding_state_from_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.rat_sliding_state_from_prefill.restype = i
     lib.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, ip, ip, f, i, vp, sz,
                                     vp]
     lib.rat_decode_step.restype = i
@@ -456,3 +462,59 @@ def decode_step(q, k_new, v_new, gate_new, state, kc, vc, kw, vw, T, D, W, L=Non
                              _stream())
     _raise("rat_decode_step", rc, lib)
     return out
+
+
+def decode_step_sliding(q, k_new, v_new, gate_new, rk, rv, rg, kc, vc, kw, vw, T, D, W, scale=None, out=None,
+                        workspace=None):
+    """One decode-loop step at context length T under a SLIDING recurrence
+    window of L = rk.shape[2] tokens: the new state is the recurrence from
+    zero over the ring (rk, rv, rg: [B,H,L,d], raw key / value / gate logit
+    of position p in slot p mod L) plus the new token, which takes its slot;
+    then as decode_step (history kc, vc; raw ring kw, vw; attention)."""
+    lib = load_library()
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("gate_new", gate_new)):
+        _check_tensor(name, t, q.dtype, (B, H, d))
+    L = rk.shape[2]
+    for name, t in (("rk", rk), ("rv", rv), ("rg", rg)):
+        _check_tensor(name, t, q.dtype, (B, H, L, d))
+    n_cap = kc.shape[2]
+    _check_tensor("kc", kc, q.dtype, (B, H, n_cap, d))
+    _check_tensor("vc", vc, q.dtype, (B, H, n_cap, d))
+    w_cap = 0 if kw is None else kw.shape[2]
+    if kw is not None:
+        _check_tensor("kw", kw, q.dtype, (B, H, w_cap, d))
+        _check_tensor("vw", vw, q.dtype, (B, H, w_cap, d))
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, q.dtype, (B, H, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    Dh, Wh = _heads(D, H), _heads(W, H)
+    nbytes = lib.rat_decode_workspace_bytes(B, H, d, int(T), Dh, Wh)
+    if workspace is None and nbytes:
+        workspace = attn_workspace(nbytes, q.device)
+    rc = lib.rat_decode_step_sliding(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(gate_new), _ptr(rk), _ptr(rv),
+                                     _ptr(rg), L, _ptr(kc), _ptr(vc), n_cap, _ptr(kw), _ptr(vw), w_cap, _ptr(out),
+                                     B, int(T), H, d, Dh, Wh, scale, _DTYPES[q.dtype], _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(), _stream())
+    _raise("rat_decode_step_sliding", rc, lib)
+    return out
+
+
+def sliding_state_from_prefill(k, v, gate_logits, L, rk=None, rv=None, rg=None):
+    """The SLIDING decode state of a finished prefill: the raw key, value and
+    gate logit of its last L positions into rings [B,H,L,d] (slot p mod L).
+    Returns (rk, rv, rg)."""
+    lib = load_library()
+    B, T, H, d = k.shape
+    for name, t in (("k", k), ("v", v), ("gate_logits", gate_logits)):
+        _check_tensor(name, t, k.dtype, k.shape)
+    L = int(L)
+    rk = torch.zeros((B, H, L, d), dtype=k.dtype, device=k.device) if rk is None else rk
+    rv = torch.zeros_like(rk) if rv is None else rv
+    rg = torch.zeros_like(rk) if rg is None else rg
+    for name, t in (("rk", rk), ("rv", rv), ("rg", rg)):
+        _check_tensor(name, t, k.dtype, (B, H, L, d))
+    rc = lib.rat_sliding_state_from_prefill(_ptr(k), _ptr(v), _ptr(gate_logits), _ptr(rk), _ptr(rv), _ptr(rg),
+                                            B, T, H, d, L, _DTYPES[k.dtype], _stream())
+    _raise("rat_sliding_state_from_prefill", rc, lib)
+    return rk, rv, rg

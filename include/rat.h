@@ -184,7 +184,8 @@ rat_status rat_dilated_attn_decode_static(const void* q, const void* kd, const v
  *   state  : fp32 [B,H,2,d], in: the key and value states at T-2 (zeros
  *            for T = 1, or rat_scan_prefill's final_state), out: the states
  *            at T-1.  With L < T the state is cleared first when (T-1) mod
- *            L == 0 (RESTART); SLIDING windows are not supported here.
+ *            L == 0 (RESTART); SLIDING windows have their own step,
+ *            rat_decode_step_sliding.
  *   kc, vc : [B,H,n_cap,d] history of the states, kept per residue: the
  *            state of position p of head h is row
  *            (p mod D[h]) * (n_cap / D[h]) + p / D[h], so that the entries a
@@ -203,6 +204,40 @@ rat_status rat_decode_step(const void* q, const void* k_new, const void* v_new, 
                     void* out, int B, int T, int H, int d, int L, const int* D, const int* W,
                     float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* One step of a decode loop under a SLIDING recurrence window of L tokens
+ * (Deep Dive 2.1: a fixed window that looks back L* = 64 tokens; SLIDING in
+ * rat_scan_prefill), then the decode attention above.  Such a window keeps
+ * no single running state: the state at position p sums exactly the gated
+ * inputs of positions max(0, p-L+1) .. p, so the loop keeps those positions'
+ * raw inputs and runs the recurrence from a zero state over them.
+ *   q, k_new, v_new, gate_new : [B,H,d], the token at position T-1;
+ *   rk, rv, rg : [B,H,L,d] ring of the raw key, value and gate logit of the
+ *            last L positions, position p in slot p mod L; in: positions
+ *            max(0, T-L) .. T-2 (rat_sliding_state_from_prefill after a
+ *            prefill, nothing before the first token); this call writes
+ *            the new token into slot (T-1) mod L;  1 <= L <= 1024;
+ *   kc, vc, n_cap, kw, vw, w_cap, out, D, W, scale, workspace : as
+ *            rat_decode_step (the new state goes to the history row of
+ *            position T-1, the raw token to ring slot (T-1) mod W[h]).
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED (L > 1024, d, dtype, sizes),
+ * _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
+rat_status rat_decode_step_sliding(const void* q, const void* k_new, const void* v_new, const void* gate_new,
+                                   void* rk, void* rv, void* rg, int L,
+                                   void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
+                                   void* out, int B, int T, int H, int d, const int* D, const int* W,
+                                   float scale, rat_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* The SLIDING decode state of a finished prefill (what rat_decode_step_sliding
+ * continues from): the raw key, value and gate logit of positions
+ * max(0, T-L) .. T-1 of k, v, gate_logits ([B,T,H,d]) into slot p mod L of
+ * rk, rv, rg ([B,H,L,d]); slots with no such position are left alone.
+ * 1 <= L <= 1024.  Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS,
+ * _ALIGN, _HIP. */
+rat_status rat_sliding_state_from_prefill(const void* k, const void* v, const void* gate_logits,
+                                          void* rk, void* rv, void* rg, int B, int T, int H, int d, int L,
+                                          rat_dtype dtype, void* stream);
 
 /* The whole prefill of the layer in one call, handing a decode loop its
  * caches: the recurrence of rat_scan_prefill (Deep Dive 2.1), then the

@@ -337,3 +337,40 @@ def test_static_decode_validation(lib):
     assert call(out=P[0]) == ALIAS
     assert call(q=MIS) == ALIGN
     assert call(scale=float("nan")) == SHAPE
+
+
+def test_sliding_decode_validation(lib):
+    """The SLIDING decode step and its state fill validate before any HIP call."""
+    D, W = heads([4, 4]), heads([0, 8])
+
+    X = [ctypes.c_void_p(0x2000000 + 0x100000 * i) for i in range(4)]  # q, k_new, v_new, gate_new
+
+    def step(q=X[0], rk=P[1], rv=P[2], rg=P[3], L=64, kc=P[4], vc=P[5], n_cap=128, kw=P[6], vw=P[7], w_cap=8,
+             out=P[0], B=1, T=100, H=2, d=64, scale=0.125, dtype=1):
+        return lib.rat_decode_step_sliding(q, X[1], X[2], X[3], rk, rv, rg, L, kc, vc, n_cap, kw, vw, w_cap, out,
+                                           B, T, H, d, D, W, scale, dtype, None, 0, None)
+
+    assert step(q=None) == NULL
+    assert step(rg=None) == NULL
+    assert step(kw=None) == NULL
+    assert step(L=0) == SHAPE
+    assert step(L=1025) == UNSUP
+    assert step(n_cap=16) == SHAPE      # (T-1) / 4 = 24 needs n_cap / 4 > 24
+    assert step(w_cap=4) == SHAPE
+    assert step(d=96) == UNSUP
+    assert step(rk=P[2]) == ALIAS        # two outputs share memory
+    assert step(out=X[0]) == ALIAS       # an output is the query
+    assert step(rk=MIS) == ALIGN
+    assert step(scale=float("nan")) == SHAPE
+
+    def fill(k=P[0], v=P[1], g=P[2], rk=P[3], rv=P[4], rg=P[5], B=1, T=100, H=2, d=64, L=64, dtype=1):
+        return lib.rat_sliding_state_from_prefill(k, v, g, rk, rv, rg, B, T, H, d, L, dtype, None)
+
+    assert fill(g=None) == NULL
+    assert fill(T=0) == SHAPE
+    assert fill(L=0) == SHAPE
+    assert fill(L=2000) == UNSUP
+    assert fill(d=32) == UNSUP
+    assert fill(rk=P[0]) == ALIAS
+    assert fill(rg=P[3]) == ALIAS
+    assert fill(rv=MIS) == ALIGN

@@ -236,3 +236,102 @@ def test_prefill_caches_then_decode(case):
         got.append(out.clone())
     torch.cuda.synchronize()
     assert_parity(torch.stack(got), want, torch.bfloat16, "decode after the library's caches")
+
+
+# (B, T0, steps, H, d, D, W, L): decode loops continued from a SLIDING
+# prefill (the recurrence window of the long workload, L = 64, and a general
+# L), and from the first token
+SLIDING_CASES = [
+    (2, 100, 40, 2, 128, [64, 5], [128, 7], 64),
+    (1, 0, 70, 2, 64, [16, 3], [16, 0], 64),
+    (1, 300, 20, 3, 128, [64, 1, 9], [128, 0, 4], 33),
+]
+SLIDING_LOOP_CASES = [(c, torch.bfloat16) for c in SLIDING_CASES] + [(SLIDING_CASES[0], torch.float32),
+                                                                       (SLIDING_CASES[2], torch.float32)]
+
+
+def _sliding_loop(B, T0, steps, H, d, D, W, L, dtype, seed=5):
+    """Prefill T0 tokens with the SLIDING window (states -> history, last L
+    raw rows -> recurrence ring, last W -> attention ring), then decode
+    `steps` tokens; returns (outputs [steps,B,H,d], oracle rows, kc, vc)."""
+    Tt = T0 + steps
+    x = inputs.make_random_prefill(B, Tt, H, d, dtype, seed=seed, gate_mean=1.0)
+    q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
+    n_cap = max(Dh * ((Tt + Dh - 1) // Dh) for Dh in D) + 16
+    w_cap = max(W) + 3
+    if T0 > 0:
+        pre = [t[:, :T0].contiguous() for t in (k, v, g)]
+        ks, vs = rat.scan_prefill(*pre, L=L if L < T0 else T0, mode=rat.SLIDING)
+        kc, vc = _history(ks, vs, T0, D, n_cap)
+        rk, rv, rg = rat.sliding_state_from_prefill(*pre, L)
+    else:
+        kc = torch.zeros((B, H, n_cap, d), dtype=dtype, device="cuda")
+        vc = torch.zeros_like(kc)
+        rk = torch.zeros((B, H, L, d), dtype=dtype, device="cuda")
+        rv, rg = torch.zeros_like(rk), torch.zeros_like(rk)
+    kw, vw = _ring(k, v, T0, W, w_cap)
+    got = []
+    for T in range(T0 + 1, Tt + 1):
+        t = T - 1
+        out = rat.decode_step_sliding(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                      g[:, t].contiguous(), rk, rv, rg, kc, vc, kw, vw, T, D, W)
+        got.append(out.clone())
+    torch.cuda.synchronize()
+    wk, wv = oracle.scan(x["k"], x["v"], x["gate"], L, oracle.MODE_SLIDING)
+    rows = np.array([(b, t, h) for t in range(T0, Tt) for b in range(B) for h in range(H)], np.int32)
+    want = oracle.attn_prefill_rows(x["q"], wk, wv, x["k"], x["v"], rows, D, W, 1 / math.sqrt(d))
+    return torch.stack(got), want.reshape(steps, B, H, d), (kc, vc, wk, wv, n_cap)
+
+
+@pytest.mark.parametrize("case,dtype", SLIDING_LOOP_CASES,
+                         ids=lambda c: f"B{c[0]}T{c[1]}+{c[2]}H{c[3]}d{c[4]}D{c[5]}W{c[6]}L{c[7]}"
+                         if isinstance(c, tuple) else str(c)[6:])
+def test_decode_loop_sliding(case, dtype):
+    """Every step's output equals the oracle's prefill output at that
+    position with the SLIDING states (explicit window sums), and the states
+    the loop appended to the history equal the oracle's."""
+    B, T0, steps, H, d, D, W, L = case
+    announce("sliding decode loop", case, dtype)
+    got, want, (kc, vc, wk, wv, n_cap) = _sliding_loop(B, T0, steps, H, d, D, W, L, dtype)
+    assert_parity(got, want, dtype, "sliding decode loop outputs")
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    for h, Dh in enumerate(D):
+        p = np.arange(T0, T0 + steps)
+        hr = (p % Dh) * (n_cap // Dh) + p // Dh
+        assert_parity(kc_h[:, h, hr], wk[:, T0:T0 + steps, h], dtype, f"k history head {h}")
+        assert_parity(vc_h[:, h, hr], wv[:, T0:T0 + steps, h], dtype, f"v history head {h}")
+
+
+def test_sliding_state_from_prefill_exact():
+    """The recurrence ring of a prefill holds the raw rows of its last L
+    positions bit for bit in slots p mod L; slots with no position (T < L)
+    keep their contents."""
+    for (B, T, H, d, L) in ((2, 150, 3, 128, 64), (1, 40, 2, 64, 64), (1, 64, 1, 128, 64), (2, 77, 2, 64, 10)):
+        x = inputs.make_random_prefill(B, T, H, d, torch.bfloat16, seed=9)
+        k, v, g = (x[n].cuda() for n in ("k", "v", "gate"))
+        sentinel = 7.0
+        rk = torch.full((B, H, L, d), sentinel, dtype=torch.bfloat16, device="cuda")
+        rv, rg = torch.full_like(rk, sentinel), torch.full_like(rk, sentinel)
+        announce("sliding state fill", (B, T, H, d, L))
+        rat.sliding_state_from_prefill(k, v, g, L, rk=rk, rv=rv, rg=rg)
+        torch.cuda.synchronize()
+        for name, ring, src in (("k", rk, x["k"]), ("v", rv, x["v"]), ("g", rg, x["gate"])):
+            ring = ring.cpu()
+            for slot in range(L):
+                p = (T - 1) - ((T - 1 - slot) % L)
+                if p >= 0:
+                    assert torch.equal(ring[:, :, slot], src[:, p]), (name, slot, p)
+                else:
+                    assert (ring[:, :, slot] == sentinel).all(), (name, slot)
+
+
+@pytest.mark.slow
+def test_decode_loop_sliding_long_workload():
+    """A decode loop continued from a prefill of the 16K windowed workload's
+    shape (H=16, d=128, D=64, W=128, SLIDING L=64, gate logits ~ N(1,1))."""
+    w = inputs.PREFILL_LONG
+    B, steps = 1, 6
+    T0 = w.T - steps
+    announce("sliding decode loop, long workload shape")
+    got, want, _ = _sliding_loop(B, T0, steps, w.H, w.d, list(w.D), list(w.W), w.L, w.dtype, seed=12)
+    assert_parity(got, want, w.dtype, "sliding decode after the long prefill")
