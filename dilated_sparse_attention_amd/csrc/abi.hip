@@ -10,6 +10,7 @@
 
 #include "rat.h"
 #include "rat_internal.h"
+#include "rat_plan.h"
 
 using namespace rat;
 
@@ -51,26 +52,9 @@ bool caches_ok(int B, int H, int d, int nd_cap, int w_cap)
     return size_ok(B, H, d, 1) && (int64_t)nd_cap * d < kMaxElems && (int64_t)std::max(w_cap, 1) * d < kMaxElems;
 }
 
-struct ScanPlan {
-    int chunk, nblk, nseq, nchunk, nwg;
-    size_t agg_off, incl_off, bytes;
-};
-
 ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
 {
-    ScanPlan p;
-    p.chunk = kScanChunk;
-    const int N = H * d;
-    const int bw = dtype == RAT_DTYPE_BF16 ? ScanBlock<uint16_t>::value : ScanBlock<float>::value;
-    p.nblk = (N + bw - 1) / bw;
-    p.nseq = B * p.nblk;
-    p.nchunk = (T + p.chunk - 1) / p.chunk;
-    p.nwg = p.nchunk * p.nseq;
-    const size_t slots = (size_t)p.nwg;
-    p.agg_off = sizeof(ScanHeader);
-    p.incl_off = p.agg_off + slots * 3 * bw * sizeof(uint64_t);
-    p.bytes = p.incl_off + slots * 2 * bw * sizeof(uint64_t);
-    return p;
+    return rat::scan_plan(B, T, H, d, dtype == RAT_DTYPE_BF16);
 }
 
 // compute units of the current device (cached per device)
@@ -253,56 +237,11 @@ rat_status attn_prefill_bf16(const void* q, const void* k_state, const void* v_s
         const size_t need = (size_t)B * T * H * 2 * sizeof(float);
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RAT_ERR_WORKSPACE;
     }
-    struct Cls { int D, W; std::vector<int> heads; double item_cost; };
-    std::vector<Cls> cls;
-    for (int h = 0; h < H; ++h) {
-        auto it = std::find_if(cls.begin(), cls.end(), [&](const Cls& c) { return c.D == D[h] && c.W == W[h]; });
-        if (it == cls.end()) {
-            cls.push_back(Cls{D[h], W[h], {}, 0.0});
-            it = cls.end() - 1;
-        }
-        it->heads.push_back(h);
-    }
-    if ((int)cls.size() > kAttnMaxClasses) return RAT_ERR_UNSUPPORTED;
-    for (auto& c : cls) {
-        const int Mmax = (T + c.D - 1) / c.D;
-        c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
-    }
-    std::stable_sort(cls.begin(), cls.end(), [](const Cls& x, const Cls& y) { return x.item_cost > y.item_cost; });
-
     AttnArgs dil, band;
     memset(&dil, 0, sizeof(dil));
     dil.q = q; dil.ks = k_state; dil.vs = v_state; dil.kr = k_raw; dil.vr = v_raw; dil.out = out;
     dil.ml = static_cast<float*>(workspace);
-    dil.B = B; dil.T = T; dil.H = H;
-    dil.scale_log2 = scale * 1.4426950408889634f;
-    band = dil;
-    dil.chunk = chunk;
-    dil.n_cap = n_cap;  // states as a per-residue history (0: [B][T][H][d])
-    int64_t items = 0, blocks = 0;
-    int hoff = 0;
-    for (const Cls& c : cls) {
-        AttnClass& k = dil.cls[dil.nclass++];
-        k.D = c.D; k.W = c.W;
-        k.nheads = (int)c.heads.size(); k.head_off = hoff;
-        for (int hh : c.heads) { dil.heads[hoff] = hh; band.heads[hoff] = hh; ++hoff; }
-        const int Mmax = (T + c.D - 1) / c.D;
-        k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
-        k.per_level = B * k.nheads * c.D;
-        k.block_begin = (int)items;
-        items += (int64_t)k.levels * k.per_level;
-        if (c.W > 0) {
-            AttnClass& kb = band.cls[band.nclass++];
-            kb = k;
-            kb.levels = (T + kAttnRowsA - 1) / kAttnRowsA;
-            kb.per_level = B * k.nheads;
-            kb.block_begin = (int)blocks;
-            blocks += (int64_t)kb.levels * kb.per_level;
-        }
-        if (items >= ((int64_t)1 << 31) || blocks >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
-    }
-    dil.nblocks = (int)items;
-    band.nblocks = (int)blocks;
+    if (!attn_plan(B, T, H, D, W, scale, chunk, n_cap, dil, band)) return RAT_ERR_UNSUPPORTED;
     if (band.nblocks > 0) {
         const rat_status rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, device_cu_count()), s));
         if (rc != RAT_OK) return rc;
@@ -406,8 +345,6 @@ size_t rat_decode_workspace_bytes(int B, int H, int d, int T, const int* D, cons
     return (size_t)B * H * ns * (d + 2) * sizeof(float);
 }
 
-constexpr bool kLayerPrefillEnabled = false;
-
 rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits, void* out, void* kc,
                       void* vc, int n_cap, void* kw, void* vw, int w_cap, float* final_state, int B, int T, int H,
                       int d, int L, rat_recur_mode mode, const int* D, const int* W, float scale, rat_dtype dtype,
@@ -454,11 +391,6 @@ rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const 
         const size_t need = (size_t)B * T * H * 2 * sizeof(float);
         if (!attn_workspace || attn_workspace_bytes < need || !aligned16(attn_workspace)) return RAT_ERR_WORKSPACE;
     }
-    // The launch path below (history-writing scan instances, the history
-    // instances of the dilated kernel, the ring fill) is switched off: a run
-    // of it faulted the device, and reading the code and checking every
-    // address it forms on the host has not yet shown the cause.
-    if (!kLayerPrefillEnabled) return RAT_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
 
     // 1. the recurrence, its states written straight into the history

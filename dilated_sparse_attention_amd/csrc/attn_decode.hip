@@ -17,6 +17,7 @@
 
 #include "rat_device.h"
 #include "rat_internal.h"
+#include "rat_plan.h"
 
 namespace rat {
 
@@ -415,23 +416,10 @@ template <typename E>
 __global__ __launch_bounds__(256) void ring_fill_kernel(RingFillArgs a)
 {
     constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte vector
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const int vpr = a.d / EPV;           // vectors per row
-    if (idx >= (size_t)a.B * a.H * a.w_cap * vpr) return;
-    const int c = (int)(idx % vpr) * EPV;
-    const size_t row = idx / vpr;        // (b H + h) w_cap + slot
-    const int slot = (int)(row % a.w_cap);
-    const size_t bh = row / a.w_cap;
-    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-    const int W = a.W[h];
-    if (slot >= W) return;
-    const int p = (a.T - 1) - ((a.T - 1 - slot) % W + W) % W;  // latest position of the slot
-    if (p < 0) return;
-    const size_t src = (((size_t)b * a.T + p) * a.H + h) * a.d + c;
-    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + row * a.d + c) =
-        *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + src);
-    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + row * a.d + c) =
-        *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + src);
+    size_t src, dst;
+    if (!ring_fill_at(a, (size_t)blockIdx.x * 256 + threadIdx.x, EPV, src, dst)) return;
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.kw) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k) + src);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.vw) + dst) = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v) + src);
 }
 
 hipError_t launch_ring_fill(const RingFillArgs& a, bool bf16, hipStream_t stream)

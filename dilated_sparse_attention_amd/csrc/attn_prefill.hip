@@ -37,6 +37,7 @@
 #include "rat_device.h"
 #include "rat_internal.h"
 #include "rat_mfma.h"
+#include "rat_plan.h"
 
 namespace rat {
 
@@ -179,116 +180,7 @@ struct Frag {
 };
 
 // ------------------------------------------------------------------ path A
-constexpr int kWavesA = 8;
-constexpr int kTileA = 64;   // keys per K/V tile
-constexpr int kRingA = 4;    // LDS ring depth
-
-struct ItemA {
-    int b, h, D, W, r, R0, R1;
-    int kbeg;  // first key (0, or the start of a band item's key range)
-    int kres;  // residue of the key rows: r, or D - 1 on the chunk grid (0 for a band item)
-    int nkey;  // key rows the item's queries can see: R1, or R1 - 1 on the chunk grid
-    bool valid;
-};
-
-// Item `item` of the cost-sorted list: class by block range, levels (the
-// 256-row chunk index) most expensive first, then head fastest, residue,
-// batch -- consecutive items read the same positions of different heads,
-// i.e. whole contiguous token rows.
-template <bool BAND, bool CHUNK>
-__device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int item)
-{
-    ItemA it;
-    it.valid = false;
-    if (item < 0 || item >= a.nblocks) return it;
-    int c = 0;
-    while (c + 1 < a.nclass && item >= a.cls[c + 1].block_begin) ++c;
-    const AttnClass& k = a.cls[c];
-    const int local = item - k.block_begin;
-    it.W = k.W;
-    if (BAND) {
-        // band item: 256 contiguous queries of (b, h), keys t0-W+1 .. t0+255
-        const int idx = local % k.per_level;
-        it.h = a.heads[k.head_off + idx % k.nheads];
-        it.b = idx / k.nheads;
-        it.r = 0;
-        it.D = 1;
-        it.R0 = (local / k.per_level) * kAttnRowsA;
-        it.R1 = min(it.R0 + kAttnRowsA, a.T);
-        it.kbeg = max(0, it.R0 - k.W + 1) & ~(kTileA - 1);
-        it.kres = 0;
-        it.nkey = it.R1;
-        it.valid = it.R0 < a.T;
-        return it;
-    }
-    const int level = k.levels - 1 - local / k.per_level;
-    int idx = local % k.per_level;
-    it.h = a.heads[k.head_off + idx % k.nheads];
-    idx /= k.nheads;
-    it.r = idx % k.D;
-    it.b = idx / k.D;
-    it.D = k.D;
-    const int M = it.r < a.T ? (a.T - it.r + k.D - 1) / k.D : 0;
-    it.R0 = level * kAttnRowsA;
-    it.R1 = min(it.R0 + kAttnRowsA, M);
-    it.kbeg = 0;
-    // chunk grid: query row i (position r + iD) sees the chunk ends
-    // jD + D - 1 with j < i, all of which exist
-    it.kres = CHUNK ? k.D - 1 : it.r;
-    it.nkey = CHUNK ? it.R1 - 1 : it.R1;
-    it.valid = it.R0 < M;
-    return it;
-}
-
-// Walks this workgroup's items (snake order over rounds of gridDim.x) and
-// the ring steps of each: nq slots of query rows (128 rows each), for
-// windowed classes as many slots of partial outputs, then the key tiles.
-// The DMA issue cursor and the compute cursor are two copies.
-constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
-
-template <bool BAND, bool CHUNK, bool HIST>
-struct CursorA {
-    int round, t, nq, no, nown, ntile;
-    int rowidx;   // (b T + r) H + h: first row of the item in units of head rows
-    int krowidx;  // the same for its key rows (residue kres); with HIST the first
-                  // history row of the residue, (b H + h) n_cap + r n_cap / D
-    int dstride;  // min(D, T) H: head rows between consecutive rows of the item
-    ItemA it;
-
-    __device__ __forceinline__ int item_of(int rnd) const
-    {
-        const int G = gridDim.x;
-        return rnd * G + ((rnd & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
-    }
-    // first valid item at or after round `rnd`; it.valid false when none
-    __device__ __forceinline__ void seek(const AttnArgs& a, int rnd)
-    {
-        for (round = rnd; round * (int)gridDim.x < a.nblocks; ++round) {
-            it = decode_item_a<BAND, CHUNK>(a, item_of(round));
-            if (it.valid) {
-                t = 0;
-                nq = (it.R1 - it.R0 + kSlotRows - 1) / kSlotRows;
-                no = (!BAND && it.W > 0) ? nq : 0;
-                // chunk grid: the item's own states, 64 query rows per step
-                nown = CHUNK ? (it.R1 - it.R0 + kTileA - 1) / kTileA : 0;
-                ntile = max(0, (CHUNK ? it.nkey : it.R1) - it.kbeg + kTileA - 1) / kTileA;
-                rowidx = (it.b * a.T + it.r) * a.H + it.h;
-                krowidx = HIST    ? (it.b * a.H + it.h) * a.n_cap + it.r * (a.n_cap / it.D)
-                          : CHUNK ? (it.b * a.T + it.kres) * a.H + it.h
-                                  : rowidx;
-                // a residue of D >= T holds one row: min(D, T) keeps byte
-                // strides below 2^32 without changing any address
-                dstride = min(it.D, a.T) * a.H;
-                return;
-            }
-        }
-        it.valid = false;
-    }
-    __device__ __forceinline__ void advance(const AttnArgs& a)
-    {
-        if (++t == nq + no + (CHUNK ? nown : 0) + ntile) seek(a, round + 1);
-    }
-};
+// (items, the cursor over ring steps and the copies' addresses: rat_plan.h)
 
 // Source tensors of the ring DMA, held in scalar registers for the whole
 // kernel and handed to the issue as values (a selection among kernel
@@ -309,95 +201,47 @@ __device__ __forceinline__ DmaSrc dma_sources(const AttnArgs& a, int wv)
     return DmaSrc{q, out, kv};
 }
 
-// Per-lane constants of the ring DMA: row lq = lane / CH of each RPI-row
-// copy, and the swizzled 16-byte chunk the lane fetches for a copy whose
-// first slot row is a multiple of RPI (the XOR key is linear in the row
-// bits, so copy j only XORs in the key of row RPI j, a uniform value).
+// Per-lane constants of the ring DMA (dma_lane_a)
 template <int DK>
 struct DmaLane {
     uint32_t lq, col16;
-    __device__ __forceinline__ void init()
-    {
-        const int lane = threadIdx.x & (kWave - 1);
-        lq = lane / Geo<DK>::CH;
-        col16 = (uint32_t)(((lane % Geo<DK>::CH) ^ swz_key<DK>(lq)) << 4);
-    }
+    __device__ __forceinline__ void init() { dma_lane_a<DK>((int)(threadIdx.x & (kWave - 1)), lq, col16); }
 };
 
-// DMA of the cursor's ring step into slot `buf` (every wave issues the same
-// PER_WAVE row copies of RPI rows each; partial-output steps add one copy
-// of their (m, l) words into `side` on waves 0-3).  Rows past the item's
-// last row R1 - 1 are clamped to it.
+// DMA of the cursor's ring step into slot `buf`: the wave's copies as
+// step_copies_a / step_lane_offset_a form them, and for partial-output
+// steps the (m, l) words into `side` on waves 0-3 (step_side_word_a).
 template <int DK, int NW, bool BAND, bool CHUNK, bool HIST>
 __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK, HIST>& c, uint64_t src_q,
                                              uint64_t src_out, uint64_t src_kv, const DmaLane<DK>& dl, uint32_t buf,
                                              uint32_t side)
 {
-    typedef Geo<DK> G;
-    constexpr int INSTR = kSlotRows / G::RPI;
-    constexpr int PER_WAVE = INSTR / NW;
-    static_assert(PER_WAVE * G::RPI <= kTileA && kTileA % (PER_WAVE * G::RPI) == 0, "a wave copies K or V rows only");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
-    const int ko = c.t - c.nq - c.no;  // own-state step, then key tile; < 0 for query / partial steps
-    const bool own = CHUNK && ko >= 0 && ko < c.nown;
-    const int kt = CHUNK && ko >= 0 ? ko - c.nown : ko;  // key tile index (< 0 also for own-state steps)
-    // first row of the wave's share of the slot, and the tensor it comes from
-    int row0;
-    uint64_t tsrc;
-    if (ko < 0) {  // query rows, or partial outputs, R0 + 128 s + 16 PER_WAVE wv ...
-        const int s = c.t < c.nq ? c.t : c.t - c.nq;
-        row0 = c.it.R0 + s * kSlotRows + wv * PER_WAVE * G::RPI;
-        tsrc = c.t < c.nq ? src_q : src_out;
-    } else if (own) {  // K rows (waves 0 .. NW/2-1) or V rows of the own states, R0 + 64 ko ...
-        row0 = c.it.R0 + ko * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
-        tsrc = src_kv;
-    } else {       // K rows (waves 0 .. NW/2-1) or V rows of key tile kt
-        row0 = c.it.kbeg + kt * kTileA + (wv * PER_WAVE * G::RPI) % kTileA;
-        tsrc = src_kv;
-    }
-    // a key tile read elsewhere than the query rows: the chunk ends
-    // (residue kres), or the residue's contiguous rows of a state history
-    const bool keys = (CHUNK || HIST) && ko >= 0 && !own;
-    const uint32_t item_el = (uint32_t)(keys ? c.krowidx : c.rowidx) * DK;
-    // bytes between rows r and r + 1 of the item
-    const uint32_t dp2 = (HIST && keys ? 1u : (uint32_t)c.dstride) * (2 * DK);
-    const int last = (CHUNK && ko >= 0 && !own ? c.it.nkey : c.it.R1) - 1;
-    const uint32_t slot = buf + wv * PER_WAVE * 1024;  // LDS byte address of the wave's first copy
-    if (row0 + PER_WAVE * G::RPI - 1 <= last) {
-        // every row of the wave's share exists: copy j starts RPI rows after
-        // copy j - 1 (one 64-bit scalar add), lane offsets need no clamp
-        uint64_t base = tsrc + 2ull * item_el + (uint64_t)(uint32_t)row0 * dp2;
-        const uint64_t step = (uint64_t)G::RPI * dp2;
-        const uint32_t lrow = dl.lq * dp2;  // < 2^32: the row exists
+    StepCopiesA<DK, NW> sc;
+    step_copies_a<DK, NW>(a, c, wv, buf, sc);
+    // (the source as step_copies_a picks it, selected here from the cursor
+    // itself so that the choice stays in scalar registers)
+    const int ko = c.t - c.nq - c.no;
+    const uint64_t tsrc = ko < 0 ? (c.t < c.nq ? src_q : src_out) : src_kv;
+    // m0[j] = m0[0] + 1024 j: one M0, the copy's immediate offset supplies the rest
+    constexpr int PW = StepCopiesA<DK, NW>::PER_WAVE;
+    uint64_t base[PW];
+    uint32_t voff[PW];
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int instr = wv * PER_WAVE + j;
-            const uint32_t voff = lrow + (dl.col16 ^ (uint32_t)(swz_key<DK>(instr * G::RPI) << 4));
-            dma16_s(base, voff, slot + j * 1024);
-            base += step;
-        }
+    for (int j = 0; j < PW; ++j) base[j] = tsrc + sc.rel[j] - 1024u * j;
+    if (sc.whole) {  // (uniform: the common case computes only its own lane offsets)
+#pragma unroll
+        for (int j = 0; j < PW; ++j) voff[j] = step_lane_offset_whole_a<DK, NW>(sc, wv, j, dl.lq, dl.col16);
     } else {
-        // the item ends inside the wave's share: rows past R1 - 1 read row R1 - 1
-        const uint64_t lrow64 = (uint64_t)dl.lq * dp2;  // saturated: only its min with lim is used
-        const uint32_t lrow = lrow64 > 0xffffffffull ? 0xffffffffu : (uint32_t)lrow64;
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int instr = wv * PER_WAVE + j;
-            const int first = min(row0 + j * G::RPI, last);
-            const uint32_t lim = (uint32_t)(last - first) * dp2;
-            const uint64_t base = tsrc + 2ull * (item_el + (uint32_t)first * (dp2 >> 1));
-            const uint32_t voff = min(lrow, lim) + (dl.col16 ^ (uint32_t)(swz_key<DK>(instr * G::RPI) << 4));
-            dma16_s(base, voff, slot + j * 1024);
-        }
+        for (int j = 0; j < PW; ++j) voff[j] = step_lane_offset_clamped_a<DK, NW>(sc, wv, j, dl.lq, dl.col16);
     }
-    if (ko < 0 && c.t >= c.nq && wv < 4) {
-        // (m, l) of the slot's 128 rows: 64 words per wave on waves 0-3, lane l -> word l
-        const int w = wv * kWave + lane;
-        const int row = min(c.it.R0 + (c.t - c.nq) * kSlotRows + (w >> 1), c.it.R1 - 1);
-        const size_t t = (size_t)c.it.b * a.T + c.it.r + (size_t)row * c.it.D;
-        const float* p = a.ml + (t * a.H + c.it.h) * 2 + (w & 1);
-        asm volatile("global_load_lds_dword %0, off" ::"v"(p), "{m0}"(side + wv * 256) : "memory");
+    dma16_group<PW>(base, voff, sc.m0[0]);
+    const int64_t side_word = step_side_word_a(a, c, wv, lane);
+    if (side_word >= 0) {
+        const float* p = a.ml + side_word;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(p), "{m0}"(side + wv * 256) : "memory");
     }
 }
 
@@ -536,7 +380,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int i = lane & 15;
-    const int pitch = a.H * DK;
     // keys strictly before the query (chunk grid) or up to it
     constexpr int sh = CHUNK ? 1 : 0;
 
@@ -546,7 +389,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     dl.init();
     const DmaSrc dsrc = dma_sources<NW, BAND>(a, wv);
     CursorA<BAND, CHUNK, HIST> issue, comp;
-    issue.seek(a, 0);
+    issue.seek(a, 0, gridDim.x, blockIdx.x);
     comp = issue;
     // ring steps issued and consumed; step n lives in slot n mod RING (a
     // wrapping slot counter instead raises the register use of the band
@@ -559,7 +402,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         issue_step_a<DK, NW, BAND, CHUNK, HIST>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
                                    side_lds + sl * 1024);
         ++issued;
-        issue.advance(a);
+        issue.advance(a, gridDim.x, blockIdx.x);
     };
     auto consume = [&]() { ++consumed; };
 #pragma unroll
@@ -581,8 +424,6 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     Frag<DK> f[NB];
     while (comp.it.valid) {
         const ItemA it = comp.it;
-        const size_t base = ((size_t)it.b * a.T * a.H + it.h) * DK;
-        uint16_t* op = static_cast<uint16_t*>(a.out) + base;
         int rs[NB];    // first row of each block
         bool has[NB];  // block holds rows of the item
 #pragma unroll
@@ -752,17 +593,19 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             pv(all, consumed % RING, pb);
             consume();
         }
+        uint16_t* const out16 = static_cast<uint16_t*>(a.out);
+        const size_t orow0 = item_out_row0(a, it);
         if (BAND) {  // partial state for the dilated pass: o in `out`, (m, l) in the workspace
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const size_t row = (size_t)it.b * a.T + rs[j] + i;
-                f[j].store_partial(op + (size_t)(rs[j] + i) * pitch, a.ml + (row * a.H + it.h) * 2, rs[j] + i < it.R1);
+                const size_t orow = item_out_row(a, it, orow0, rs[j] + i);
+                f[j].store_partial(out16 + orow * DK, a.ml + orow * 2, rs[j] + i < it.R1);
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) f[j].store(op + (size_t)(it.r + (rs[j] + i) * it.D) * pitch, rs[j] + i < it.R1);
+            for (int j = 0; j < NB; ++j) f[j].store(out16 + item_out_row(a, it, orow0, rs[j] + i) * DK, rs[j] + i < it.R1);
         }
-        comp.seek(a, comp.round + 1);
+        comp.seek(a, comp.round + 1, gridDim.x, blockIdx.x);
     }
 }
 

@@ -87,18 +87,43 @@ __device__ __forceinline__ void wait_vmcnt()
 __device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+    // (s_nop: the wait state between the scalar write of M0 and the LDS
+    // copy that reads it, which the compiler cannot see inside the asm)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
-// global_load_lds_dwordx4 with a scalar base and a 32-bit per-lane byte
-// offset: lane l's 16 bytes at base + voff land at dst + 16 l (M0 = dst).
-__device__ __forceinline__ void dma16_s(uint64_t base, uint32_t voff, uint32_t m0)
+// N global_load_lds_dwordx4 copies issued back to back under one M0.  Copy
+// j reads 16 bytes per lane at base[j] + voff[j] + 1024 j and writes them
+// to LDS at m0 + 1024 j + 16 lane: the instruction's immediate offset moves
+// both addresses, so the caller passes base[j] already lowered by 1024 j
+// and the copies need no M0 write of their own.  The hardware needs 5 wait
+// states between a VALU write of an SGPR (a base moved from vector
+// registers by readfirstlane) and a copy that reads it, and 1 between the
+// write of M0 and the copy; the compiler does not see inside the asm, so
+// its leading s_nop provides both for the first copy (later copies' bases
+// are older still).
+template <int N>
+__device__ __forceinline__ void dma16_group(const uint64_t (&base)[N], const uint32_t (&voff)[N], uint32_t m0);
+
+template <>
+__device__ __forceinline__ void dma16_group<2>(const uint64_t (&base)[2], const uint32_t (&voff)[2], uint32_t m0)
 {
-    // readfirstlane returns int: widen each half through uint32_t (no sign extension)
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
-    base = ((uint64_t)hi << 32) | lo;
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 4\n\t"
+                 "global_load_lds_dwordx4 %0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %3 offset:1024"
+                 ::"v"(voff[0]), "v"(voff[1]), "s"(base[0]), "s"(base[1]), "{m0}"(m0) : "memory");
+}
+
+template <>
+__device__ __forceinline__ void dma16_group<4>(const uint64_t (&base)[4], const uint32_t (&voff)[4], uint32_t m0)
+{
+    asm volatile("s_nop 4\n\t"
+                 "global_load_lds_dwordx4 %0, %4\n\t"
+                 "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %2, %6 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %3, %7 offset:3072"
+                 ::"v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                   "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]), "{m0}"(m0) : "memory");
 }
 
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads()

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace rat {
@@ -279,5 +280,19 @@ struct BwdArgs {
     int mitem[kAttnMaxHeads + 1];  // first MFMA work item of each head; [H] = total
 };
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+
+// Kernel-argument layouts, asserted in both the host and the device
+// compilation (a struct laid out differently by the two would hand the
+// kernels shifted fields), and within the 4 KiB kernel-argument segment.
+static_assert(sizeof(StateHist) == 1036, "StateHist layout");
+static_assert(sizeof(ScanFullArgs) == 1144 && offsetof(ScanFullArgs, fin) == 96 &&
+              offsetof(ScanFullArgs, hist) == 108, "ScanFullArgs layout");
+static_assert(sizeof(ScanSlideArgs) == 1096 && offsetof(ScanSlideArgs, hist) == 60, "ScanSlideArgs layout");
+static_assert(sizeof(AttnArgs) == 1336 && offsetof(AttnArgs, cls) == 88 && offsetof(AttnArgs, heads) == 312,
+              "AttnArgs layout");
+static_assert(sizeof(RingFillArgs) == 1080 && sizeof(DecodeArgs) == 3160 && sizeof(StepArgs) == 2136 &&
+              sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3248 && sizeof(AttnF32Args) == 2128 &&
+              sizeof(SlideStepArgs) == 2160 && sizeof(SlideFillArgs) == 72, "kernel-argument sizes");
+static_assert(sizeof(BwdArgs) < 4096 && sizeof(DecodeArgs) < 4096, "kernel arguments fit their segment");
 
 }  // namespace rat

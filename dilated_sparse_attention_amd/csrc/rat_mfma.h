@@ -32,7 +32,7 @@ struct Geo {
 // one logical chunk), and over CH/2 consecutive rows it maps the chunk pair
 // (2j, 2j+1) onto CH distinct chunks (conflict-free transposing V reads).
 template <int DK>
-__device__ __forceinline__ int swz_key(int r)
+__host__ __device__ __forceinline__ int swz_key(int r)
 {
     constexpr int HALF = Geo<DK>::CH / 2;
     return ((r & (HALF - 1)) << 1) | ((r / HALF) & 1);
@@ -40,7 +40,7 @@ __device__ __forceinline__ int swz_key(int r)
 
 // byte offset of chunk c of row r in a swizzled tile
 template <int DK>
-__device__ __forceinline__ int swz(int r, int c)
+__host__ __device__ __forceinline__ int swz(int r, int c)
 {
     return r * Geo<DK>::ROWB + ((c ^ swz_key<DK>(r)) << 4);
 }

@@ -48,6 +48,7 @@
 //   subtraction or division.  Each lane keeps its X_j in LDS.
 #include "rat_device.h"
 #include "rat_internal.h"
+#include "rat_plan.h"
 
 namespace rat {
 
@@ -57,27 +58,6 @@ constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before th
 #define RAT_SCAN_LOOKBACK 1
 #endif
 constexpr int kLookbackWindow = RAT_SCAN_LOOKBACK;  // predecessors examined per round
-
-// Row of position t in a StateHist head with dilation D and mcap = n_cap / D
-// rows per residue, walked token by token without a division.
-struct HistRow {
-    int res, q, D, mcap;
-    __device__ __forceinline__ void init(int t, int D_, int n_cap)
-    {
-        D = D_;
-        mcap = n_cap / D_;
-        q = t / D_;
-        res = t - q * D_;
-    }
-    __device__ __forceinline__ int row() const { return res * mcap + q; }
-    __device__ __forceinline__ void next()
-    {
-        if (++res == D) {
-            res = 0;
-            ++q;
-        }
-    }
-};
 
 template <typename E, bool HIST>
 __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(ScanFullArgs a)
@@ -113,18 +93,13 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     __syncthreads();
     const uint32_t ticket = s_ticket;
     const uint32_t tag = s_epoch + 1u;
-    const int chunk = (int)(ticket / (uint32_t)a.nseq);
-    const int seq = (int)(ticket % (uint32_t)a.nseq);
-    const int b = seq / a.nblk;
-    const int cblk = (seq % a.nblk) * BW;  // first channel of the block
-    const int tb = chunk * CT;              // first token of the chunk
-
     // lane (r, c): channels cblk + CPL c .. +CPL, tokens t0 .. t0 + TPL - 1
-    const int c = lane % LPR;
-    const int seg = w * GPW + lane / LPR;
-    const int ch0 = cblk + c * CPL;
-    const bool cvalid = ch0 < a.N;
-    const int t0 = tb + seg * TPL;
+    const ScanLane sl = scan_lane<CPL>(a, ticket, w, lane);
+    const int chunk = sl.chunk, seq = sl.seq, b = sl.b;
+    const int cblk = sl.cblk;  // first channel of the block
+    const int tb = sl.tb;      // first token of the chunk
+    const int c = sl.c, seg = sl.seg, ch0 = sl.ch0, t0 = sl.t0;
+    const bool cvalid = sl.cvalid;
     // element offset of the lane's first token row; token t0 + i is i N further
     // (one 64-bit offset per lane, the i N terms uniform)
     const size_t obase = ((size_t)b * a.T + t0) * a.N + ch0;
@@ -371,9 +346,8 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     HistRow hr;
     size_t hbase = 0;
     if (HIST) {  // the lane's head, its history block and the row of t0
-        const int hh = ch0 / a.d;
-        hr.init(t0, a.hist.D[cvalid ? hh : 0], a.hist.n_cap);
-        hbase = ((size_t)b * a.hist.H + hh) * a.hist.n_cap * a.d + (ch0 - hh * a.d);
+        hr.init(t0, scan_hist_D(a, sl), a.hist.n_cap);
+        hbase = scan_hist_base(a, sl);
     }
     float ck[CPL], cv[CPL];
 #pragma unroll
@@ -392,10 +366,7 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     // the last position's states in fp32, for a decode loop to continue from
     // (a lane's CPL channels lie in one head: d is a multiple of 64)
     float* fin = nullptr;
-    if (a.fin && cvalid) {
-        const int hh = ch0 / a.d;
-        fin = a.fin + ((size_t)(b * (a.N / a.d) + hh) * 2) * a.d + (ch0 - hh * a.d);
-    }
+    if (a.fin && cvalid) fin = a.fin + scan_fin_offset(a, sl);
     auto pass2 = [&](auto fast_form) {
         constexpr bool FAST = decltype(fast_form)::value;
 #pragma unroll

@@ -263,10 +263,7 @@ rat_status rat_sliding_state_from_prefill(const void* k, const void* v, const vo
  *   scan_workspace : rat_scan_workspace_bytes(...) bytes, the same
  *            zero-filled-once buffer rules as rat_scan_prefill;
  *   attn_workspace : rat_attn_prefill_workspace_bytes(...) bytes.
- * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP.
- * In this build the call validates its arguments and then returns
- * RAT_ERR_UNSUPPORTED without launching anything: its launch path is
- * switched off until a device fault seen in it is explained. */
+ * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */
 rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const void* gate_logits,
                       void* out, void* kc, void* vc, int n_cap, void* kw, void* vw, int w_cap,
                       float* final_state, int B, int T, int H, int d, int L, rat_recur_mode mode,

@@ -1,0 +1,251 @@
+// Host-side walk of the global addresses the RAT+ kernels form, over whole
+// launch grids.  TEST INFRASTRUCTURE: compiled for the host only; it calls
+// the same address functions (rat_plan.h) the kernels call and checks every
+// access against the extent of the buffer it falls in.  It launches
+// nothing and needs no GPU.
+//
+//   addr_walk B T H d L mode dtype n_cap w_cap fin D0,D1,.. W0,W1,..
+//     mode: 0 RESTART, 1 SLIDING; dtype: 0 fp32, 1 bf16; n_cap 0: the
+//     plain [B,T,H,d] state layout (no history); fin: 1 if the fp32 final
+//     state is written.
+// Prints one line per check and "OK" or the first failures; exit status 1
+// on any out-of-range access.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <set>
+#include <string>
+#include <vector>
+
+#include "rat_plan.h"
+
+using namespace rat;
+
+static long g_fail = 0;
+static long g_checked = 0;
+
+static void check(bool ok, const char* what, long long a, long long b, long long c)
+{
+    ++g_checked;
+    if (!ok) {
+        if (g_fail < 20) fprintf(stderr, "OUT OF RANGE: %s (%lld, %lld, %lld)\n", what, a, b, c);
+        ++g_fail;
+    }
+}
+
+static std::vector<int> parse_list(const char* s)
+{
+    std::vector<int> v;
+    for (const char* p = s; *p;) {
+        v.push_back(atoi(p));
+        const char* q = strchr(p, ',');
+        if (!q) break;
+        p = q + 1;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- scan
+template <typename E, bool HIST>
+static void walk_scan(int B, int T, int H, int d, int L, int n_cap, bool fin, const std::vector<int>& D)
+{
+    constexpr int CPL = 16 / (int)sizeof(E);
+    const ScanPlan p = scan_plan(B, T, H, d, sizeof(E) == 2);
+    ScanFullArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T = T; a.N = H * d; a.nblk = p.nblk; a.nseq = p.nseq; a.nchunk = p.nchunk;
+    a.L = L >= T ? 0 : L; a.nwg = p.nwg; a.d = d;
+    if (HIST) {
+        a.hist.n_cap = n_cap; a.hist.d = d; a.hist.H = H;
+        for (int h = 0; h < H; ++h) a.hist.D[h] = D[h];
+    }
+    const long long in_el = (long long)B * T * H * d;
+    const long long hist_el = (long long)B * H * n_cap * d;
+    const long long fin_el = (long long)B * H * 2 * d;
+    std::vector<unsigned char> written(HIST ? (size_t)hist_el / CPL : 0, 0);
+    for (uint32_t ticket = 0; ticket < (uint32_t)p.nwg; ++ticket) {
+        for (int w = 0; w < kScanFullWaves; ++w) {
+            for (int lane = 0; lane < 64; ++lane) {
+                const ScanLane sl = scan_lane<CPL>(a, ticket, w, lane);
+                check((size_t)sl.chunk * a.nseq + sl.seq < (size_t)p.nwg, "scan workspace slot", ticket, w, lane);
+                const size_t obase = ((size_t)sl.b * a.T + sl.t0) * a.N + sl.ch0;
+                HistRow hr;
+                size_t hbase = 0;
+                if (HIST) {
+                    hr.init(sl.t0, scan_hist_D(a, sl), a.hist.n_cap);
+                    hbase = scan_hist_base(a, sl);
+                }
+                for (int i = 0; i < kScanTpl; ++i) {
+                    const bool live = sl.cvalid && sl.t0 + i < T;
+                    if (live) {
+                        const long long o = (long long)(obase + (size_t)i * a.N);
+                        check(o >= 0 && o + CPL <= in_el, "scan input row", ticket, lane, i);
+                        if (HIST) {
+                            const long long ho = (long long)(hbase + (size_t)hr.row() * a.d);
+                            check(ho >= 0 && ho + CPL <= hist_el, "scan history store", ticket, lane, ho);
+                            if (ho >= 0 && ho + CPL <= hist_el) {
+                                check(written[ho / CPL] == 0, "history element written twice", ticket, lane, ho);
+                                written[ho / CPL] = 1;
+                            }
+                        }
+                        if (fin && sl.t0 + i == T - 1) {
+                            const long long fo = (long long)scan_fin_offset(a, sl);
+                            check(fo >= 0 && fo + a.d + CPL <= fin_el, "scan final state", ticket, lane, fo);
+                        }
+                    }
+                    if (HIST) hr.next();
+                }
+            }
+        }
+    }
+    if (HIST) {  // every position of every head written exactly once, where the decode step reads it
+        long long n = 0;
+        for (unsigned char x : written) n += x;
+        check(n == in_el / CPL, "history elements written", n, in_el / CPL, 0);
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < H; ++h)
+                for (int t = 0; t < T; ++t) {
+                    const long long row = (long long)(t % D[h]) * (n_cap / D[h]) + t / D[h];
+                    const long long el = ((long long)(b * H + h) * n_cap + row) * d;
+                    check(written[el / CPL] == 1, "history row of a position", b, h, t);
+                }
+    }
+    printf("scan%s %s: %d chunks x 512 lanes\n", HIST ? " (history)" : "", sizeof(E) == 2 ? "bf16" : "fp32", p.nwg);
+}
+
+// ---------------------------------------------------------------- ring fill
+static void walk_ring(int B, int T, int H, int d, int w_cap, const std::vector<int>& W, bool bf16)
+{
+    RingFillArgs r;
+    memset(&r, 0, sizeof(r));
+    r.B = B; r.T = T; r.H = H; r.d = d; r.w_cap = w_cap;
+    for (int h = 0; h < H; ++h) r.W[h] = W[h];
+    const int epv = bf16 ? 8 : 4;
+    const size_t n = (size_t)B * H * w_cap * (d / epv);
+    const size_t grid = (n + 255) / 256 * 256;  // the launch's threads
+    long copies = 0;
+    for (size_t idx = 0; idx < grid; ++idx) {
+        size_t src, dst;
+        if (!ring_fill_at(r, idx, epv, src, dst)) continue;
+        ++copies;
+        check(src + epv <= (size_t)B * T * H * d, "ring source", (long long)idx, (long long)src, 0);
+        check(dst + epv <= (size_t)B * H * w_cap * d, "ring slot", (long long)idx, (long long)dst, 0);
+    }
+    printf("ring fill: %zu threads, %ld copies\n", grid, copies);
+}
+
+// ---------------------------------------------------------------- attention
+template <int DK, int RING, bool BAND, bool CHUNK, bool HIST>
+static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const char* what)
+{
+    constexpr int NW = kWavesA;
+    const long long row_bytes = (long long)a.B * a.T * a.H * DK * 2;  // q and out
+    const long long tile = (long long)kSlotRows * DK * 2;
+    const long long lds = RING > 4 ? RING * tile : RING * (tile + 1024);
+    long steps = 0, items = 0;
+    for (int blk = 0; blk < grid; ++blk) {
+        CursorA<BAND, CHUNK, HIST> c;
+        c.seek(a, 0, grid, blk);
+        int issued = 0;
+        int last_round = -1;
+        while (c.it.valid) {
+            if (c.round != last_round) {
+                ++items;
+                last_round = c.round;
+                for (int row = c.it.R0; row < c.it.R1; ++row) {
+                    const long long orow = (long long)item_out_row(a, c.it, item_out_row0(a, c.it), row);
+                    check(orow >= 0 && orow < (long long)a.B * a.T * a.H, "output row", blk, c.round, row);
+                }
+            }
+            const uint32_t buf = (uint32_t)((issued % RING) * tile);
+            for (int wv = 0; wv < NW; ++wv) {
+                for (int lane = 0; lane < 64; ++lane) {
+                    uint32_t lq, col16;
+                    dma_lane_a<DK>(lane, lq, col16);
+                    StepCopiesA<DK, NW> s;
+                    step_copies_a<DK, NW>(a, c, wv, buf, s);
+                    const long long lim = s.src == 2 ? kv_bytes : row_bytes;
+                    for (int j = 0; j < StepCopiesA<DK, NW>::PER_WAVE; ++j) {
+                        const long long addr =
+                            (long long)s.rel[j] + step_lane_offset_a<DK, NW>(s, wv, j, lq, col16);
+                        check(addr >= 0 && addr + 16 <= lim, what, blk, c.t, addr);
+                        check((long long)s.m0[j] + 16 * lane + 16 <= lds, "ring slot in LDS", blk, c.t, s.m0[j]);
+                    }
+                    const int64_t side_word = step_side_word_a(a, c, wv, lane);
+                    if (side_word >= 0)
+                        check(side_word < (long long)a.B * a.T * a.H * 2, "partial (m, l) word", blk, c.t,
+                              side_word);
+                }
+            }
+            ++issued;
+            ++steps;
+            c.advance(a, grid, blk);
+        }
+    }
+    printf("%s: %d workgroups, %ld items, %ld ring steps\n", what, grid, items, steps);
+}
+
+template <int DK>
+static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, const std::vector<int>& W, int n_cap)
+{
+    AttnArgs dil, band;
+    memset(&dil, 0, sizeof(dil));
+    if (!attn_plan(B, T, H, D.data(), W.data(), 0.1f, 0, n_cap, dil, band)) {
+        printf("attention plan refused\n");
+        ++g_fail;
+        return;
+    }
+    bool windowed = false;
+    for (int i = 0; i < dil.nclass; ++i) windowed |= dil.cls[i].W > 0;
+    const long long raw_bytes = (long long)B * T * H * DK * 2;
+    const int cu = 256;
+    if (band.nblocks > 0)
+        walk_attn<DK, 5, true, false, false>(band, std::min(band.nblocks, cu), raw_bytes, "band pass copies");
+    const int grid = std::min(dil.nblocks, cu);
+    if (n_cap > 0) {
+        const long long hist_bytes = (long long)B * H * n_cap * DK * 2;
+        if (windowed) walk_attn<DK, 4, false, false, true>(dil, grid, hist_bytes, "dilated copies (history, 4 slots)");
+        else walk_attn<DK, 5, false, false, true>(dil, grid, hist_bytes, "dilated copies (history, 5 slots)");
+    } else {
+        if (windowed) walk_attn<DK, 4, false, false, false>(dil, grid, raw_bytes, "dilated copies (4 slots)");
+        else walk_attn<DK, 5, false, false, false>(dil, grid, raw_bytes, "dilated copies (5 slots)");
+    }
+}
+
+int main(int argc, char** argv)
+{
+    if (argc != 13) {
+        fprintf(stderr, "usage: addr_walk B T H d L mode dtype n_cap w_cap fin D0,.. W0,..\n");
+        return 2;
+    }
+    const int B = atoi(argv[1]), T = atoi(argv[2]), H = atoi(argv[3]), d = atoi(argv[4]), L = atoi(argv[5]);
+    const int mode = atoi(argv[6]), dtype = atoi(argv[7]), n_cap = atoi(argv[8]), w_cap = atoi(argv[9]);
+    const bool fin = atoi(argv[10]) != 0;
+    const std::vector<int> D = parse_list(argv[11]), W = parse_list(argv[12]);
+    if ((int)D.size() != H || (int)W.size() != H) {
+        fprintf(stderr, "need H values of D and W\n");
+        return 2;
+    }
+    const bool bf16 = dtype == 1;
+    const bool full_or_restart = L >= T || mode == 0;
+    if (full_or_restart) {
+        if (n_cap > 0) {
+            if (bf16) walk_scan<uint16_t, true>(B, T, H, d, L, n_cap, fin, D);
+            else walk_scan<float, true>(B, T, H, d, L, n_cap, fin, D);
+        } else {
+            if (bf16) walk_scan<uint16_t, false>(B, T, H, d, L, 1, fin, D);
+            else walk_scan<float, false>(B, T, H, d, L, 1, fin, D);
+        }
+    }
+    bool any_w = false;
+    for (int x : W) any_w |= x > 0;
+    if (any_w && w_cap > 0) walk_ring(B, T, H, d, w_cap, W, bf16);
+    if (bf16) {
+        if (d == 128) walk_prefill_attn<128>(B, T, H, D, W, n_cap);
+        else walk_prefill_attn<64>(B, T, H, D, W, n_cap);
+    }
+    printf("%ld accesses checked, %ld out of range\n", g_checked, g_fail);
+    if (g_fail == 0) printf("OK\n");
+    return g_fail ? 1 : 0;
+}

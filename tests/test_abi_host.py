@@ -233,8 +233,6 @@ def test_layer_prefill_validation(lib):
     assert layer(lib, sws=None) == WSPACE              # the full recurrence needs its workspace
     assert layer(lib, sws=ctypes.c_void_p(0x10040)) == WSPACE
     assert layer(lib, aws=None) == WSPACE              # a windowed head needs the attention workspace
-    # valid arguments: the launch path is switched off in this build
-    assert layer(lib) == UNSUP
 
 
 def backward(lib, q=P[0], k=P[1], v=P[2], g=P[3], ks=P[4], vs=P[5], dout=P[7],
