@@ -106,7 +106,7 @@ def stats_fields(prefix, st, nbytes=None, flops=None):
 def load_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when it is absent or was taken from other kernel sources."""
-    path = os.path.join(PROFILES, "scan_full_attn_dilated_prefill_1p5b_hbm_traffic.json")
+    path = os.path.join(PROFILES, "prefill_1.5B_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -282,6 +282,52 @@ def run_decode_caches(torch, rat, w, steps, warmup, nsets=3):
     s = 2
     nbytes = 2 * 2 * w.B * w.T * w.H * w.d * s + 2 * 2 * w.B * w.d * s * sum(min(Wh, w.T) for Wh in W)
     return st, nbytes
+
+
+def run_layer_prefill(torch, rat, w, steps, warmup, mode=0, nsets=2):
+    """The one-call layer prefill (recurrence with its states written into
+    the per-residue decode history, attention, raw ring) against the same
+    outputs from separate calls: the recurrence and the attention alone,
+    and those followed by the decode-cache build.  Each timed per call."""
+    from dilated_sparse_attention_amd import inputs
+
+    D, W = list(w.D), list(w.W)
+    need_raw = any(x > 0 for x in W)
+    n_cap = rat.history_rows(w.T, D)
+    w_cap = max(W) if need_raw else 0
+    sliding = mode == 1 and w.L < w.T
+    sets = []
+    for i in range(nsets):
+        x = inputs.make_prefill(w, seed=i, device="cuda")
+        kc = torch.empty((w.B, w.H, n_cap, w.d), dtype=w.dtype, device="cuda")
+        ring = (lambda: torch.zeros((w.B, w.H, w_cap, w.d), dtype=w.dtype, device="cuda")) if need_raw else (lambda: None)
+        sets.append(dict(x, out=torch.empty_like(x["q"]), ks=torch.empty_like(x["k"]), vs=torch.empty_like(x["v"]),
+                         kc=kc, vc=torch.empty_like(kc), kw=ring(), vw=ring(),
+                         st=None if sliding else torch.empty((w.B, w.H, 2, w.d), dtype=torch.float32, device="cuda")))
+        del x
+
+    def fused(i):
+        x = sets[i % nsets]
+        rat.layer_prefill(x["q"], x["k"], x["v"], x["gate"], D, W, L=w.L, mode=mode, n_cap=n_cap, w_cap=w_cap,
+                          final_state=False if sliding else x["st"], out=x["out"], kc=x["kc"], vc=x["vc"],
+                          kw=x["kw"], vw=x["vw"])
+
+    def two_calls(i, caches):
+        x = sets[i % nsets]
+        rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode, k_state=x["ks"], v_state=x["vs"])
+        rat.dilated_attn_prefill(x["q"], x["ks"], x["vs"], x["k"] if need_raw else None,
+                                 x["v"] if need_raw else None, D=D, W=W, out=x["out"])
+        if caches:
+            rat.build_decode_caches(x["ks"], x["vs"], x["k"], x["v"], D, W, n_cap=n_cap, w_cap=w_cap,
+                                    kc=x["kc"], vc=x["vc"], kw=x["kw"], vw=x["vw"])
+
+    n = max(steps, MIN_TIMED)
+    st_f = time_launches(torch, fused, n, warmup)
+    st_2 = time_launches(torch, lambda i: two_calls(i, False), n, warmup)
+    st_c = time_launches(torch, lambda i: two_calls(i, True), n, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return st_f, st_2, st_c
 
 
 def run_decode_step(torch, rat, w, steps, warmup, nsets=2):
@@ -571,6 +617,23 @@ def main():
                           **stats_fields("step", sst, nbytes=sbytes), "algorithmic_bytes": sbytes,
                           "config": dict(sw.describe(), history_rows_per_head=max(
                               Dh * ((sw.T + Dh - 1) // Dh) for Dh in sw.D))}
+
+        for lw in (inputs.PREFILL_1P5B, inputs.PREFILL_LONG):
+            for mode in lw.modes:
+                key = "layer_prefill_" + lw.name + ("" if len(lw.modes) == 1 else
+                                                    ("_restart" if mode == 0 else "_sliding"))
+                if args.only is not None and args.only != key:
+                    continue
+                progress("one-call layer prefill", key)
+                st_f, st_2, st_c = run_layer_prefill(torch, rat, lw, args.steps, args.warmup, mode=mode)
+                toks = lw.B * lw.T
+                extra[key] = {"prefill_tokens_per_s": toks / (st_f["median"] / 1e3),
+                              **stats_fields("layer", st_f), **stats_fields("two_calls", st_2),
+                              **stats_fields("two_calls_and_caches", st_c),
+                              "two_calls_tokens_per_s": toks / (st_2["median"] / 1e3),
+                              "config": dict(lw.describe(), mode="restart" if mode == 0 else "sliding",
+                                             compared="one call (states into the decode history, ring) vs "
+                                                      "scan + attention, and those + the decode-cache build")}
 
         cw = inputs.PREFILL_LONG
         key = "decode_caches_" + cw.name
