@@ -42,14 +42,13 @@
 namespace rat {
 
 
-// max of three scores in one v_max3_f32: the operands are MFMA results,
-// -inf masks or maxima of these, so the quieting of signalling NaNs that
-// fmaxf implies (an extra v_max per operand) is not needed
+// max of three scores: IEEE maximum (NaN-propagating), which gfx950 issues
+// as one v_maximum3_f32 with no quieting of its operands.  Written as a
+// builtin rather than asm so that the compiler sees the operation and
+// needs no hazard padding around it.
 __device__ __forceinline__ float max3(float a, float b, float c)
 {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // max over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows) with
@@ -211,10 +210,13 @@ struct DmaLane {
 // DMA of the cursor's ring step into slot `buf`: the wave's copies as
 // step_copies_a / step_lane_offset_a form them, and for partial-output
 // steps the (m, l) words into `side` on waves 0-3 (step_side_word_a).
+// When the step is a whole key tile, its plan and lane offsets go to
+// `run` / `run_voff` for the key tiles that follow, and it returns true.
 template <int DK, int NW, bool BAND, bool CHUNK, bool HIST>
-__device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK, HIST>& c, uint64_t src_q,
+__device__ __forceinline__ bool issue_step_a(const AttnArgs& a, const CursorA<BAND, CHUNK, HIST>& c, uint64_t src_q,
                                              uint64_t src_out, uint64_t src_kv, const DmaLane<DK>& dl, uint32_t buf,
-                                             uint32_t side)
+                                             uint32_t side, KeyRunA& run,
+                                             uint32_t (&run_voff)[StepCopiesA<DK, NW>::PER_WAVE])
 {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
@@ -230,9 +232,16 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BA
     uint32_t voff[PW];
 #pragma unroll
     for (int j = 0; j < PW; ++j) base[j] = tsrc + sc.rel[j] - 1024u * j;
+    bool keys = false;
     if (sc.whole) {  // (uniform: the common case computes only its own lane offsets)
 #pragma unroll
         for (int j = 0; j < PW; ++j) voff[j] = step_lane_offset_whole_a<DK, NW>(sc, wv, j, dl.lq, dl.col16);
+        if (step_key_tile_a(c) >= 0) {
+            run = KeyRunA{sc.rel[0], sc.dp2, sc.row0, sc.last};
+#pragma unroll
+            for (int j = 0; j < PW; ++j) run_voff[j] = voff[j];
+            keys = true;
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < PW; ++j) voff[j] = step_lane_offset_clamped_a<DK, NW>(sc, wv, j, dl.lq, dl.col16);
@@ -243,6 +252,24 @@ __device__ __forceinline__ void issue_step_a(const AttnArgs& a, const CursorA<BA
         const float* p = a.ml + side_word;
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(p), "{m0}"(side + wv * 256) : "memory");
     }
+    return keys;
+}
+
+// DMA of the next key tile of a run (key_run_next_a has moved `run` to it):
+// the copy bases one add apart, the lane offsets those of the run's first tile.
+template <int DK, int NW>
+__device__ __forceinline__ void issue_key_run_a(const KeyRunA& run, const uint32_t (&voff)[StepCopiesA<DK, NW>::PER_WAVE],
+                                                uint64_t src_kv, uint32_t buf)
+{
+    constexpr int PW = StepCopiesA<DK, NW>::PER_WAVE;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // copy j at src + key_run_rel_a(run, j), lowered by 1024 j for its immediate offset
+    const uint64_t step = (uint64_t)Geo<DK>::RPI * run.dp2 - 1024u;
+    uint64_t base[PW];
+    base[0] = src_kv + run.rel0;
+#pragma unroll
+    for (int j = 1; j < PW; ++j) base[j] = base[j - 1] + step;
+    dma16_group<PW>(base, voff, buf + wv * PW * 1024);
 }
 
 // Per-lane byte offsets inside a swizzled tile: K fragment of k-step ks for
@@ -397,10 +424,18 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
     int issued = 0, consumed = 0;
     const uint32_t smem_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
     const uint32_t side_lds = smem_lds + (uint32_t)(side - smem);
+    // the key tile last issued, when it was whole (key_run_next_a)
+    KeyRunA run{};
+    bool run_ok = false;
+    uint32_t run_voff[PER_WAVE];
     auto issue_next = [&]() {
         const int sl = issued % RING;
-        issue_step_a<DK, NW, BAND, CHUNK, HIST>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl, smem_lds + sl * TILE_BYTES,
-                                   side_lds + sl * 1024);
+        if (run_ok && key_run_next_a<DK, NW>(issue, run))
+            issue_key_run_a<DK, NW>(run, run_voff, dsrc.kv, smem_lds + sl * TILE_BYTES);
+        else
+            run_ok = issue_step_a<DK, NW, BAND, CHUNK, HIST>(a, issue, dsrc.q, dsrc.out, dsrc.kv, dl,
+                                                             smem_lds + sl * TILE_BYTES, side_lds + sl * 1024, run,
+                                                             run_voff);
         ++issued;
         issue.advance(a, gridDim.x, blockIdx.x);
     };

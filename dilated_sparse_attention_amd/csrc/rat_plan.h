@@ -275,6 +275,7 @@ struct StepCopiesA {
     int src;
     bool whole;               // every row of the wave's share exists (no clamp)
     uint32_t dp2;             // bytes between consecutive rows of the item
+    int row0, last;           // the wave's first row of the step; the item's last row
     uint64_t rel[PER_WAVE];
     uint32_t lim[PER_WAVE];   // clamped copies: the lane row offset is at most lim
     uint32_t m0[PER_WAVE];
@@ -311,6 +312,8 @@ __host__ __device__ __forceinline__ void step_copies_a(const AttnArgs& a, const 
     s.dp2 = (HIST && keys ? 1u : (uint32_t)c.dstride) * (2 * DK);
     const int last = (CHUNK && ko >= 0 && !own ? c.it.nkey : c.it.R1) - 1;
     const uint32_t slot = buf + wv * PER_WAVE * 1024;  // LDS byte address of the wave's first copy
+    s.row0 = row0;
+    s.last = last;
     s.whole = row0 + PER_WAVE * G::RPI - 1 <= last;
     if (s.whole) {
         // every row of the wave's share exists: copy j starts RPI rows after
@@ -334,6 +337,47 @@ __host__ __device__ __forceinline__ void step_copies_a(const AttnArgs& a, const 
             s.lim[j] = (uint32_t)(last - first) * s.dp2;
         }
     }
+}
+
+// A key-tile step of the cursor: a step past the item's query, partial and
+// own-state steps.
+template <bool BAND, bool CHUNK, bool HIST>
+__host__ __device__ __forceinline__ int step_key_tile_a(const CursorA<BAND, CHUNK, HIST>& c)
+{
+    return c.t - c.nq - c.no - (CHUNK ? c.nown : 0);  // key tile index, < 0 for other steps
+}
+
+// Runs of key tiles.  Key tile kt + 1 of an item is key tile kt moved by
+// kTileA rows: the same tensor, row stride and last row, so while the
+// wave's share of the tile stays whole its copy j starts at
+// rel0 + j RPI dp2, rel0 one add further than the tile before.  KeyRunA
+// holds a wave's plan of the key tile last issued (taken from a whole
+// step_copies_a); key_run_next_a moves it to the cursor's step when that
+// step is the next key tile of the same item and still whole, and returns
+// false otherwise (the step then takes the full plan).
+struct KeyRunA {
+    uint64_t rel0;  // byte offset of copy 0 from the key tensor's start
+    uint32_t dp2;   // bytes between consecutive rows
+    int row0, last;
+};
+
+template <int DK, int NW, bool BAND, bool CHUNK, bool HIST>
+__host__ __device__ __forceinline__ bool key_run_next_a(const CursorA<BAND, CHUNK, HIST>& c, KeyRunA& k)
+{
+    constexpr int SPAN = StepCopiesA<DK, NW>::PER_WAVE * Geo<DK>::RPI;  // rows of the wave's share
+    if (step_key_tile_a(c) < 1) return false;  // the step before was no key tile of this item
+    const int row0 = k.row0 + kTileA;
+    if (row0 + SPAN - 1 > k.last) return false;
+    k.row0 = row0;
+    k.rel0 += (uint64_t)kTileA * k.dp2;
+    return true;
+}
+
+// Byte offset of copy j of a key run's tile (what step_copies_a's rel[j] is)
+template <int DK>
+__host__ __device__ __forceinline__ uint64_t key_run_rel_a(const KeyRunA& k, int j)
+{
+    return k.rel0 + (uint64_t)j * Geo<DK>::RPI * k.dp2;
 }
 
 // The lane's byte offset within copy j: its row lq of the copy (clamped to

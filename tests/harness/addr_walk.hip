@@ -143,12 +143,15 @@ static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const cha
     const long long row_bytes = (long long)a.B * a.T * a.H * DK * 2;  // q and out
     const long long tile = (long long)kSlotRows * DK * 2;
     const long long lds = RING > 4 ? RING * tile : RING * (tile + 1024);
-    long steps = 0, items = 0;
+    long steps = 0, items = 0, run_steps = 0;
     for (int blk = 0; blk < grid; ++blk) {
         CursorA<BAND, CHUNK, HIST> c;
         c.seek(a, 0, grid, blk);
         int issued = 0;
         int last_round = -1;
+        // each wave's key run, kept as the kernel keeps it
+        KeyRunA run[NW];
+        bool run_ok[NW] = {};
         while (c.it.valid) {
             if (c.round != last_round) {
                 ++items;
@@ -160,6 +163,19 @@ static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const cha
             }
             const uint32_t buf = (uint32_t)((issued % RING) * tile);
             for (int wv = 0; wv < NW; ++wv) {
+                // the kernel's choice: the next tile of a key run, or the full plan
+                StepCopiesA<DK, NW> full;
+                step_copies_a<DK, NW>(a, c, wv, buf, full);
+                if (run_ok[wv] && key_run_next_a<DK, NW>(c, run[wv])) {
+                    ++run_steps;
+                    check(full.whole && full.src == 2, "key run on a step that is no whole key tile", blk, c.t, wv);
+                    for (int j = 0; j < StepCopiesA<DK, NW>::PER_WAVE; ++j)
+                        check(key_run_rel_a<DK>(run[wv], j) == full.rel[j] && full.dp2 == run[wv].dp2,
+                              "key run copy offset differs from the full plan", blk, c.t, j);
+                } else {
+                    run_ok[wv] = full.whole && step_key_tile_a(c) >= 0;
+                    if (run_ok[wv]) run[wv] = KeyRunA{full.rel[0], full.dp2, full.row0, full.last};
+                }
                 for (int lane = 0; lane < 64; ++lane) {
                     uint32_t lq, col16;
                     dma_lane_a<DK>(lane, lq, col16);
@@ -183,7 +199,8 @@ static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const cha
             c.advance(a, grid, blk);
         }
     }
-    printf("%s: %d workgroups, %ld items, %ld ring steps\n", what, grid, items, steps);
+    printf("%s: %d workgroups, %ld items, %ld ring steps (%ld wave steps as key runs)\n", what, grid, items, steps,
+           run_steps);
 }
 
 template <int DK>
