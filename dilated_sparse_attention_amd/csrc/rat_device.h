@@ -102,12 +102,23 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
 // write of M0 and the copy; the compiler does not see inside the asm, so
 // its leading s_nop provides both for the first copy (later copies' bases
 // are older still).
+// The bases are uniform by construction; readfirstlane states it to the
+// compiler (free when a base already sits in scalar registers), so that a
+// base its analysis takes for divergent still lands in scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t x)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 template <int N>
 __device__ __forceinline__ void dma16_group(const uint64_t (&base)[N], const uint32_t (&voff)[N], uint32_t m0);
 
 template <>
-__device__ __forceinline__ void dma16_group<2>(const uint64_t (&base)[2], const uint32_t (&voff)[2], uint32_t m0)
+__device__ __forceinline__ void dma16_group<2>(const uint64_t (&base_in)[2], const uint32_t (&voff)[2], uint32_t m0)
 {
+    const uint64_t base[2] = {uniform64(base_in[0]), uniform64(base_in[1])};
     asm volatile("s_nop 4\n\t"
                  "global_load_lds_dwordx4 %0, %2\n\t"
                  "global_load_lds_dwordx4 %1, %3 offset:1024"
@@ -115,8 +126,10 @@ __device__ __forceinline__ void dma16_group<2>(const uint64_t (&base)[2], const 
 }
 
 template <>
-__device__ __forceinline__ void dma16_group<4>(const uint64_t (&base)[4], const uint32_t (&voff)[4], uint32_t m0)
+__device__ __forceinline__ void dma16_group<4>(const uint64_t (&base_in)[4], const uint32_t (&voff)[4], uint32_t m0)
 {
+    const uint64_t base[4] = {uniform64(base_in[0]), uniform64(base_in[1]), uniform64(base_in[2]),
+                              uniform64(base_in[3])};
     asm volatile("s_nop 4\n\t"
                  "global_load_lds_dwordx4 %0, %4\n\t"
                  "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
