@@ -237,17 +237,26 @@ rat_status attn_prefill_bf16(const void* q, const void* k_state, const void* v_s
         const size_t need = (size_t)B * T * H * 2 * sizeof(float);
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return RAT_ERR_WORKSPACE;
     }
-    AttnArgs dil, band;
-    memset(&dil, 0, sizeof(dil));
-    dil.q = q; dil.ks = k_state; dil.vs = v_state; dil.kr = k_raw; dil.vr = v_raw; dil.out = out;
-    dil.ml = static_cast<float*>(workspace);
-    if (!attn_plan(B, T, H, D, W, scale, chunk, n_cap, dil, band)) return RAT_ERR_UNSUPPORTED;
+    AttnArgs lng, sht, band;
+    memset(&lng, 0, sizeof(lng));
+    lng.q = q; lng.ks = k_state; lng.vs = v_state; lng.kr = k_raw; lng.vr = v_raw; lng.out = out;
+    lng.ml = static_cast<float*>(workspace);
+    sht = lng;
+    if (!attn_launch_plans(B, T, H, D, W, scale, chunk, n_cap, lng, sht, band)) return RAT_ERR_UNSUPPORTED;
+    // the band pass first: windowed classes continue from its partial
+    // state.  Long residues: one eight-wave workgroup per CU; the band and
+    // short residues: two four-wave workgroups per CU.
+    const int cu = device_cu_count();
     if (band.nblocks > 0) {
-        const rat_status rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, device_cu_count()), s));
+        const rat_status rc = hip_status(launch_attn_band_bf16(band, d, std::min(band.nblocks, 2 * cu), s));
         if (rc != RAT_OK) return rc;
     }
-    const int grid = std::min(dil.nblocks, device_cu_count());
-    return hip_status(launch_attn_dilated_bf16(dil, d, grid, s));
+    if (lng.nblocks > 0) {
+        const rat_status rc = hip_status(launch_attn_dilated_bf16(lng, d, std::min(lng.nblocks, cu), s));
+        if (rc != RAT_OK) return rc;
+    }
+    if (sht.nblocks > 0) return hip_status(launch_attn_dilated_bf16(sht, d, std::min(sht.nblocks, 2 * cu), s));
+    return RAT_OK;
 }
 
 }  // namespace

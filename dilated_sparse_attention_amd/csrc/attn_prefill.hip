@@ -231,7 +231,7 @@ __device__ __forceinline__ bool issue_step_a(const AttnArgs& a, const CursorA<BA
     uint64_t base[PW];
     uint32_t voff[PW];
 #pragma unroll
-    for (int j = 0; j < PW; ++j) base[j] = tsrc + sc.rel[j] - 1024u * j;
+    for (int j = 0; j < PW; ++j) base[j] = tsrc + sc.rel[j] - 1024u * (j % 4);
     bool keys = false;
     if (sc.whole) {  // (uniform: the common case computes only its own lane offsets)
 #pragma unroll
@@ -263,12 +263,13 @@ __device__ __forceinline__ void issue_key_run_a(const KeyRunA& run, const uint32
 {
     constexpr int PW = StepCopiesA<DK, NW>::PER_WAVE;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    // copy j at src + key_run_rel_a(run, j), lowered by 1024 j for its immediate offset
-    const uint64_t step = (uint64_t)Geo<DK>::RPI * run.dp2 - 1024u;
+    // copy j at src + key_run_rel_a(run, j), lowered by 1024 (j mod 4) for
+    // its immediate offset
+    const uint64_t step = (uint64_t)Geo<DK>::RPI * run.dp2;
     uint64_t base[PW];
     base[0] = src_kv + run.rel0;
 #pragma unroll
-    for (int j = 1; j < PW; ++j) base[j] = base[j - 1] + step;
+    for (int j = 1; j < PW; ++j) base[j] = base[j - 1] + step + (j % 4 ? (uint64_t)0 - 1024u : (uint64_t)3072);
     dma16_group<PW>(base, voff, buf + wv * PW * 1024);
 }
 
@@ -377,25 +378,26 @@ struct Mask {
     static constexpr int value = BITS;
 };
 
-// NW waves per workgroup, NB = 16 / NW row blocks of 16 queries per wave
-// (block w and its mirror 15 - w, with NB = 4 also 7 - w and 8 + w, so that
-// every wave has the same causal work).  Every K / V fragment read from LDS
-// feeds NB MFMAs: more rows per wave means less LDS traffic per FLOP.
-template <int NB>
+// NW waves per workgroup, two row blocks of 16 queries per wave: block w
+// and its mirror 2 NW - 1 - w, so that every wave has the same causal work.
+// Every K / V fragment read from LDS feeds both blocks' MFMAs.
+template <int NW>
 __device__ __forceinline__ int row_block(int wv, int j)
 {
-    return j == 0 ? wv : j == 1 ? 15 - wv : j == 2 ? 7 - wv : 8 + wv;
+    return j == 0 ? wv : 2 * NW - 1 - wv;
 }
 
 // CHUNK: the chunk grid (keys of residue D - 1 strictly before the query,
 // the softmax started from the query's own state).  HIST: the states are a
 // per-residue history ([B][H][n_cap][d], a residue's rows contiguous).
+// Items of 32 NW query rows.  Eight waves run one workgroup per CU on a
+// deep ring; four waves on a two-slot ring run two workgroups per CU.
 template <int DK, int NW, int RING, bool BAND, bool CHUNK, bool HIST>
-__global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
+__global__ __launch_bounds__(NW * kWave, NW == 4 ? 2 : 1) void attn_dilated_kernel(AttnArgs a)
 {
     typedef Geo<DK> G;
-    constexpr int NB = 16 / NW;
-    static_assert(NB == 2 || NB == 4, "two or four row blocks per wave");
+    constexpr int NB = 2;  // row blocks per wave
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     constexpr int TILE_BYTES = kSlotRows * G::ROWB;
     constexpr int PER_WAVE = (kSlotRows / G::RPI) / NW;
     static_assert((kSlotRows / G::RPI) % NW == 0, "slot loads split evenly over waves");
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         bool has[NB];  // block holds rows of the item
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            rs[j] = it.R0 + 16 * row_block<NB>(wv, j);
+            rs[j] = it.R0 + 16 * row_block<NW>(wv, j);
             has[j] = rs[j] < it.R1;
             f[j].reset();
 #pragma unroll
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             const lds_char* qt = smem + (consumed % RING) * TILE_BYTES;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int r = 16 * row_block<NB>(wv, j);
+                const int r = 16 * row_block<NW>(wv, j);
                 if (r / kSlotRows == s) {
 #pragma unroll
                     for (int ks = 0; ks < G::KS; ++ks) f[j].q[ks] = lds_b128(qt + (r % kSlotRows) * G::ROWB + (off.k0 ^ (ks << 6)));
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             const float* ml = reinterpret_cast<const float*>(side + (consumed % RING) * 1024);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int r = 16 * row_block<NB>(wv, j);
+                const int r = 16 * row_block<NW>(wv, j);
                 if (r / kSlotRows == s)
                     f[j].init_partial_lds(ot + (r % kSlotRows) * G::ROWB, ml + (r % kSlotRows) * 2, rs[j] + i < it.R1);
             }
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
             const lds_char* sl = smem + (consumed % RING) * TILE_BYTES;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int r = 16 * row_block<NB>(wv, j);
+                const int r = 16 * row_block<NW>(wv, j);
                 if (r / kTileA == u)
                     f[j].init_own_lds(sl + (r % kTileA) * G::ROWB, off.k0, sl + (kTileA + r % kTileA) * G::ROWB,
                                       a.scale_log2);
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
         // while the softmax of another is computed.
         const int nfull = BAND ? 0 : min(it.R0 / kTileA, comp.ntile - 1);
         bool have_scores = false;
-        if constexpr (NB == 2 && !BAND) {
+        if constexpr (!BAND && RING >= 3) {  // (the pipelined tiles keep two slots busy)
             if (nfull > 0) {
                 wait_tile(0);
                 qk(all, consumed % RING, sc);
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void attn_dilated_kernel(AttnArgs a)
 // the workspace -- from which the dilated pass continues.
 
 // ring slots plus the (m, l) side buffers of path A
-size_t attn_lds_bytes_a(int d) { return (size_t)kRingA * (2 * kTileA * d * 2 + 1024); }
+size_t attn_lds_bytes_a(int d, int ring) { return (size_t)ring * (2 * kTileA * d * 2 + 1024); }
 // five slots, no side buffers (no windowed classes): 160 KiB at d = 128
 size_t attn_lds_bytes_a5(int d) { return (size_t)5 * 2 * kTileA * d * 2; }
 
@@ -666,41 +668,39 @@ static void set_lds(K kernel, size_t lds, bool& done)
     }
 }
 
-#ifndef RAT_ATTN_WAVES
-#define RAT_ATTN_WAVES 8
-#endif
-constexpr int kWavesDil = RAT_ATTN_WAVES;  // waves per workgroup of the dilated kernel
-
-template <bool BAND, bool CHUNK, bool HIST>
-static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool ring5, hipStream_t stream)
+template <int DK, int NW, int RING, bool BAND, bool CHUNK, bool HIST>
+static hipError_t launch_a(const AttnArgs& a, int grid, size_t lds, hipStream_t stream)
 {
-    static bool s[2][2] = {{false, false}, {false, false}};
-    const dim3 block(kWavesDil * kWave);
-    if (ring5) {  // deeper prefetch: five ring slots (no side buffers)
-        const size_t lds = attn_lds_bytes_a5(d);
-        if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK, HIST>, lds, s[0][0]);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, 5, BAND, CHUNK, HIST>), dim3(grid), block, lds, stream, a);
-        } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK, HIST>, lds, s[0][1]);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, 5, BAND, CHUNK, HIST>), dim3(grid), block, lds, stream, a);
-        }
-        return hipGetLastError();
+    static bool done = false;
+    set_lds(attn_dilated_kernel<DK, NW, RING, BAND, CHUNK, HIST>, lds, done);
+    hipLaunchKernelGGL((attn_dilated_kernel<DK, NW, RING, BAND, CHUNK, HIST>), dim3(grid), dim3(NW * kWave), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// The kernel shape follows the plan's rows per item: 256 -> eight waves,
+// five slots (four and the (m, l) buffers when a class is windowed); 128 ->
+// four waves, two slots with the buffers.
+template <bool BAND, bool CHUNK, bool HIST>
+static hipError_t launch_path_a(const AttnArgs& a, int d, int grid, bool windowed, hipStream_t stream)
+{
+    if (a.rows == kAttnRowsShort) {
+        const size_t lds = attn_lds_bytes_a(d, 2);
+        return d == 128 ? launch_a<128, 4, 2, BAND, CHUNK, HIST>(a, grid, lds, stream)
+                        : launch_a<64, 4, 2, BAND, CHUNK, HIST>(a, grid, lds, stream);
     }
-    if constexpr (CHUNK) {
-        return hipErrorInvalidValue;  // the chunk grid has no windowed classes
+    if (a.rows != kAttnRowsLong) return hipErrorInvalidValue;
+    if (!windowed) {
+        const size_t lds = attn_lds_bytes_a5(d);
+        return d == 128 ? launch_a<128, 8, 5, BAND, CHUNK, HIST>(a, grid, lds, stream)
+                        : launch_a<64, 8, 5, BAND, CHUNK, HIST>(a, grid, lds, stream);
+    }
+    if constexpr (CHUNK || BAND) {
+        return hipErrorInvalidValue;  // the chunk grid has no windowed classes; the band runs on four waves
     } else {
-        const size_t lds = attn_lds_bytes_a(d);
-        if (d == 128) {
-            set_lds(attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false, HIST>, lds, s[1][0]);
-            hipLaunchKernelGGL((attn_dilated_kernel<128, kWavesDil, kRingA, BAND, false, HIST>), dim3(grid), block, lds,
-                               stream, a);
-        } else {
-            set_lds(attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false, HIST>, lds, s[1][1]);
-            hipLaunchKernelGGL((attn_dilated_kernel<64, kWavesDil, kRingA, BAND, false, HIST>), dim3(grid), block, lds,
-                               stream, a);
-        }
-        return hipGetLastError();
+        const size_t lds = attn_lds_bytes_a(d, kRingA);
+        return d == 128 ? launch_a<128, 8, kRingA, false, false, HIST>(a, grid, lds, stream)
+                        : launch_a<64, 8, kRingA, false, false, HIST>(a, grid, lds, stream);
     }
 }
 
@@ -708,14 +708,14 @@ hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStrea
 {
     bool windowed = false;
     for (int c = 0; c < a.nclass; ++c) windowed |= a.cls[c].W > 0;
-    if (a.chunk) return launch_path_a<false, true, false>(a, d, grid, true, stream);  // no windowed classes
-    if (a.n_cap > 0) return launch_path_a<false, false, true>(a, d, grid, !windowed, stream);
-    return launch_path_a<false, false, false>(a, d, grid, !windowed, stream);
+    if (a.chunk) return launch_path_a<false, true, false>(a, d, grid, false, stream);  // no windowed classes
+    if (a.n_cap > 0) return launch_path_a<false, false, true>(a, d, grid, windowed, stream);
+    return launch_path_a<false, false, false>(a, d, grid, windowed, stream);
 }
 
 hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream)
 {
-    return launch_path_a<true, false, false>(a, d, grid, true, stream);
+    return launch_path_a<true, false, false>(a, d, grid, false, stream);
 }
 
 // ------------------------------------------------------------------ fp32

@@ -92,11 +92,12 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_char* dst)
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
-// N global_load_lds_dwordx4 copies issued back to back under one M0.  Copy
-// j reads 16 bytes per lane at base[j] + voff[j] + 1024 j and writes them
-// to LDS at m0 + 1024 j + 16 lane: the instruction's immediate offset moves
-// both addresses, so the caller passes base[j] already lowered by 1024 j
-// and the copies need no M0 write of their own.  The hardware needs 5 wait
+// N global_load_lds_dwordx4 copies issued back to back under one M0 (four
+// at most per M0: the immediate offset reaches 4095).  Copy j reads 16
+// bytes per lane at base[j] + voff[j] + 1024 (j mod 4) and writes them to
+// LDS at m0 + 1024 j + 16 lane: the instruction's immediate offset moves
+// both addresses, so the caller passes base[j] already lowered by
+// 1024 (j mod 4) and the copies need no M0 write of their own.  The hardware needs 5 wait
 // states between a VALU write of an SGPR (a base moved from vector
 // registers by readfirstlane) and a copy that reads it, and 1 between the
 // write of M0 and the copy; the compiler does not see inside the asm, so
@@ -137,6 +138,19 @@ __device__ __forceinline__ void dma16_group<4>(const uint64_t (&base_in)[4], con
                  "global_load_lds_dwordx4 %3, %7 offset:3072"
                  ::"v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
                    "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]), "{m0}"(m0) : "memory");
+}
+
+// Eight copies: two groups of four under M0 and M0 + 4096 (each base
+// lowered by 1024 (j mod 4) for its immediate offset).
+template <>
+__device__ __forceinline__ void dma16_group<8>(const uint64_t (&base_in)[8], const uint32_t (&voff)[8], uint32_t m0)
+{
+    const uint64_t b0[4] = {base_in[0], base_in[1], base_in[2], base_in[3]};
+    const uint64_t b1[4] = {base_in[4], base_in[5], base_in[6], base_in[7]};
+    const uint32_t v0[4] = {voff[0], voff[1], voff[2], voff[3]};
+    const uint32_t v1[4] = {voff[4], voff[5], voff[6], voff[7]};
+    dma16_group<4>(b0, v0, m0);
+    dma16_group<4>(b1, v1, m0 + 4096);
 }
 
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads()

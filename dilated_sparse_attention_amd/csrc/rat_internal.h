@@ -80,7 +80,6 @@ hipError_t launch_scan_slide64(const ScanSlideArgs& a, bool hist, hipStream_t st
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnMaxClasses = 8;
-constexpr int kAttnRowsA = 256;   // query rows of one residue per path-A item / band block
 
 struct AttnClass {
     int D, W;
@@ -105,14 +104,18 @@ struct AttnArgs {
     int n_cap;         // > 0: ks / vs are a StateHist with n_cap rows per head (relative dilation only)
     int nclass;
     int nblocks;
+    int rows;          // query rows per item: 32 per wave of the kernel that runs the plan
     AttnClass cls[kAttnMaxClasses];
     int heads[kAttnMaxHeads];  // 32-bit: scalar loads have no 16-bit form
 };
 
-// dilated states, every head: persistent kernel, `grid` workgroups (nblocks = items)
+// dilated states of the plan's classes: persistent kernel, `grid`
+// workgroups (nblocks = items) of a.rows / 32 waves -- eight waves on a
+// deep ring, one workgroup per CU (a.rows = 256), or four waves on a
+// two-slot ring, two workgroups per CU (a.rows = 128)
 hipError_t launch_attn_dilated_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
-// raw-key band of heads with W > 0: persistent kernel, `grid` workgroups,
-// items of 256 contiguous queries (nblocks = items)
+// raw-key band of heads with W > 0: the same kernel over items of a.rows
+// contiguous queries (four waves, a.rows = 128)
 hipError_t launch_attn_band_bf16(const AttnArgs& a, int d, int grid, hipStream_t stream);
 
 // Simple fp32 path (one workgroup per query row; exact fp32 arithmetic).
@@ -288,7 +291,7 @@ static_assert(sizeof(StateHist) == 1036, "StateHist layout");
 static_assert(sizeof(ScanFullArgs) == 1144 && offsetof(ScanFullArgs, fin) == 96 &&
               offsetof(ScanFullArgs, hist) == 108, "ScanFullArgs layout");
 static_assert(sizeof(ScanSlideArgs) == 1096 && offsetof(ScanSlideArgs, hist) == 60, "ScanSlideArgs layout");
-static_assert(sizeof(AttnArgs) == 1336 && offsetof(AttnArgs, cls) == 88 && offsetof(AttnArgs, heads) == 312,
+static_assert(sizeof(AttnArgs) == 1344 && offsetof(AttnArgs, cls) == 92 && offsetof(AttnArgs, heads) == 316,
               "AttnArgs layout");
 static_assert(sizeof(RingFillArgs) == 1080 && sizeof(DecodeArgs) == 3160 && sizeof(StepArgs) == 2136 &&
               sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3248 && sizeof(AttnF32Args) == 2128 &&

@@ -140,7 +140,6 @@ __host__ __device__ __forceinline__ bool ring_fill_at(const RingFillArgs& a, siz
 }
 
 // ---------------------------------------------------------------- attention
-constexpr int kWavesA = 8;
 constexpr int kTileA = 64;   // keys per K/V tile
 constexpr int kRingA = 4;    // LDS ring depth
 constexpr int kSlotRows = 2 * kTileA;  // rows of one ring slot
@@ -175,8 +174,8 @@ __host__ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int i
         it.b = idx / k.nheads;
         it.r = 0;
         it.D = 1;
-        it.R0 = (local / k.per_level) * kAttnRowsA;
-        it.R1 = imin(it.R0 + kAttnRowsA, a.T);
+        it.R0 = (local / k.per_level) * a.rows;
+        it.R1 = imin(it.R0 + a.rows, a.T);
         it.kbeg = imax(0, it.R0 - k.W + 1) & ~(kTileA - 1);
         it.kres = 0;
         it.nkey = it.R1;
@@ -191,8 +190,8 @@ __host__ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int i
     it.b = idx / k.D;
     it.D = k.D;
     const int M = it.r < a.T ? (a.T - it.r + k.D - 1) / k.D : 0;
-    it.R0 = level * kAttnRowsA;
-    it.R1 = imin(it.R0 + kAttnRowsA, M);
+    it.R0 = level * a.rows;
+    it.R1 = imin(it.R0 + a.rows, M);
     it.kbeg = 0;
     // chunk grid: query row i (position r + iD) sees the chunk ends
     // jD + D - 1 with j < i, all of which exist
@@ -451,7 +450,7 @@ __host__ __device__ __forceinline__ size_t item_out_row(const AttnArgs& a, const
 // items of the classes with W > 0.  Returns false when there are more than
 // kAttnMaxClasses classes or more than 2^31 items.
 inline bool attn_plan(int B, int T, int H, const int* D, const int* W, float scale, int chunk, int n_cap,
-                      AttnArgs& dil, AttnArgs& band)
+                      int rows, AttnArgs& dil, AttnArgs& band)
 {
     struct Cls { int D, W; std::vector<int> heads; double item_cost; };
     std::vector<Cls> cls;
@@ -466,12 +465,13 @@ inline bool attn_plan(int B, int T, int H, const int* D, const int* W, float sca
     if ((int)cls.size() > kAttnMaxClasses) return false;
     for (auto& c : cls) {
         const int Mmax = (T + c.D - 1) / c.D;
-        c.item_cost = (double)std::min(Mmax, kAttnRowsA) * Mmax;
+        c.item_cost = (double)std::min(Mmax, rows) * Mmax;
     }
     std::stable_sort(cls.begin(), cls.end(), [](const Cls& x, const Cls& y) { return x.item_cost > y.item_cost; });
     dil.B = B; dil.T = T; dil.H = H;
     dil.scale_log2 = scale * 1.4426950408889634f;
     dil.nclass = 0;
+    dil.rows = rows;
     band = dil;
     dil.chunk = chunk;
     dil.n_cap = n_cap;  // states as a per-residue history (0: [B][T][H][d])
@@ -483,14 +483,14 @@ inline bool attn_plan(int B, int T, int H, const int* D, const int* W, float sca
         k.nheads = (int)c.heads.size(); k.head_off = hoff;
         for (int hh : c.heads) { dil.heads[hoff] = hh; band.heads[hoff] = hh; ++hoff; }
         const int Mmax = (T + c.D - 1) / c.D;
-        k.levels = (Mmax + kAttnRowsA - 1) / kAttnRowsA;
+        k.levels = (Mmax + rows - 1) / rows;
         k.per_level = B * k.nheads * c.D;
         k.block_begin = (int)items;
         items += (int64_t)k.levels * k.per_level;
         if (c.W > 0) {
             AttnClass& kb = band.cls[band.nclass++];
             kb = k;
-            kb.levels = (T + kAttnRowsA - 1) / kAttnRowsA;
+            kb.levels = (T + rows - 1) / rows;
             kb.per_level = B * k.nheads;
             kb.block_begin = (int)blocks;
             blocks += (int64_t)kb.levels * kb.per_level;
@@ -499,6 +499,36 @@ inline bool attn_plan(int B, int T, int H, const int* D, const int* W, float sca
     }
     dil.nblocks = (int)items;
     band.nblocks = (int)blocks;
+    return true;
+}
+
+// Rows per item of the two kernel shapes, and the residue length from which
+// a plan runs on the long-item shape.  Eight waves on a five-slot ring (one
+// workgroup per CU) software-pipeline the unmasked key tiles, which pays
+// once residues are long; four waves on a two-slot ring run two workgroups
+// per CU whose phases overlap, which pays on short residues and the band.
+constexpr int kAttnRowsLong = 256;
+constexpr int kAttnRowsShort = 128;
+constexpr int kAttnLongResidue = 1024;
+
+// The launches of a prefill attention: the raw-window band of every
+// windowed class on the four-wave kernel, then every class in one launch,
+// on the eight-wave kernel (`lng`) when some class has residues longer
+// than kAttnLongResidue rows, else on the four-wave kernel (`sht`); the
+// other of the two has no items.  (One launch keeps the short classes
+// filling the long classes' tail.)  Returns false when attn_plan refuses
+// the heads.
+inline bool attn_launch_plans(int B, int T, int H, const int* D, const int* W, float scale, int chunk, int n_cap,
+                              AttnArgs& lng, AttnArgs& sht, AttnArgs& band)
+{
+    AttnArgs unused;
+    if (!attn_plan(B, T, H, D, W, scale, chunk, n_cap, kAttnRowsLong, lng, unused)) return false;
+    if (!attn_plan(B, T, H, D, W, scale, chunk, n_cap, kAttnRowsShort, sht, band)) return false;
+    bool any_long = false;
+    for (int c = 0; c < lng.nclass; ++c) any_long |= (T + lng.cls[c].D - 1) / lng.cls[c].D > kAttnLongResidue;
+    AttnArgs& idle = any_long ? sht : lng;
+    idle.nclass = 0;
+    idle.nblocks = 0;
     return true;
 }
 

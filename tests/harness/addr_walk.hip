@@ -136,10 +136,9 @@ static void walk_ring(int B, int T, int H, int d, int w_cap, const std::vector<i
 }
 
 // ---------------------------------------------------------------- attention
-template <int DK, int RING, bool BAND, bool CHUNK, bool HIST>
+template <int DK, int NW, int RING, bool BAND, bool CHUNK, bool HIST>
 static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const char* what)
 {
-    constexpr int NW = kWavesA;
     const long long row_bytes = (long long)a.B * a.T * a.H * DK * 2;  // q and out
     const long long tile = (long long)kSlotRows * DK * 2;
     const long long lds = RING > 4 ? RING * tile : RING * (tile + 1024);
@@ -206,27 +205,49 @@ static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const cha
 template <int DK>
 static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, const std::vector<int>& W, int n_cap)
 {
-    AttnArgs dil, band;
-    memset(&dil, 0, sizeof(dil));
-    if (!attn_plan(B, T, H, D.data(), W.data(), 0.1f, 0, n_cap, dil, band)) {
+    // the launches as the library makes them: the band pass on four-wave
+    // workgroups (two per CU, two ring slots), the classes on eight-wave
+    // workgroups (five slots, four with windows) when a residue is long,
+    // else on four-wave ones
+    AttnArgs lng, sht, band;
+    memset(&lng, 0, sizeof(lng));
+    sht = lng;
+    if (!attn_launch_plans(B, T, H, D.data(), W.data(), 0.1f, 0, n_cap, lng, sht, band)) {
         printf("attention plan refused\n");
         ++g_fail;
         return;
     }
+    AttnArgs all, unused;
+    memset(&all, 0, sizeof(all));
+    attn_plan(B, T, H, D.data(), W.data(), 0.1f, 0, n_cap, kAttnRowsShort, all, unused);
+    long long short_rows = 0, all_rows = 0;  // query rows the short plan covers, against the whole plan's
+    for (int c = 0; c < sht.nclass; ++c) short_rows += (long long)sht.cls[c].nheads * B * T;
+    for (int c = 0; c < all.nclass; ++c) all_rows += (long long)all.cls[c].nheads * B * T;
+    long long long_rows = 0;
+    for (int c = 0; c < lng.nclass; ++c) long_rows += (long long)lng.cls[c].nheads * B * T;
+    check(short_rows + long_rows == all_rows && (sht.nblocks == 0 || lng.nblocks == 0),
+          "one of the two plans covers every head once", short_rows, long_rows, all_rows);
     bool windowed = false;
-    for (int i = 0; i < dil.nclass; ++i) windowed |= dil.cls[i].W > 0;
+    for (int i = 0; i < lng.nclass; ++i) windowed |= lng.cls[i].W > 0;
     const long long raw_bytes = (long long)B * T * H * DK * 2;
+    const long long kv_bytes = n_cap > 0 ? (long long)B * H * n_cap * DK * 2 : raw_bytes;
     const int cu = 256;
     if (band.nblocks > 0)
-        walk_attn<DK, 5, true, false, false>(band, std::min(band.nblocks, cu), raw_bytes, "band pass copies");
-    const int grid = std::min(dil.nblocks, cu);
-    if (n_cap > 0) {
-        const long long hist_bytes = (long long)B * H * n_cap * DK * 2;
-        if (windowed) walk_attn<DK, 4, false, false, true>(dil, grid, hist_bytes, "dilated copies (history, 4 slots)");
-        else walk_attn<DK, 5, false, false, true>(dil, grid, hist_bytes, "dilated copies (history, 5 slots)");
-    } else {
-        if (windowed) walk_attn<DK, 4, false, false, false>(dil, grid, raw_bytes, "dilated copies (4 slots)");
-        else walk_attn<DK, 5, false, false, false>(dil, grid, raw_bytes, "dilated copies (5 slots)");
+        walk_attn<DK, 4, 2, true, false, false>(band, std::min(band.nblocks, 2 * cu), raw_bytes, "band pass copies");
+    if (lng.nblocks > 0) {
+        const int grid = std::min(lng.nblocks, cu);
+        if (n_cap > 0) {
+            if (windowed) walk_attn<DK, 8, 4, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 4 slots)");
+            else walk_attn<DK, 8, 5, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 5 slots)");
+        } else {
+            if (windowed) walk_attn<DK, 8, 4, false, false, false>(lng, grid, kv_bytes, "eight waves (4 slots)");
+            else walk_attn<DK, 8, 5, false, false, false>(lng, grid, kv_bytes, "eight waves (5 slots)");
+        }
+    }
+    if (sht.nblocks > 0) {
+        const int grid = std::min(sht.nblocks, 2 * cu);
+        if (n_cap > 0) walk_attn<DK, 4, 2, false, false, true>(sht, grid, kv_bytes, "four waves (history, 2 slots)");
+        else walk_attn<DK, 4, 2, false, false, false>(sht, grid, kv_bytes, "four waves (2 slots)");
     }
 }
 
