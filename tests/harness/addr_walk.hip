@@ -202,6 +202,54 @@ static void walk_attn(const AttnArgs& a, int grid, long long kv_bytes, const cha
            run_steps);
 }
 
+// The kernel's ring schedule at step granularity: per item the waits
+// (wait_tile(d): step consumed + d must have landed) and consumes the kernel
+// makes, with one free slot refilled after each wait's barrier.  Checks that
+// each awaited step has been issued by then, and that every issued step is
+// consumed.
+template <int NW, int RING, bool BAND, bool CHUNK, bool HIST>
+static void walk_ring_schedule(const AttnArgs& a, int grid, const char* what)
+{
+    long waits = 0;
+    for (int blk = 0; blk < grid; ++blk) {
+        CursorA<BAND, CHUNK, HIST> issue, comp;
+        issue.seek(a, 0, grid, blk);
+        comp = issue;
+        long issued = 0, consumed = 0;
+        for (int j = 0; j < RING - 1 && issue.it.valid; ++j) {
+            ++issued;
+            issue.advance(a, grid, blk);
+        }
+        auto wait = [&](int d) {
+            ++waits;
+            check(issued > consumed + d, what, blk, consumed, d);
+            if (issue.it.valid && issued < consumed + RING) {
+                ++issued;
+                issue.advance(a, grid, blk);
+            }
+        };
+        while (comp.it.valid) {
+            for (int s = 0; s < comp.nq + comp.no + (CHUNK ? comp.nown : 0); ++s) { wait(0); ++consumed; }
+            int tt = 0;
+            bool have = false;
+            const int nfull = BAND ? 0 : std::min(comp.it.R0 / kTileA, comp.ntile - 1);
+            if (!BAND && RING >= 3 && nfull > 0) {
+                wait(0);
+                for (; tt < nfull; ++tt) { wait(1); ++consumed; }
+                have = true;
+            }
+            for (; tt < comp.ntile; ++tt) {
+                if (!have) wait(0);
+                have = false;
+                ++consumed;
+            }
+            comp.seek(a, comp.round + 1, grid, blk);
+        }
+        check(consumed == issued, "every issued step consumed", blk, consumed, issued);
+    }
+    printf("%s: %ld waits, every awaited step issued in time\n", what, waits);
+}
+
 template <int DK>
 static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, const std::vector<int>& W, int n_cap)
 {
@@ -232,22 +280,53 @@ static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, co
     const long long raw_bytes = (long long)B * T * H * DK * 2;
     const long long kv_bytes = n_cap > 0 ? (long long)B * H * n_cap * DK * 2 : raw_bytes;
     const int cu = 256;
-    if (band.nblocks > 0)
-        walk_attn<DK, 4, 2, true, false, false>(band, std::min(band.nblocks, 2 * cu), raw_bytes, "band pass copies");
+    if (band.nblocks > 0) {
+        const int grid = std::min(band.nblocks, 2 * cu);
+        walk_attn<DK, 4, 2, true, false, false>(band, grid, raw_bytes, "band pass copies");
+        walk_ring_schedule<4, 2, true, false, false>(band, grid, "band pass ring");
+    }
     if (lng.nblocks > 0) {
         const int grid = std::min(lng.nblocks, cu);
-        if (n_cap > 0) {
-            if (windowed) walk_attn<DK, 8, 4, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 4 slots)");
-            else walk_attn<DK, 8, 5, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 5 slots)");
+        if (n_cap > 0 && windowed) {
+            walk_attn<DK, 8, 4, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 4 slots)");
+            walk_ring_schedule<8, 4, false, false, true>(lng, grid, "eight-wave ring (history, 4 slots)");
+        } else if (n_cap > 0) {
+            walk_attn<DK, 8, 5, false, false, true>(lng, grid, kv_bytes, "eight waves (history, 5 slots)");
+            walk_ring_schedule<8, 5, false, false, true>(lng, grid, "eight-wave ring (history, 5 slots)");
+        } else if (windowed) {
+            walk_attn<DK, 8, 4, false, false, false>(lng, grid, kv_bytes, "eight waves (4 slots)");
+            walk_ring_schedule<8, 4, false, false, false>(lng, grid, "eight-wave ring (4 slots)");
         } else {
-            if (windowed) walk_attn<DK, 8, 4, false, false, false>(lng, grid, kv_bytes, "eight waves (4 slots)");
-            else walk_attn<DK, 8, 5, false, false, false>(lng, grid, kv_bytes, "eight waves (5 slots)");
+            walk_attn<DK, 8, 5, false, false, false>(lng, grid, kv_bytes, "eight waves (5 slots)");
+            walk_ring_schedule<8, 5, false, false, false>(lng, grid, "eight-wave ring (5 slots)");
         }
     }
     if (sht.nblocks > 0) {
         const int grid = std::min(sht.nblocks, 2 * cu);
-        if (n_cap > 0) walk_attn<DK, 4, 2, false, false, true>(sht, grid, kv_bytes, "four waves (history, 2 slots)");
-        else walk_attn<DK, 4, 2, false, false, false>(sht, grid, kv_bytes, "four waves (2 slots)");
+        if (n_cap > 0) {
+            walk_attn<DK, 4, 2, false, false, true>(sht, grid, kv_bytes, "four waves (history, 2 slots)");
+            walk_ring_schedule<4, 2, false, false, true>(sht, grid, "four-wave ring (history)");
+        } else {
+            walk_attn<DK, 4, 2, false, false, false>(sht, grid, kv_bytes, "four waves (2 slots)");
+            walk_ring_schedule<4, 2, false, false, false>(sht, grid, "four-wave ring");
+        }
+    }
+    // the chunk grid (own-state steps, no windows) on the same shapes
+    AttnArgs clng, csht, cband;
+    memset(&clng, 0, sizeof(clng));
+    csht = clng;
+    std::vector<int> W0(H, 0);
+    if (n_cap == 0 && attn_launch_plans(B, T, H, D.data(), W0.data(), 0.1f, 1, 0, clng, csht, cband)) {
+        if (clng.nblocks > 0) {
+            const int grid = std::min(clng.nblocks, cu);
+            walk_attn<DK, 8, 5, false, true, false>(clng, grid, raw_bytes, "chunk grid, eight waves");
+            walk_ring_schedule<8, 5, false, true, false>(clng, grid, "chunk grid ring, eight waves");
+        }
+        if (csht.nblocks > 0) {
+            const int grid = std::min(csht.nblocks, 2 * cu);
+            walk_attn<DK, 4, 2, false, true, false>(csht, grid, raw_bytes, "chunk grid, four waves");
+            walk_ring_schedule<4, 2, false, true, false>(csht, grid, "chunk grid ring, four waves");
+        }
     }
 }
 
