@@ -36,7 +36,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 # kernel names as the profiler lists them (bf16, d = 128, full recurrence)
 SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, false>"
-ATTN_KERNEL = "rat::attn_dilated_kernel<128, 8, 5, false, false, false>"
+ATTN_KERNEL = "rat::attn_dilated_kernel<128, 4, 2, false, false, false>"  # the 1.5B plan: short residues, four waves
 
 # launches timed per kernel (each between its own pair of HIP events)
 MIN_TIMED = 50
