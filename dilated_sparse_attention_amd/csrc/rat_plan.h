@@ -182,8 +182,26 @@ __host__ __device__ __forceinline__ ItemA decode_item_a(const AttnArgs& a, int i
         it.valid = it.R0 < a.T;
         return it;
     }
-    const int level = k.levels - 1 - local / k.per_level;
-    int idx = local % k.per_level;
+    // Levels most expensive first.  With a few levels (short residues, the
+    // four-wave kernel), the items of eight residues alternate by level in
+    // groups of eight: a residue's items lie eight apart, so workgroups on
+    // one XCD (workgroup i runs on XCD i mod 8) take them in the same round
+    // and its L2 serves the key tiles they share.  Residues past the last
+    // whole group of eight keep the level-major order.
+    int level, idx;
+    const int p8 = (k.per_level / 8) * 8;
+    if (k.levels > 1 && k.levels <= 4 && local < p8 * k.levels) {
+        const int w = local % (8 * k.levels);
+        level = k.levels - 1 - w / 8;
+        idx = (local / (8 * k.levels)) * 8 + w % 8;
+    } else if (k.levels > 1 && k.levels <= 4) {
+        const int rest = k.per_level - p8, r = local - p8 * k.levels;
+        level = k.levels - 1 - r / rest;
+        idx = p8 + r % rest;
+    } else {
+        level = k.levels - 1 - local / k.per_level;
+        idx = local % k.per_level;
+    }
     it.h = a.heads[k.head_off + idx % k.nheads];
     idx /= k.nheads;
     it.r = idx % k.D;

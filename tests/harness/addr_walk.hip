@@ -250,6 +250,38 @@ static void walk_ring_schedule(const AttnArgs& a, int grid, const char* what)
     printf("%s: %ld waits, every awaited step issued in time\n", what, waits);
 }
 
+// Every (class, level, residue) of a plan is exactly one item: the item
+// order is a permutation of the plan's work.
+template <bool BAND, bool CHUNK>
+static void check_items(const AttnArgs& a, const char* what)
+{
+    std::vector<char> seen;
+    long long valid = 0;
+    for (int c = 0; c < a.nclass; ++c) {
+        const AttnClass& k = a.cls[c];
+        seen.assign((size_t)k.levels * k.per_level, 0);
+        for (int local = 0; local < k.levels * k.per_level; ++local) {
+            const ItemA it = decode_item_a<BAND, CHUNK>(a, k.block_begin + local);
+            // recover (level, idx) from the item: level from R0, idx from (b, head, residue)
+            const int level = it.R0 / a.rows;
+            int hslot = -1;
+            for (int hh = 0; hh < k.nheads; ++hh)
+                if (a.heads[k.head_off + hh] == it.h) hslot = hh;
+            const long long idx = BAND ? (long long)it.b * k.nheads + hslot
+                                       : ((long long)it.b * k.D + it.r) * k.nheads + hslot;
+            const bool in = hslot >= 0 && level >= 0 && level < k.levels && idx >= 0 && idx < k.per_level;
+            check(in, what, c, local, idx);
+            if (!in) continue;
+            char& s = seen[(size_t)level * k.per_level + idx];
+            check(s == 0, "item decoded twice", c, local, idx);
+            s = 1;
+            valid += it.valid;
+        }
+        for (size_t q = 0; q < seen.size(); ++q) check(seen[q] == 1, "item never decoded", c, (long long)q, 0);
+    }
+    printf("%s: every item once (%lld with rows)\n", what, valid);
+}
+
 template <int DK>
 static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, const std::vector<int>& W, int n_cap)
 {
@@ -280,6 +312,9 @@ static void walk_prefill_attn(int B, int T, int H, const std::vector<int>& D, co
     const long long raw_bytes = (long long)B * T * H * DK * 2;
     const long long kv_bytes = n_cap > 0 ? (long long)B * H * n_cap * DK * 2 : raw_bytes;
     const int cu = 256;
+    check_items<true, false>(band, "band items");
+    check_items<false, false>(lng, "eight-wave items");
+    check_items<false, false>(sht, "four-wave items");
     if (band.nblocks > 0) {
         const int grid = std::min(band.nblocks, 2 * cu);
         walk_attn<DK, 4, 2, true, false, false>(band, grid, raw_bytes, "band pass copies");
