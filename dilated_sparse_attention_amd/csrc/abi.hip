@@ -52,9 +52,9 @@ bool caches_ok(int B, int H, int d, int nd_cap, int w_cap)
     return size_ok(B, H, d, 1) && (int64_t)nd_cap * d < kMaxElems && (int64_t)std::max(w_cap, 1) * d < kMaxElems;
 }
 
-ScanPlan scan_plan(int B, int T, int H, int d, rat_dtype dtype)
+ScanPlan scan_plan(int B, int T, int H, int d, int L, rat_dtype dtype)
 {
-    return rat::scan_plan(B, T, H, d, dtype == RAT_DTYPE_BF16);
+    return rat::scan_plan(B, T, H, d, L, dtype == RAT_DTYPE_BF16);
 }
 
 // compute units of the current device (cached per device)
@@ -84,7 +84,7 @@ rat_status run_scan(const void* k, const void* v, const void* g, void* ks, void*
 {
     const bool bf16 = dtype == RAT_DTYPE_BF16;
     if (scan_uses_workspace(T, L, mode)) {
-        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        const ScanPlan p = scan_plan(B, T, H, d, L, dtype);
         ScanFullArgs a;
         memset(&a, 0, sizeof(a));
         a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs;
@@ -97,7 +97,7 @@ rat_status run_scan(const void* k, const void* v, const void* g, void* ks, void*
         a.fin = final_state;
         a.d = d;
         if (hist) a.hist = *hist;
-        return hip_status(launch_scan_full(a, bf16, hist != nullptr, s));
+        return hip_status(launch_scan_full(a, bf16, hist != nullptr, p.wide, s));
     }
     ScanSlideArgs a;
     memset(&a, 0, sizeof(a));
@@ -161,7 +161,7 @@ size_t rat_scan_workspace_bytes(int B, int T, int H, int d, int L, rat_recur_mod
 {
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1 || !dtype_ok(dtype)) return 0;
     if (!scan_uses_workspace(T, L, mode)) return 0;
-    return scan_plan(B, T, H, d, dtype).bytes;
+    return scan_plan(B, T, H, d, L, dtype).bytes;
 }
 
 rat_status rat_scan_prefill(const void* k, const void* v, const void* gate_logits, void* k_state, void* v_state,
@@ -187,7 +187,7 @@ rat_status rat_scan_prefill(const void* k, const void* v, const void* gate_logit
         if (!aligned16(final_state)) return RAT_ERR_ALIGN;
     }
     if (scan_uses_workspace(T, L, mode)) {
-        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        const ScanPlan p = scan_plan(B, T, H, d, L, dtype);
         if (!workspace || workspace_bytes < p.bytes || ((uintptr_t)workspace & 255u)) return RAT_ERR_WORKSPACE;
     }
     return run_scan(k, v, gate_logits, k_state, v_state, B, T, H, d, L, mode, dtype, workspace, final_state,
@@ -391,7 +391,7 @@ rat_status rat_layer_prefill(const void* q, const void* k, const void* v, const 
     for (const void* x : outs)
         if (x && !aligned16(x)) return RAT_ERR_ALIGN;
     if (scan_uses_workspace(T, L, mode)) {
-        const ScanPlan p = scan_plan(B, T, H, d, dtype);
+        const ScanPlan p = scan_plan(B, T, H, d, L, dtype);
         if (!scan_workspace || scan_workspace_bytes < p.bytes || ((uintptr_t)scan_workspace & 255u))
             return RAT_ERR_WORKSPACE;
     }

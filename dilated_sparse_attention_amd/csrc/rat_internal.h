@@ -20,18 +20,27 @@ struct StateHist {
 };
 
 // ---------------------------------------------------------------- scan
-// Tile of the full / RESTART scan: a workgroup of kScanWaves waves covers
-// one block of channels (128 bf16 / 64 fp32: a 256-byte row segment) x
-// kScanChunk tokens; each lane holds 16 bytes of a row (8 bf16 / 4 fp32
-// channels) for kScanTpl consecutive tokens.
+// Tile of the full / RESTART scan: a workgroup of kScanFullWaves waves
+// covers one block of BW channels x CT tokens; each lane holds 16 bytes of a
+// row (CPL = 8 bf16 / 4 fp32 channels) for kScanTpl consecutive tokens, LPR
+// lanes per token row.  Narrow: 16 lanes (256-byte row segments, four token
+// segments per wave).  Wide (bf16 only): 8 lanes (128-byte segments of 64
+// channels, eight token segments per wave), so a chunk holds twice the
+// tokens and a sequence half the chunks: shorter look-back chains, a
+// longer in-chunk segment prefix.
 constexpr int kScanWaves = 8;  // the SLIDING L = 64 kernel's workgroup
 #ifndef RAT_SCAN_FULL_WAVES
 #define RAT_SCAN_FULL_WAVES 8
 #endif
 constexpr int kScanFullWaves = RAT_SCAN_FULL_WAVES;  // the full / RESTART kernel's workgroup
 constexpr int kScanTpl = 4;
-constexpr int kScanChunk = kScanFullWaves * 4 * kScanTpl;  // 4 token segments per wave
-template <typename E> struct ScanBlock { static constexpr int value = 256 / sizeof(E); };
+template <typename E, bool WIDE>
+struct ScanGeo {
+    static constexpr int CPL = 16 / (int)sizeof(E);
+    static constexpr int LPR = (WIDE && sizeof(E) == 2) ? 8 : 16;
+    static constexpr int BW = LPR * CPL;                               // channels per block
+    static constexpr int CT = kScanFullWaves * (64 / LPR) * kScanTpl;  // tokens per chunk
+};
 
 struct ScanHeader {
     // low 32 bits: next chunk ticket of the running call; high 32 bits:
@@ -73,7 +82,7 @@ struct ScanSlideArgs {
 };
 
 // hist: write the states as a StateHist instead of [B][T][H][d]
-hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, hipStream_t stream);
+hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, bool wide, hipStream_t stream);
 hipError_t launch_scan_sliding(const ScanSlideArgs& a, int nblocks, bool bf16, bool hist, hipStream_t stream);
 // SLIDING with L = 64 in bf16 (N a multiple of 64)
 hipError_t launch_scan_slide64(const ScanSlideArgs& a, bool hist, hipStream_t stream);

@@ -23,20 +23,27 @@ __host__ __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : 
 __host__ __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- scan
-// Workspace plan of the full / RESTART scan: chunks of kScanChunk tokens
-// of one ScanBlock-channel block, a 256-byte header, then per chunk the
-// tagged aggregate words [3][block] and inclusive words [2][block].
+// Workspace plan of the full / RESTART scan: chunks of CT tokens of one
+// BW-channel block (ScanGeo), a 256-byte header, then per chunk the tagged
+// aggregate words [3][block] and inclusive words [2][block].  `wide`: the
+// wide bf16 geometry, taken unless the recurrence restarts every 256 tokens
+// or sooner (then every chunk starts at, or right after, a restart and
+// needs no long look-back, and the narrow chunk's shorter prefix wins).
 struct ScanPlan {
     int chunk, nblk, nseq, nchunk, nwg;
+    bool wide;
     size_t agg_off, incl_off, bytes;
 };
 
-inline ScanPlan scan_plan(int B, int T, int H, int d, bool bf16)
+inline bool scan_wide(int T, int L, bool bf16) { return bf16 && !(L < T && L <= 256); }
+
+inline ScanPlan scan_plan(int B, int T, int H, int d, int L, bool bf16)
 {
     ScanPlan p;
-    p.chunk = kScanChunk;
+    p.wide = scan_wide(T, L, bf16);
+    p.chunk = !bf16 ? ScanGeo<float, false>::CT : p.wide ? ScanGeo<uint16_t, true>::CT : ScanGeo<uint16_t, false>::CT;
+    const int bw = !bf16 ? ScanGeo<float, false>::BW : p.wide ? ScanGeo<uint16_t, true>::BW : ScanGeo<uint16_t, false>::BW;
     const int N = H * d;
-    const int bw = bf16 ? ScanBlock<uint16_t>::value : ScanBlock<float>::value;
     p.nblk = (N + bw - 1) / bw;
     p.nseq = B * p.nblk;
     p.nchunk = (T + p.chunk - 1) / p.chunk;
@@ -50,16 +57,16 @@ inline ScanPlan scan_plan(int B, int T, int H, int d, bool bf16)
 
 // Where lane `lane` of wave `w` works in the chunk of ticket `ticket`:
 // channels ch0 .. ch0 + CPL - 1 (CPL = 16 / element size) of tokens t0 ..
-// t0 + kScanTpl - 1 (16 lanes per 256-byte row segment, 4 segments per wave).
+// t0 + kScanTpl - 1 (LPR lanes per row segment, 64 / LPR segments per wave).
 struct ScanLane {
     int chunk, seq, b, cblk, tb, c, seg, ch0, t0;
     bool cvalid;
 };
 
-template <int CPL>
+template <int CPL, int LPR>
 __host__ __device__ __forceinline__ ScanLane scan_lane(const ScanFullArgs& a, uint32_t ticket, int w, int lane)
 {
-    constexpr int LPR = 16, BW = LPR * CPL, GPW = 64 / LPR, CT = kScanFullWaves * GPW * kScanTpl;
+    constexpr int BW = LPR * CPL, GPW = 64 / LPR, CT = kScanFullWaves * GPW * kScanTpl;
     ScanLane s;
     s.chunk = (int)(ticket / (uint32_t)a.nseq);
     s.seq = (int)(ticket % (uint32_t)a.nseq);

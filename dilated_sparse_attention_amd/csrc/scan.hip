@@ -59,12 +59,12 @@ constexpr uint32_t kLookbackSpinLimit = 1u << 22;  // look-back rounds before th
 #endif
 constexpr int kLookbackWindow = RAT_SCAN_LOOKBACK;  // predecessors examined per round
 
-template <typename E, bool HIST>
+template <typename E, bool HIST, bool WIDE>
 __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(ScanFullArgs a)
 {
     typedef Row16<E> R16;
-    constexpr int CPL = R16::CPL;           // channels per lane
-    constexpr int LPR = 16;                 // lanes per token row of the block
+    constexpr int CPL = R16::CPL;                // channels per lane
+    constexpr int LPR = ScanGeo<E, WIDE>::LPR;  // lanes per token row of the block
     constexpr int BW = LPR * CPL;           // channels per block
     constexpr int GPW = kWave / LPR;        // token segments per wave
     constexpr int NSEG = kScanFullWaves * GPW;  // segments per chunk
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     constexpr int C0 = BW / kWave;          // channels per lane of the single-wave steps
     constexpr int PW = C0 > 1 ? 2 : 1;      // waves of the segment prefix step
     constexpr int CP = BW / (PW * kWave);   // channels per lane there
-    static_assert(CT == kScanChunk && BW == ScanBlock<E>::value, "geometry shared with the host plan");
+    static_assert(CT == ScanGeo<E, WIDE>::CT && BW == ScanGeo<E, WIDE>::BW, "geometry shared with the host plan");
     // segment maps (A, K, V) per channel; then their exclusive prefixes
     __shared__ float s_seg[NSEG][3][BW];
     __shared__ float s_carry[2][BW];  // chunk carry-in (hk, hv)
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kScanFullWaves * kWave, 4) void scan_full_kernel(Sc
     const uint32_t ticket = s_ticket;
     const uint32_t tag = s_epoch + 1u;
     // lane (r, c): channels cblk + CPL c .. +CPL, tokens t0 .. t0 + TPL - 1
-    const ScanLane sl = scan_lane<CPL>(a, ticket, w, lane);
+    const ScanLane sl = scan_lane<CPL, LPR>(a, ticket, w, lane);
     const int chunk = sl.chunk, seq = sl.seq, b = sl.b;
     const int cblk = sl.cblk;  // first channel of the block
     const int tb = sl.tb;      // first token of the chunk
@@ -689,13 +689,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_slide64_kernel(ScanSlideArg
 }
 
 // ---------------------------------------------------------------- launches
-hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, hipStream_t stream)
+hipError_t launch_scan_full(const ScanFullArgs& a, bool bf16, bool hist, bool wide, hipStream_t stream)
 {
     const dim3 grid(a.nwg), block(kScanFullWaves * kWave);
-    if (bf16 && hist) hipLaunchKernelGGL((scan_full_kernel<uint16_t, true>), grid, block, 0, stream, a);
-    else if (bf16) hipLaunchKernelGGL((scan_full_kernel<uint16_t, false>), grid, block, 0, stream, a);
-    else if (hist) hipLaunchKernelGGL((scan_full_kernel<float, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((scan_full_kernel<float, false>), grid, block, 0, stream, a);
+    if (bf16 && wide && hist) hipLaunchKernelGGL((scan_full_kernel<uint16_t, true, true>), grid, block, 0, stream, a);
+    else if (bf16 && wide) hipLaunchKernelGGL((scan_full_kernel<uint16_t, false, true>), grid, block, 0, stream, a);
+    else if (bf16 && hist) hipLaunchKernelGGL((scan_full_kernel<uint16_t, true, false>), grid, block, 0, stream, a);
+    else if (bf16) hipLaunchKernelGGL((scan_full_kernel<uint16_t, false, false>), grid, block, 0, stream, a);
+    else if (hist) hipLaunchKernelGGL((scan_full_kernel<float, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((scan_full_kernel<float, false, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -47,11 +47,12 @@ static std::vector<int> parse_list(const char* s)
 }
 
 // ---------------------------------------------------------------- scan
-template <typename E, bool HIST>
+template <typename E, bool HIST, bool WIDE>
 static void walk_scan(int B, int T, int H, int d, int L, int n_cap, bool fin, const std::vector<int>& D)
 {
     constexpr int CPL = 16 / (int)sizeof(E);
-    const ScanPlan p = scan_plan(B, T, H, d, sizeof(E) == 2);
+    const ScanPlan p = scan_plan(B, T, H, d, L, sizeof(E) == 2);
+    check(p.wide == WIDE, "scan geometry as the launcher picks it", T, L, p.wide);
     ScanFullArgs a;
     memset(&a, 0, sizeof(a));
     a.T = T; a.N = H * d; a.nblk = p.nblk; a.nseq = p.nseq; a.nchunk = p.nchunk;
@@ -67,7 +68,7 @@ static void walk_scan(int B, int T, int H, int d, int L, int n_cap, bool fin, co
     for (uint32_t ticket = 0; ticket < (uint32_t)p.nwg; ++ticket) {
         for (int w = 0; w < kScanFullWaves; ++w) {
             for (int lane = 0; lane < 64; ++lane) {
-                const ScanLane sl = scan_lane<CPL>(a, ticket, w, lane);
+                const ScanLane sl = scan_lane<CPL, ScanGeo<E, WIDE>::LPR>(a, ticket, w, lane);
                 check((size_t)sl.chunk * a.nseq + sl.seq < (size_t)p.nwg, "scan workspace slot", ticket, w, lane);
                 const size_t obase = ((size_t)sl.b * a.T + sl.t0) * a.N + sl.ch0;
                 HistRow hr;
@@ -382,12 +383,15 @@ int main(int argc, char** argv)
     const bool bf16 = dtype == 1;
     const bool full_or_restart = L >= T || mode == 0;
     if (full_or_restart) {
+        const bool wide = scan_wide(T, L, bf16);
         if (n_cap > 0) {
-            if (bf16) walk_scan<uint16_t, true>(B, T, H, d, L, n_cap, fin, D);
-            else walk_scan<float, true>(B, T, H, d, L, n_cap, fin, D);
+            if (bf16 && wide) walk_scan<uint16_t, true, true>(B, T, H, d, L, n_cap, fin, D);
+            else if (bf16) walk_scan<uint16_t, true, false>(B, T, H, d, L, n_cap, fin, D);
+            else walk_scan<float, true, false>(B, T, H, d, L, n_cap, fin, D);
         } else {
-            if (bf16) walk_scan<uint16_t, false>(B, T, H, d, L, 1, fin, D);
-            else walk_scan<float, false>(B, T, H, d, L, 1, fin, D);
+            if (bf16 && wide) walk_scan<uint16_t, false, true>(B, T, H, d, L, 1, fin, D);
+            else if (bf16) walk_scan<uint16_t, false, false>(B, T, H, d, L, 1, fin, D);
+            else walk_scan<float, false, false>(B, T, H, d, L, 1, fin, D);
         }
     }
     bool any_w = false;
