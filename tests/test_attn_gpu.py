@@ -34,6 +34,8 @@ CASES = [
     (1, 300, 3, 128, [4, 1, 5], [8, 16, 300], torch.bfloat16), # windows with D < 16, W >= T
     (2, 257, 2, 64, [16, 7], [16, 5], torch.bfloat16),
     (1, 2048, 4, 128, [1, 1, 64, 64], [0, 0, 256, 256], torch.bfloat16),  # head-wise hybrid
+    (1, 2500, 1, 128, [1], [0], torch.bfloat16),               # dense residue > 1024 rows, no window (8 waves, 5 slots)
+    (2, 3000, 2, 64, [1, 2], [0, 0], torch.bfloat16),          # the same at d = 64, ragged item tails
     (1, 256, 2, 64, [4, 4], [0, 0], torch.float32),            # the tiny fp32 workload's shape
     (1, 200, 3, 128, [1, 5, 64], [0, 7, 100], torch.float32),
 ]
