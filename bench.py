@@ -408,6 +408,37 @@ def run_backward_arl(torch, rat, w, steps, warmup):
     return st, flops, nbytes
 
 
+def run_backward_windowed(torch, rat, w, steps, warmup):
+    """The layer backward of a windowed prefill workload `w` (every head at
+    its (D, W), RESTART recurrence): the dilated states and the raw window
+    in one softmax.  The forward's states come from the scan kernel,
+    outside the timed region."""
+    from dilated_sparse_attention_amd import inputs
+
+    x = inputs.make_prefill(w, seed=9, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(10)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(w.dtype)
+    ks, vs = rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=rat.RESTART)
+    grads = tuple(torch.empty(x["q"].shape, dtype=torch.float32, device="cuda") for _ in range(4))
+    ws = torch.empty(rat.ops.load_library().rat_layer_backward_workspace_bytes(w.B, w.T, w.H, w.d),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        rat.layer_backward(x["q"], x["k"], x["v"], x["gate"], ks, vs, dout, list(w.D), list(w.W), L=w.L,
+                           mode=rat.RESTART, grads=grads, workspace=ws)
+
+    st = time_launches(torch, step, max(steps, MIN_TIMED), warmup)
+    # the same units as the ARL backward, over the dilated and the window pairs
+    pairs = w.B * sum(sum(attn_pairs(w.T, Dh, Wh)) for Dh, Wh in zip(w.D, w.W))
+    flops = 10 * w.d * pairs
+    E = w.B * w.T * w.H * w.d
+    nbytes = 7 * E * 2 + 4 * E * 4
+    del x, ks, vs, grads, ws
+    torch.cuda.empty_cache()
+    return st, flops, nbytes
+
+
 def run_copy_reference(torch, nbytes, steps, nsets=3):
     """A plain device-to-device copy moving ``nbytes`` (half read, half
     written), over rotating buffer sets that together exceed the caches: the
@@ -653,6 +684,16 @@ def main():
                           "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
                           "config": dict(bw.describe(), D="half the batch at 1, half at 64", W=0,
                                          recurrence="full")}
+
+        bw = inputs.PREFILL_LONG
+        key = "backward_windowed_" + bw.name
+        if args.only is None or args.only == key:
+            progress("backward (windowed heads, RESTART)", bw.name)
+            bst, bflops, bbytes = run_backward_windowed(torch, rat, bw, args.steps, 2)
+            extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bst["median"] / 1e3),
+                          **stats_fields("backward", bst, nbytes=bbytes, flops=bflops),
+                          "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                          "config": dict(bw.describe(), recurrence="RESTART")}
 
     if ms is None:  # a profiling run of one extra workload
         print(json.dumps({"extra": extra}))

@@ -114,11 +114,12 @@ rat_status run_scan(const void* k, const void* v, const void* g, void* ks, void*
 }
 
 
-// Workspace of the backward: per query row (lse, delta), the state
-// gradients, the per-chunk maps and carries; every part 256-byte aligned.
+// Workspace of the backward: per query row (lse, delta) and its raw
+// window's partial softmax sums, the state gradients, the per-chunk maps and
+// carries; every part 256-byte aligned.
 struct BwdPlan {
     int nchunk;
-    size_t off_lse, off_delta, off_dks, off_dvs, off_maps, off_carry, bytes;
+    size_t off_lse, off_delta, off_bstat, off_dks, off_dvs, off_maps, off_carry, bytes;
 };
 
 BwdPlan bwd_plan(int B, int T, int H, int d)
@@ -129,7 +130,8 @@ BwdPlan bwd_plan(int B, int T, int H, int d)
     const size_t rows = (size_t)B * T * H, elems = rows * d, cells = (size_t)p.nchunk * B * H * d;
     p.off_lse = 0;
     p.off_delta = up(p.off_lse + rows * 4);
-    p.off_dks = up(p.off_delta + rows * 4);
+    p.off_bstat = up(p.off_delta + rows * 4);
+    p.off_dks = up(p.off_bstat + rows * 3 * 4);
     p.off_dvs = up(p.off_dks + elems * 4);
     p.off_maps = up(p.off_dvs + elems * 4);
     p.off_carry = up(p.off_maps + cells * 5 * 4);
@@ -519,6 +521,7 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
     a.dvs = reinterpret_cast<float*>(ws + p.off_dvs);
     a.maps = reinterpret_cast<float*>(ws + p.off_maps);
     a.carry = reinterpret_cast<float*>(ws + p.off_carry);
+    a.bstat = reinterpret_cast<float*>(ws + p.off_bstat);
     a.B = B; a.T = T; a.H = H; a.d = d;
     a.L = L >= T ? 0 : L;
     a.nchunk = p.nchunk;
@@ -530,7 +533,7 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
         a.D[h] = D[h];
         a.W[h] = W[h];
         a.mitem[h] = (int)items;
-        if (a.mfma && W[h] == 0) {
+        if (a.mfma) {
             // B x min(D, T) residues x blocks of 16 kBwdWaves rows of the longest residue
             const int64_t nb = ((T + D[h] - 1) / D[h] + 16 * kBwdWaves - 1) / (16 * kBwdWaves);
             items += (int64_t)B * std::min(D[h], T) * nb;
@@ -538,6 +541,9 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
         if (items >= ((int64_t)1 << 31)) return RAT_ERR_UNSUPPORTED;
     }
     a.mitem[H] = (int)items;
+    // the band passes: one item per (head, batch, block of 16 kBwdWaves positions)
+    if (a.mfma && any_w && (int64_t)H * B * ((T + 16 * kBwdWaves - 1) / (16 * kBwdWaves)) >= ((int64_t)1 << 31))
+        return RAT_ERR_UNSUPPORTED;
     return hip_status(launch_backward(a, dtype == RAT_DTYPE_BF16, (hipStream_t)stream));
 }
 

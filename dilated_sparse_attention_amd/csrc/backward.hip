@@ -20,16 +20,21 @@
 // running-max rescaling, then divided by the softmax sum.
 //
 // Kernels (all arithmetic fp32, gradients written in fp32):
-//   bwd_query_kernel  one wave per query row: log-sum-exp of its softmax
-//                     and delta_t, then dq_t (two passes over its keys);
-//   bwd_key_kernel    one wave per key row: the state key's gradients from
-//                     the queries t = s, s + D, ... and the raw key's from
-//                     t = s .. s + W - 1;
-//   bwd_q_mfma / bwd_kv_mfma  the same for bf16 heads without a raw window,
-//                     on MFMA: a residue is a dense causal problem over the
-//                     states r, r + D, ..., so a workgroup takes 64 rows of
-//                     one residue (queries for dq, keys for dk / dv) and
-//                     walks the other side's 64-row tiles through LDS;
+//   bwd_q_mfma / bwd_kv_mfma  bf16, on MFMA: a residue is a dense causal
+//                     problem over the states r, r + D, ..., so a workgroup
+//                     takes 64 rows of one residue (queries for dq, keys for
+//                     dk / dv) and walks the other side's 64-row tiles
+//                     through LDS.  A raw window is the same problem over
+//                     consecutive positions with a band mask: its passes
+//                     leave each query's partial softmax sums, from which
+//                     the dilated pass forms the one softmax's statistics,
+//                     then add the window's dq and give the raw keys' dk / dv
+//                     (the forward's two-pass split, backwards);
+//   bwd_query_kernel  fp32: one wave per query row: log-sum-exp of its
+//                     softmax and delta_t, then dq_t (two passes over its keys);
+//   bwd_key_kernel    fp32: one wave per key row: the state key's gradients
+//                     from the queries t = s, s + D, ... and the raw key's
+//                     from t = s .. s + W - 1;
 //   bwd_scan_*        the reverse recurrence in chunks of kBwdChunk tokens:
 //                     per-chunk affine maps (forward state map and backward
 //                     carry map), a sequential pass over the chunks of each
@@ -103,7 +108,6 @@ __global__ __launch_bounds__(kWave) void bwd_query_kernel(BwdArgs a)
     const int bh = blockIdx.x / a.T;
     const int h = bh % a.H, b = bh / a.H;
     const int d = a.d, D = a.D[h], W = a.W[h];
-    if (a.mfma && W == 0) return;  // the MFMA kernels take this head
     const size_t pitch = (size_t)a.H * d;
     const size_t base = ((size_t)b * a.T * a.H + h) * d;  // row 0 of (b, h)
     const size_t rt = base + (size_t)t * pitch;
@@ -240,9 +244,8 @@ __global__ __launch_bounds__(kWave) void bwd_key_kernel(BwdArgs a)
             *reinterpret_cast<float2*>(dv_out + rs + 2 * lane) = float2{va, vb};
         }
     };
-    // the state at s: queries s, s + D, ... (< T); the MFMA kernels take
-    // heads without a raw window
-    if (!(a.mfma && W == 0)) key_grads(a.ks, a.vs, (a.T - 1 - s) / D + 1, D, a.dks, a.dvs);
+    // the state at s: queries s, s + D, ... (< T)
+    key_grads(a.ks, a.vs, (a.T - 1 - s) / D + 1, D, a.dks, a.dvs);
     // the raw token at s: queries s .. s + W - 1 (< T); none writes zeros
     key_grads(a.k, a.v, min(W, a.T - s), 1, a.dk, a.dv);
 }
@@ -395,18 +398,48 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
     lo[e] = (__bf16)(x - (float)h);
 }
 
+// Band work item, for the raw windows: (head, batch, block of kBwdOwn
+// consecutive positions), the item list covering every head; the window is
+// the residue of D = 1 over the whole sequence with the raw tokens as keys.
+// Items of heads without a window return, or in bwd_kv_mfma write zeros
+// for their raw keys' gradients.
+__device__ __forceinline__ BwdItem band_item(const BwdArgs& a, int item)
+{
+    BwdItem it;
+    const int nb = (a.T + kBwdOwn - 1) / kBwdOwn;
+    it.h = item / (a.B * nb);
+    const int rest = item % (a.B * nb);
+    it.b = rest / nb;
+    it.blk = rest % nb;
+    it.r = 0;
+    it.D = 1;
+    it.M = a.T;
+    it.valid = it.h < a.H;
+    return it;
+}
+
 // dq (and each query row's log-sum-exp and delta): wave w owns queries
 // 16w .. 16w+15 of the block; lane (g, i) query i.  Scores are S^T = K Q^T
 // (lane: keys 16kb + 4g + j of its query), dP^T = V dO^T, and
 // dQ^T += K^T dS^T with dS^T packed to bf16 as the B operand.
-template <int DK>
+// MODE 0: the dilated states of every head (a head with a window starts its
+// softmax statistics from the window's partial sums); MODE 1: the raw
+// window's partial sums only (max, sum of e^(z - max), sum of e^(z - max) dp
+// per query, into bstat); MODE 2: the raw window's share of dq, added to
+// the dilated share, with the query's final log-sum-exp and delta.
+template <int DK, int MODE>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char kt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char vt[kBwdRows * G::ROWB];
-    const BwdItem it = bwd_item<true>(a, xcd_item(blockIdx.x, gridDim.x));
+    const int wi = xcd_item(blockIdx.x, gridDim.x);
+    const BwdItem it = MODE == 0 ? bwd_item<true>(a, wi) : band_item(a, wi);
     if (!it.valid) return;
+    const int Wh = a.W[it.h];
+    if (MODE != 0 && Wh == 0) return;
+    const void* const ksrc = MODE == 0 ? a.ks : a.k;
+    const void* const vsrc = MODE == 0 ? a.vs : a.v;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int g = lane >> 4, i = lane & 15;
@@ -414,11 +447,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
     const int qr = it.blk * kBwdOwn + 16 * wv + i;
     const bool qvalid = qr < it.M;
     const size_t qe = qvalid ? res_row<DK>(a, it, qr) : 0;
+    const size_t rrow = qvalid ? ((size_t)it.b * a.T + it.r + (size_t)qr * it.D) * a.H + it.h : 0;
     bf16x8 qf[G::KS], gf[G::KS];
     load_frag<DK>(qf, a.q, qe, qvalid);
     load_frag<DK>(gf, a.dout, qe, qvalid);
-    // key tiles up to the block's last query
-    const int ntile = (min(it.M, (it.blk + 1) * kBwdOwn) - 1) / kBwdRows + 1;
+    // key tiles tlo .. thi-1: up to the block's last query, and for the
+    // window from the tile holding its first query's first window key
+    const int thi = (min(it.M, (it.blk + 1) * kBwdOwn) - 1) / kBwdRows + 1;
+    const int tlo = MODE == 0 ? 0 : max(0, it.blk * kBwdOwn - Wh + 1) / kBwdRows;
+    const int nt = thi - tlo;
+    constexpr int NSWEEP = MODE == 0 ? 2 : 1;
+    // key row kr is seen by the lane's query: up to it, within the window
+    auto visible = [&](int kr) { return kr <= qr && (MODE == 0 || kr > qr - Wh); };
     auto scores = [&](floatx4 (&st)[4], floatx4 (&dpt)[4]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -431,71 +471,97 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
             }
         }
     };
-    // key / value tiles t = 0 .. 2 ntile - 1 (both sweeps) through registers
+    // the key / value tiles of every sweep in turn, through registers: step
+    // n of the sequence is tile tlo + n mod nt
     TileRegs<DK> rk, rv;
-    rk.load(a.ks, a, it, 0);
-    rv.load(a.vs, a, it, 0);
-    auto next_tile = [&](int t) {  // tile t into LDS, tile t + 1 into registers
+    rk.load(ksrc, a, it, tlo * kBwdRows);
+    rv.load(vsrc, a, it, tlo * kBwdRows);
+    int seq = 0;
+    auto next_tile = [&]() {  // the fetched tile into LDS, the following one into registers
         __syncthreads();
         rk.store(kt);
         rv.store(vt);
         __syncthreads();
-        const int tn = (t + 1) % ntile;
-        if (t + 1 < 2 * ntile) {
-            rk.load(a.ks, a, it, tn * kBwdRows);
-            rv.load(a.vs, a, it, tn * kBwdRows);
+        ++seq;
+        if (seq < NSWEEP * nt) {
+            const int tn = tlo + seq % nt;
+            rk.load(ksrc, a, it, tn * kBwdRows);
+            rv.load(vsrc, a, it, tn * kBwdRows);
         }
     };
-    // sweep 1: per lane group, (max, sum of e^(z - max), sum of e^(z - max) dp)
-    // over its keys, rescaled once per tile: the tile's 16 scores of the lane
-    // (-inf past the query) give the new max first
-    float m = -INFINITY, l = 0.f, u = 0.f;
-    for (int t = 0; t < ntile; ++t) {
-        next_tile(t);
-        floatx4 st[4], dpt[4];
-        scores(st, dpt);
-        float tm = m;
+    float lse2, delta;  // log2-domain log-sum-exp and delta of the lane's query
+    if (MODE != 2) {
+        // sweep 1: per lane group, (max, sum of e^(z - max), sum of
+        // e^(z - max) dp) over its keys, rescaled once per tile: the tile's 16
+        // scores of the lane (-inf where not seen) give the new max first
+        float m = -INFINITY, l = 0.f, u = 0.f;
+        for (int t = tlo; t < thi; ++t) {
+            next_tile();
+            floatx4 st[4], dpt[4];
+            scores(st, dpt);
+            float tm = m;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
-                st[kb][j] = kr <= qr ? st[kb][j] * c : -INFINITY;
-                tm = fmaxf(tm, st[kb][j]);
+                for (int j = 0; j < 4; ++j) {
+                    const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
+                    st[kb][j] = visible(kr) ? st[kb][j] * c : -INFINITY;
+                    tm = fmaxf(tm, st[kb][j]);
+                }
+            const float ts = tm == -INFINITY ? 0.f : tm;  // no visible key yet: every term is 0
+            const float sc = __builtin_amdgcn_exp2f(m - ts);
+            l *= sc;
+            u *= sc;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(st[kb][j] - ts);
+                    l += e;
+                    u = fmaf(e, dpt[kb][j], u);
+                }
+            m = tm;
+        }
+        // combine the four lane groups of the query
+        float mall = m;
+        mall = fmaxf(mall, __shfl_xor(mall, 16));
+        mall = fmaxf(mall, __shfl_xor(mall, 32));
+        const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mall);
+        float lall = l * w, uall = u * w;
+        lall += __shfl_xor(lall, 16);
+        lall += __shfl_xor(lall, 32);
+        uall += __shfl_xor(uall, 16);
+        uall += __shfl_xor(uall, 32);
+        if (MODE == 1) {
+            if (qvalid && g == 0) {
+                a.bstat[rrow * 3 + 0] = mall;
+                a.bstat[rrow * 3 + 1] = lall;
+                a.bstat[rrow * 3 + 2] = uall;
             }
-        const float ts = tm == -INFINITY ? 0.f : tm;  // no visible key yet: every term is 0
-        const float sc = __builtin_amdgcn_exp2f(m - ts);
-        l *= sc;
-        u *= sc;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(st[kb][j] - ts);
-                l += e;
-                u = fmaf(e, dpt[kb][j], u);
-            }
-        m = tm;
+            return;
+        }
+        if (Wh > 0 && qvalid) {  // the window's keys join the same softmax
+            const float mb = a.bstat[rrow * 3 + 0], lb = a.bstat[rrow * 3 + 1], ub = a.bstat[rrow * 3 + 2];
+            const float mn = fmaxf(mall, mb);
+            const float wa = mall == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mall - mn);
+            const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - mn);
+            lall = fmaf(lall, wa, lb * wb);
+            uall = fmaf(uall, wa, ub * wb);
+            mall = mn;
+        }
+        lse2 = mall + __log2f(lall);
+        delta = uall / lall;
+    } else {
+        lse2 = qvalid ? a.lse[rrow] * kLog2e : INFINITY;  // (a row past the sequence: p = 0)
+        delta = qvalid ? a.delta[rrow] : 0.f;
     }
-    // combine the four lane groups of the query
-    float mall = m;
-    mall = fmaxf(mall, __shfl_xor(mall, 16));
-    mall = fmaxf(mall, __shfl_xor(mall, 32));
-    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mall);
-    float lall = l * w, uall = u * w;
-    lall += __shfl_xor(lall, 16);
-    lall += __shfl_xor(lall, 32);
-    uall += __shfl_xor(uall, 16);
-    uall += __shfl_xor(uall, 32);
-    const float lse2 = mall + __log2f(lall);  // log2-domain log-sum-exp
-    const float delta = uall / lall;
     // sweep 2: dQ^T
     const int toff = tr_offset<DK>();
     floatx4 dqt[G::DB];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) dqt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < ntile; ++t) {
-        next_tile(ntile + t);
+    for (int t = tlo; t < thi; ++t) {
+        next_tile();
         floatx4 st[4], dpt[4];
         scores(st, dpt);
         bf16x8 sh[2], sl[2];
@@ -504,7 +570,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int kr = t * kBwdRows + 16 * kb + 4 * g + j;
-                const float p = kr <= qr ? __builtin_amdgcn_exp2f(fmaf(st[kb][j], c, -lse2)) : 0.f;
+                const float p = visible(kr) ? __builtin_amdgcn_exp2f(fmaf(st[kb][j], c, -lse2)) : 0.f;
                 split_bf16(p * (dpt[kb][j] - delta) * a.scale, sh[kb >> 1], sl[kb >> 1], 4 * (kb & 1) + j);
             }
 #pragma unroll
@@ -517,31 +583,41 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_q_mfma(BwdArgs a)
             }
     }
     if (qvalid) {
-        const size_t o = qe;  // same [B][T][H][DK] position, fp32
+        float* const o = a.dq + qe;  // same [B][T][H][DK] position, fp32
+        if (MODE == 2) {  // the dilated share is there already (MODE 0 ran first)
 #pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-            *reinterpret_cast<floatx4*>(a.dq + o + 16 * db + 4 * g) = dqt[db];
-        if (g == 0) {
-            const size_t rrow = ((size_t)it.b * a.T + it.r + (size_t)qr * it.D) * a.H + it.h;
-            a.lse[rrow] = lse2 * 0.6931471805599453f;  // natural log
-            a.delta[rrow] = delta;
+            for (int db = 0; db < G::DB; ++db) {
+                floatx4* const p = reinterpret_cast<floatx4*>(o + 16 * db + 4 * g);
+                *p = *p + dqt[db];
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) *reinterpret_cast<floatx4*>(o + 16 * db + 4 * g) = dqt[db];
+            if (g == 0) {
+                a.lse[rrow] = lse2 * 0.6931471805599453f;  // natural log
+                a.delta[rrow] = delta;
+            }
         }
     }
 }
 
-// dk, dv of the states: wave w owns keys 16w .. 16w+15 of the block; lane
-// (g, i) key i.  Scores S = Q K^T (lane: queries 16qb + 4g + j of its key),
-// dP = dO V^T, dV^T += dO^T P and dK^T += Q^T dS with P and dS packed to
-// bf16 as B operands.
-template <int DK>
+// dk, dv: wave w owns keys 16w .. 16w+15 of the block; lane (g, i) key i.
+// Scores S = Q K^T (lane: queries 16qb + 4g + j of its key), dP = dO V^T,
+// dV^T += dO^T P and dK^T += Q^T dS with P and dS packed to bf16 as B
+// operands.  BAND: the raw tokens of a window against the queries up to
+// W - 1 after them (heads without a window write zeros); otherwise the
+// states against the queries of their residue.
+template <int DK, bool BAND>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
 {
     typedef Geo<DK> G;
     __shared__ __attribute__((aligned(1024))) char qt[kBwdRows * G::ROWB];
     __shared__ __attribute__((aligned(1024))) char gt[kBwdRows * G::ROWB];
     __shared__ float s_lse2[kBwdRows], s_dl[kBwdRows];
-    const BwdItem it = bwd_item<false>(a, xcd_item(blockIdx.x, gridDim.x));
+    const int wi = xcd_item(blockIdx.x, gridDim.x);
+    const BwdItem it = BAND ? band_item(a, wi) : bwd_item<false>(a, wi);
     if (!it.valid) return;
+    const int Wh = a.W[it.h];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int g = lane >> 4, i = lane & 15;
@@ -549,9 +625,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
     const int kr = it.blk * kBwdOwn + 16 * wv + i;
     const bool kvalid = kr < it.M;
     const size_t ke = kvalid ? res_row<DK>(a, it, kr) : 0;
+    float* const dko = BAND ? a.dk : a.dks;
+    float* const dvo = BAND ? a.dv : a.dvs;
+    if (BAND && Wh == 0) {  // no window: the raw keys take no gradient from attention
+        if (kvalid) {
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                *reinterpret_cast<floatx4*>(dko + ke + 16 * db + 4 * g) = floatx4{0.f, 0.f, 0.f, 0.f};
+                *reinterpret_cast<floatx4*>(dvo + ke + 16 * db + 4 * g) = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        return;
+    }
     bf16x8 kf[G::KS], vf[G::KS];
-    load_frag<DK>(kf, a.ks, ke, kvalid);
-    load_frag<DK>(vf, a.vs, ke, kvalid);
+    load_frag<DK>(kf, BAND ? a.k : a.ks, ke, kvalid);
+    load_frag<DK>(vf, BAND ? a.v : a.vs, ke, kvalid);
     const int toff = tr_offset<DK>();
     floatx4 dkt[G::DB], dvt[G::DB];
 #pragma unroll
@@ -559,7 +647,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
         dkt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
         dvt[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    const int ntile = (it.M + kBwdRows - 1) / kBwdRows;
+    // query tiles from the one holding the block's first key, to the one
+    // holding the last query that sees the block's last key
+    const int ntile = BAND ? (min(it.M, it.blk * kBwdOwn + kBwdOwn - 1 + Wh) - 1) / kBwdRows + 1
+                           : (it.M + kBwdRows - 1) / kBwdRows;
+    // query row q sees the lane's key: from it on, within the window
+    auto sees = [&](int q) { return q >= kr && (!BAND || q < kr + Wh); };
     // query tiles from the block's own on, staged through registers
     TileRegs<DK> rq, rg;
     float rl = INFINITY, rd = 0.f;  // the tile's (lse, delta) of row threadIdx.x (< 64)
@@ -600,7 +693,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
             for (int j = 0; j < 4; ++j) {
                 const int ql = 16 * qb + 4 * g + j;
                 const int q = t * kBwdRows + ql;
-                const float p = q >= kr ? __builtin_amdgcn_exp2f(fmaf(sv[j], c, -s_lse2[ql])) : 0.f;
+                const float p = sees(q) ? __builtin_amdgcn_exp2f(fmaf(sv[j], c, -s_lse2[ql])) : 0.f;
                 pb[qb >> 1][4 * (qb & 1) + j] = (__bf16)p;
                 split_bf16(p * (dp[j] - s_dl[ql]) * a.scale, sh[qb >> 1], sl[qb >> 1], 4 * (qb & 1) + j);
             }
@@ -618,8 +711,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_kv_mfma(BwdArgs a)
     if (kvalid) {
 #pragma unroll
         for (int db = 0; db < G::DB; ++db) {
-            *reinterpret_cast<floatx4*>(a.dks + ke + 16 * db + 4 * g) = dkt[db];
-            *reinterpret_cast<floatx4*>(a.dvs + ke + 16 * db + 4 * g) = dvt[db];
+            *reinterpret_cast<floatx4*>(dko + ke + 16 * db + 4 * g) = dkt[db];
+            *reinterpret_cast<floatx4*>(dvo + ke + 16 * db + 4 * g) = dvt[db];
         }
     }
 }
@@ -832,19 +925,26 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
     const unsigned cells = (unsigned)(((size_t)a.nchunk * a.B * N + 255) / 256);
     const unsigned chans = (unsigned)(((size_t)a.B * N + 15) / 16);  // 16 channels per carry workgroup
     if (bf16) {
+        // every head on the MFMA kernels; with a window somewhere, the band
+        // passes around the dilated ones: the window's partial sums, then the
+        // dilated dq with the full softmax statistics, then the window's dq;
+        // the states' and the raw keys' gradients from those statistics
         const unsigned items = (unsigned)a.mitem[a.H];
-        if (a.mfma && items > 0) {
-            if (a.d == 128) hipLaunchKernelGGL(bwd_q_mfma<128>, dim3(items), dim3(kBwdThreads), 0, stream, a);
-            else hipLaunchKernelGGL(bwd_q_mfma<64>, dim3(items), dim3(kBwdThreads), 0, stream, a);
+        const unsigned bands = a.raw ? (unsigned)((size_t)a.H * a.B * ((a.T + kBwdOwn - 1) / kBwdOwn)) : 0u;
+        const dim3 blk(kBwdThreads);
+        if (a.d == 128) {
+            if (bands) hipLaunchKernelGGL((bwd_q_mfma<128, 1>), dim3(bands), blk, 0, stream, a);
+            if (items) hipLaunchKernelGGL((bwd_q_mfma<128, 0>), dim3(items), blk, 0, stream, a);
+            if (bands) hipLaunchKernelGGL((bwd_q_mfma<128, 2>), dim3(bands), blk, 0, stream, a);
+            if (items) hipLaunchKernelGGL((bwd_kv_mfma<128, false>), dim3(items), blk, 0, stream, a);
+            if (bands) hipLaunchKernelGGL((bwd_kv_mfma<128, true>), dim3(bands), blk, 0, stream, a);
+        } else {
+            if (bands) hipLaunchKernelGGL((bwd_q_mfma<64, 1>), dim3(bands), blk, 0, stream, a);
+            if (items) hipLaunchKernelGGL((bwd_q_mfma<64, 0>), dim3(items), blk, 0, stream, a);
+            if (bands) hipLaunchKernelGGL((bwd_q_mfma<64, 2>), dim3(bands), blk, 0, stream, a);
+            if (items) hipLaunchKernelGGL((bwd_kv_mfma<64, false>), dim3(items), blk, 0, stream, a);
+            if (bands) hipLaunchKernelGGL((bwd_kv_mfma<64, true>), dim3(bands), blk, 0, stream, a);
         }
-        // the per-row kernels: heads with a raw window (and the raw-window
-        // gradients, zero for the other heads); none when no head has one
-        if (a.raw) hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
-        if (a.mfma && items > 0) {
-            if (a.d == 128) hipLaunchKernelGGL(bwd_kv_mfma<128>, dim3(items), dim3(kBwdThreads), 0, stream, a);
-            else hipLaunchKernelGGL(bwd_kv_mfma<64>, dim3(items), dim3(kBwdThreads), 0, stream, a);
-        }
-        if (a.raw) hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(bwd_scan_apply_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);

@@ -281,12 +281,14 @@ struct BwdArgs {
     float* dvs;        // [B][T][H][d] gradients of the states
     float* maps;       // [nchunk][B][H d][5] per-chunk maps
     float* carry;      // [nchunk][B][H d][4] state before / carry into each chunk
+    float* bstat;      // [B][T][H][3] per query row: (max, sum, sum p dp) over its raw window
     int B, T, H, d;
     int L;             // RESTART period, 0 for the full recurrence
     int nchunk;        // ceil(T / kBwdChunk)
     float scale;
-    int mfma;          // bf16: heads without a raw window run on the MFMA kernels
-    int raw;           // some head has a raw window (the per-row kernels run); always 1 for fp32
+    int mfma;          // bf16: every head runs on the MFMA kernels (fp32: the per-row kernels)
+    int raw;           // dk / dv hold raw-window gradients before the recurrence adds its own:
+                       // some head has a window (bf16), always (fp32)
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
     int mitem[kAttnMaxHeads + 1];  // first MFMA work item of each head; [H] = total
@@ -303,7 +305,7 @@ static_assert(sizeof(ScanSlideArgs) == 1096 && offsetof(ScanSlideArgs, hist) == 
 static_assert(sizeof(AttnArgs) == 1344 && offsetof(AttnArgs, cls) == 92 && offsetof(AttnArgs, heads) == 316,
               "AttnArgs layout");
 static_assert(sizeof(RingFillArgs) == 1080 && sizeof(DecodeArgs) == 3160 && sizeof(StepArgs) == 2136 &&
-              sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3248 && sizeof(AttnF32Args) == 2128 &&
+              sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3256 && sizeof(AttnF32Args) == 2128 &&
               sizeof(SlideStepArgs) == 2160 && sizeof(SlideFillArgs) == 72, "kernel-argument sizes");
 static_assert(sizeof(BwdArgs) < 4096 && sizeof(DecodeArgs) < 4096, "kernel arguments fit their segment");
 

@@ -291,9 +291,9 @@ rat_status rat_build_decode_caches(const void* k_state, const void* v_state, con
                             void* stream);
 
 /* Bytes of device workspace rat_layer_backward needs: per query row the
- * log-sum-exp and dout.out, the fp32 gradients of the states, and per
- * 16-token chunk of every channel its recurrence maps and carries.
- * 256-byte aligned; no initialisation. */
+ * log-sum-exp, dout.out and the raw window's partial softmax sums, the fp32
+ * gradients of the states, and per 16-token chunk of every channel its
+ * recurrence maps and carries.  256-byte aligned; no initialisation. */
 size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d);
 
 /* Backward of the layer (the training of Deep Dive 2.2, Active Recurrence

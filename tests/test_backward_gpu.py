@@ -62,6 +62,7 @@ CASES = [
     (2, 130, 2, 64, [16, 7], [16, 5], 64, torch.bfloat16),       # RESTART every 64, ragged chunks
     (1, 300, 2, 128, [1, 64], [0, 0], 33, torch.bfloat16),        # RESTART cutting inside the 16-token chunks
     (1, 40, 2, 128, [64, 100], [0, 3], None, torch.bfloat16),     # D > T: own state only
+    (1, 400, 3, 128, [4, 64, 1], [150, 70, 0], None, torch.bfloat16),  # windows over several 64-key tiles
     (1, 96, 2, 128, [1, 3], [0, 5], None, torch.float32),
     (2, 77, 2, 64, [5, 1], [2, 0], 20, torch.float32),
 ]
