@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 # kernel names as the profiler lists them (bf16, d = 128, full recurrence)
-SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, false>"
+SCAN_KERNEL = "rat::scan_full_kernel<unsigned short, false, true>"  # bf16, no history, 256-token chunks
 ATTN_KERNEL = "rat::attn_dilated_kernel<128, 4, 2, false, false, false>"  # the 1.5B plan: short residues, four waves
 
 # launches timed per kernel (each between its own pair of HIP events)

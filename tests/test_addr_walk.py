@@ -46,6 +46,7 @@ LAYER_CASES = [
     (1, 200, 2, 64, [3, 5], [0, 4], 50, 1, 1),
     (1, 2048, 4, 128, [1, 1, 64, 64], [0, 0, 256, 256], None, 0, 1),
     (1, 40, 2, 128, [64, 100], [0, 3], None, 0, 1),
+    (2, 1, 2, 128, [1, 16], [4, 0], None, 0, 1),
     (1, 256, 2, 64, [4, 4], [0, 0], None, 0, 0),
     (2, 1000, 4, 128, [16, 16, 1, 64], [0, 64, 0, 128], None, 0, 1),
 ]

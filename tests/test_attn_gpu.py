@@ -26,6 +26,8 @@ def _attn_inputs(B, T, H, d, dtype, seed, std=1.0):
 CASES = [
     # (B, T, H, d, D per head, W per head, dtype)
     (1, 64, 1, 128, [1], [0], torch.bfloat16),                 # dense, one tile
+    (2, 1, 3, 128, [1, 16, 4], [0, 8, 1], torch.bfloat16),     # one token: its own state and raw key only
+    (1, 2, 2, 64, [1, 2], [2, 0], torch.bfloat16),             # two tokens
     (1, 600, 2, 128, [1, 1], [0, 0], torch.bfloat16),          # dense, 3 chunks of 256 rows
     (2, 300, 2, 64, [3, 16], [0, 0], torch.bfloat16),          # ragged residues, d = 64
     (1, 4096, 2, 128, [16, 16], [0, 0], torch.bfloat16),       # the 1.5B head shape

@@ -63,6 +63,8 @@ CASES = [
     (1, 300, 2, 128, [1, 64], [0, 0], 33, torch.bfloat16),        # RESTART cutting inside the 16-token chunks
     (1, 40, 2, 128, [64, 100], [0, 3], None, torch.bfloat16),     # D > T: own state only
     (1, 400, 3, 128, [4, 64, 1], [150, 70, 0], None, torch.bfloat16),  # windows over several 64-key tiles
+    (2, 1, 2, 128, [1, 8], [4, 0], None, torch.bfloat16),          # one token
+    (1, 2, 2, 64, [1, 2], [2, 0], None, torch.bfloat16),           # two tokens
     (1, 96, 2, 128, [1, 3], [0, 5], None, torch.float32),
     (2, 77, 2, 64, [5, 1], [2, 0], 20, torch.float32),
 ]

@@ -29,6 +29,7 @@ CASES = [
     (1, 200, 2, 64, [3, 5], [0, 4], 50, rat.SLIDING, torch.bfloat16),                 # general sliding window
     (1, 2048, 4, 128, [1, 1, 64, 64], [0, 0, 256, 256], None, rat.RESTART, torch.bfloat16),  # head-wise hybrid
     (1, 40, 2, 128, [64, 100], [0, 3], None, rat.RESTART, torch.bfloat16),            # D > T
+    (2, 1, 2, 128, [1, 16], [4, 0], None, rat.RESTART, torch.bfloat16),               # one token
     (1, 256, 2, 64, [4, 4], [0, 0], None, rat.RESTART, torch.float32),                # the tiny fp32 shape
     (1, 200, 3, 128, [1, 5, 64], [0, 7, 100], 33, rat.SLIDING, torch.float32),
 ]
