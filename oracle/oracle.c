@@ -438,8 +438,8 @@ int oracle_chunk_attn_prefill_rows(const double* q, const double* k_state, const
  * Deep Dive S1 / RAT+ abstract), by the chain rule applied to those
  * definitions.  This is what the training of Deep Dive S2.2 (Active
  * Recurrence Learning: half of a batch at D = 1, half at D = 64, recurrence
- * over the full sequence) differentiates.  Full recurrence (L >= T) and
- * RESTART only; a SLIDING window returns -5.
+ * over the full sequence) differentiates.  Every recurrence: full (L >= T),
+ * RESTART and SLIDING.
  *
  * Given dout = dLoss/dout [B,T,H,d]:
  *   attention, per query t with keys/values (kappa_j, nu_j), j over the
@@ -456,6 +456,12 @@ int oracle_chunk_attn_prefill_rows(const double* q, const double* k_state, const
  *     dx_t += (1 - g_t) lambda_t,
  *     dlogit_t = g_t (1 - g_t) sum_{x in k, v} lambda_t (h_{t-1} - x_t)
  *   (the gate is shared by keys and values; dsigma/dl = sigma (1 - sigma)).
+ *   A SLIDING window (L < T) makes each state its own window: h_t is w after
+ *   the steps w <- g_u w + (1 - g_u) x_u, u = max(0, t-L+1) .. t, from w = 0,
+ *   and lambda_t = dh_t carries nothing.  With Q_u = g_{u+1} ... g_t (the
+ *   steps after u) and w_u the value of w before step u:
+ *     dx_u += (1 - g_u) Q_u lambda_t,
+ *     dlogit_u += g_u (1 - g_u) sum_{x in k, v} Q_u lambda_t (w_u - x_u).
  * Outputs dq, dk, dv, dlogit: [B,T,H,d]; dk and dv sum the state path and
  * the raw-window path. */
 int oracle_layer_backward(const double* q, const double* k, const double* v, const double* logit,
@@ -467,7 +473,7 @@ int oracle_layer_backward(const double* q, const double* k, const double* v, con
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return -2;
     if (mode != ORACLE_MODE_RESTART && mode != ORACLE_MODE_SLIDING) return -3;
     const int full = (L >= T);
-    if (!full && mode == ORACLE_MODE_SLIDING) return -5;
+    const int sliding = !full && mode == ORACLE_MODE_SLIDING;
     int need_raw, max_keys;
     if (check_heads(H, D, W, &need_raw, &max_keys, T)) return -3;
     const size_t n = (size_t)B * T * H * d;
@@ -541,6 +547,47 @@ int oracle_layer_backward(const double* q, const double* k, const double* v, con
                     }
         }
         free(kp); free(vp); free(dkp); free(dvp); free(z); free(p);
+    }
+    if (sliding) {
+        /* each window on its own: the chain rule through its steps */
+#pragma omp parallel
+        {
+            double* Q = (double*)malloc(sizeof(double) * L);
+            if (!Q) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for collapse(2) schedule(dynamic)
+                for (int b = 0; b < B; ++b)
+                    for (int h = 0; h < H; ++h)
+                        for (int c = 0; c < d; ++c)
+                            for (int t = 0; t < T; ++t) {
+                                const int lo = t - L + 1 < 0 ? 0 : t - L + 1;
+                                double g, gb;
+                                Q[t - lo] = 1.0;
+                                for (int u = t; u > lo; --u) {
+                                    gate_pair(logit[idx4(b, u, h, c, T, H, d)], &g, &gb);
+                                    Q[u - 1 - lo] = Q[u - lo] * g;
+                                }
+                                const size_t it = idx4(b, t, h, c, T, H, d);
+                                const double lamk = dks[it], lamv = dvs[it];
+                                double wk = 0.0, wv = 0.0;
+                                for (int u = lo; u <= t; ++u) {
+                                    const size_t i = idx4(b, u, h, c, T, H, d);
+                                    gate_pair(logit[i], &g, &gb);
+                                    const double qk = Q[u - lo] * lamk, qv = Q[u - lo] * lamv;
+                                    dk[i] += gb * qk;
+                                    dv[i] += gb * qv;
+                                    dlogit[i] += g * gb * (qk * (wk - k[i]) + qv * (wv - v[i]));
+                                    wk = g * wk + gb * k[i];
+                                    wv = g * wv + gb * v[i];
+                                }
+                            }
+            }
+            free(Q);
+        }
+        free(ks); free(vs); free(dks); free(dvs);
+        return bad ? -4 : 0;
     }
     /* recurrence, backwards in time, one channel at a time */
 #pragma omp parallel for collapse(2) schedule(dynamic)

@@ -212,7 +212,7 @@ class Oracle:
 
     def layer_backward(self, q, k, v, logit, dout, L, mode, D, W, scale):
         """Gradients (dq, dk, dv, dlogit), each [B,T,H,d], of <dout, out>
-        through the recurrence (full or RESTART) and the attention."""
+        through the recurrence (full, RESTART or SLIDING) and the attention."""
         q, k, v, logit, dout = (_f64(x) for x in (q, k, v, logit, dout))
         B, T, H, d = q.shape
         Da, Wa = _heads(D, W, H)

@@ -417,13 +417,15 @@ def _layer_loss(o, q, k, v, lg, dout, L, mode, D, W, scale):
 
 def pin_backward_finite_differences(o):
     """The backward against central differences of the (separately pinned)
-    forward, element by element, for the full recurrence and RESTART, dense,
-    dilated and windowed heads together: every input of every tensor."""
+    forward, element by element, for the full recurrence, RESTART and a
+    SLIDING window, dense, dilated and windowed heads together: every input
+    of every tensor."""
     eps = 1e-5
-    for (T, L, D, W) in [(10, 10, [1, 3], [0, 2]), (11, 4, [2, 1], [3, 0]), (9, 9, [4, 20], [1, 0])]:
-        q, k, v, lg = _inputs(40 + T, 1, T, 2, 3, gate_mean=0.5)
-        dout = _rng(41 + T).standard_normal(q.shape)
-        args = (L, 0, D, W, 0.7)
+    for (T, L, mode, D, W) in [(10, 10, 0, [1, 3], [0, 2]), (11, 4, 0, [2, 1], [3, 0]), (9, 9, 0, [4, 20], [1, 0]),
+                               (12, 4, 1, [1, 3], [0, 2]), (10, 3, 1, [2, 1], [3, 0]), (8, 5, 1, [1, 20], [0, 1])]:
+        q, k, v, lg = _inputs(40 + T + 7 * mode, 1, T, 2, 3, gate_mean=0.5)
+        dout = _rng(41 + T + 7 * mode).standard_normal(q.shape)
+        args = (L, mode, D, W, 0.7)
         grads = o.layer_backward(q, k, v, lg, dout, *args)
         for which, (x, g) in enumerate(zip((q, k, v, lg), grads)):
             fd = np.empty_like(x)
@@ -435,7 +437,7 @@ def pin_backward_finite_differences(o):
                 dn = _layer_loss(o, q, k, v, lg, dout, *args)
                 x[idx] = saved
                 fd[idx] = (up - dn) / (2 * eps)
-            np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=f"input {which} T={T} L={L}")
+            np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=f"input {which} T={T} L={L} mode={mode}")
 
 
 def pin_backward_own_state_only(o):
@@ -461,14 +463,21 @@ def pin_backward_own_state_only(o):
     np.testing.assert_allclose(dl, g * (1 - g) * lam * (prev - v), rtol=1e-11, atol=1e-13)
 
 
-def pin_backward_rejects_sliding(o):
-    """A SLIDING window below T has no backward here: the call is refused."""
-    q, k, v, lg = _inputs(47, 1, 8, 1, 2)
-    try:
-        o.layer_backward(q, k, v, lg, q, 4, 1, [1], [0], 1.0)
-    except ValueError:
-        return
-    raise AssertionError("SLIDING backward was accepted")
+def pin_backward_sliding_one_token(o):
+    """SLIDING at L = 1: each state is (1 - g_t) x_t alone, so with
+    lambda = dLoss/dstate (from the attention) dx_t = (1 - g_t) lambda_t and
+    dlogit_t = -g_t (1 - g_t) sum_{x in k, v} lambda_t x_t.  With D >= T, no
+    window and a zero query, each query's only key is its own state with
+    weight one, so lambda_v = dout and lambda_k = 0."""
+    B, T, H, d = 1, 9, 2, 4
+    _, k, v, lg = _inputs(47, B, T, H, d)
+    q = np.zeros_like(k)
+    dout = _rng(48).standard_normal(q.shape)
+    dq, dk, dv, dl = o.layer_backward(q, k, v, lg, dout, 1, 1, [T, T], [0, 0], 0.9)
+    g = 1.0 / (1.0 + np.exp(-lg))
+    np.testing.assert_allclose(dv, (1 - g) * dout, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk, np.zeros_like(dk), atol=1e-14)
+    np.testing.assert_allclose(dl, -g * (1 - g) * dout * v, rtol=1e-11, atol=1e-14)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -53,6 +53,11 @@ MUTANTS = {
                                "kp[nk] = k + o; vp[nk] = v + o; dkp[nk] = dks + o; dvp[nk] = dvs + o;"),
     "bwd_prev_state_off_by_one": ("double hv_prev = cut ? 0.0 : vs[idx4(b, t - 1, h, c, T, H, d)];",
                                   "double hv_prev = cut ? 0.0 : vs[idx4(b, t, h, c, T, H, d)];"),
+    "bwd_sliding_window_long": ("const int lo = t - L + 1 < 0 ? 0 : t - L + 1;\n                                double g, gb;",
+                                "const int lo = t - L < 0 ? 0 : t - L;\n                                double g, gb;"),
+    "bwd_sliding_suffix_shifted": ("Q[u - 1 - lo] = Q[u - lo] * g;", "Q[u - 1 - lo] = Q[u - lo];"),
+    "bwd_sliding_state_after_step": ("dlogit[i] += g * gb * (qk * (wk - k[i]) + qv * (wv - v[i]));\n                                    wk = g * wk + gb * k[i];\n                                    wv = g * wv + gb * v[i];",
+                                     "wk = g * wk + gb * k[i];\n                                    wv = g * wv + gb * v[i];\n                                    dlogit[i] += g * gb * (qk * (wk - k[i]) + qv * (wv - v[i]));"),
     "count_window_short": ("for (int w = 0; w < W && t - w >= 0; ++w) {\n        if (loc)",
                            "for (int w = 1; w < W && t - w >= 0; ++w) {\n        if (loc)"),
 }
