@@ -408,25 +408,25 @@ def run_backward_arl(torch, rat, w, steps, warmup):
     return st, flops, nbytes
 
 
-def run_backward_windowed(torch, rat, w, steps, warmup):
+def run_backward_windowed(torch, rat, w, steps, warmup, mode):
     """The layer backward of a windowed prefill workload `w` (every head at
-    its (D, W), RESTART recurrence): the dilated states and the raw window
-    in one softmax.  The forward's states come from the scan kernel,
-    outside the timed region."""
+    its (D, W), recurrence `mode` with its L): the dilated states and the
+    raw window in one softmax.  The forward's states come from the scan
+    kernel, outside the timed region."""
     from dilated_sparse_attention_amd import inputs
 
     x = inputs.make_prefill(w, seed=9, device="cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(10)
     dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(w.dtype)
-    ks, vs = rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=rat.RESTART)
+    ks, vs = rat.scan_prefill(x["k"], x["v"], x["gate"], L=w.L, mode=mode)
     grads = tuple(torch.empty(x["q"].shape, dtype=torch.float32, device="cuda") for _ in range(4))
     ws = torch.empty(rat.ops.load_library().rat_layer_backward_workspace_bytes(w.B, w.T, w.H, w.d),
                      dtype=torch.uint8, device="cuda")
 
     def step(_):
         rat.layer_backward(x["q"], x["k"], x["v"], x["gate"], ks, vs, dout, list(w.D), list(w.W), L=w.L,
-                           mode=rat.RESTART, grads=grads, workspace=ws)
+                           mode=mode, grads=grads, workspace=ws)
 
     st = time_launches(torch, step, max(steps, MIN_TIMED), warmup)
     # the same units as the ARL backward, over the dilated and the window pairs
@@ -686,14 +686,15 @@ def main():
                                          recurrence="full")}
 
         bw = inputs.PREFILL_LONG
-        key = "backward_windowed_" + bw.name
-        if args.only is None or args.only == key:
-            progress("backward (windowed heads, RESTART)", bw.name)
-            bst, bflops, bbytes = run_backward_windowed(torch, rat, bw, args.steps, 2)
-            extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bst["median"] / 1e3),
-                          **stats_fields("backward", bst, nbytes=bbytes, flops=bflops),
-                          "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
-                          "config": dict(bw.describe(), recurrence="RESTART")}
+        for mode, mname in ((rat.RESTART, "restart"), (rat.SLIDING, "sliding")):
+            key = f"backward_windowed_{bw.name}_{mname}"
+            if args.only is None or args.only == key:
+                progress(f"backward (windowed heads, {mname})", bw.name)
+                bst, bflops, bbytes = run_backward_windowed(torch, rat, bw, args.steps, 2, mode)
+                extra[key] = {"train_tokens_per_s": bw.B * bw.T / (bst["median"] / 1e3),
+                              **stats_fields("backward", bst, nbytes=bbytes, flops=bflops),
+                              "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                              "config": dict(bw.describe(), recurrence=mname)}
 
     if ms is None:  # a profiling run of one extra workload
         print(json.dumps({"extra": extra}))

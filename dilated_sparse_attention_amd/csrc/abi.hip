@@ -495,7 +495,6 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
     const rat_status hc = check_heads(H, D, W, &any_w);
     if (hc != RAT_OK) return hc;
     if (!dtype_ok(dtype) || !d_ok(d) || !size_ok(B, T, H, d)) return RAT_ERR_UNSUPPORTED;
-    if (mode == RAT_RECUR_SLIDING && L < T) return RAT_ERR_UNSUPPORTED;  // no backward of a sliding window
     if (!(scale == scale)) return RAT_ERR_SHAPE;
     for (int i = 0; i < 4; ++i) {
         for (const void* x : ins)
@@ -523,7 +522,8 @@ rat_status rat_layer_backward(const void* q, const void* k, const void* v, const
     a.carry = reinterpret_cast<float*>(ws + p.off_carry);
     a.bstat = reinterpret_cast<float*>(ws + p.off_bstat);
     a.B = B; a.T = T; a.H = H; a.d = d;
-    a.L = L >= T ? 0 : L;
+    a.sliding = (mode == RAT_RECUR_SLIDING && L < T) ? 1 : 0;
+    a.L = L >= T ? 0 : L;  // the RESTART period, or the SLIDING window
     a.nchunk = p.nchunk;
     a.scale = scale;
     a.mfma = dtype == RAT_DTYPE_BF16 ? 1 : 0;

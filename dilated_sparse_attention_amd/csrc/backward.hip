@@ -35,6 +35,8 @@
 //   bwd_key_kernel    fp32: one wave per key row: the state key's gradients
 //                     from the queries t = s, s + D, ... and the raw key's
 //                     from t = s .. s + W - 1;
+//   bwd_slide_kernel  the SLIDING window (L < T): per token and channel
+//                     over the windows that hold it;
 //   bwd_scan_*        the reverse recurrence in chunks of kBwdChunk tokens:
 //                     per-chunk affine maps (forward state map and backward
 //                     carry map), a sequential pass over the chunks of each
@@ -918,12 +920,82 @@ __global__ __launch_bounds__(256) void bwd_scan_apply_kernel(BwdArgs a)
     }
 }
 
+// SLIDING window below T: each state is its own window of L tokens, so the
+// state gradients lambda (from the attention) carry nothing.  Per token u
+// and channel, with P(a, b) = g_a ... g_b:
+//   mu = sum_{t = u .. u+L-1} lambda_t P(u+1, t),   dx_u = (1 - g_u) mu,
+//   dlogit_u = g_u (1 - g_u) sum_{x in k, v} (sum_t lambda_t P(u+1, t) C_t - x_u mu),
+// C_t = sum_{s = max(0, t-L+1) .. u-1} P(s+1, u-1) (1 - g_s) x_s being the
+// window of t up to u - 1.  The products are exponentials of window-local
+// sums of log g (no division by a gate, no overflow): one pass over s < u
+// forms C for t = u, a second over t >= u drops each s as it leaves the
+// window.  One thread per (b, u, channel), channel fastest.
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_slide_kernel(BwdArgs a)
+{
+    const size_t N = (size_t)a.H * a.d;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)a.B * a.T * N) return;
+    const size_t n = idx % N, bt = idx / N;
+    const int T = a.T, L = a.L;
+    const int u = (int)(bt % T), b = (int)(bt / T);
+    auto at = [&](int t) { return ((size_t)b * T + t) * N + n; };
+    // log g = -softplus(-logit), held above -80 (a gate below e^-80 is 0 here)
+    auto log_gate = [](float l) { return fmaxf(-(fmaxf(-l, 0.f) + log1pf(__expf(-fabsf(l)))), -80.f); };
+    const int lo = max(0, u - L + 1);
+    float R = 0.f, ck = 0.f, cv = 0.f;  // R: sum of log g over s+1 .. u-1
+    for (int s = u - 1; s >= lo; --s) {
+        const size_t i = at(s);
+        const float l = ldx<E>(a.g, i);
+        float g, gb;
+        forget_gate(l, g, gb);
+        const float e = __expf(R);
+        ck = fmaf(gb * ldx<E>(a.k, i), e, ck);
+        cv = fmaf(gb * ldx<E>(a.v, i), e, cv);
+        R += log_gate(l);
+    }
+    // the next s to leave the window, and its R (sum over s+1 .. u-1)
+    int sr = lo;
+    float rs = lo <= u - 1 ? R - log_gate(ldx<E>(a.g, at(lo))) : 0.f;
+    const int tmax = min(T - 1, u + L - 1);
+    float F = 0.f, mk = 0.f, mv = 0.f, sk = 0.f, sv = 0.f;  // F: sum of log g over u+1 .. t
+    for (int t = u; t <= tmax; ++t) {
+        if (t > u) {
+            F += log_gate(ldx<E>(a.g, at(t)));
+            if (t - L >= 0) {  // s = t - L (= sr) is not in the window of t
+                const size_t i = at(sr);
+                float g, gb;
+                forget_gate(ldx<E>(a.g, i), g, gb);
+                const float e = __expf(rs);
+                ck = fmaf(-gb * ldx<E>(a.k, i), e, ck);
+                cv = fmaf(-gb * ldx<E>(a.v, i), e, cv);
+                ++sr;
+                if (sr <= u - 1) rs -= log_gate(ldx<E>(a.g, at(sr)));
+            }
+        }
+        const size_t it = at(t);
+        const float p = __expf(F);
+        const float lk = a.dks[it] * p, lv = a.dvs[it] * p;
+        mk += lk;
+        mv += lv;
+        sk = fmaf(lk, ck, sk);
+        sv = fmaf(lv, cv, sv);
+    }
+    const size_t iu = at(u);
+    float g, gb;
+    forget_gate(ldx<E>(a.g, iu), g, gb);
+    a.dk[iu] = a.raw ? fmaf(gb, mk, a.dk[iu]) : gb * mk;
+    a.dv[iu] = a.raw ? fmaf(gb, mv, a.dv[iu]) : gb * mv;
+    a.dg[iu] = g * gb * (sk - ldx<E>(a.k, iu) * mk + sv - ldx<E>(a.v, iu) * mv);
+}
+
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
 {
     const unsigned rows = (unsigned)((size_t)a.B * a.H * a.T);
     const size_t N = (size_t)a.H * a.d;
     const unsigned cells = (unsigned)(((size_t)a.nchunk * a.B * N + 255) / 256);
     const unsigned chans = (unsigned)(((size_t)a.B * N + 15) / 16);  // 16 channels per carry workgroup
+    const unsigned elems = (unsigned)(((size_t)a.B * a.T * N + 255) / 256);  // one thread per element
     if (bf16) {
         // every head on the MFMA kernels; with a window somewhere, the band
         // passes around the dilated ones: the window's partial sums, then the
@@ -945,15 +1017,23 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
             if (items) hipLaunchKernelGGL((bwd_kv_mfma<64, false>), dim3(items), blk, 0, stream, a);
             if (bands) hipLaunchKernelGGL((bwd_kv_mfma<64, true>), dim3(bands), blk, 0, stream, a);
         }
-        hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_scan_apply_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
+        if (a.sliding) {
+            hipLaunchKernelGGL(bwd_slide_kernel<uint16_t>, dim3(elems), dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(bwd_scan_apply_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
+        }
     } else {
         hipLaunchKernelGGL(bwd_query_kernel<float>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_key_kernel<float>, dim3(rows), dim3(kWave), 0, stream, a);
-        hipLaunchKernelGGL(bwd_scan_maps_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_scan_apply_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
+        if (a.sliding) {
+            hipLaunchKernelGGL(bwd_slide_kernel<float>, dim3(elems), dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL(bwd_scan_maps_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(bwd_scan_apply_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
+        }
     }
     return hipGetLastError();
 }

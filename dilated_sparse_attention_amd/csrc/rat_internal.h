@@ -289,6 +289,7 @@ struct BwdArgs {
     int mfma;          // bf16: every head runs on the MFMA kernels (fp32: the per-row kernels)
     int raw;           // dk / dv hold raw-window gradients before the recurrence adds its own:
                        // some head has a window (bf16), always (fp32)
+    int sliding;       // SLIDING window L < T: each state its own window (L is then the window)
     int D[kAttnMaxHeads];
     int W[kAttnMaxHeads];
     int mitem[kAttnMaxHeads + 1];  // first MFMA work item of each head; [H] = total
@@ -305,7 +306,7 @@ static_assert(sizeof(ScanSlideArgs) == 1096 && offsetof(ScanSlideArgs, hist) == 
 static_assert(sizeof(AttnArgs) == 1344 && offsetof(AttnArgs, cls) == 92 && offsetof(AttnArgs, heads) == 316,
               "AttnArgs layout");
 static_assert(sizeof(RingFillArgs) == 1080 && sizeof(DecodeArgs) == 3160 && sizeof(StepArgs) == 2136 &&
-              sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3256 && sizeof(AttnF32Args) == 2128 &&
+              sizeof(CacheArgs) == 2136 && sizeof(BwdArgs) == 3264 && sizeof(AttnF32Args) == 2128 &&
               sizeof(SlideStepArgs) == 2160 && sizeof(SlideFillArgs) == 72, "kernel-argument sizes");
 static_assert(sizeof(BwdArgs) < 4096 && sizeof(DecodeArgs) < 4096, "kernel arguments fit their segment");
 

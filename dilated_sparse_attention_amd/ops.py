@@ -406,7 +406,7 @@ def layer_backward(q, k, v, gate_logits, k_state, v_state, dout, D, W, L=None, m
                    grads=None, workspace=None):
     """Gradients (dq, dk, dv, dgate), fp32 [B,T,H,d], of a loss with
     incoming gradient ``dout`` through the layer's forward (the states it
-    produced are passed in).  Full recurrence or RESTART."""
+    produced are passed in).  Full recurrence, RESTART or a SLIDING window."""
     lib = load_library()
     B, T, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("gate_logits", gate_logits), ("k_state", k_state),

@@ -311,9 +311,10 @@ size_t rat_layer_backward_workspace_bytes(int B, int T, int H, int d);
  *                          row term <dout_t, out_t> is formed from it, so
  *                          the forward output is not an input;
  *   dq, dk, dv, dgate    : [B,T,H,d] fp32 outputs;
- *   L, mode              : the forward's recurrence; the full recurrence
- *                          (L >= T) and RESTART only -- a SLIDING window
- *                          below T returns RAT_ERR_UNSUPPORTED;
+ *   L, mode              : the forward's recurrence: full (L >= T),
+ *                          RESTART, or a SLIDING window of L tokens (each
+ *                          state its own window, the gradients summed over
+ *                          the windows that hold a token);
  *   D, W, scale          : as rat_dilated_attn_prefill;
  *   workspace            : rat_layer_backward_workspace_bytes(...) bytes.
  * Errors: RAT_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIAS, _ALIGN, _WORKSPACE, _HIP. */

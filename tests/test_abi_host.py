@@ -250,7 +250,8 @@ def test_backward_validation(lib):
     assert backward(lib, T=0) == SHAPE
     assert backward(lib, D=(0, 1)) == SHAPE
     assert backward(lib, d=96) == UNSUP
-    assert backward(lib, mode=1, L=64) == UNSUP      # no backward of a sliding window
+    assert backward(lib, mode=1, L=64, dq=P[0]) == ALIAS  # a SLIDING window validates like the rest
+    assert backward(lib, mode=2) == SHAPE            # no such recurrence mode
     assert backward(lib, dq=P[0]) == ALIAS
     assert backward(lib, dv=ctypes.c_void_p(0x10000 + 0x100000 * 9)) == ALIAS  # two gradients share memory
     assert backward(lib, ks=MIS) == ALIGN

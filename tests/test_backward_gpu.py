@@ -70,6 +70,30 @@ CASES = [
 ]
 
 
+SLIDING_CASES = [
+    # (B, T, H, d, D per head, W per head, L (the window), dtype)
+    (1, 300, 2, 128, [1, 16], [0, 8], 64, torch.bfloat16),        # L* = 64
+    (2, 130, 2, 64, [4, 7], [16, 0], 16, torch.bfloat16),
+    (1, 200, 3, 128, [1, 4, 64], [0, 0, 100], 33, torch.bfloat16),  # window not a power of two
+    (1, 70, 2, 128, [2, 1], [3, 0], 1, torch.bfloat16),           # L = 1: each state its own token
+    (1, 96, 2, 64, [1, 3], [0, 5], 20, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", SLIDING_CASES, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}D{c[4]}W{c[5]}L{c[6]}{str(c[7])[6:]}")
+def test_backward_sliding_parity(case):
+    """The backward of a SLIDING window below T (the states from the
+    sliding scan kernels) against the oracle's."""
+    B, T, H, d, D, W, L, dtype = case
+    x = inputs.make_random_prefill(B, T, H, d, dtype, seed=35, gate_mean=1.5)
+    dout = torch.randn((B, T, H, d), generator=torch.Generator().manual_seed(36)).to(dtype)
+    announce("backward sliding", case)
+    got = forward_and_backward(x, D, W, L, rat.SLIDING, dout, dtype)
+    want = oracle.layer_backward(x["q"], x["k"], x["v"], x["gate"], dout, L, 1, D, W, 1 / math.sqrt(d))
+    for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
+        assert_grad(g_, w_, dtype, name)
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}D{c[4]}W{c[5]}L{c[6]}{str(c[7])[6:]}")
 def test_backward_parity(case):
     B, T, H, d, D, W, L, dtype = case
