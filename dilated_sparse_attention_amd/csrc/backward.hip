@@ -989,6 +989,107 @@ __global__ __launch_bounds__(256) void bwd_slide_kernel(BwdArgs a)
     a.dg[iu] = g * gb * (sk - ldx<E>(a.k, iu) * mk + sv - ldx<E>(a.v, iu) * mv);
 }
 
+// The same for windows of up to kSlideMaxL tokens, from an LDS tile: a
+// workgroup takes kSlideTok tokens of kSlideCh channels (one thread each)
+// and first stages, for every token its windows reach, the gate, 1 - gate,
+// log gate, k, v and the two state gradients.  A wave's reads then fall on
+// 64 consecutive words (eight tokens of eight channels).
+constexpr int kSlideTok = 32, kSlideCh = 8, kSlideMaxL = 64;
+constexpr int kSlideSpan = kSlideTok + 2 * (kSlideMaxL - 1);
+static_assert(kSlideTok * kSlideCh == 256, "one thread per tile element");
+
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a)
+{
+    __shared__ float s_g[kSlideSpan][kSlideCh], s_gb[kSlideSpan][kSlideCh], s_lg[kSlideSpan][kSlideCh];
+    __shared__ float s_k[kSlideSpan][kSlideCh], s_v[kSlideSpan][kSlideCh];
+    __shared__ float s_lk[kSlideSpan][kSlideCh], s_lv[kSlideSpan][kSlideCh];
+    const size_t N = (size_t)a.H * a.d;
+    const int T = a.T, L = a.L;
+    const size_t n0 = (size_t)blockIdx.x * kSlideCh;
+    const int u0 = blockIdx.y * kSlideTok, b = blockIdx.z;
+    // tokens ts .. te: the windows of the tile's first token back, of its last forward
+    const int ts = max(0, u0 - (L - 1)), te = min(T - 1, u0 + kSlideTok - 1 + (L - 1));
+    const int span = te - ts + 1;
+    for (int idx = threadIdx.x; idx < span * kSlideCh; idx += kSlideTok * kSlideCh) {
+        const int j = idx / kSlideCh, c = idx % kSlideCh;
+        float g = 0.f, gb = 0.f, lg = 0.f, k = 0.f, v = 0.f, lk = 0.f, lv = 0.f;
+        if (n0 + c < N) {
+            const size_t i = ((size_t)b * T + ts + j) * N + n0 + c;
+            const float l = ldx<E>(a.g, i);
+            forget_gate(l, g, gb);
+            lg = fmaxf(-(fmaxf(-l, 0.f) + log1pf(__expf(-fabsf(l)))), -80.f);
+            k = ldx<E>(a.k, i);
+            v = ldx<E>(a.v, i);
+            lk = a.dks[i];
+            lv = a.dvs[i];
+        }
+        s_g[j][c] = g;
+        s_gb[j][c] = gb;
+        s_lg[j][c] = lg;
+        s_k[j][c] = k;
+        s_v[j][c] = v;
+        s_lk[j][c] = lk;
+        s_lv[j][c] = lv;
+    }
+    __syncthreads();
+    const int c = threadIdx.x % kSlideCh, u = u0 + threadIdx.x / kSlideCh;
+    if (u >= T || n0 + c >= N) return;
+    const int lo = max(0, u - L + 1);
+    // pass 1 over s = u-1 .. lo: C for t = u, with P = P(s+1, u-1) as a product
+    float P = 1.f, R = 0.f, ck = 0.f, cv = 0.f;
+    for (int s = u - 1; s >= lo; --s) {
+        const int j = s - ts;
+        ck = fmaf(s_gb[j][c] * s_k[j][c], P, ck);
+        cv = fmaf(s_gb[j][c] * s_v[j][c], P, cv);
+        P *= s_g[j][c];
+        R += s_lg[j][c];
+    }
+    int sr = lo;
+    float rs = lo <= u - 1 ? R - s_lg[lo - ts][c] : 0.f;
+    const int tmax = min(T - 1, u + L - 1);
+    float P2 = 1.f, mk = 0.f, mv = 0.f, sk = 0.f, sv = 0.f;
+    for (int t = u; t <= tmax; ++t) {
+        const int j = t - ts;
+        if (t > u) {
+            P2 *= s_g[j][c];
+            if (t - L >= 0) {  // s = t - L (= sr) is not in the window of t
+                const int jr = sr - ts;
+                const float e = __expf(rs);
+                ck = fmaf(-s_gb[jr][c] * s_k[jr][c], e, ck);
+                cv = fmaf(-s_gb[jr][c] * s_v[jr][c], e, cv);
+                ++sr;
+                if (sr <= u - 1) rs -= s_lg[sr - ts][c];
+            }
+        }
+        const float lk = s_lk[j][c] * P2, lv = s_lv[j][c] * P2;
+        mk += lk;
+        mv += lv;
+        sk = fmaf(lk, ck, sk);
+        sv = fmaf(lv, cv, sv);
+    }
+    const int ju = u - ts;
+    const float g = s_g[ju][c], gb = s_gb[ju][c];
+    const size_t iu = ((size_t)b * T + u) * N + n0 + c;
+    a.dk[iu] = a.raw ? fmaf(gb, mk, a.dk[iu]) : gb * mk;
+    a.dv[iu] = a.raw ? fmaf(gb, mv, a.dv[iu]) : gb * mv;
+    a.dg[iu] = g * gb * (sk - s_k[ju][c] * mk + sv - s_v[ju][c] * mv);
+}
+
+// the SLIDING recurrence's backward: tiled for windows up to kSlideMaxL
+template <typename E>
+static void launch_slide(const BwdArgs& a, unsigned elems, hipStream_t stream)
+{
+    const size_t N = (size_t)a.H * a.d;
+    if (a.L <= kSlideMaxL) {
+        const dim3 grid((unsigned)((N + kSlideCh - 1) / kSlideCh), (unsigned)((a.T + kSlideTok - 1) / kSlideTok),
+                        (unsigned)a.B);
+        hipLaunchKernelGGL(bwd_slide_tiled_kernel<E>, grid, dim3(kSlideTok * kSlideCh), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(bwd_slide_kernel<E>, dim3(elems), dim3(256), 0, stream, a);
+    }
+}
+
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
 {
     const unsigned rows = (unsigned)((size_t)a.B * a.H * a.T);
@@ -1018,7 +1119,7 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
             if (bands) hipLaunchKernelGGL((bwd_kv_mfma<64, true>), dim3(bands), blk, 0, stream, a);
         }
         if (a.sliding) {
-            hipLaunchKernelGGL(bwd_slide_kernel<uint16_t>, dim3(elems), dim3(256), 0, stream, a);
+            launch_slide<uint16_t>(a, elems, stream);
         } else {
             hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
             hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
@@ -1028,7 +1129,7 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
         hipLaunchKernelGGL(bwd_query_kernel<float>, dim3(rows), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL(bwd_key_kernel<float>, dim3(rows), dim3(kWave), 0, stream, a);
         if (a.sliding) {
-            hipLaunchKernelGGL(bwd_slide_kernel<float>, dim3(elems), dim3(256), 0, stream, a);
+            launch_slide<float>(a, elems, stream);
         } else {
             hipLaunchKernelGGL(bwd_scan_maps_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
             hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);

@@ -94,6 +94,24 @@ def test_backward_sliding_parity(case):
         assert_grad(g_, w_, dtype, name)
 
 
+def test_backward_sliding_long_window():
+    """A SLIDING window above 64 tokens (the per-element kernel; the forward
+    scan kernels stop at 64, so the states here are the oracle's, rounded to
+    the layer's dtype as the forward would store them)."""
+    B, T, H, d, D, W, L = 1, 300, 2, 128, [1, 8], [0, 16], 100
+    x = inputs.make_random_prefill(B, T, H, d, torch.bfloat16, seed=37, gate_mean=1.5)
+    dout = torch.randn((B, T, H, d), generator=torch.Generator().manual_seed(38)).to(torch.bfloat16)
+    ks, vs = oracle.scan(x["k"], x["v"], x["gate"], L, 1)
+    ks, vs = (torch.from_numpy(t).to(torch.bfloat16).cuda() for t in (ks, vs))
+    announce("backward sliding", "L", L)
+    q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
+    got = rat.layer_backward(q, k, v, g, ks, vs, dout.cuda(), D, W, L=L, mode=rat.SLIDING)
+    torch.cuda.synchronize()
+    want = oracle.layer_backward(x["q"], x["k"], x["v"], x["gate"], dout, L, 1, D, W, 1 / math.sqrt(d))
+    for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
+        assert_grad(g_, w_, torch.bfloat16, name)
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}D{c[4]}W{c[5]}L{c[6]}{str(c[7])[6:]}")
 def test_backward_parity(case):
     B, T, H, d, D, W, L, dtype = case
