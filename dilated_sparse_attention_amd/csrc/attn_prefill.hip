@@ -21,12 +21,15 @@
 // global->LDS loads.
 //
 // Path A (every head, including dense D = 1): work items are
-// (b, h, r, 256-row chunk).  Persistent workgroups of 8 waves take items in
-// a snake order over the cost-sorted item list; each wave owns two 16-row
-// blocks (w and 15-w, which balances the causal work) so that every K/V
-// fragment read from LDS feeds two MFMA row blocks.  K/V tiles of 64 keys
-// stream through a 4-deep LDS ring whose prefetch runs on into the next
-// item, so every state row is read from HBM once per chunk.
+// (b, h, r, chunk of rows of residue r).  Persistent workgroups take items
+// in rounds over the cost-sorted item list, in one of two shapes: eight
+// waves over 256-row chunks on a four- or five-slot LDS ring (one workgroup
+// per CU; launches with residues longer than 1024 rows), or four waves over
+// 128-row chunks on a two-slot ring (two per CU).  Each wave owns two 16-row
+// blocks (w and 2 NW - 1 - w, which balances the causal work) so that every
+// K/V fragment read from LDS feeds two MFMA row blocks.  K/V tiles of 64
+// keys stream through the ring, whose prefetch runs on into the next item,
+// so every state row is read from HBM once per chunk.
 //
 // Local window (heads with W > 0): the raw-key band runs first, over
 // contiguous queries (where the band is dense), in a kernel that leaves a

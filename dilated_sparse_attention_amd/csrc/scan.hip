@@ -9,24 +9,27 @@
 // (each lane owns two adjacent channels) and the scan along T is a per-lane
 // sequential recurrence with no cross-lane traffic.
 //
-// FULL / RESTART kernel (one pass over HBM):
-//   * a workgroup owns a chunk of 128 tokens of one block of channels (a
-//     256-byte row segment: 128 bf16 / 64 fp32 channels); lane (r, c) of a
-//     wave holds 16 bytes of the row (8 bf16 / 4 fp32 channels) for 4
-//     consecutive tokens, so every access is a 16-byte load or store and a
-//     wave instruction covers 4 whole row segments.  The chunk stays in
-//     registers from load to store (no LDS staging); 2 workgroups fit on a
-//     compute unit;
+// FULL / RESTART kernel (one pass over HBM), eight waves per workgroup:
+//   * a workgroup owns a chunk of tokens of one block of channels; lane
+//     (r, c) of a wave holds 16 bytes of a token row (8 bf16 / 4 fp32
+//     channels) for 4 consecutive tokens, so every access is a 16-byte load
+//     or store.  Two geometries (ScanGeo): the narrow one spans a 256-byte
+//     row segment (128 bf16 / 64 fp32 channels, 16 lanes) with 128-token
+//     chunks; the wide one, for the bf16 full recurrence and RESTART periods
+//     above 256, a 128-byte segment (64 channels, 8 lanes) with 256-token
+//     chunks, half as many chunks per sequence and so half the look-back
+//     chain.  The chunk stays in registers from load to store (no LDS
+//     staging); 2 workgroups fit on a compute unit;
 //   * pass 1: each lane runs the recurrence over its 4 tokens from a zero
 //     state; the last state with the gate product forms the segment's
 //     affine map h -> A*h + B per channel (the raw inputs stay in
 //     registers);
-//   * two waves (half of the channels each) turn the 32 segment maps into
-//     exclusive prefixes (and the chunk's map, which they publish) while
-//     another finds the chunk's carry-in by a decoupled look-back over the
-//     chunks before it (Merrill & Garland's single-pass scan), through
-//     64-bit words that carry (value, epoch tag) and so need no memory
-//     fence;
+//   * one or two waves turn the chunk's 32 (narrow) or 64 (wide) segment
+//     maps into exclusive prefixes (and the chunk's map, which they
+//     publish) while another finds the chunk's carry-in by a decoupled
+//     look-back over the chunks before it (Merrill & Garland's single-pass
+//     scan), through 64-bit words that carry (value, epoch tag) and so need
+//     no memory fence;
 //   * pass 2 runs the recurrence again from the segment's carry-in (gates
 //     evaluated again) and stores the states.
 //   Chunk order comes from a ticket counter so that every chunk a
