@@ -463,13 +463,22 @@ int oracle_chunk_attn_prefill_rows(const double* q, const double* k_state, const
  *     dx_u += (1 - g_u) Q_u lambda_t,
  *     dlogit_u += g_u (1 - g_u) sum_{x in k, v} Q_u lambda_t (w_u - x_u).
  * Outputs dq, dk, dv, dlogit: [B,T,H,d]; dk and dv sum the state path and
- * the raw-window path. */
-int oracle_layer_backward(const double* q, const double* k, const double* v, const double* logit,
-                          const double* dout, double* dq, double* dk, double* dv, double* dlogit,
-                          int B, int T, int H, int d, int L, int mode, const int* D, const int* W,
-                          double scale)
+ * the raw-window path.
+ *
+ * oracle_layer_backward_states is the same chain rule evaluated at given
+ * states (ks, vs) [B,T,H,d] instead of the ones the recurrence produces from
+ * (k, v, logit): the keys / values of the attention and the h_{t-1} of the
+ * recurrence's gate derivative are read from them.  This is what a backward
+ * that is handed the forward's saved states computes; oracle_layer_backward
+ * is this function at the oracle's own fp64 states, so the two share every
+ * line of arithmetic.  (A SLIDING window below T re-walks each window from
+ * the raw inputs, as above, and reads no state.) */
+int oracle_layer_backward_states(const double* q, const double* k, const double* v, const double* logit,
+                                 const double* ks, const double* vs, const double* dout, double* dq,
+                                 double* dk, double* dv, double* dlogit, int B, int T, int H, int d, int L,
+                                 int mode, const int* D, const int* W, double scale)
 {
-    if (!q || !k || !v || !logit || !dout || !dq || !dk || !dv || !dlogit || !D || !W) return -1;
+    if (!q || !k || !v || !logit || !ks || !vs || !dout || !dq || !dk || !dv || !dlogit || !D || !W) return -1;
     if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return -2;
     if (mode != ORACLE_MODE_RESTART && mode != ORACLE_MODE_SLIDING) return -3;
     const int full = (L >= T);
@@ -477,15 +486,12 @@ int oracle_layer_backward(const double* q, const double* k, const double* v, con
     int need_raw, max_keys;
     if (check_heads(H, D, W, &need_raw, &max_keys, T)) return -3;
     const size_t n = (size_t)B * T * H * d;
-    double* ks = (double*)malloc(sizeof(double) * n);
-    double* vs = (double*)malloc(sizeof(double) * n);
     double* dks = (double*)calloc(n, sizeof(double));  /* dLoss/d state (from attention) */
     double* dvs = (double*)calloc(n, sizeof(double));
-    if (!ks || !vs || !dks || !dvs) {
-        free(ks); free(vs); free(dks); free(dvs);
+    if (!dks || !dvs) {
+        free(dks); free(dvs);
         return -4;
     }
-    oracle_scan(k, v, logit, ks, vs, B, T, H, d, L, mode);
     for (size_t i = 0; i < n; ++i) { dq[i] = 0.0; dk[i] = 0.0; dv[i] = 0.0; dlogit[i] = 0.0; }
     int bad = 0;
     /* attention: the accumulations of one (b, h) touch only that head */
@@ -586,7 +592,7 @@ int oracle_layer_backward(const double* q, const double* k, const double* v, con
             }
             free(Q);
         }
-        free(ks); free(vs); free(dks); free(dvs);
+        free(dks); free(dvs);
         return bad ? -4 : 0;
     }
     /* recurrence, backwards in time, one channel at a time */
@@ -610,8 +616,30 @@ int oracle_layer_backward(const double* q, const double* k, const double* v, con
                     lv = cut ? 0.0 : g * lamv;
                 }
             }
-    free(ks); free(vs); free(dks); free(dvs);
+    free(dks); free(dvs);
     return bad ? -4 : 0;
+}
+
+int oracle_layer_backward(const double* q, const double* k, const double* v, const double* logit,
+                          const double* dout, double* dq, double* dk, double* dv, double* dlogit,
+                          int B, int T, int H, int d, int L, int mode, const int* D, const int* W,
+                          double scale)
+{
+    if (!q || !k || !v || !logit || !dout || !dq || !dk || !dv || !dlogit || !D || !W) return -1;
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || L < 1) return -2;
+    if (mode != ORACLE_MODE_RESTART && mode != ORACLE_MODE_SLIDING) return -3;
+    const size_t n = (size_t)B * T * H * d;
+    double* ks = (double*)malloc(sizeof(double) * n);
+    double* vs = (double*)malloc(sizeof(double) * n);
+    if (!ks || !vs) {
+        free(ks); free(vs);
+        return -4;
+    }
+    oracle_scan(k, v, logit, ks, vs, B, T, H, d, L, mode);
+    const int rc = oracle_layer_backward_states(q, k, v, logit, ks, vs, dout, dq, dk, dv, dlogit, B, T, H, d, L,
+                                                mode, D, W, scale);
+    free(ks); free(vs);
+    return rc;
 }
 
 /* Counting mode for the FLOP / KV-size invariants [Deep Dive S3.1 table:

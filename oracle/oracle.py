@@ -98,6 +98,8 @@ class Oracle:
         lib.oracle_chunk_attn_prefill_rows.argtypes = [dp, dp, dp, ip, i, dp, i, i, i, i, ip, d]
         lib.oracle_layer_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                               i, i, i, i, i, i, ip, ip, d]
+        lib.oracle_layer_backward_states.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                     i, i, i, i, i, i, ip, ip, d]
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -223,6 +225,19 @@ class Oracle:
                "oracle_layer_backward")
         return dq, dk, dv, dl
 
+    def layer_backward_states(self, q, k, v, logit, k_state, v_state, dout, L, mode, D, W, scale):
+        """The same gradients evaluated at given states (k_state, v_state),
+        as a backward handed the forward's saved states computes them."""
+        q, k, v, logit, ks, vs, dout = (_f64(x) for x in (q, k, v, logit, k_state, v_state, dout))
+        B, T, H, d = q.shape
+        Da, Wa = _heads(D, W, H)
+        dq, dk, dv, dl = (np.empty_like(q) for _ in range(4))
+        _check(self.lib.oracle_layer_backward_states(_ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(ks), _ptr(vs),
+                                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dl), B, T, H,
+                                                     d, int(L), int(mode), _iptr(Da), _iptr(Wa), float(scale)),
+               "oracle_layer_backward_states")
+        return dq, dk, dv, dl
+
 
 _default = None
 
@@ -279,3 +294,7 @@ def chunk_attn_prefill(q, k_state, v_state, D, scale):
 
 def layer_backward(q, k, v, logit, dout, L, mode, D, W, scale):
     return default().layer_backward(q, k, v, logit, dout, L, mode, D, W, scale)
+
+
+def layer_backward_states(q, k, v, logit, k_state, v_state, dout, L, mode, D, W, scale):
+    return default().layer_backward_states(q, k, v, logit, k_state, v_state, dout, L, mode, D, W, scale)

@@ -480,4 +480,72 @@ def pin_backward_sliding_one_token(o):
     np.testing.assert_allclose(dl, -g * (1 - g) * dout * v, rtol=1e-11, atol=1e-14)
 
 
+def pin_backward_states_at_scan_states(o):
+    """The backward at given states, handed the recurrence's own states, is
+    the layer backward (which the finite differences above pin): full,
+    RESTART and SLIDING."""
+    for (T, L, mode) in [(11, 11, 0), (11, 4, 0), (10, 3, 1)]:
+        q, k, v, lg = _inputs(50 + T + L, 2, T, 2, 3)
+        dout = _rng(51 + T).standard_normal(q.shape)
+        args = (L, mode, [1, 3], [0, 2], 0.6)
+        ks, vs = o.scan(k, v, lg, L, mode)
+        want = o.layer_backward(q, k, v, lg, dout, *args)
+        got = o.layer_backward_states(q, k, v, lg, ks, vs, dout, *args)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w)
+
+
+def pin_backward_states_dq_finite_differences(o):
+    """At states that no recurrence produced (random ones), dq is still the
+    gradient of <dout, attention(q, states, raw window)> in q with the states
+    held fixed: central differences of the forward attention, every element,
+    with dense, dilated and windowed heads."""
+    eps = 1e-5
+    B, T, H, d = 1, 10, 3, 3
+    q, k, v, lg = _inputs(52, B, T, H, d)
+    r = _rng(53)
+    ks, vs = r.standard_normal(q.shape), r.standard_normal(q.shape)
+    dout = r.standard_normal(q.shape)
+    D, W, scale = [1, 3, 20], [0, 2, 4], 0.8
+    dq = o.layer_backward_states(q, k, v, lg, ks, vs, dout, T, 0, D, W, scale)[0]
+    loss = lambda: float(np.sum(dout * o.attn_prefill(q, ks, vs, k, v, D, W, scale)))
+    fd = np.empty_like(q)
+    for idx in np.ndindex(q.shape):
+        saved = q[idx]
+        q[idx] = saved + eps
+        up = loss()
+        q[idx] = saved - eps
+        dn = loss()
+        q[idx] = saved
+        fd[idx] = (up - dn) / (2 * eps)
+    np.testing.assert_allclose(dq, fd, rtol=1e-6, atol=1e-8)
+
+
+def pin_backward_states_gate_term(o):
+    """The given states enter the recurrence's backward through h_{t-1} in the
+    gate derivative.  With D >= T, no window and a zero query, each query's
+    only key is its own state with weight one, whatever the states are: so
+    lambda_v is the reverse recurrence of dout, lambda_k = 0, dk = 0, dv =
+    (1 - g) lambda_v and dlogit_t = g (1 - g) lambda_v,t (vs_{t-1} - v_t) with
+    vs the given (random) value states."""
+    B, T, H, d = 2, 9, 2, 4
+    _, k, v, _ = _inputs(54, B, T, H, d)
+    q = np.zeros_like(k)
+    lg = np.full(q.shape, 0.4)
+    r = _rng(55)
+    ks, vs = r.standard_normal(q.shape), r.standard_normal(q.shape)
+    dout = r.standard_normal(q.shape)
+    dq, dk, dv, dl = o.layer_backward_states(q, k, v, lg, ks, vs, dout, T, 0, [T, 40], [0, 0], 0.5)
+    g = 1.0 / (1.0 + math.exp(-0.4))
+    lam = np.zeros_like(dout)
+    for t in range(T):
+        for s_ in range(t, T):
+            lam[:, t] += g ** (s_ - t) * dout[:, s_]
+    prev = np.concatenate([np.zeros_like(vs[:, :1]), vs[:, :-1]], axis=1)
+    assert np.array_equal(dq, np.zeros_like(dq))
+    assert np.array_equal(dk, np.zeros_like(dk))
+    np.testing.assert_allclose(dv, (1 - g) * lam, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dl, g * (1 - g) * lam * (prev - v), rtol=1e-11, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -15,6 +15,10 @@ per gradient tensor r with got g:
   mean of 2 (sigmoid(2) = 0.88).  Two such factors give about 3%; 5e-2
   bounds it.  Sums with cancellation make the tensor's RMS the floor.
   fp32 inputs: rtol = 1e-4 (fp32 arithmetic over sums of a few hundred terms).
+
+A second comparison (test_backward_at_saved_states) evaluates the oracle's
+chain rule at the GPU forward's own saved states, so the rounding of the
+states drops out and much tighter bounds hold (RTOL_SAVED below).
 """
 import math
 
@@ -123,6 +127,48 @@ def test_backward_parity(case):
     want = oracle.layer_backward(x["q"], x["k"], x["v"], x["gate"], dout, Lr, 0, D, W, 1 / math.sqrt(d))
     for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
         assert_grad(g_, w_, dtype, name)
+
+
+# Tolerances at the forward's saved states (the oracle's chain rule
+# evaluated at the same states, so the forward's rounding of the states drops
+# out), |g - r| <= rtol * (|r| + rms(r)):
+#   bf16 dq, dk: dS enters the MFMA products as a hi + lo pair of bf16 values
+#     (about 2^-17 relative), P and every sum are fp32: 2e-4;
+#   bf16 dv, dgate: P enters dV = dO^T P as one bf16 rounding (2^-9 per
+#     term); a key is seen by up to n = 400 queries here, whose signed terms
+#     leave the worst element about sqrt(n) 2^-9 = 3.9e-2 of the RMS: 4e-2
+#     (dgate takes it through the value path's lambda);
+#   fp32: fp32 sums of a few hundred terms: 2e-5.
+RTOL_SAVED = {torch.bfloat16: {"dq": 2e-4, "dk": 2e-4, "dv": 4e-2, "dgate": 4e-2},
+              torch.float32: {"dq": 2e-5, "dk": 2e-5, "dv": 2e-5, "dgate": 2e-5}}
+
+
+@pytest.mark.parametrize("case", [c + (rat.RESTART,) for c in CASES] + [c + (rat.SLIDING,) for c in SLIDING_CASES],
+                         ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}d{c[3]}D{c[4]}W{c[5]}L{c[6]}{str(c[7])[6:]}m{c[8]}")
+def test_backward_at_saved_states(case):
+    """The backward against the oracle's chain rule evaluated at the same
+    saved states the GPU forward produced (layer_backward_states): only the
+    backward's own arithmetic is compared, at the tolerances above."""
+    B, T, H, d, D, W, L, dtype, mode = case
+    Lr = T if L is None else L
+    x = inputs.make_random_prefill(B, T, H, d, dtype, seed=39, gate_mean=1.5)
+    dout = torch.randn((B, T, H, d), generator=torch.Generator().manual_seed(40)).to(dtype)
+    announce("backward at saved states", case)
+    q, k, v, g = (x[n].cuda() for n in ("q", "k", "v", "gate"))
+    ks, vs = rat.scan_prefill(k, v, g, L=Lr, mode=mode)
+    got = rat.layer_backward(q, k, v, g, ks, vs, dout.cuda(), D, W, L=Lr, mode=mode)
+    torch.cuda.synchronize()
+    want = oracle.layer_backward_states(x["q"], x["k"], x["v"], x["gate"], to_f64(ks), to_f64(vs), dout, Lr,
+                                        0 if mode == rat.RESTART else 1, D, W, 1 / math.sqrt(d))
+    for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
+        gg = to_f64(g_)
+        ww = np.asarray(w_, np.float64)
+        assert np.isfinite(gg).all(), name
+        rms = float(np.sqrt(np.mean(ww * ww)))
+        err = np.abs(gg - ww)
+        bad = err > RTOL_SAVED[dtype][name] * (np.abs(ww) + rms)
+        assert not bad.any(), (f"{name}: {int(bad.sum())} of {bad.size} out of tolerance, worst ratio "
+                               f"{float((err / (np.abs(ww) + rms)).max()):.3g}")
 
 
 def test_backward_deterministic():

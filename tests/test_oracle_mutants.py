@@ -60,6 +60,12 @@ MUTANTS = {
                                      "wk = g * wk + gb * k[i];\n                                    wv = g * wv + gb * v[i];\n                                    dlogit[i] += g * gb * (qk * (wk - k[i]) + qv * (wv - v[i]));"),
     "count_window_short": ("for (int w = 0; w < W && t - w >= 0; ++w) {\n        if (loc)",
                            "for (int w = 1; w < W && t - w >= 0; ++w) {\n        if (loc)"),
+    # the backward at given states: states handed over swapped, or the gate
+    # term reading the state at t instead of t - 1
+    "bwd_states_swapped": ("oracle_layer_backward_states(q, k, v, logit, ks, vs, dout,",
+                           "oracle_layer_backward_states(q, k, v, logit, vs, ks, dout,"),
+    "bwd_states_prev_is_current": ("double hv_prev = cut ? 0.0 : vs[idx4(b, t - 1, h, c, T, H, d)];",
+                                   "double hv_prev = cut ? 0.0 : vs[idx4(b, t, h, c, T, H, d)];"),
 }
 
 
