@@ -999,7 +999,7 @@ constexpr int kSlideSpan = kSlideTok + 2 * (kSlideMaxL - 1);
 static_assert(kSlideTok * kSlideCh == 256, "one thread per tile element");
 
 template <typename E>
-__global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a)
+__global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a, int ubase)
 {
     __shared__ float s_g[kSlideSpan][kSlideCh], s_gb[kSlideSpan][kSlideCh], s_lg[kSlideSpan][kSlideCh];
     __shared__ float s_k[kSlideSpan][kSlideCh], s_v[kSlideSpan][kSlideCh];
@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a)
     const size_t N = (size_t)a.H * a.d;
     const int T = a.T, L = a.L;
     const size_t n0 = (size_t)blockIdx.x * kSlideCh;
-    const int u0 = blockIdx.y * kSlideTok, b = blockIdx.z;
+    const int u0 = ubase + blockIdx.y * kSlideTok, b = blockIdx.z;
     // tokens ts .. te: the windows of the tile's first token back, of its last forward
     const int ts = max(0, u0 - (L - 1)), te = min(T - 1, u0 + kSlideTok - 1 + (L - 1));
     const int span = te - ts + 1;
@@ -1076,18 +1076,234 @@ __global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a)
     a.dg[iu] = g * gb * (sk - s_k[ju][c] * mk + sv - s_v[ju][c] * mv);
 }
 
-// the SLIDING recurrence's backward: tiled for windows up to kSlideMaxL
+// Windows of exactly kSlideMaxL = 64 tokens, by tiles of 64 tokens (a tile
+// starts at a = 64 k) whose neighbour tiles lie inside the sequence: every
+// quantity of a tile comes from the tile and its two neighbours, with no
+// carry between tiles.  With lambda the state gradient and P(r, s) =
+// g_r ... g_s, for a token u of the tile:
+//   h_u  = H_u + P(a, u) Y_{u-63}: the window's state; H runs the tile's own
+//          recurrence from zero, Y_j sums the previous tile's terms s >= j
+//          carried to a - 1 (P(s+1, a-1) (1 - g_s) x_s);
+//   mu_u = sum_{t = u .. u+63} lambda_t P(u+1, t) = M_u + P(u+1, a+63) F_{u+63}:
+//          M the tile's own reverse sum, F the next tile's prefix sum of
+//          lambda_t P(a+64, t);
+//   Z_u  = the sum of lambda_t (1 - g_s) x_s P(s+1, t) over the pairs
+//          s < u <= t, t - s < 64.  Going from u+1 to u, the pairs that end at
+//          u join (lambda_u (h_u - (1 - g_u) x_u)) and those that start at u
+//          leave ((1 - g_u) x_u (mu_u - lambda_u)), so Z_u is the tile's suffix
+//          sum of lambda_v h_v - (1 - g_v) x_v mu_v on top of Z at the next
+//          tile's start, sum_{s in tile} (1 - g_s) x_s P(s+1, a+63) F_{s+63}.
+// Then dx_u = (1 - g_u) mu_u and dlogit_u = (1 - g_u) (Z_u - g_u x_u mu_u),
+// summed over x in k, v: the gradient through every gate factor of every
+// window that holds u, with no division by a gate.
+// Four waves take 16 tokens of the tile each, and lane 2c + x channel c of
+// tensor x (k, v) of 32 channels; a wave also walks the 16 positions of the
+// previous tile that its tokens' windows start from (j = u - 63) and the 16
+// of the next tile their gradients end at (t = u + 63).  The waves exchange
+// the affine maps of their 16 positions of each chain through LDS, then the
+// tile's suffix sums.
+constexpr int kSlideSub = 16;  // tokens per wave
+
+template <typename E>
+__global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
+{
+    constexpr int LT = kSlideMaxL, SUB = kSlideSub;
+    static_assert(4 * SUB == LT, "four waves per tile");
+    __shared__ float s_map[4][7][kWave];  // per wave: H end, P own, Y sum, P prev, N sum, F sum, P next
+    __shared__ float s_fin[4][2][kWave];  // per wave: its sum of z, its part of Z at the next tile
+    const size_t N = (size_t)a.H * a.d;
+    const int T = a.T;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int xv = lane & 1;  // 0: k, 1: v
+    // workgroup: (b, tile 1 + k, block of 32 channels), channels fastest, so
+    // the tiles that re-read one tile run close together
+    const unsigned ncb = (unsigned)((N + 31) / 32), ntile = (unsigned)(T / LT - 2);
+    const unsigned cb = blockIdx.x % ncb, rest = blockIdx.x / ncb;
+    const int a0 = (int)(1 + rest % ntile) * LT, b = (int)(rest / ntile);
+    const size_t n = (size_t)cb * 32 + lane / 2;
+    const bool cok = n < N;
+    // a lane past the last channel reads the last channel's words and writes nothing
+    const size_t base = (size_t)b * T * N + (cok ? n : N - 1);
+    const void* xp = xv ? a.v : a.k;
+    const float* lam = xv ? a.dvs : a.dks;
+    float* dx = xv ? a.dv : a.dk;
+    // Each phase takes the lane's base through an empty asm (fresh()), so that
+    // it forms its addresses again instead of 48 of them staying live across
+    // the phases; within a phase the loads are free to be scheduled together.
+    size_t cur = base;
+    auto fresh = [&]() { asm volatile("" : "+v"(cur)); };
+    auto at = [&](int t) { return cur + (size_t)t * N; };
+    const int u0 = a0 + SUB * w;           // the wave's tokens u0 .. u0 + 15
+    const int j0 = u0 - (LT - 1);          // j = u - 63; j = a0 (wave 3) adds no term
+    const int t0 = u0 + (LT - 1);          // t = u + 63; t = a0 + 63 (wave 0) adds no term
+    // Those two positions are loaded like the others (both lie in the tile)
+    // and enter as a factor 1 and a term 0, without a branch, so that the
+    // compiler can batch each phase's loads.
+    const bool p_last = w == 3, n_first = w == 0;
+    auto prev_gate = [&](size_t e, int i, float& g, float& gb) {
+        forget_gate(ldx<E>(a.g, e), g, gb);
+        const bool none = p_last && i == SUB - 1;
+        g = none ? 1.f : g;
+        gb = none ? 0.f : gb;
+    };
+    auto next_gate = [&](size_t e, int i, float& g, float& l) {
+        float gb;
+        forget_gate(ldx<E>(a.g, e), g, gb);
+        const bool none = n_first && i == 0;
+        g = none ? 1.f : g;
+        l = none ? 0.f : lam[e];
+    };
+
+    // 1. the maps of the wave's positions in each chain, from zero
+    fresh();
+    float go[SUB], gbo[SUB];
+    float Hl = 0.f, Po = 1.f;  // own tokens forwards: H at the end, the gate product
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const size_t e = at(u0 + i);
+        forget_gate(ldx<E>(a.g, e), go[i], gbo[i]);
+        Hl = fmaf(go[i], Hl, gbo[i] * ldx<E>(xp, e));
+        Po *= go[i];
+    }
+    // own tokens backwards: N_u = g_u (lambda_u + N_{u+1}) from N = 0 after the last
+    fresh();
+    float Nl = 0.f;
+#pragma unroll
+    for (int i = SUB - 1; i >= 0; --i) Nl = go[i] * (lam[at(u0 + i)] + Nl);
+    float Yl = 0.f, Pp = 1.f;  // previous tile backwards
+    fresh();
+#pragma unroll
+    for (int i = SUB - 1; i >= 0; --i) {
+        const size_t e = at(j0 + i);
+        float g, gb;
+        prev_gate(e, i, g, gb);
+        Yl = fmaf(gb * ldx<E>(xp, e), Pp, Yl);
+        Pp *= g;
+    }
+    float Fl = 0.f, Pn = 1.f;  // next tile forwards
+    fresh();
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const size_t e = at(t0 + i);
+        float g, l;
+        next_gate(e, i, g, l);
+        Pn *= g;
+        Fl = fmaf(l, Pn, Fl);
+    }
+    s_map[w][0][lane] = Hl;
+    s_map[w][1][lane] = Po;
+    s_map[w][2][lane] = Yl;
+    s_map[w][3][lane] = Pp;
+    s_map[w][4][lane] = Nl;
+    s_map[w][5][lane] = Fl;
+    s_map[w][6][lane] = Pn;
+    __syncthreads();
+    // 2. the carries: from the waves before (H, F) and after (Y, N, products)
+    float Hc = 0.f, Pa = 1.f;  // H before u0, P(a, u0 - 1)
+    float Fc = 0.f, Pf = 1.f;  // F before t0, P(a + 64, t0 - 1)
+    for (int v = 0; v < w; ++v) {
+        Hc = fmaf(s_map[v][1][lane], Hc, s_map[v][0][lane]);
+        Pa *= s_map[v][1][lane];
+        Fc = fmaf(Pf, s_map[v][5][lane], Fc);
+        Pf *= s_map[v][6][lane];
+    }
+    float Yc = 0.f, Py = 1.f;  // Y after j0 + 15, P(j0 + 16, a - 1)
+    float Nc = 0.f, Ps = 1.f;  // N after u0 + 15, P(u0 + 16, a + 63)
+    for (int v = 3; v > w; --v) {
+        Yc = fmaf(Py, s_map[v][2][lane], Yc);
+        Py *= s_map[v][3][lane];
+        Nc = fmaf(s_map[v][1][lane], Nc, s_map[v][4][lane]);
+        Ps *= s_map[v][1][lane];
+    }
+    // 3. forwards: H, P(a, u) and F at the wave's positions
+    fresh();
+    float HH[SUB], PP[SUB], FF[SUB];
+    float Hs = Hc, Pu = Pa, Fs = Fc, Pq = Pf;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        Hs = fmaf(go[i], Hs, gbo[i] * ldx<E>(xp, at(u0 + i)));
+        Pu *= go[i];
+        HH[i] = Hs;
+        PP[i] = Pu;
+        {
+            const size_t e = at(t0 + i);
+            float g, l;
+            next_gate(e, i, g, l);
+            Pq *= g;
+            Fs = fmaf(l, Pq, Fs);
+        }
+        FF[i] = Fs;
+    }
+    // 4. backwards: Y, M, mu; dx; the suffix sum of z and the part of Z at the next tile
+    fresh();
+    float W[SUB];
+    float Ys = Yc, Pys = Py, Nn = Nc, SP = Ps, Sl = 0.f, Zp = 0.f;
+#pragma unroll
+    for (int i = SUB - 1; i >= 0; --i) {
+        {
+            const size_t e = at(j0 + i);
+            float g, gb;
+            prev_gate(e, i, g, gb);
+            Ys = fmaf(gb * ldx<E>(xp, e), Pys, Ys);
+            Pys *= g;
+        }
+        const size_t e = at(u0 + i);
+        const float x = ldx<E>(xp, e), l = lam[e];
+        const float h = fmaf(PP[i], Ys, HH[i]);
+        const float M = l + Nn;
+        Nn = go[i] * M;
+        if (i < SUB - 1) SP *= go[i + 1];
+        const float G = SP * FF[i];
+        const float mu = M + G;
+        if (cok) dx[e] = a.raw ? fmaf(gbo[i], mu, dx[e]) : gbo[i] * mu;
+        const float xm = gbo[i] * x * mu;
+        Sl += fmaf(l, h, -xm);
+        Zp = fmaf(gbo[i] * x, G, Zp);
+        W[i] = fmaf(gbo[i], Sl, -go[i] * xm);
+    }
+    s_fin[w][0][lane] = Sl;
+    s_fin[w][1][lane] = Zp;
+    __syncthreads();
+    // 5. Z = Z at the next tile + the suffix sums of the waves after + the wave's own
+    fresh();
+    float add = 0.f;
+    for (int v = 0; v < 4; ++v) add += s_fin[v][1][lane] + (v > w ? s_fin[v][0][lane] : 0.f);
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const float part = fmaf(gbo[i], add, W[i]);
+        const float other = __shfl_xor(part, 1);
+        if (cok && xv == 0) a.dg[at(u0 + i)] = part + other;
+    }
+}
+
+// the SLIDING recurrence's backward: at L = 64 the tiles whose neighbours
+// lie inside the sequence take the four-wave kernel, the first tile and the
+// tail the per-token LDS kernel, which also serves every other L up to 64;
+// one thread per element beyond
 template <typename E>
 static void launch_slide(const BwdArgs& a, unsigned elems, hipStream_t stream)
 {
     const size_t N = (size_t)a.H * a.d;
-    if (a.L <= kSlideMaxL) {
-        const dim3 grid((unsigned)((N + kSlideCh - 1) / kSlideCh), (unsigned)((a.T + kSlideTok - 1) / kSlideTok),
-                        (unsigned)a.B);
-        hipLaunchKernelGGL(bwd_slide_tiled_kernel<E>, grid, dim3(kSlideTok * kSlideCh), 0, stream, a);
-    } else {
+    const unsigned cx = (unsigned)((N + kSlideCh - 1) / kSlideCh);
+    auto tiled = [&](int u_lo, int u_hi) {  // tokens u_lo .. u_hi - 1
+        if (u_hi > u_lo)
+            hipLaunchKernelGGL(bwd_slide_tiled_kernel<E>, dim3(cx, (unsigned)((u_hi - u_lo + kSlideTok - 1) / kSlideTok),
+                                                               (unsigned)a.B),
+                               dim3(kSlideTok * kSlideCh), 0, stream, a, u_lo);
+    };
+    if (a.L > kSlideMaxL) {
         hipLaunchKernelGGL(bwd_slide_kernel<E>, dim3(elems), dim3(256), 0, stream, a);
+        return;
     }
+    const int inner = a.L == kSlideMaxL ? std::max(0, a.T / kSlideMaxL - 2) : 0;  // tiles 1 .. inner
+    if (inner == 0) {
+        tiled(0, a.T);
+        return;
+    }
+    const size_t wgs = (N + 31) / 32 * (size_t)inner * a.B;
+    hipLaunchKernelGGL(bwd_slide64_kernel<E>, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
+    tiled(0, kSlideMaxL);
+    tiled((1 + inner) * kSlideMaxL, a.T);
 }
 
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)

@@ -203,3 +203,25 @@ def test_backward_arl_full_size_sampled():
                                          dout[b0 + b:b0 + b + 1, :, h:h + 1], w.T, 0, [Dv], [0], w.scale)
             for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
                 assert_grad(g_[b:b + 1, :, h:h + 1], w_, w.dtype, f"D={Dv} b={b} h={h} {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", [rat.RESTART, rat.SLIDING], ids=["restart", "sliding"])
+def test_backward_windowed_full_size_sampled(mode):
+    """The layer backward of the 16K windowed prefill (B = 1, T = 16384,
+    H = 16, d = 128, D = 64, W = 128, L = 64) in the launch configuration
+    the bench times: one sampled head checked in full against the oracle run
+    on that head alone (the attention and the recurrence of a head touch no
+    other head).  The SLIDING case runs the 64-token tile kernel on all but
+    the first and last tiles."""
+    w = inputs.PREFILL_LONG
+    x = inputs.make_prefill(w, seed=7)
+    dout = (torch.randn((w.B, w.T, w.H, w.d), generator=torch.Generator().manual_seed(8)) * 0.05).to(w.dtype)
+    announce("backward windowed full size", "mode", mode)
+    got = forward_and_backward(x, list(w.D), list(w.W), w.L, mode, dout, w.dtype)
+    h = 5
+    sl = {n: x[n][:, :, h:h + 1].contiguous() for n in ("q", "k", "v", "gate")}
+    want = oracle.layer_backward(sl["q"], sl["k"], sl["v"], sl["gate"], dout[:, :, h:h + 1].contiguous(), w.L,
+                                 0 if mode == rat.RESTART else 1, [w.D[h]], [w.W[h]], w.scale)
+    for name, g_, w_ in zip(("dq", "dk", "dv", "dgate"), got, want):
+        assert_grad(g_[:, :, h:h + 1], w_, w.dtype, f"h={h} {name}")
