@@ -171,3 +171,15 @@ def make_random_prefill(B, T, H, d, dtype, seed, qkv_std=1.0, gate_mean=2.0, dev
     v = (_randn(gen, shape, device) * qkv_std).to(dtype)
     g = (_randn(gen, shape, device) + gate_mean).to(dtype)
     return {"q": q, "k": k, "v": v, "gate": g}
+
+
+def sha256_of(tensors: dict) -> dict:
+    """SHA-256 of each tensor's bytes (contiguous, on the CPU), by name: the
+    fingerprint of a drawn workload."""
+    import hashlib
+
+    out = {}
+    for name, t in tensors.items():
+        c = t.detach().contiguous().cpu()
+        out[name] = hashlib.sha256(c.view(torch.uint8).numpy().tobytes()).hexdigest()
+    return out
