@@ -1276,6 +1276,144 @@ __global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
     }
 }
 
+// RESTART at L = kSlideMaxL: every 64-token tile is one window, so a tile's
+// gradients need nothing outside it.  Per token u of the tile (a = its
+// start), with Lambda_u = lambda_u + g_{u+1} Lambda_{u+1} (Lambda past the
+// tile's end 0) the gradient that reaches the state h_u:
+//   dx_u = (1 - g_u) Lambda_u,   dlogit_u = g_u (1 - g_u) Lambda_u (h_{u-1} - x_u),
+// summed over x in k, v, with h_{a-1} = 0.  A workgroup takes the tile for
+// 32 channels: it first copies the tile's rows of every input (gate
+// logits, k, v, the two state gradients, and dk / dv when the raw windows
+// have written them) into LDS with 16-byte loads, so that many bytes are in
+// flight per load, then four waves take 16 tokens each (lane 2c + x:
+// channel c, tensor k or v) and exchange the maps of their 16 tokens in the
+// forward state chain and the backward gradient chain through LDS.  Rows
+// past T are zero and enter as a factor 1 and a term 0.  dk, dv and dlogit
+// go back through LDS and leave with 16-byte stores.
+constexpr int kTileCh = 32;  // channels per workgroup of the 64-token tile kernels
+
+// Copies rows r0 .. r0 + nrows - 1 of a [B*T][N] tensor's channel segment
+// c0 .. c0 + kTileCh - 1 (EB bytes per element) into LDS, rows past T as
+// zero, 16 bytes per lane.
+template <int EB>
+__device__ __forceinline__ void stage_rows(const void* src, char* dst, size_t rowbase, int t0, int nrows, int T,
+                                           size_t N, size_t c0)
+{
+    constexpr int RB = kTileCh * EB, PR = RB / 16;  // bytes and 16-byte pieces per row
+    for (int idx = threadIdx.x; idx < nrows * PR; idx += blockDim.x) {
+        const int r = idx / PR, p = idx % PR;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t0 + r < T && t0 + r >= 0)
+            v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) +
+                                                ((rowbase + t0 + r) * N + c0) * EB + 16 * p);
+        *reinterpret_cast<u32x4*>(dst + r * RB + 16 * p) = v;
+    }
+}
+
+// The reverse: fp32 rows of LDS back to a [B*T][N] tensor's channel
+// segment, rows at or past T skipped.
+__device__ __forceinline__ void unstage_rows(const char* src, float* dst, size_t rowbase, int t0, int nrows, int T,
+                                             size_t N, size_t c0)
+{
+    constexpr int RB = kTileCh * 4, PR = RB / 16;
+    for (int idx = threadIdx.x; idx < nrows * PR; idx += blockDim.x) {
+        const int r = idx / PR, p = idx % PR;
+        if (t0 + r < T)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + ((rowbase + t0 + r) * N + c0) * 4 + 16 * p) =
+                *reinterpret_cast<const u32x4*>(src + r * RB + 16 * p);
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256, 2) void bwd_restart64_kernel(BwdArgs a)
+{
+    constexpr int LT = kSlideMaxL, SUB = kSlideSub, EB = (int)sizeof(E);
+    constexpr int RE = kTileCh * EB, RF = kTileCh * 4;  // row bytes: inputs, fp32 gradients
+    __shared__ __attribute__((aligned(16))) char s_g[LT * RE], s_k[LT * RE], s_v[LT * RE];
+    __shared__ __attribute__((aligned(16))) char s_lk[LT * RF], s_lv[LT * RF], s_dk[LT * RF], s_dv[LT * RF];
+    __shared__ float s_map[4][3][kWave];  // per wave: H end, gate product, N sum
+    const size_t N = (size_t)a.H * a.d;
+    const int T = a.T;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int xv = lane & 1;  // 0: k, 1: v
+    const unsigned ncb = (unsigned)(N / kTileCh), ntile = (unsigned)((T + LT - 1) / LT);
+    const unsigned cb = blockIdx.x % ncb, rest = blockIdx.x / ncb;
+    const int a0 = (int)(rest % ntile) * LT, b = (int)(rest / ntile);
+    const size_t c0 = (size_t)cb * kTileCh, rowbase = (size_t)b * T;
+    stage_rows<EB>(a.g, s_g, rowbase, a0, LT, T, N, c0);
+    stage_rows<EB>(a.k, s_k, rowbase, a0, LT, T, N, c0);
+    stage_rows<EB>(a.v, s_v, rowbase, a0, LT, T, N, c0);
+    stage_rows<4>(a.dks, s_lk, rowbase, a0, LT, T, N, c0);
+    stage_rows<4>(a.dvs, s_lv, rowbase, a0, LT, T, N, c0);
+    if (a.raw) {
+        stage_rows<4>(a.dk, s_dk, rowbase, a0, LT, T, N, c0);
+        stage_rows<4>(a.dv, s_dv, rowbase, a0, LT, T, N, c0);
+    }
+    __syncthreads();
+    const int c = lane / 2;
+    const char* sx = xv ? s_v : s_k;
+    const float* sl = reinterpret_cast<const float*>(xv ? s_lv : s_lk);
+    const float* sd = reinterpret_cast<const float*>(xv ? s_dv : s_dk);
+    auto in = [&](const char* t, int r) {  // element (row r, channel c) of a staged input
+        return EB == 2 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(t)[r * kTileCh + c] << 16)
+                       : reinterpret_cast<const float*>(t)[r * kTileCh + c];
+    };
+    const int r0 = SUB * w;  // the wave's rows r0 .. r0 + 15 of the tile
+
+    // 1. the wave's maps from zero: H forwards, N_u = g_u (lambda_u + N_{u+1}) backwards
+    float go[SUB], gbo[SUB], xs[SUB], ls[SUB];
+    float Hl = 0.f, Po = 1.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        forget_gate(in(s_g, r0 + i), go[i], gbo[i]);
+        const bool on = a0 + r0 + i < T;
+        go[i] = on ? go[i] : 1.f;
+        gbo[i] = on ? gbo[i] : 0.f;
+        xs[i] = in(sx, r0 + i);
+        ls[i] = sl[(r0 + i) * kTileCh + c];
+        Hl = fmaf(go[i], Hl, gbo[i] * xs[i]);
+        Po *= go[i];
+    }
+    float Nl = 0.f;
+#pragma unroll
+    for (int i = SUB - 1; i >= 0; --i) Nl = go[i] * (ls[i] + Nl);
+    s_map[w][0][lane] = Hl;
+    s_map[w][1][lane] = Po;
+    s_map[w][2][lane] = Nl;
+    __syncthreads();
+    float Hc = 0.f, Nc = 0.f;  // the state before the wave's rows, N after them
+    for (int v = 0; v < w; ++v) Hc = fmaf(s_map[v][1][lane], Hc, s_map[v][0][lane]);
+    for (int v = 3; v > w; --v) Nc = fmaf(s_map[v][1][lane], Nc, s_map[v][2][lane]);
+    // 2. the states before each token
+    float hp[SUB];
+    float Hs = Hc;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        hp[i] = Hs;
+        Hs = fmaf(go[i], Hs, gbo[i] * xs[i]);
+    }
+    // 3. backwards: Lambda, dx, and the gate gradient (k and v of a channel
+    // summed), into LDS: dx over the staged dk / dv, dlogit over the state
+    // gradient of k, which no wave reads any more
+    float* sdx = reinterpret_cast<float*>(xv ? s_dv : s_dk);
+    float* sdg = reinterpret_cast<float*>(s_lk);
+    float Nn = Nc;
+#pragma unroll
+    for (int i = SUB - 1; i >= 0; --i) {
+        const float Lm = ls[i] + Nn;
+        Nn = go[i] * Lm;
+        const float part = go[i] * gbo[i] * Lm * (hp[i] - xs[i]);
+        const float other = __shfl_xor(part, 1);
+        const int o = (r0 + i) * kTileCh + c;
+        sdx[o] = a.raw ? fmaf(gbo[i], Lm, sd[o]) : gbo[i] * Lm;
+        if (xv == 0) sdg[o] = part + other;
+    }
+    __syncthreads();
+    unstage_rows(s_dk, a.dk, rowbase, a0, LT, T, N, c0);
+    unstage_rows(s_dv, a.dv, rowbase, a0, LT, T, N, c0);
+    unstage_rows(s_lk, a.dg, rowbase, a0, LT, T, N, c0);
+}
+
 // the SLIDING recurrence's backward: at L = 64 the tiles whose neighbours
 // lie inside the sequence take the four-wave kernel, the first tile and the
 // tail the per-token LDS kernel, which also serves every other L up to 64;
@@ -1304,6 +1442,15 @@ static void launch_slide(const BwdArgs& a, unsigned elems, hipStream_t stream)
     hipLaunchKernelGGL(bwd_slide64_kernel<E>, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
     tiled(0, kSlideMaxL);
     tiled((1 + inner) * kSlideMaxL, a.T);
+}
+
+// RESTART at L = 64: one workgroup per 64-token window and 32 channels
+template <typename E>
+static void launch_restart64(const BwdArgs& a, hipStream_t stream)
+{
+    const size_t N = (size_t)a.H * a.d;
+    const size_t wgs = N / kTileCh * (size_t)((a.T + kSlideMaxL - 1) / kSlideMaxL) * a.B;
+    hipLaunchKernelGGL(bwd_restart64_kernel<E>, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
 }
 
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
@@ -1336,6 +1483,8 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
         }
         if (a.sliding) {
             launch_slide<uint16_t>(a, elems, stream);
+        } else if (a.L == kSlideMaxL) {
+            launch_restart64<uint16_t>(a, stream);
         } else {
             hipLaunchKernelGGL(bwd_scan_maps_kernel<uint16_t>, dim3(cells), dim3(256), 0, stream, a);
             hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);
@@ -1346,6 +1495,8 @@ hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
         hipLaunchKernelGGL(bwd_key_kernel<float>, dim3(rows), dim3(kWave), 0, stream, a);
         if (a.sliding) {
             launch_slide<float>(a, elems, stream);
+        } else if (a.L == kSlideMaxL) {
+            launch_restart64<float>(a, stream);
         } else {
             hipLaunchKernelGGL(bwd_scan_maps_kernel<float>, dim3(cells), dim3(256), 0, stream, a);
             hipLaunchKernelGGL(bwd_scan_carry_kernel, dim3(chans), dim3(256), 0, stream, a);

@@ -71,6 +71,7 @@ CASES = [
     (1, 2, 2, 64, [1, 2], [2, 0], None, torch.bfloat16),           # two tokens
     (1, 96, 2, 128, [1, 3], [0, 5], None, torch.float32),
     (2, 77, 2, 64, [5, 1], [2, 0], 20, torch.float32),
+    (1, 150, 2, 128, [3, 1], [4, 0], 64, torch.float32),          # RESTART every 64: one window per tile, ragged tail
 ]
 
 
