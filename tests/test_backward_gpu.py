@@ -82,6 +82,8 @@ SLIDING_CASES = [
     (1, 200, 3, 128, [1, 4, 64], [0, 0, 100], 33, torch.bfloat16),  # window not a power of two
     (1, 70, 2, 128, [2, 1], [3, 0], 1, torch.bfloat16),           # L = 1: each state its own token
     (1, 96, 2, 64, [1, 3], [0, 5], 20, torch.float32),
+    (2, 330, 3, 64, [1, 64, 4], [0, 0, 9], 64, torch.bfloat16),   # L* = 64 tile kernel: two sequences, ragged tail
+    (1, 260, 2, 64, [1, 4], [0, 8], 64, torch.float32),           # the tile kernel in fp32
 ]
 
 
