@@ -1445,6 +1445,7 @@ static void launch_slide(const BwdArgs& a, unsigned elems, hipStream_t stream)
 }
 
 // RESTART at L = 64: one workgroup per 64-token window and 32 channels
+// (H d is a multiple of 64: the boundary takes d = 64 or 128)
 template <typename E>
 static void launch_restart64(const BwdArgs& a, hipStream_t stream)
 {
