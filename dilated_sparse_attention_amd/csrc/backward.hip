@@ -1096,21 +1096,28 @@ __global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a, int uba
 // Then dx_u = (1 - g_u) mu_u and dlogit_u = (1 - g_u) (Z_u - g_u x_u mu_u),
 // summed over x in k, v: the gradient through every gate factor of every
 // window that holds u, with no division by a gate.
-// Four waves take 16 tokens of the tile each, and lane 2c + x channel c of
-// tensor x (k, v) of 32 channels; a wave also walks the 16 positions of the
-// previous tile that its tokens' windows start from (j = u - 63) and the 16
-// of the next tile their gradients end at (t = u + 63).  The waves exchange
-// the affine maps of their 16 positions of each chain through LDS, then the
-// tile's suffix sums.
-constexpr int kSlideSub = 16;  // tokens per wave
+// Each wave takes kSlideSub consecutive tokens of the tile, and lane 2c + x
+// channel c of tensor x (k, v) of 32 channels; a wave also walks as many
+// positions of the previous tile, those its tokens' windows start from
+// (j = u - 63), and of the next tile, those their gradients end at
+// (t = u + 63).  The waves exchange the affine maps of their positions in
+// each chain through LDS, then the tile's suffix sums.
+// tokens per wave of the 64-token tile kernels, and their waves per tile:
+// sixteen waves of 4 tokens for SLIDING, eight of 8 for RESTART (same-box
+// A/B at the 16K windowed shape: SLIDING 713 / 686 / 641 us at four /
+// eight / sixteen waves, RESTART 318 / 252 / 321 us)
+constexpr int kSlideSub = 4;
+constexpr int kSlideWaves = kSlideMaxL / kSlideSub;
+constexpr int kRestartSub = 8;
+constexpr int kRestartWaves = kSlideMaxL / kRestartSub;
 
 template <typename E>
-__global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
+__global__ __launch_bounds__(kSlideWaves * kWave) void bwd_slide64_kernel(BwdArgs a)
 {
     constexpr int LT = kSlideMaxL, SUB = kSlideSub;
-    static_assert(4 * SUB == LT, "four waves per tile");
-    __shared__ float s_map[4][7][kWave];  // per wave: H end, P own, Y sum, P prev, N sum, F sum, P next
-    __shared__ float s_fin[4][2][kWave];  // per wave: its sum of z, its part of Z at the next tile
+    constexpr int NWV = kSlideWaves;
+    __shared__ float s_map[NWV][7][kWave];  // per wave: H end, P own, Y sum, P prev, N sum, F sum, P next
+    __shared__ float s_fin[NWV][2][kWave];  // per wave: its sum of z, its part of Z at the next tile
     const size_t N = (size_t)a.H * a.d;
     const int T = a.T;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -1133,13 +1140,13 @@ __global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
     size_t cur = base;
     auto fresh = [&]() { asm volatile("" : "+v"(cur)); };
     auto at = [&](int t) { return cur + (size_t)t * N; };
-    const int u0 = a0 + SUB * w;           // the wave's tokens u0 .. u0 + 15
-    const int j0 = u0 - (LT - 1);          // j = u - 63; j = a0 (wave 3) adds no term
+    const int u0 = a0 + SUB * w;           // the wave's tokens u0 .. u0 + SUB - 1
+    const int j0 = u0 - (LT - 1);          // j = u - 63; j = a0 (last wave) adds no term
     const int t0 = u0 + (LT - 1);          // t = u + 63; t = a0 + 63 (wave 0) adds no term
     // Those two positions are loaded like the others (both lie in the tile)
     // and enter as a factor 1 and a term 0, without a branch, so that the
     // compiler can batch each phase's loads.
-    const bool p_last = w == 3, n_first = w == 0;
+    const bool p_last = w == NWV - 1, n_first = w == 0;
     auto prev_gate = [&](size_t e, int i, float& g, float& gb) {
         forget_gate(ldx<E>(a.g, e), g, gb);
         const bool none = p_last && i == SUB - 1;
@@ -1207,9 +1214,9 @@ __global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
         Fc = fmaf(Pf, s_map[v][5][lane], Fc);
         Pf *= s_map[v][6][lane];
     }
-    float Yc = 0.f, Py = 1.f;  // Y after j0 + 15, P(j0 + 16, a - 1)
-    float Nc = 0.f, Ps = 1.f;  // N after u0 + 15, P(u0 + 16, a + 63)
-    for (int v = 3; v > w; --v) {
+    float Yc = 0.f, Py = 1.f;  // Y after j0 + SUB - 1, P(j0 + SUB, a - 1)
+    float Nc = 0.f, Ps = 1.f;  // N after u0 + SUB - 1, P(u0 + SUB, a + 63)
+    for (int v = NWV - 1; v > w; --v) {
         Yc = fmaf(Py, s_map[v][2][lane], Yc);
         Py *= s_map[v][3][lane];
         Nc = fmaf(s_map[v][1][lane], Nc, s_map[v][4][lane]);
@@ -1267,7 +1274,7 @@ __global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
     // 5. Z = Z at the next tile + the suffix sums of the waves after + the wave's own
     fresh();
     float add = 0.f;
-    for (int v = 0; v < 4; ++v) add += s_fin[v][1][lane] + (v > w ? s_fin[v][0][lane] : 0.f);
+    for (int v = 0; v < NWV; ++v) add += s_fin[v][1][lane] + (v > w ? s_fin[v][0][lane] : 0.f);
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
         const float part = fmaf(gbo[i], add, W[i]);
@@ -1285,8 +1292,8 @@ __global__ __launch_bounds__(256, 3) void bwd_slide64_kernel(BwdArgs a)
 // 32 channels: it first copies the tile's rows of every input (gate
 // logits, k, v, the two state gradients, and dk / dv when the raw windows
 // have written them) into LDS with 16-byte loads, so that many bytes are in
-// flight per load, then four waves take 16 tokens each (lane 2c + x:
-// channel c, tensor k or v) and exchange the maps of their 16 tokens in the
+// flight per load, then each wave takes kRestartSub tokens (lane 2c + x:
+// channel c, tensor k or v) and the waves exchange the maps of their tokens in the
 // forward state chain and the backward gradient chain through LDS.  Rows
 // past T are zero and enter as a factor 1 and a term 0.  dk, dv and dlogit
 // go back through LDS and leave with 16-byte stores.
@@ -1325,13 +1332,14 @@ __device__ __forceinline__ void unstage_rows(const char* src, float* dst, size_t
 }
 
 template <typename E>
-__global__ __launch_bounds__(256, 2) void bwd_restart64_kernel(BwdArgs a)
+__global__ __launch_bounds__(kRestartWaves * kWave) void bwd_restart64_kernel(BwdArgs a)
 {
-    constexpr int LT = kSlideMaxL, SUB = kSlideSub, EB = (int)sizeof(E);
+    constexpr int LT = kSlideMaxL, SUB = kRestartSub, EB = (int)sizeof(E);
     constexpr int RE = kTileCh * EB, RF = kTileCh * 4;  // row bytes: inputs, fp32 gradients
     __shared__ __attribute__((aligned(16))) char s_g[LT * RE], s_k[LT * RE], s_v[LT * RE];
     __shared__ __attribute__((aligned(16))) char s_lk[LT * RF], s_lv[LT * RF], s_dk[LT * RF], s_dv[LT * RF];
-    __shared__ float s_map[4][3][kWave];  // per wave: H end, gate product, N sum
+    constexpr int NWV = kRestartWaves;
+    __shared__ float s_map[NWV][3][kWave];  // per wave: H end, gate product, N sum
     const size_t N = (size_t)a.H * a.d;
     const int T = a.T;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -1383,7 +1391,7 @@ __global__ __launch_bounds__(256, 2) void bwd_restart64_kernel(BwdArgs a)
     __syncthreads();
     float Hc = 0.f, Nc = 0.f;  // the state before the wave's rows, N after them
     for (int v = 0; v < w; ++v) Hc = fmaf(s_map[v][1][lane], Hc, s_map[v][0][lane]);
-    for (int v = 3; v > w; --v) Nc = fmaf(s_map[v][1][lane], Nc, s_map[v][2][lane]);
+    for (int v = NWV - 1; v > w; --v) Nc = fmaf(s_map[v][1][lane], Nc, s_map[v][2][lane]);
     // 2. the states before each token
     float hp[SUB];
     float Hs = Hc;
@@ -1439,7 +1447,7 @@ static void launch_slide(const BwdArgs& a, unsigned elems, hipStream_t stream)
         return;
     }
     const size_t wgs = (N + 31) / 32 * (size_t)inner * a.B;
-    hipLaunchKernelGGL(bwd_slide64_kernel<E>, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL(bwd_slide64_kernel<E>, dim3((unsigned)wgs), dim3(kSlideWaves * kWave), 0, stream, a);
     tiled(0, kSlideMaxL);
     tiled((1 + inner) * kSlideMaxL, a.T);
 }
@@ -1451,7 +1459,7 @@ static void launch_restart64(const BwdArgs& a, hipStream_t stream)
 {
     const size_t N = (size_t)a.H * a.d;
     const size_t wgs = N / kTileCh * (size_t)((a.T + kSlideMaxL - 1) / kSlideMaxL) * a.B;
-    hipLaunchKernelGGL(bwd_restart64_kernel<E>, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, a);
+    hipLaunchKernelGGL(bwd_restart64_kernel<E>, dim3((unsigned)wgs), dim3(kRestartWaves * kWave), 0, stream, a);
 }
 
 hipError_t launch_backward(const BwdArgs& a, bool bf16, hipStream_t stream)
