@@ -72,6 +72,7 @@ CASES = [
     (1, 96, 2, 128, [1, 3], [0, 5], None, torch.float32),
     (2, 77, 2, 64, [5, 1], [2, 0], 20, torch.float32),
     (1, 150, 2, 128, [3, 1], [4, 0], 64, torch.float32),          # RESTART every 64: one window per tile, ragged tail
+    (2, 128, 2, 64, [1, 4], [0, 0], 64, torch.bfloat16),          # RESTART every 64, T = two whole windows
 ]
 
 
@@ -84,6 +85,7 @@ SLIDING_CASES = [
     (1, 96, 2, 64, [1, 3], [0, 5], 20, torch.float32),
     (2, 330, 3, 64, [1, 64, 4], [0, 0, 9], 64, torch.bfloat16),   # L* = 64 tile kernel: two sequences, ragged tail
     (1, 260, 2, 64, [1, 4], [0, 8], 64, torch.float32),           # the tile kernel in fp32
+    (1, 256, 2, 128, [1, 16], [0, 8], 64, torch.bfloat16),        # T a multiple of 64: the last tile from the LDS kernel
 ]
 
 
