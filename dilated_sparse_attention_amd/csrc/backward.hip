@@ -1103,10 +1103,10 @@ __global__ __launch_bounds__(256) void bwd_slide_tiled_kernel(BwdArgs a, int uba
 // (t = u + 63).  The waves exchange the affine maps of their positions in
 // each chain through LDS, then the tile's suffix sums.
 // tokens per wave of the 64-token tile kernels, and their waves per tile:
-// sixteen waves of 4 tokens for SLIDING, eight of 8 for RESTART (same-box
-// A/B at the 16K windowed shape: SLIDING 713 / 686 / 641 us at four /
-// eight / sixteen waves, RESTART 318 / 252 / 321 us)
-constexpr int kSlideSub = 4;
+// eight waves of 8 tokens for both (same-box A/B at the 16K windowed shape:
+// SLIDING, with every input loaded once up front, 382 / 370 us at sixteen /
+// eight waves; RESTART 318 / 252 / 321 us at four / eight / sixteen)
+constexpr int kSlideSub = 8;
 constexpr int kSlideWaves = kSlideMaxL / kSlideSub;
 constexpr int kRestartSub = 8;
 constexpr int kRestartWaves = kSlideMaxL / kRestartSub;
@@ -1134,68 +1134,64 @@ __global__ __launch_bounds__(kSlideWaves * kWave) void bwd_slide64_kernel(BwdArg
     const void* xp = xv ? a.v : a.k;
     const float* lam = xv ? a.dvs : a.dks;
     float* dx = xv ? a.dv : a.dk;
-    // Each phase takes the lane's base through an empty asm (fresh()), so that
-    // it forms its addresses again instead of 48 of them staying live across
-    // the phases; within a phase the loads are free to be scheduled together.
-    size_t cur = base;
-    auto fresh = [&]() { asm volatile("" : "+v"(cur)); };
-    auto at = [&](int t) { return cur + (size_t)t * N; };
+    auto at = [&](int t) { return base + (size_t)t * N; };
     const int u0 = a0 + SUB * w;           // the wave's tokens u0 .. u0 + SUB - 1
     const int j0 = u0 - (LT - 1);          // j = u - 63; j = a0 (last wave) adds no term
     const int t0 = u0 + (LT - 1);          // t = u + 63; t = a0 + 63 (wave 0) adds no term
     // Those two positions are loaded like the others (both lie in the tile)
-    // and enter as a factor 1 and a term 0, without a branch, so that the
-    // compiler can batch each phase's loads.
+    // and enter as a factor 1 and a term 0, without a branch.
     const bool p_last = w == NWV - 1, n_first = w == 0;
-    auto prev_gate = [&](size_t e, int i, float& g, float& gb) {
-        forget_gate(ldx<E>(a.g, e), g, gb);
-        const bool none = p_last && i == SUB - 1;
-        g = none ? 1.f : g;
-        gb = none ? 0.f : gb;
-    };
-    auto next_gate = [&](size_t e, int i, float& g, float& l) {
+
+    // 0. every input of the wave's positions, loaded once, together (one
+    // memory round trip per workgroup): the own tokens' gate, x, lambda (and
+    // the raw windows' dx), the previous tile's gate and x, the next tile's
+    // gate and lambda
+    float go[SUB], gbo[SUB], xo[SUB], lo[SUB], dxr[SUB];
+    float gpv[SUB], gbp[SUB], xpv[SUB], gnx[SUB], lnx[SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const size_t e = at(u0 + i), ep = at(j0 + i), en = at(t0 + i);
+        forget_gate(ldx<E>(a.g, e), go[i], gbo[i]);
+        xo[i] = ldx<E>(xp, e);
+        lo[i] = lam[e];
+        dxr[i] = a.raw ? dx[e] : 0.f;
+        forget_gate(ldx<E>(a.g, ep), gpv[i], gbp[i]);
+        xpv[i] = ldx<E>(xp, ep);
         float gb;
-        forget_gate(ldx<E>(a.g, e), g, gb);
-        const bool none = n_first && i == 0;
-        g = none ? 1.f : g;
-        l = none ? 0.f : lam[e];
-    };
+        forget_gate(ldx<E>(a.g, en), gnx[i], gb);
+        lnx[i] = lam[en];
+    }
+    if (p_last) {
+        gpv[SUB - 1] = 1.f;
+        gbp[SUB - 1] = 0.f;
+    }
+    if (n_first) {
+        gnx[0] = 1.f;
+        lnx[0] = 0.f;
+    }
 
     // 1. the maps of the wave's positions in each chain, from zero
-    fresh();
-    float go[SUB], gbo[SUB];
     float Hl = 0.f, Po = 1.f;  // own tokens forwards: H at the end, the gate product
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-        const size_t e = at(u0 + i);
-        forget_gate(ldx<E>(a.g, e), go[i], gbo[i]);
-        Hl = fmaf(go[i], Hl, gbo[i] * ldx<E>(xp, e));
+        Hl = fmaf(go[i], Hl, gbo[i] * xo[i]);
         Po *= go[i];
     }
     // own tokens backwards: N_u = g_u (lambda_u + N_{u+1}) from N = 0 after the last
-    fresh();
     float Nl = 0.f;
 #pragma unroll
-    for (int i = SUB - 1; i >= 0; --i) Nl = go[i] * (lam[at(u0 + i)] + Nl);
+    for (int i = SUB - 1; i >= 0; --i) Nl = go[i] * (lo[i] + Nl);
     float Yl = 0.f, Pp = 1.f;  // previous tile backwards
-    fresh();
 #pragma unroll
     for (int i = SUB - 1; i >= 0; --i) {
-        const size_t e = at(j0 + i);
-        float g, gb;
-        prev_gate(e, i, g, gb);
-        Yl = fmaf(gb * ldx<E>(xp, e), Pp, Yl);
-        Pp *= g;
+        Yl = fmaf(gbp[i] * xpv[i], Pp, Yl);
+        Pp *= gpv[i];
     }
     float Fl = 0.f, Pn = 1.f;  // next tile forwards
-    fresh();
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-        const size_t e = at(t0 + i);
-        float g, l;
-        next_gate(e, i, g, l);
-        Pn *= g;
-        Fl = fmaf(l, Pn, Fl);
+        Pn *= gnx[i];
+        Fl = fmaf(lnx[i], Pn, Fl);
     }
     s_map[w][0][lane] = Hl;
     s_map[w][1][lane] = Po;
@@ -1223,46 +1219,34 @@ __global__ __launch_bounds__(kSlideWaves * kWave) void bwd_slide64_kernel(BwdArg
         Ps *= s_map[v][1][lane];
     }
     // 3. forwards: H, P(a, u) and F at the wave's positions
-    fresh();
     float HH[SUB], PP[SUB], FF[SUB];
     float Hs = Hc, Pu = Pa, Fs = Fc, Pq = Pf;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-        Hs = fmaf(go[i], Hs, gbo[i] * ldx<E>(xp, at(u0 + i)));
+        Hs = fmaf(go[i], Hs, gbo[i] * xo[i]);
         Pu *= go[i];
         HH[i] = Hs;
         PP[i] = Pu;
-        {
-            const size_t e = at(t0 + i);
-            float g, l;
-            next_gate(e, i, g, l);
-            Pq *= g;
-            Fs = fmaf(l, Pq, Fs);
-        }
+        Pq *= gnx[i];
+        Fs = fmaf(lnx[i], Pq, Fs);
         FF[i] = Fs;
     }
     // 4. backwards: Y, M, mu; dx; the suffix sum of z and the part of Z at the next tile
-    fresh();
     float W[SUB];
     float Ys = Yc, Pys = Py, Nn = Nc, SP = Ps, Sl = 0.f, Zp = 0.f;
 #pragma unroll
     for (int i = SUB - 1; i >= 0; --i) {
-        {
-            const size_t e = at(j0 + i);
-            float g, gb;
-            prev_gate(e, i, g, gb);
-            Ys = fmaf(gb * ldx<E>(xp, e), Pys, Ys);
-            Pys *= g;
-        }
+        Ys = fmaf(gbp[i] * xpv[i], Pys, Ys);
+        Pys *= gpv[i];
         const size_t e = at(u0 + i);
-        const float x = ldx<E>(xp, e), l = lam[e];
+        const float x = xo[i], l = lo[i];
         const float h = fmaf(PP[i], Ys, HH[i]);
         const float M = l + Nn;
         Nn = go[i] * M;
         if (i < SUB - 1) SP *= go[i + 1];
         const float G = SP * FF[i];
         const float mu = M + G;
-        if (cok) dx[e] = a.raw ? fmaf(gbo[i], mu, dx[e]) : gbo[i] * mu;
+        if (cok) dx[e] = a.raw ? fmaf(gbo[i], mu, dxr[i]) : gbo[i] * mu;
         const float xm = gbo[i] * x * mu;
         Sl += fmaf(l, h, -xm);
         Zp = fmaf(gbo[i] * x, G, Zp);
@@ -1272,7 +1256,6 @@ __global__ __launch_bounds__(kSlideWaves * kWave) void bwd_slide64_kernel(BwdArg
     s_fin[w][1][lane] = Zp;
     __syncthreads();
     // 5. Z = Z at the next tile + the suffix sums of the waves after + the wave's own
-    fresh();
     float add = 0.f;
     for (int v = 0; v < NWV; ++v) add += s_fin[v][1][lane] + (v > w ? s_fin[v][0][lane] : 0.f);
 #pragma unroll
